@@ -1,0 +1,327 @@
+"""Pins of the CPU oracle against facts fixed outside the oracle itself.
+
+Each test checks one oracle function against something other than its own formula:
+a library routine (numpy's stable argsort, numpy float64 matmuls, torch's e4m3 cast),
+a closed form derived by hand (tests/golden/*.txt), a brute-force enumeration, or an
+invariant of the method (bijection, gate sums, k = E mixture, token-order
+equivariance, the 6*H*M FLOPs per token-expert pair of the AFD article's §2.1).
+"""
+import itertools
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _rows(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                yield [c.strip() for c in line.split("|")]
+
+
+# ----------------------------------------------------------------------------- routing
+@pytest.mark.parametrize("T,E,k,seed", [(50, 8, 2, 0), (40, 128, 8, 1), (30, 256, 8, 2), (20, 48, 3, 3),
+                                        (10, 5, 5, 4), (16, 1, 1, 5)])
+def test_route_ids_match_stable_argsort(T, E, k, seed):
+    rng = np.random.default_rng(seed)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    ids, _ = oracle.route(logits, k)
+    ref = np.argsort(-logits, axis=1, kind="stable")[:, :k]
+    np.testing.assert_array_equal(ids, ref)
+
+
+def test_route_ids_bruteforce_with_ties():
+    """Integer logits in [-2, 2] force many ties.  Brute force: the selected set is the
+    lexicographically first among the k-subsets with the largest logit sum, and the
+    slots order it by (logit desc, index asc)."""
+    rng = np.random.default_rng(7)
+    for E in (2, 3, 5, 8):
+        for k in range(1, E + 1):
+            logits = rng.integers(-2, 3, size=(40, E)).astype(np.float32)
+            ids, gates = oracle.route(logits, k)
+            for t in range(logits.shape[0]):
+                l = logits[t].astype(np.int64)
+                best = max(itertools.combinations(range(E), k), key=lambda s: (sum(l[list(s)]), [-i for i in s]))
+                slots = sorted(best, key=lambda i: (-l[i], i))
+                assert list(ids[t]) == slots
+                # equal logits -> equal gates
+                for a in range(k):
+                    for b in range(k):
+                        if l[slots[a]] == l[slots[b]]:
+                            assert gates[t, a] == gates[t, b]
+
+
+def test_route_golden_cases():
+    for name, k, logits, ids, gates, tol in _rows("route_cases.txt"):
+        lg = np.array([float(v) for v in logits.split(",")], np.float32)[None, :]
+        got_ids, got_g = oracle.route(lg, int(k))
+        assert list(got_ids[0]) == [int(v) for v in ids.split(",")], name
+        np.testing.assert_allclose(got_g[0], [float(v) for v in gates.split(",")], rtol=0, atol=float(tol),
+                                   err_msg=name)
+
+
+@pytest.mark.parametrize("E,k", [(8, 2), (128, 8), (256, 8), (48, 3)])
+def test_gates_renormalised_and_equal_to_softmax_of_selected(E, k):
+    """The page's router takes the top-k logits and then a softmax over those k; the
+    workload definition takes a softmax over all E, then top-k, then renormalises.
+    Both are exp(l_j) / sum_selected exp(l_i) in exact arithmetic."""
+    rng = np.random.default_rng(E * 31 + k)
+    logits = (rng.standard_normal((64, E)) * 3).astype(np.float32)
+    ids, gates = oracle.route(logits, k)
+    np.testing.assert_allclose(gates.sum(axis=1), 1.0, rtol=0, atol=1e-14)
+    assert np.all(np.diff(gates, axis=1) <= 0)
+    sel = np.take_along_axis(logits.astype(np.float64), ids, axis=1)
+    p = np.exp(sel - sel.max(axis=1, keepdims=True))
+    np.testing.assert_allclose(gates, p / p.sum(axis=1, keepdims=True), rtol=1e-13, atol=1e-15)
+
+
+# ----------------------------------------------------------------------------- permute
+@pytest.mark.parametrize("T,E,k,seed", [(64, 8, 2, 0), (6, 128, 8, 1), (300, 256, 8, 2), (1, 4, 4, 3), (0, 8, 2, 4)])
+def test_permute_is_stable_counting_sort(T, E, k, seed):
+    rng = np.random.default_rng(seed)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    ids, _ = oracle.route(logits, k) if T else (np.zeros((0, k), np.int32), None)
+    counts, offsets, sp, pp = oracle.permute(ids, E)
+    np.testing.assert_array_equal(counts, np.bincount(ids.ravel(), minlength=E))
+    assert counts.sum() == T * k and offsets[-1] == T * k and offsets[0] == 0
+    np.testing.assert_array_equal(np.diff(offsets), counts)
+    np.testing.assert_array_equal(sp, np.argsort(ids.ravel(), kind="stable"))
+    np.testing.assert_array_equal(np.sort(sp), np.arange(T * k))          # bijection
+    np.testing.assert_array_equal(pp[sp], np.arange(T * k))                # inverse
+    flat = ids.ravel()
+    for e in range(E):                                                      # segments
+        seg = sp[offsets[e]:offsets[e + 1]]
+        assert np.all(flat[seg] == e) and np.all(np.diff(seg) > 0)
+
+
+# ----------------------------------------------------------------------------- expert FFN
+def _silu(z):
+    return z / (1.0 + np.exp(-z))
+
+
+def _dense_swiglu(x, wgu, wd):
+    M = wd.shape[0]
+    a = x @ wgu
+    return (_silu(a[:, :M]) * a[:, M:]) @ wd
+
+
+def _to_np64(t):
+    return t.detach().to(torch.float64).cpu().numpy()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_single_expert_equals_dense_swiglu(dtype):
+    """E = 1, k = 1: every token goes to the one expert with gate 1, so the layer is a
+    dense SwiGLU FFN; numpy float64 matmuls are the reference."""
+    H, M, T = 64, 96, 12
+    g = torch.Generator().manual_seed(11)
+    wgu = torch.randn(1, H, 2 * M, generator=g) / math.sqrt(H)
+    wd = torch.randn(1, M, H, generator=g) / math.sqrt(M)
+    x = torch.randn(T, H, generator=g)
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    wgu, wd, x = wgu.to(tdt), wd.to(tdt), x.to(tdt)
+    logits = np.zeros((T, 1), np.float32)
+    ids, gates, y, macs = oracle.layer(x.float().numpy(), logits, H=H, M=M, E=1, k=1, dtype=dtype,
+                                       w_gu=[wgu[0]], w_d=[wd[0]])
+    ref = _dense_swiglu(_to_np64(x), _to_np64(wgu[0]), _to_np64(wd[0]))
+    np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-12)
+    assert np.all(gates == 1.0) and np.all(ids == 0)
+    assert 2 * macs == 6 * T * 1 * H * M
+
+
+def test_gate_up_split_and_down_orientation():
+    """Gate columns [0, M) go through SiLU, up columns [M, 2M) do not; W_down is
+    [M, H].  Swapping the halves or transposing W_down changes y, so the dense
+    reference above fails on either mistake; this checks it does on this data."""
+    H, M, T = 32, 48, 5
+    rng = np.random.default_rng(3)
+    wgu = rng.standard_normal((H, 2 * M)).astype(np.float32) / math.sqrt(H)
+    wd = rng.standard_normal((M, H)).astype(np.float32) / math.sqrt(M)
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    _, _, y, _ = oracle.layer(x, np.zeros((T, 1), np.float32), H=H, M=M, E=1, k=1, dtype="f32",
+                              w_gu=[wgu], w_d=[wd])
+    swapped = np.concatenate([wgu[:, M:], wgu[:, :M]], axis=1).astype(np.float64)
+    assert np.abs(y - _dense_swiglu(x.astype(np.float64), swapped, wd.astype(np.float64))).max() > 1e-3
+    np.testing.assert_allclose(y, _dense_swiglu(x.astype(np.float64), wgu.astype(np.float64), wd.astype(np.float64)),
+                               rtol=1e-12, atol=1e-12)
+
+
+def test_diagonal_weights_closed_form():
+    """H = M with W_gate = a_e I, W_up = b_e I, W_down = c_e I gives, per channel,
+    y_i = sum_j g_j c_e SiLU(a_e x_i) b_e x_i (e = expert of slot j)."""
+    H = M = 16
+    E, k, T = 4, 2, 9
+    a = [0.5, -1.25, 2.0, 0.75]
+    b = [1.5, 0.25, -0.5, 1.0]
+    c = [2.0, -1.0, 0.5, 3.0]
+    wgu = [np.concatenate([a[e] * np.eye(H), b[e] * np.eye(H)], axis=1).astype(np.float32) for e in range(E)]
+    wd = [(c[e] * np.eye(M)).astype(np.float32) for e in range(E)]
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    ids, gates, y, _ = oracle.layer(x, logits, H=H, M=M, E=E, k=k, dtype="f32", w_gu=wgu, w_d=wd)
+    for t in range(T):
+        for i in range(H):
+            xi = float(x[t, i])
+            ref = 0.0
+            for j in range(k):
+                e = ids[t, j]
+                z = a[e] * xi
+                ref += gates[t, j] * c[e] * (z / (1.0 + math.exp(-z))) * b[e] * xi
+            assert abs(y[t, i] - ref) <= 1e-13 * max(1.0, abs(ref))
+
+
+def test_k_equals_E_is_dense_softmax_mixture():
+    """With k = E renormalisation is the identity: y = sum_e softmax(l)_e FFN_e(x)."""
+    H, M, E, T = 32, 32, 4, 6
+    rng = np.random.default_rng(9)
+    wgu = [rng.standard_normal((H, 2 * M)).astype(np.float32) / math.sqrt(H) for _ in range(E)]
+    wd = [rng.standard_normal((M, H)).astype(np.float32) / math.sqrt(M) for _ in range(E)]
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    _, _, y, _ = oracle.layer(x, logits, H=H, M=M, E=E, k=E, dtype="f32", w_gu=wgu, w_d=wd)
+    l64 = logits.astype(np.float64)
+    p = np.exp(l64 - l64.max(1, keepdims=True))
+    p /= p.sum(1, keepdims=True)
+    ref = sum(p[:, e:e + 1] * _dense_swiglu(x.astype(np.float64), wgu[e].astype(np.float64),
+                                            wd[e].astype(np.float64)) for e in range(E))
+    np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_token_order_equivariance_and_shared_expert():
+    """Permuting the token order of (x, logits) permutes y; the shared expert adds a
+    dense SwiGLU FFN with gate 1."""
+    H, M, Ms, E, k, T = 32, 64, 48, 6, 2, 10
+    rng = np.random.default_rng(13)
+    wgu = [rng.standard_normal((H, 2 * M)).astype(np.float32) / math.sqrt(H) for _ in range(E)]
+    wd = [rng.standard_normal((M, H)).astype(np.float32) / math.sqrt(M) for _ in range(E)]
+    sgu = rng.standard_normal((H, 2 * Ms)).astype(np.float32) / math.sqrt(H)
+    sd = rng.standard_normal((Ms, H)).astype(np.float32) / math.sqrt(Ms)
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    kw = dict(H=H, M=M, E=E, k=k, dtype="f32", w_gu=wgu, w_d=wd)
+    _, _, y0, m0 = oracle.layer(x, logits, **kw)
+    _, _, y1, m1 = oracle.layer(x, logits, Ms=Ms, ws_gu=sgu, ws_d=sd, **kw)
+    shared = _dense_swiglu(x.astype(np.float64), sgu.astype(np.float64), sd.astype(np.float64))
+    np.testing.assert_allclose(y1, y0 + shared, rtol=1e-12, atol=1e-12)
+    assert 2 * m1 == 6 * T * k * H * M + 6 * T * H * Ms
+    perm = rng.permutation(T)
+    _, _, yp, _ = oracle.layer(x[perm], logits[perm], Ms=Ms, ws_gu=sgu, ws_d=sd, **kw)
+    np.testing.assert_array_equal(yp, y1[perm])
+
+
+def test_mac_count_matches_work_model():
+    """The oracle's loop-counted multiply-adds times 2 equal the 6*T*k*H*M (+6*T*H*Ms)
+    FLOPs of the work model; the fixture also holds the model's values for the five
+    workloads and the 3M/dtype_size intensity."""
+    rows = list(_rows("work_model.txt"))
+    for name, T, H, M, k, Ms, flops in [r for r in rows if r[0] != "ai"]:
+        T, H, M, k, Ms, flops = map(int, (T, H, M, k, Ms, flops))
+        assert 6 * T * k * H * M + 6 * T * H * Ms == flops, name
+    for _, M, dsz, ai in [r for r in rows if r[0] == "ai"]:
+        B, H = 7, 64
+        assert (6 * B * H * int(M)) / (2 * B * H * int(dsz)) == int(ai)
+    H, M, E, k, T, Ms = 64, 128, 5, 3, 7, 128
+    rng = np.random.default_rng(1)
+    wgu = [rng.standard_normal((H, 2 * M)).astype(np.float32) for _ in range(E)]
+    wd = [rng.standard_normal((M, H)).astype(np.float32) for _ in range(E)]
+    sgu = rng.standard_normal((H, 2 * Ms)).astype(np.float32)
+    sd = rng.standard_normal((Ms, H)).astype(np.float32)
+    _, _, _, macs = oracle.layer(rng.standard_normal((T, H)).astype(np.float32),
+                                 rng.standard_normal((T, E)).astype(np.float32), H=H, M=M, E=E, k=k, dtype="f32",
+                                 w_gu=wgu, w_d=wd, Ms=Ms, ws_gu=sgu, ws_d=sd)
+    assert 2 * macs == 6 * T * k * H * M + 6 * T * H * Ms
+
+
+# ----------------------------------------------------------------------------- fp8
+def test_fp8_decode_every_code_matches_torch():
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = np.array([oracle.fp8_decode(c) for c in range(256)])
+    nan = np.isnan(ref)
+    assert list(np.nonzero(nan)[0]) == [0x7F, 0xFF]
+    np.testing.assert_array_equal(np.isnan(got), nan)
+    np.testing.assert_array_equal(got[~nan], ref[~nan])
+    assert oracle.fp8_decode(0x7E) == 448.0 and oracle.fp8_decode(0x38) == 1.0
+    assert oracle.fp8_decode(0x08) == 2.0 ** -6 and oracle.fp8_decode(0x01) == 2.0 ** -9
+
+
+def test_fp8_encode_matches_torch_cast_including_ties():
+    rng = np.random.default_rng(2)
+    vals = list((rng.standard_normal(3000) * rng.choice([1e-3, 0.1, 1, 30, 200], 3000)).astype(np.float32))
+    finite = [oracle.fp8_decode(c) for c in range(127)]
+    vals += [np.float32(0.5 * (finite[i] + finite[i + 1])) for i in range(126)]   # exact midpoints
+    vals += [np.float32(-v) for v in vals[-126:]] + [np.float32(448.0), np.float32(-0.0)]
+    v = np.array(vals, np.float32)
+    v = v[np.abs(v) <= 448]
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([oracle.fp8_encode(float(a)) for a in v], np.uint8)
+    np.testing.assert_array_equal(got, ref)
+    for c in range(127):                                                         # round trip
+        assert oracle.fp8_encode(oracle.fp8_decode(c)) == c
+    assert oracle.fp8_encode(1000.0) == 0x7E and oracle.fp8_encode(-1000.0) == 0xFE
+
+
+def test_fp8_row_quant_against_torch():
+    """Per-128 quantisation: scale = amax/448 (fp32), codes = RNE(v/scale) (fp32);
+    torch's fp32 ops and e4m3 cast are the reference.  Dequantisation error is at most
+    half an e4m3 step times the scale."""
+    rng = np.random.default_rng(4)
+    v = (rng.standard_normal(512) * np.repeat([0.01, 1.0, 50.0, 0.0], 128)).astype(np.float32)
+    codes, scales, deq = oracle.quant_row_fp8(v)
+    tv = torch.from_numpy(v).view(4, 128)
+    amax = tv.abs().amax(dim=1)
+    ts = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+    tq = (tv / ts[:, None]).to(torch.float8_e4m3fn)
+    np.testing.assert_array_equal(scales, ts.numpy())
+    np.testing.assert_array_equal(codes, tq.view(torch.uint8).numpy().ravel())
+    np.testing.assert_array_equal(deq, (tq.to(torch.float64) * ts[:, None].double()).numpy().ravel())
+    for g in range(4):
+        seg = v[g * 128:(g + 1) * 128].astype(np.float64)
+        err = np.abs(deq[g * 128:(g + 1) * 128] - seg)
+        step = np.maximum(2.0 ** (np.floor(np.log2(np.maximum(np.abs(seg) / scales[g], 2.0 ** -6))) - 3), 2.0 ** -9)
+        assert np.all(err <= 0.5 * step * scales[g] * (1 + 1e-12))
+
+
+def test_fp8_layer_equals_dequantised_reference():
+    """fp8 weights: W = code * block scale; activations x and h are quantised per 128
+    channels before each product.  Reference: torch's e4m3 decode and cast with numpy
+    float64 matmuls."""
+    H, M, T = 256, 128, 4
+    g = torch.Generator().manual_seed(21)
+    w = [torch.randn(H, 2 * M, generator=g) / math.sqrt(H), torch.randn(M, H, generator=g) / math.sqrt(M)]
+    qs = []
+    for m in w:
+        R, C = m.shape
+        blk = m.view(R // 128, 128, C // 128, 128)
+        s = blk.abs().amax(dim=(1, 3)) / 448.0
+        q = (blk / s[:, None, :, None]).to(torch.float8_e4m3fn).view(R, C)
+        qs.append((q, s))
+    x = torch.randn(T, H, generator=g).to(torch.bfloat16).float()
+    _, _, y, _ = oracle.layer(x.numpy(), np.zeros((T, 1), np.float32), H=H, M=M, E=1, k=1, dtype="fp8",
+                              w_gu=[qs[0][0]], w_d=[qs[1][0]], s_gu=[qs[0][1]], s_d=[qs[1][1]])
+
+    def deq_w(q, s):
+        R, C = q.shape
+        return (q.to(torch.float64).view(R // 128, 128, C // 128, 128) * s.double()[:, None, :, None]).view(R, C)
+
+    def quant_act(a32):
+        n = a32.shape[1]
+        blk = a32.view(a32.shape[0], n // 128, 128)
+        amax = blk.abs().amax(dim=2)
+        s = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+        q = (blk / s[..., None]).to(torch.float8_e4m3fn)
+        return (q.to(torch.float64) * s.double()[..., None]).view(a32.shape[0], n)
+
+    a = quant_act(x) @ deq_w(*qs[0])
+    h = torch.nn.functional.silu(a[:, :M]) * a[:, M:]
+    ref = quant_act(h.float()) @ deq_w(*qs[1])
+    np.testing.assert_allclose(y, ref.numpy(), rtol=1e-9, atol=1e-9)
