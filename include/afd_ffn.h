@@ -1,0 +1,156 @@
+/*
+ * afd_ffn.h -- C ABI of the MI355X (gfx950) MoE expert-FFN layer: the compute an
+ * FFN instance runs under Attention-FFN disaggregation.
+ *
+ * The operation.  The FFN service of a disaggregated deployment has no scheduler,
+ * no API traffic and no KV cache; per step it receives a batch of hidden states,
+ * runs gate routing plus expert computation, and returns the layer output
+ * ("大模型推理的内存与计算解耦：AFD 架构解析与性能验证", §3, the FFN service and
+ * the data-flow loop of one decode iteration).  For T tokens x[T,H] with fp32
+ * router logits[T,E]:
+ *
+ *   route   : per token, the top_k experts with the largest logits (ties to the
+ *             lower expert index) and gates = their softmax probabilities
+ *             renormalised to sum to 1 (the router of "MoE 大规模分布式推理工程实战：
+ *             从 All-to-All 通信到动态专家放置", §4.1, which normalises the selected
+ *             logits with a softmax);
+ *             then the (token, slot) pairs are sorted by expert with per-expert
+ *             counts, an exclusive prefix sum and a placement pass (the count /
+ *             prefix-offset / pack steps of the same page's §2.2; the pre-sorting of
+ *             routed tokens that the omica.com.cn AFD article's §3.3 recommends);
+ *   forward : per pair (t, e): h = SiLU(x_t Wgu[e][:, :M]) * (x_t Wgu[e][:, M:]),
+ *             o = h Wd[e]; y_t = sum_j gate_tj o_tj in slot order, plus a shared
+ *             expert's output with gate 1 when the layer has one.  6*H*M FLOPs per
+ *             pair (the omica.com.cn AFD article, §2.1).
+ *
+ * Data types (afd_ffn_config.dtype):
+ *   AFD_F32      x, weights and y are float32.
+ *   AFD_BF16     x, weights and y are bfloat16.
+ *   AFD_FP8_E4M3 weights are OCP e4m3 codes with one float32 scale per 128x128
+ *                block; x and y are bfloat16; x and h are quantised to e4m3 per
+ *                token and per 128 channels (scale amax/448) inside forward (the
+ *                FP8/BF16 mixed precision of the omica.com.cn AFD article, §3.3).
+ * All accumulation is float32.
+ *
+ * Memory.  Every pointer argument is a device pointer (HIP, same device as the
+ * handle), except `cfg`, `out` and the route struct itself, which are host
+ * pointers.  Row-major layouts throughout.  The caller owns all buffers it passes;
+ * the library never frees them.  afd_ffn_create copies the weights into a layout
+ * of its own (tiles ordered for the matrix cores) and owns that copy and a
+ * workspace sized from max_tokens until afd_ffn_destroy; the caller's weight
+ * buffers may be freed once create has returned.
+ *
+ * Streams.  `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ * route and forward only enqueue work on it: no host synchronisation, no device
+ * read-back and no allocation, so both can be captured in a HIP graph.  A fault
+ * in a kernel surfaces at the caller's next synchronisation.  Calls on one handle
+ * share its workspace: two forwards in flight at once on different streams race.
+ *
+ * Errors.  Every int-returning function returns AFD_OK (0) or a negative code;
+ * afd_ffn_strerror names the code and afd_ffn_last_error gives the detail of the
+ * calling thread's last failure.  Arguments are checked on the host before any
+ * work is enqueued; a failed call enqueues nothing.  T = 0 is a successful no-op.
+ * Logits must be finite (not checked).
+ */
+#ifndef AFD_FFN_H_
+#define AFD_FFN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define AFD_OK 0
+#define AFD_EINVAL -1       /* a null pointer, a size out of range or misaligned */
+#define AFD_EUNSUPPORTED -2 /* a data type or shape this build does not implement */
+#define AFD_ENOMEM -3       /* device allocation failed in create */
+#define AFD_EHIP -4         /* a HIP runtime call or kernel launch failed */
+
+typedef enum afd_dtype { AFD_F32 = 0, AFD_BF16 = 1, AFD_FP8_E4M3 = 2 } afd_dtype;
+
+/* Layer shape.  hidden, inter and shared_inter must be multiples of 128;
+ * 1 <= top_k <= min(num_experts, 32); 1 <= num_experts <= 1024;
+ * 1 <= max_tokens and max_tokens * top_k < 2^31. */
+typedef struct afd_ffn_config {
+  int32_t hidden;       /* H */
+  int32_t inter;        /* M, intermediate size of each routed expert */
+  int32_t num_experts;  /* E */
+  int32_t top_k;        /* k */
+  int32_t max_tokens;   /* largest T any call will pass */
+  int32_t shared_inter; /* intermediate size of the always-on shared expert, 0 = none */
+  int32_t dtype;        /* afd_dtype */
+} afd_ffn_config;
+
+/* Routing result of one batch, in caller-owned device buffers sized for
+ * max_tokens (P = T * top_k pairs; pair p = t * top_k + j is slot j of token t). */
+typedef struct afd_route {
+  int32_t* topk_ids;       /* [max_tokens * k] expert of each pair, slots by rank */
+  float* topk_gates;       /* [max_tokens * k] renormalised gates */
+  int32_t* expert_counts;  /* [E] pairs routed to each expert */
+  int32_t* expert_offsets; /* [E + 1] exclusive prefix sum of counts; [E] = P */
+  int32_t* sorted_pair;    /* [max_tokens * k] pair id at each expert-sorted position,
+                              ascending token order inside an expert */
+  int32_t* pair_pos;       /* [max_tokens * k] inverse: sorted position of each pair */
+} afd_route;
+
+typedef struct afd_ffn* afd_ffn_t;
+
+/* Create a layer.  w_gate_up [E, H, 2M] (columns [0, M) gate, [M, 2M) up) and
+ * w_down [E, M, H] in the config's dtype.  For AFD_FP8_E4M3, s_gate_up
+ * [E, H/128, 2M/128] and s_down [E, M/128, H/128] are the fp32 block scales
+ * (weight = code * scale); they must be NULL otherwise.  With shared_inter > 0,
+ * ws_gate_up [H, 2*shared_inter] and ws_down [shared_inter, H] (and for fp8
+ * ss_gate_up [H/128, 2*shared_inter/128], ss_down [shared_inter/128, H/128]) hold
+ * the shared expert; NULL otherwise.  Enqueues the weight repack on `stream` and
+ * synchronises it before returning.  On success *out holds the handle. */
+int afd_ffn_create(const afd_ffn_config* cfg, const void* w_gate_up, const void* w_down,
+                   const float* s_gate_up, const float* s_down, const void* ws_gate_up,
+                   const void* ws_down, const float* ss_gate_up, const float* ss_down, void* stream,
+                   afd_ffn_t* out);
+
+/* Route T tokens: fp32 logits [T, E] -> every field of *r (see afd_route).
+ * 0 <= T <= max_tokens. */
+int afd_ffn_route(afd_ffn_t h, const float* logits, int32_t T, const afd_route* r, void* stream);
+
+/* Expert FFN of T routed tokens: x [T, H] (fp32 for AFD_F32, else bf16) and the
+ * result of afd_ffn_route for the same T -> y [T, H] (fp32 for AFD_F32, else bf16).
+ * x and y must not overlap. */
+int afd_ffn_forward(afd_ffn_t h, const void* x, int32_t T, const afd_route* r, void* y, void* stream);
+
+/* Release the handle's weights and workspace.  The caller must have synchronised
+ * every stream with work of this handle.  NULL is a no-op. */
+int afd_ffn_destroy(afd_ffn_t h);
+
+/* Static description of an error code. */
+const char* afd_ffn_strerror(int code);
+
+/* Detail of the calling thread's last failed call ("" if none). */
+const char* afd_ffn_last_error(void);
+
+/* Device bytes the handle owns (repacked weights plus workspace). */
+size_t afd_ffn_device_bytes(afd_ffn_t h);
+
+/* Per-kernel timing.  With profiling on, route and forward bracket each kernel
+ * with HIP events on the launch stream.  afd_ffn_profile_read synchronises on the
+ * recorded events, writes the summed milliseconds and launch counts of each stage
+ * (index = afd_stage) into ms[n_stages] and launches[n_stages], and clears them.
+ * Timing adds an event pair per kernel; leave it off for throughput runs. */
+typedef enum afd_stage {
+  AFD_STAGE_ROUTER = 0,  /* top-k softmax router */
+  AFD_STAGE_PERMUTE = 1, /* histogram, prefix scan, scatter */
+  AFD_STAGE_QUANT_X = 2, /* fp8 quantisation of x */
+  AFD_STAGE_GATE_UP = 3, /* grouped gate/up GEMM with SwiGLU epilogue */
+  AFD_STAGE_DOWN = 4,    /* grouped down-projection GEMM */
+  AFD_STAGE_COMBINE = 5, /* gate-weighted combine back to token order */
+  AFD_NUM_STAGES = 6
+} afd_stage;
+int afd_ffn_set_profiling(afd_ffn_t h, int on);
+int afd_ffn_profile_read(afd_ffn_t h, double* ms, int64_t* launches, int n_stages);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AFD_FFN_H_ */

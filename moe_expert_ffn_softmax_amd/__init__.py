@@ -1,0 +1,91 @@
+"""MI355X (gfx950) MoE expert-FFN layer -- the FFN side of Attention-FFN
+disaggregation -- as hand-written HIP kernels behind a C ABI (include/afd_ffn.h).
+
+`_ffi` is the ctypes binding with the C function names.  `MoeExpertFFN` is a thin
+convenience wrapper that allocates the caller-owned route buffers with torch (device
+memory) and calls route/forward on torch's current stream.  There is no CPU or
+PyTorch fallback: if libafd_ffn.so is missing, constructing a layer raises.
+"""
+from __future__ import annotations
+
+from ._ffi import (AFD_BF16, AFD_F32, AFD_FP8_E4M3, STAGES, AfdError, afd_ffn_config,  # noqa: F401
+                   afd_ffn_create, afd_ffn_destroy, afd_ffn_device_bytes, afd_ffn_forward,
+                   afd_ffn_last_error, afd_ffn_profile_read, afd_ffn_route, afd_ffn_set_profiling,
+                   afd_ffn_strerror, afd_route, load)
+
+DTYPES = {"f32": AFD_F32, "bf16": AFD_BF16, "fp8": AFD_FP8_E4M3}
+
+
+def _stream_handle(torch, stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+class RouteBuffers:
+    """Caller-owned device buffers of one routing result (one per batch in flight)."""
+
+    def __init__(self, max_tokens: int, num_experts: int, top_k: int, device):
+        import torch
+        P = max_tokens * top_k
+        i32 = dict(dtype=torch.int32, device=device)
+        self.topk_ids = torch.zeros(P, **i32)
+        self.topk_gates = torch.zeros(P, dtype=torch.float32, device=device)
+        self.expert_counts = torch.zeros(num_experts, **i32)
+        self.expert_offsets = torch.zeros(num_experts + 1, **i32)
+        self.sorted_pair = torch.zeros(P, **i32)
+        self.pair_pos = torch.zeros(P, **i32)
+        self.c = afd_route(self.topk_ids.data_ptr(), self.topk_gates.data_ptr(), self.expert_counts.data_ptr(),
+                           self.expert_offsets.data_ptr(), self.sorted_pair.data_ptr(), self.pair_pos.data_ptr())
+
+
+class MoeExpertFFN:
+    """One MoE layer's routed experts (+ optional shared expert) on the current device.
+
+    w_gate_up [E,H,2M], w_down [E,M,H] (float32 / bfloat16 / float8_e4m3fn tensors on
+    the GPU); for fp8 also s_gate_up, s_down fp32 block scales; ws_* / ss_* for the
+    shared expert.  The library copies the weights at construction."""
+
+    def __init__(self, *, hidden, inter, num_experts, top_k, max_tokens, dtype, w_gate_up, w_down,
+                 s_gate_up=None, s_down=None, shared_inter=0, ws_gate_up=None, ws_down=None, ss_gate_up=None,
+                 ss_down=None):
+        import torch
+        load()
+        self.cfg = afd_ffn_config(hidden, inter, num_experts, top_k, max_tokens, shared_inter, DTYPES[dtype])
+        self.dtype = dtype
+        self.device = w_gate_up.device
+        self.handle = afd_ffn_create(self.cfg, w_gate_up, w_down, s_gate_up, s_down, ws_gate_up, ws_down,
+                                     ss_gate_up, ss_down, _stream_handle(torch))
+
+    def new_route(self) -> RouteBuffers:
+        return RouteBuffers(self.cfg.max_tokens, self.cfg.num_experts, self.cfg.top_k, self.device)
+
+    def route(self, logits, T: int, rb: RouteBuffers, stream=None) -> None:
+        import torch
+        afd_ffn_route(self.handle, logits, T, rb.c, _stream_handle(torch, stream))
+
+    def forward(self, x, T: int, rb: RouteBuffers, y, stream=None) -> None:
+        import torch
+        afd_ffn_forward(self.handle, x, T, rb.c, y, _stream_handle(torch, stream))
+
+    def __call__(self, x, logits, rb: RouteBuffers = None, y=None):
+        """route + forward of a whole batch; returns y (allocated if not given)."""
+        import torch
+        T = x.shape[0]
+        rb = rb or self.new_route()
+        if y is None:
+            y = torch.empty((T, self.cfg.hidden), dtype=torch.float32 if self.dtype == "f32" else torch.bfloat16,
+                            device=x.device)
+        self.route(logits, T, rb)
+        self.forward(x, T, rb, y)
+        return y
+
+    def close(self):
+        if getattr(self, "handle", None):
+            afd_ffn_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,126 @@
+"""ctypes binding of libafd_ffn.so: the C ABI declared in include/afd_ffn.h, with the
+same function names.  Argument marshalling only -- every step of the layer runs in
+the library's HIP kernels.  Pointer arguments accept torch tensors (their
+data_ptr()), plain integers or None."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libafd_ffn.so")
+
+AFD_OK, AFD_EINVAL, AFD_EUNSUPPORTED, AFD_ENOMEM, AFD_EHIP = 0, -1, -2, -3, -4
+AFD_F32, AFD_BF16, AFD_FP8_E4M3 = 0, 1, 2
+STAGES = ("router", "permute", "quant_x", "gate_up", "down", "combine")
+AFD_NUM_STAGES = len(STAGES)
+
+
+class afd_ffn_config(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("inter", ctypes.c_int32), ("num_experts", ctypes.c_int32),
+                ("top_k", ctypes.c_int32), ("max_tokens", ctypes.c_int32), ("shared_inter", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
+
+
+class afd_route(ctypes.Structure):
+    _fields_ = [("topk_ids", ctypes.c_void_p), ("topk_gates", ctypes.c_void_p), ("expert_counts", ctypes.c_void_p),
+                ("expert_offsets", ctypes.c_void_p), ("sorted_pair", ctypes.c_void_p), ("pair_pos", ctypes.c_void_p)]
+
+
+class AfdError(RuntimeError):
+    def __init__(self, code: int, detail: str):
+        super().__init__(f"{afd_ffn_strerror(code)} ({code}): {detail}")
+        self.code = code
+
+
+_lib = None
+
+
+def load():
+    """Load the library; raises if it has not been built (there is no fallback)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m moe_expert_ffn_softmax_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    V, I32, P = ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p
+    lib.afd_ffn_create.argtypes = [ctypes.POINTER(afd_ffn_config), V, V, V, V, V, V, V, V, V, ctypes.POINTER(V)]
+    lib.afd_ffn_create.restype = ctypes.c_int
+    lib.afd_ffn_route.argtypes = [V, P, I32, ctypes.POINTER(afd_route), V]
+    lib.afd_ffn_route.restype = ctypes.c_int
+    lib.afd_ffn_forward.argtypes = [V, P, I32, ctypes.POINTER(afd_route), P, V]
+    lib.afd_ffn_forward.restype = ctypes.c_int
+    lib.afd_ffn_destroy.argtypes = [V]
+    lib.afd_ffn_destroy.restype = ctypes.c_int
+    lib.afd_ffn_strerror.argtypes = [ctypes.c_int]
+    lib.afd_ffn_strerror.restype = ctypes.c_char_p
+    lib.afd_ffn_last_error.argtypes = []
+    lib.afd_ffn_last_error.restype = ctypes.c_char_p
+    lib.afd_ffn_device_bytes.argtypes = [V]
+    lib.afd_ffn_device_bytes.restype = ctypes.c_size_t
+    lib.afd_ffn_set_profiling.argtypes = [V, ctypes.c_int]
+    lib.afd_ffn_set_profiling.restype = ctypes.c_int
+    lib.afd_ffn_profile_read.argtypes = [V, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64),
+                                         ctypes.c_int]
+    lib.afd_ffn_profile_read.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    if isinstance(a, int):
+        return a
+    return a.data_ptr()
+
+
+def _check(rc: int):
+    if rc != AFD_OK:
+        raise AfdError(rc, afd_ffn_last_error())
+
+
+def afd_ffn_strerror(code: int) -> str:
+    return load().afd_ffn_strerror(int(code)).decode()
+
+
+def afd_ffn_last_error() -> str:
+    return load().afd_ffn_last_error().decode()
+
+
+def afd_ffn_create(cfg: afd_ffn_config, w_gate_up, w_down, s_gate_up=None, s_down=None, ws_gate_up=None,
+                   ws_down=None, ss_gate_up=None, ss_down=None, stream=None) -> int:
+    h = ctypes.c_void_p()
+    _check(load().afd_ffn_create(ctypes.byref(cfg), _ptr(w_gate_up), _ptr(w_down), _ptr(s_gate_up), _ptr(s_down),
+                                 _ptr(ws_gate_up), _ptr(ws_down), _ptr(ss_gate_up), _ptr(ss_down), stream,
+                                 ctypes.byref(h)))
+    return h.value
+
+
+def afd_ffn_route(h: int, logits, T: int, route: afd_route, stream=None) -> None:
+    _check(load().afd_ffn_route(h, _ptr(logits), int(T), ctypes.byref(route), stream))
+
+
+def afd_ffn_forward(h: int, x, T: int, route: afd_route, y, stream=None) -> None:
+    _check(load().afd_ffn_forward(h, _ptr(x), int(T), ctypes.byref(route), _ptr(y), stream))
+
+
+def afd_ffn_destroy(h: int) -> None:
+    _check(load().afd_ffn_destroy(h))
+
+
+def afd_ffn_device_bytes(h: int) -> int:
+    return int(load().afd_ffn_device_bytes(h))
+
+
+def afd_ffn_set_profiling(h: int, on: bool) -> None:
+    _check(load().afd_ffn_set_profiling(h, 1 if on else 0))
+
+
+def afd_ffn_profile_read(h: int):
+    """{stage name: (milliseconds, launches)} summed since the last read."""
+    ms = (ctypes.c_double * AFD_NUM_STAGES)()
+    n = (ctypes.c_int64 * AFD_NUM_STAGES)()
+    _check(load().afd_ffn_profile_read(h, ms, n, AFD_NUM_STAGES))
+    return {STAGES[i]: (ms[i], int(n[i])) for i in range(AFD_NUM_STAGES)}

@@ -1,0 +1,335 @@
+// C ABI of the expert-FFN layer: argument checks, weight repack, workspace and the
+// launch sequence of route (router -> permute) and forward (gate/up GEMM + SwiGLU
+// -> down GEMM -> combine), all asynchronous on the caller's stream.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <new>
+
+#include "afd_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) { return fail(AFD_EHIP, "%s: %s", what, hipGetErrorString(e)); }
+
+size_t elem_size(int dtype) { return dtype == AFD_F32 ? 4 : dtype == AFD_BF16 ? 2 : 1; }
+
+int check_config(const afd_ffn_config* c) {
+  if (!c) return fail(AFD_EINVAL, "config is NULL");
+  if (c->hidden <= 0 || c->hidden % 128) return fail(AFD_EINVAL, "hidden=%d must be a positive multiple of 128", c->hidden);
+  if (c->inter <= 0 || c->inter % 128) return fail(AFD_EINVAL, "inter=%d must be a positive multiple of 128", c->inter);
+  if (c->shared_inter < 0 || c->shared_inter % 128)
+    return fail(AFD_EINVAL, "shared_inter=%d must be 0 or a positive multiple of 128", c->shared_inter);
+  if (c->num_experts < 1 || c->num_experts > 1024) return fail(AFD_EINVAL, "num_experts=%d not in [1, 1024]", c->num_experts);
+  if (c->top_k < 1 || c->top_k > c->num_experts || c->top_k > 32)
+    return fail(AFD_EINVAL, "top_k=%d not in [1, min(num_experts, 32)]", c->top_k);
+  if (c->max_tokens < 1) return fail(AFD_EINVAL, "max_tokens=%d must be >= 1", c->max_tokens);
+  if ((long long)c->max_tokens * c->top_k >= (1ll << 31)) return fail(AFD_EINVAL, "max_tokens * top_k >= 2^31");
+  if (c->dtype != AFD_F32 && c->dtype != AFD_BF16 && c->dtype != AFD_FP8_E4M3)
+    return fail(AFD_EINVAL, "unknown dtype %d", c->dtype);
+  if (c->dtype == AFD_FP8_E4M3) return fail(AFD_EUNSUPPORTED, "fp8 weights are not implemented in this build");
+  return AFD_OK;
+}
+
+int check_route(const afd_ffn* h, const afd_route* r, int32_t T) {
+  if (!h) return fail(AFD_EINVAL, "handle is NULL");
+  if (!r) return fail(AFD_EINVAL, "route is NULL");
+  if (T < 0 || T > h->cfg.max_tokens) return fail(AFD_EINVAL, "T=%d not in [0, max_tokens=%d]", T, h->cfg.max_tokens);
+  if (!r->topk_ids || !r->topk_gates || !r->expert_counts || !r->expert_offsets || !r->sorted_pair || !r->pair_pos)
+    return fail(AFD_EINVAL, "a route buffer is NULL");
+  return AFD_OK;
+}
+
+void release(afd_ffn* h) {
+  void* bufs[] = {h->w_gu, h->w_d, h->ws_gu, h->ws_d, h->h_routed, h->h_shared, h->o_routed, h->o_shared, h->counters};
+  for (void* b : bufs)
+    if (b) (void)hipFree(b);
+  for (hipEvent_t e : h->ev_pool) (void)hipEventDestroy(e);
+  delete h;
+}
+
+// Brackets one kernel launch with events when profiling is on: the start event is
+// recorded on construction, the stop event by done(); a scope left without done()
+// (a failed launch) gives its start event back.
+struct StageScope {
+  afd_ffn* h;
+  hipStream_t st;
+  int stage;
+  bool on;
+  StageScope(afd_ffn* h_, hipStream_t st_, int stage_) : h(h_), st(st_), stage(stage_), on(h_->profiling) {
+    while (on && h->ev_pool.size() < h->ev_used + 2) {
+      hipEvent_t e;
+      if (hipEventCreate(&e) != hipSuccess) {
+        on = false;
+        break;
+      }
+      h->ev_pool.push_back(e);
+    }
+    if (on) (void)hipEventRecord(h->ev_pool[h->ev_used++], st);
+  }
+  void done() {
+    if (!on) return;
+    (void)hipEventRecord(h->ev_pool[h->ev_used++], st);
+    h->ev_stage.push_back(stage);
+    on = false;
+  }
+  ~StageScope() {
+    if (on) --h->ev_used;
+  }
+};
+
+}  // namespace
+
+extern "C" const char* afd_ffn_strerror(int code) {
+  switch (code) {
+    case AFD_OK: return "success";
+    case AFD_EINVAL: return "invalid argument";
+    case AFD_EUNSUPPORTED: return "unsupported data type or shape";
+    case AFD_ENOMEM: return "device memory allocation failed";
+    case AFD_EHIP: return "HIP runtime error";
+    default: return "unknown error code";
+  }
+}
+
+extern "C" const char* afd_ffn_last_error(void) { return g_last_error; }
+
+extern "C" int afd_ffn_create(const afd_ffn_config* cfg, const void* w_gate_up, const void* w_down,
+                              const float* s_gate_up, const float* s_down, const void* ws_gate_up, const void* ws_down,
+                              const float* ss_gate_up, const float* ss_down, void* stream, afd_ffn_t* out) {
+  int rc = check_config(cfg);
+  if (rc) return rc;
+  if (!out) return fail(AFD_EINVAL, "out is NULL");
+  if (!w_gate_up || !w_down) return fail(AFD_EINVAL, "expert weights are NULL");
+  const bool fp8 = cfg->dtype == AFD_FP8_E4M3;
+  if (!fp8 && (s_gate_up || s_down || ss_gate_up || ss_down))
+    return fail(AFD_EINVAL, "block scales are only taken with fp8 weights");
+  if (cfg->shared_inter > 0 && (!ws_gate_up || !ws_down)) return fail(AFD_EINVAL, "shared expert weights are NULL");
+  if (cfg->shared_inter == 0 && (ws_gate_up || ws_down)) return fail(AFD_EINVAL, "shared weights given without shared_inter");
+  *out = nullptr;
+
+  afd_ffn* h = new (std::nothrow) afd_ffn();
+  if (!h) return fail(AFD_ENOMEM, "host allocation of the handle failed");
+  h->cfg = *cfg;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = hipGetDevice(&h->device);
+  if (e != hipSuccess) {
+    release(h);
+    return hip_fail(e, "hipGetDevice");
+  }
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, h->device);
+  if (e != hipSuccess) {
+    release(h);
+    return hip_fail(e, "hipGetDeviceProperties");
+  }
+  h->num_cus = prop.multiProcessorCount;
+
+  const size_t H = cfg->hidden, M = cfg->inter, Ms = cfg->shared_inter, E = cfg->num_experts;
+  const size_t P = (size_t)cfg->max_tokens * cfg->top_k, T = cfg->max_tokens;
+  const size_t es = elem_size(cfg->dtype);
+  h->w_gu_expert_elems = H * 2 * M;
+  h->w_d_expert_elems = M * H;
+
+  struct Alloc {
+    void** dst;
+    size_t bytes;
+  } allocs[] = {
+      {&h->w_gu, E * H * 2 * M * es},  {&h->w_d, E * M * H * es},      {&h->ws_gu, H * 2 * Ms * es},
+      {&h->ws_d, Ms * H * es},         {&h->h_routed, P * M * es},     {&h->h_shared, T * Ms * es},
+      {(void**)&h->o_routed, P * H * 4}, {(void**)&h->o_shared, Ms ? T * H * 4 : 0},
+      {(void**)&h->counters, 8 * sizeof(unsigned)},
+  };
+  for (auto& a : allocs) {
+    if (a.bytes == 0) continue;
+    e = hipMalloc(a.dst, a.bytes);
+    if (e != hipSuccess) {
+      *a.dst = nullptr;
+      release(h);
+      return fail(AFD_ENOMEM, "hipMalloc of %zu bytes failed: %s", a.bytes, hipGetErrorString(e));
+    }
+    h->device_bytes += a.bytes;
+  }
+
+  if (cfg->dtype == AFD_BF16) {
+    e = afd::launch_pack_bf16(static_cast<const uint16_t*>(w_gate_up), static_cast<uint16_t*>(h->w_gu), (int)E,
+                              (int)H, (int)(2 * M), 1, st);
+    if (e == hipSuccess)
+      e = afd::launch_pack_bf16(static_cast<const uint16_t*>(w_down), static_cast<uint16_t*>(h->w_d), (int)E, (int)M,
+                                (int)H, 0, st);
+    if (e == hipSuccess && Ms)
+      e = afd::launch_pack_bf16(static_cast<const uint16_t*>(ws_gate_up), static_cast<uint16_t*>(h->ws_gu), 1, (int)H,
+                                (int)(2 * Ms), 1, st);
+    if (e == hipSuccess && Ms)
+      e = afd::launch_pack_bf16(static_cast<const uint16_t*>(ws_down), static_cast<uint16_t*>(h->ws_d), 1, (int)Ms,
+                                (int)H, 0, st);
+  } else {
+    e = hipMemcpyAsync(h->w_gu, w_gate_up, E * H * 2 * M * es, hipMemcpyDeviceToDevice, st);
+    if (e == hipSuccess) e = hipMemcpyAsync(h->w_d, w_down, E * M * H * es, hipMemcpyDeviceToDevice, st);
+    if (e == hipSuccess && Ms) e = hipMemcpyAsync(h->ws_gu, ws_gate_up, H * 2 * Ms * es, hipMemcpyDeviceToDevice, st);
+    if (e == hipSuccess && Ms) e = hipMemcpyAsync(h->ws_d, ws_down, Ms * H * es, hipMemcpyDeviceToDevice, st);
+  }
+  if (e == hipSuccess) e = hipMemsetAsync(h->counters, 0, 8 * sizeof(unsigned), st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) {
+    release(h);
+    return hip_fail(e, "weight repack");
+  }
+  *out = h;
+  return AFD_OK;
+}
+
+extern "C" int afd_ffn_destroy(afd_ffn_t h) {
+  if (h) release(h);
+  return AFD_OK;
+}
+
+extern "C" size_t afd_ffn_device_bytes(afd_ffn_t h) { return h ? h->device_bytes : 0; }
+
+extern "C" int afd_ffn_route(afd_ffn_t h, const float* logits, int32_t T, const afd_route* r, void* stream) {
+  int rc = check_route(h, r, T);
+  if (rc) return rc;
+  if (!logits) return fail(AFD_EINVAL, "logits is NULL");
+  if (T == 0) return AFD_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int E = h->cfg.num_experts, k = h->cfg.top_k;
+  {
+    StageScope s(h, st, AFD_STAGE_ROUTER);
+    hipError_t e = afd::launch_router(logits, T, E, k, r->topk_ids, r->topk_gates, st);
+    if (e != hipSuccess) return hip_fail(e, "router launch");
+    s.done();
+  }
+  {
+    StageScope s(h, st, AFD_STAGE_PERMUTE);
+    hipError_t e = afd::launch_permute(r->topk_ids, T * k, E, r->expert_counts, r->expert_offsets, r->sorted_pair,
+                                       r->pair_pos, st);
+    if (e != hipSuccess) return hip_fail(e, "permute launch");
+    s.done();
+  }
+  return AFD_OK;
+}
+
+extern "C" int afd_ffn_forward(afd_ffn_t h, const void* x, int32_t T, const afd_route* r, void* y, void* stream) {
+  int rc = check_route(h, r, T);
+  if (rc) return rc;
+  if (!x || !y) return fail(AFD_EINVAL, "x or y is NULL");
+  if (T == 0) return AFD_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const afd_ffn_config& c = h->cfg;
+  const int H = c.hidden, M = c.inter, Ms = c.shared_inter, E = c.num_experts, k = c.top_k;
+  const int P = T * k;
+  const bool f32 = c.dtype == AFD_F32;
+
+  afd::GroupedGemm g1 = {};
+  g1.counts = r->expert_counts;
+  g1.offsets = r->expert_offsets;
+  g1.sorted_pair = r->sorted_pair;
+  g1.E = E;
+  g1.k = k;
+  g1.gather_routed = 1;
+  g1.shared_rows = Ms > 0 ? T : 0;
+  g1.K_routed = H;
+  g1.K_shared = H;
+  g1.groups_routed = M / 16;
+  g1.groups_shared = Ms / 16;
+  g1.w_routed = h->w_gu;
+  g1.w_expert_elems = h->w_gu_expert_elems;
+  g1.w_shared = h->ws_gu;
+  g1.a_routed = x;
+  g1.a_shared = x;
+  g1.lda_routed = H;
+  g1.lda_shared = H;
+  g1.out_routed = h->h_routed;
+  g1.out_shared = h->h_shared;
+  g1.ldo_routed = M;
+  g1.ldo_shared = Ms;
+  g1.work_counter = h->counters;
+
+  afd::GroupedGemm g2 = g1;
+  g2.gather_routed = 0;
+  g2.K_routed = M;
+  g2.K_shared = Ms;
+  g2.groups_routed = H / afd::kGroupCols;
+  g2.groups_shared = H / afd::kGroupCols;
+  g2.w_routed = h->w_d;
+  g2.w_expert_elems = h->w_d_expert_elems;
+  g2.w_shared = h->ws_d;
+  g2.a_routed = h->h_routed;
+  g2.a_shared = h->h_shared;
+  g2.lda_routed = M;
+  g2.lda_shared = Ms;
+  g2.out_routed = h->o_routed;
+  g2.out_shared = h->o_shared;
+  g2.ldo_routed = H;
+  g2.ldo_shared = H;
+  g2.work_counter = h->counters + 2;
+
+  const long long items1 =
+      afd::grouped_items_bound(P, E, g1.groups_routed, g1.shared_rows, g1.groups_shared, afd::kTileRows);
+  const long long items2 =
+      afd::grouped_items_bound(P, E, g2.groups_routed, g2.shared_rows, g2.groups_shared, afd::kTileRows);
+  {
+    StageScope s(h, st, AFD_STAGE_GATE_UP);
+    hipError_t e = f32 ? afd::launch_gemm_f32(g1, true, items1, h->num_cus, st)
+                       : afd::launch_gemm_bf16(g1, true, items1, h->num_cus, st);
+    if (e != hipSuccess) return hip_fail(e, "gate/up GEMM launch");
+    s.done();
+  }
+  {
+    StageScope s(h, st, AFD_STAGE_DOWN);
+    hipError_t e = f32 ? afd::launch_gemm_f32(g2, false, items2, h->num_cus, st)
+                       : afd::launch_gemm_bf16(g2, false, items2, h->num_cus, st);
+    if (e != hipSuccess) return hip_fail(e, "down GEMM launch");
+    s.done();
+  }
+  {
+    StageScope s(h, st, AFD_STAGE_COMBINE);
+    hipError_t e = afd::launch_combine(h->o_routed, Ms ? h->o_shared : nullptr, r->topk_gates, r->pair_pos, T, k, H, y,
+                                       !f32, st);
+    if (e != hipSuccess) return hip_fail(e, "combine launch");
+    s.done();
+  }
+  return AFD_OK;
+}
+
+extern "C" int afd_ffn_set_profiling(afd_ffn_t h, int on) {
+  if (!h) return fail(AFD_EINVAL, "handle is NULL");
+  h->profiling = on != 0;
+  return AFD_OK;
+}
+
+extern "C" int afd_ffn_profile_read(afd_ffn_t h, double* ms, int64_t* launches, int n_stages) {
+  if (!h) return fail(AFD_EINVAL, "handle is NULL");
+  if (n_stages < 0 || (n_stages > 0 && (!ms || !launches))) return fail(AFD_EINVAL, "bad output arrays");
+  for (int i = 0; i < n_stages; ++i) {
+    ms[i] = 0.0;
+    launches[i] = 0;
+  }
+  if (h->ev_used > 0) {
+    hipError_t e = hipEventSynchronize(h->ev_pool[h->ev_used - 1]);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+  }
+  for (size_t i = 0; i < h->ev_stage.size(); ++i) {
+    float t = 0.f;
+    hipError_t e = hipEventElapsedTime(&t, h->ev_pool[2 * i], h->ev_pool[2 * i + 1]);
+    if (e != hipSuccess) return hip_fail(e, "hipEventElapsedTime");
+    const int s = h->ev_stage[i];
+    if (s < n_stages) {
+      ms[s] += t;
+      launches[s] += 1;
+    }
+  }
+  h->ev_stage.clear();
+  h->ev_used = 0;
+  return AFD_OK;
+}

@@ -1,0 +1,108 @@
+// Host-side internals of the expert-FFN library: the handle and the kernel
+// launchers each kernel file provides.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include <string>
+#include <vector>
+
+#include "afd_ffn.h"
+
+namespace afd {
+
+// Rows of one matrix-core tile of the grouped GEMMs (the token dimension).
+constexpr int kTileRows = 16;
+// Output columns of one work item: two 16-column blocks (gate + up for the gate/up
+// projection, two adjacent blocks for the down projection).
+constexpr int kGroupCols = 32;
+
+// A grouped GEMM over the routed experts plus, optionally, the shared expert.
+// Segment s < E is routed expert s: rows offsets[s] .. offsets[s] + counts[s] of the
+// expert-sorted order; segment E (when shared_rows > 0) is the shared expert over
+// all tokens.  Row r of a routed segment reads A row a_index(r) where
+// a_index = sorted_pair[r] / k when gather_routed is set (tokens) and r otherwise
+// (intermediate rows already in sorted order).
+struct GroupedGemm {
+  const int32_t* counts;
+  const int32_t* offsets;
+  const int32_t* sorted_pair;
+  int E, k;
+  int gather_routed;
+  int shared_rows;              // 0 = no shared segment
+  int K_routed, K_shared;       // reduction length
+  int groups_routed, groups_shared;  // 32-column items per row tile
+  const void* w_routed;         // packed weights of expert 0
+  size_t w_expert_elems;        // packed elements per expert
+  const void* w_shared;
+  const float* s_routed;        // fp8 block scales (packed), else null
+  size_t s_expert_elems;
+  const float* s_shared;
+  const void* a_routed;         // A matrices
+  const void* a_shared;
+  const float* as_routed;       // fp8 activation scales [rows, K/128], else null
+  const float* as_shared;
+  int lda_routed, lda_shared;   // A row stride (elements)
+  void* out_routed;             // output rows in sorted order
+  void* out_shared;
+  float* outs_routed;           // fp8: per-row per-128 scales of the output, else null
+  float* outs_shared;
+  int ldo_routed, ldo_shared;   // output row stride (elements)
+  unsigned* work_counter;       // 2 zeroed words: item queue head, finished waves;
+                                // the last wave of a launch resets both to 0
+};
+
+hipError_t launch_router(const float* logits, int T, int E, int k, int32_t* ids, float* gates,
+                         hipStream_t st);
+hipError_t launch_permute(const int32_t* ids, int P, int E, int32_t* counts, int32_t* offsets,
+                          int32_t* sorted_pair, int32_t* pair_pos, hipStream_t st);
+
+// Weight repack into matrix-core fragment order.  src [nmat][R][C] row-major with
+// R = reduction dim.  gate_up = 1 pairs column block j with block j + C/32 (gate and
+// up halves); gate_up = 0 pairs blocks 2j and 2j + 1.
+hipError_t launch_pack_bf16(const uint16_t* src, uint16_t* dst, int nmat, int R, int C, int gate_up,
+                            hipStream_t st);
+
+// Upper bound of the work items of a grouped GEMM for P routed pairs and T tokens
+// (row tiles of `tile_rows` times column items), known on the host without the counts.
+inline long long grouped_items_bound(int P, int E, int groups_routed, int shared_rows, int groups_shared,
+                                     int tile_rows) {
+  long long tiles = (P + tile_rows - 1) / tile_rows + (P < E ? P : E);
+  long long it = tiles * groups_routed;
+  if (shared_rows > 0) it += (long long)((shared_rows + tile_rows - 1) / tile_rows) * groups_shared;
+  return it;
+}
+
+hipError_t launch_gemm_bf16(const GroupedGemm& g, bool swiglu, long long max_items, int num_cus, hipStream_t st);
+hipError_t launch_gemm_f32(const GroupedGemm& g, bool swiglu, long long max_items, int num_cus, hipStream_t st);
+
+// y[t] = sum_j gate[t,j] * O[pair_pos[t*k+j]] (+ Os[t]) -> y (bf16 or fp32).
+hipError_t launch_combine(const float* O, const float* Os, const float* gates, const int32_t* pair_pos,
+                          int T, int k, int H, void* y, bool y_bf16, hipStream_t st);
+
+}  // namespace afd
+
+struct afd_ffn {
+  afd_ffn_config cfg;
+  int device;
+  int num_cus;
+  // repacked weights (owned)
+  void* w_gu;
+  void* w_d;
+  void* ws_gu;
+  void* ws_d;
+  size_t w_gu_expert_elems, w_d_expert_elems;
+  // workspace (owned)
+  void* h_routed;   // [P_max, M]
+  void* h_shared;   // [T_max, Ms]
+  float* o_routed;  // [P_max, H]
+  float* o_shared;  // [T_max, H]
+  unsigned* counters;  // [8] work-queue words of the GEMM launches (zeroed at create)
+  size_t device_bytes;
+  // profiling
+  bool profiling;
+  std::vector<hipEvent_t> ev_pool;
+  std::vector<int> ev_stage;  // stage of each recorded (start, stop) pair
+  size_t ev_used;
+};

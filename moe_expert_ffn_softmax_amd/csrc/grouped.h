@@ -1,0 +1,95 @@
+// Work decomposition shared by the grouped expert GEMM kernels.
+//
+// A launch covers the routed experts (segments 0..E-1, rows in expert-sorted order)
+// and optionally the shared expert (segment E, one row per token).  A work item is
+// one row tile of one segment times one 32-column group of its output.  Items are
+// numbered segment by segment, row tile by row tile, column group fastest, so items
+// handed out one after another stream neighbouring weight groups.
+//
+// Every workgroup first turns the per-expert counts into a prefix of item counts
+// over the segments (in LDS); waves then take item numbers from a device-wide queue
+// head (one atomic per item) until the queue runs dry, so the launch balances
+// itself whatever the expert load skew.  The last wave to finish resets the queue
+// words to zero for the next launch on the same stream (no memset in the stream,
+// so the launch can sit in a captured graph).
+#pragma once
+#include "afd_device.h"
+#include "afd_internal.h"
+
+namespace afd {
+
+constexpr int kMaxSegments = 1025;  // E <= 1024 routed + 1 shared
+
+struct Item {
+  int seg;       // segment (expert, or E for the shared expert)
+  bool shared;
+  int group;     // 32-column group
+  int row0;      // first row of the tile in the segment's output rows
+  int nrows;     // rows of the tile (1..tile_rows)
+};
+
+// Fill prefix[0..S] (S = number of segments) with item-count prefixes; returns the
+// total.  Needs blockDim.x / 64 + 1 ints of `scan_tmp`.  Contains __syncthreads().
+__device__ __forceinline__ int build_item_prefix(const GroupedGemm& g, int tile_rows, int* prefix, int* scan_tmp) {
+  const int S = g.E + (g.shared_rows > 0 ? 1 : 0);
+  int carry = 0;
+  for (int s0 = 0; s0 < S; s0 += blockDim.x) {
+    const int s = s0 + threadIdx.x;
+    int items = 0;
+    if (s < S) {
+      const bool sh = s >= g.E;
+      const int rows = sh ? g.shared_rows : g.counts[s];
+      items = (rows + tile_rows - 1) / tile_rows * (sh ? g.groups_shared : g.groups_routed);
+    }
+    int tot = 0;
+    const int ex = block_exclusive_scan(items, scan_tmp, &tot);
+    if (s < S) prefix[s] = carry + ex;
+    carry += tot;
+  }
+  if (threadIdx.x == 0) prefix[S] = carry;
+  __syncthreads();
+  return carry;
+}
+
+__device__ __forceinline__ Item decode_item(const GroupedGemm& g, int tile_rows, const int* prefix, int item) {
+  const int S = g.E + (g.shared_rows > 0 ? 1 : 0);
+  int lo = 0, hi = S;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (prefix[mid] <= item)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  Item it;
+  it.seg = lo;
+  it.shared = lo >= g.E;
+  const int local = item - prefix[lo];
+  const int groups = it.shared ? g.groups_shared : g.groups_routed;
+  const int tile = local / groups;
+  it.group = local - tile * groups;
+  const int rows = it.shared ? g.shared_rows : g.counts[lo];
+  it.row0 = (it.shared ? 0 : g.offsets[lo]) + tile * tile_rows;
+  it.nrows = min(tile_rows, rows - tile * tile_rows);
+  return it;
+}
+
+// Next item number for the calling wave (uniform across the wave).
+__device__ __forceinline__ int queue_next(unsigned* ctr) {
+  unsigned v = 0;
+  if (lane_id() == 0) v = atomicAdd(&ctr[0], 1u);
+  return __shfl(static_cast<int>(v), 0, kWave);
+}
+
+// Called once by every wave of the launch after its last item.
+__device__ __forceinline__ void queue_finish(unsigned* ctr, unsigned waves_in_launch) {
+  if (lane_id() == 0) {
+    const unsigned done = atomicAdd(&ctr[1], 1u);
+    if (done == waves_in_launch - 1) {
+      atomicExch(&ctr[0], 0u);
+      atomicExch(&ctr[1], 0u);
+    }
+  }
+}
+
+}  // namespace afd

@@ -1,0 +1,91 @@
+// Top-k softmax router: one wave64 per token.
+//
+// Selects, per token, the k experts with the largest fp32 logits (ties to the lower
+// expert index) and gates = their softmax probabilities renormalised over the k
+// (the router of "MoE 大规模分布式推理工程实战：从 All-to-All 通信到动态专家放置",
+// §4.1: top-k of the logits, then a softmax over the selected ones).  The softmax
+// denominator over all E cancels in the renormalisation, so the gate of slot j is
+// exp(l_j - l_0) / sum_i exp(l_i - l_0) over the selected experts, l_0 the largest.
+//
+// Selection compares raw fp32 logits through an order-preserving 64-bit key:
+// high word = the float's bits mapped to unsigned order (-0 folded onto +0, so the
+// two compare equal as in IEEE), low word = ~expert, so the larger key is the larger
+// logit and, on a tie, the lower expert.  k rounds of a wave-wide max pick the
+// experts in slot order; the lane that owns the winner retires it.
+#include "afd_device.h"
+#include "afd_internal.h"
+
+namespace afd {
+
+constexpr int kRouterMaxPerLane = 16;  // E <= 1024
+
+__device__ __forceinline__ uint32_t ordered_bits(float v) {
+  uint32_t b = __float_as_uint(v == 0.0f ? 0.0f : v);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+__device__ __forceinline__ float unordered_bits(uint32_t o) {
+  uint32_t b = (o & 0x80000000u) ? (o & 0x7fffffffu) : ~o;
+  return __uint_as_float(b);
+}
+
+template <int PER_LANE>
+__global__ void __launch_bounds__(256) router_topk_kernel(const float* __restrict__ logits, int T, int E, int k,
+                                                          int32_t* __restrict__ ids, float* __restrict__ gates) {
+  const int lane = lane_id();
+  const int t = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+  if (t >= T) return;
+  const float* row = logits + (size_t)t * E;
+  uint64_t key[PER_LANE];
+#pragma unroll
+  for (int i = 0; i < PER_LANE; ++i) {
+    const int e = lane + i * kWave;
+    key[i] = e < E ? ((uint64_t)ordered_bits(row[e]) << 32) | (uint32_t)(~(uint32_t)e) : 0ull;
+  }
+  float sel_val = 0.0f;  // lane j keeps the logit of slot j
+  int sel_id = 0;
+  float top = 0.0f;
+  for (int j = 0; j < k; ++j) {
+    uint64_t best = 0;
+#pragma unroll
+    for (int i = 0; i < PER_LANE; ++i) best = key[i] > best ? key[i] : best;
+    best = wave_max_u64(best);
+    const int e = (int)(~(uint32_t)best);
+    const float v = unordered_bits((uint32_t)(best >> 32));
+    if (j == 0) top = v;
+    if (lane == j) {
+      sel_val = v;
+      sel_id = e;
+    }
+    if ((e & (kWave - 1)) == lane) {
+#pragma unroll
+      for (int i = 0; i < PER_LANE; ++i)
+        if (i == e / kWave) key[i] = 0;
+    }
+  }
+  const float ex = lane < k ? expf(sel_val - top) : 0.0f;
+  const float sum = wave_sum_f32(ex);
+  if (lane < k) {
+    ids[(size_t)t * k + lane] = sel_id;
+    gates[(size_t)t * k + lane] = ex / sum;
+  }
+}
+
+hipError_t launch_router(const float* logits, int T, int E, int k, int32_t* ids, float* gates, hipStream_t st) {
+  if (T <= 0) return hipSuccess;
+  const int waves_per_block = 4;
+  dim3 grid((T + waves_per_block - 1) / waves_per_block), block(waves_per_block * kWave);
+  if (E <= 64)
+    router_topk_kernel<1><<<grid, block, 0, st>>>(logits, T, E, k, ids, gates);
+  else if (E <= 128)
+    router_topk_kernel<2><<<grid, block, 0, st>>>(logits, T, E, k, ids, gates);
+  else if (E <= 256)
+    router_topk_kernel<4><<<grid, block, 0, st>>>(logits, T, E, k, ids, gates);
+  else if (E <= 512)
+    router_topk_kernel<8><<<grid, block, 0, st>>>(logits, T, E, k, ids, gates);
+  else
+    router_topk_kernel<kRouterMaxPerLane><<<grid, block, 0, st>>>(logits, T, E, k, ids, gates);
+  return hipGetLastError();
+}
+
+}  // namespace afd
