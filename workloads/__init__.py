@@ -168,19 +168,20 @@ def expert_bias(w: Workload, T: Optional[int] = None) -> np.ndarray:
     raise ValueError(w.bias)
 
 
-def router_logits(w: Workload, T: Optional[int] = None, alpha: Optional[float] = None) -> np.ndarray:
-    """fp32 logits [T, E] = N(0,1) + per-expert bias (added in fp32)."""
+def router_logits(w: Workload, T: Optional[int] = None, alpha: Optional[float] = None, batch: int = 0) -> np.ndarray:
+    """fp32 logits [T, E] = N(0,1) + per-expert bias (added in fp32).  `batch` selects
+    an independent draw of the N(0,1) part (the bias is a property of the layer)."""
     T = w.T if T is None else T
-    base = _np_rng(w, _T_LOGITS).standard_normal((T, w.E), dtype=np.float32)
+    base = _np_rng(w, _T_LOGITS, batch).standard_normal((T, w.E), dtype=np.float32)
     if alpha is not None:
         w = dataclasses.replace(w, zipf_alpha=alpha)
     return (base + expert_bias(w)[None, :]).astype(np.float32)
 
 
-def tokens_f32(w: Workload, T: Optional[int] = None) -> np.ndarray:
+def tokens_f32(w: Workload, T: Optional[int] = None, batch: int = 0) -> np.ndarray:
     """Token activations x ~ N(0,1) as float32 [T, H] (before the dtype cast)."""
     T = w.T if T is None else T
-    return _np_rng(w, _T_X).standard_normal((T, w.H), dtype=np.float32)
+    return _np_rng(w, _T_X, batch).standard_normal((T, w.H), dtype=np.float32)
 
 
 # ----------------------------------------------------------------------------- tensors on a device
@@ -240,13 +241,14 @@ def make_weights(w: Workload, device="cpu"):
     return out
 
 
-def make_activations(w: Workload, device="cpu", T: Optional[int] = None):
-    """x [T,H] (float32 for f32 workloads, bfloat16 otherwise) and fp32 logits [T,E]."""
+def make_activations(w: Workload, device="cpu", T: Optional[int] = None, batch: int = 0):
+    """x [T,H] (float32 for f32 workloads, bfloat16 otherwise) and fp32 logits [T,E]
+    of batch number `batch` (batch 0 is the workload's reference batch)."""
     import torch
     T = w.T if T is None else T
-    x = torch.from_numpy(tokens_f32(w, T))
+    x = torch.from_numpy(tokens_f32(w, T, batch))
     x = x if w.dtype == "f32" else x.to(torch.bfloat16)
-    logits = torch.from_numpy(router_logits(w, T))
+    logits = torch.from_numpy(router_logits(w, T, batch=batch))
     return x.to(device), logits.to(device)
 
 
