@@ -52,7 +52,7 @@ int check_route(const afd_ffn* h, const afd_route* r, int32_t T) {
 }
 
 void release(afd_ffn* h) {
-  void* bufs[] = {h->w_gu, h->w_d, h->ws_gu, h->ws_d, h->h_routed, h->h_shared, h->o_routed, h->o_shared, h->counters};
+  void* bufs[] = {h->w_gu, h->w_d, h->ws_gu, h->ws_d, h->h_routed, h->h_shared, h->o_routed, h->o_shared};
   for (void* b : bufs)
     if (b) (void)hipFree(b);
   for (hipEvent_t e : h->ev_pool) (void)hipEventDestroy(e);
@@ -134,6 +134,16 @@ extern "C" int afd_ffn_create(const afd_ffn_config* cfg, const void* w_gate_up, 
     return hip_fail(e, "hipGetDeviceProperties");
   }
   h->num_cus = prop.multiProcessorCount;
+  {
+    int occ[4] = {0, 0, 0, 0};
+    e = afd::gemm_occupancy_bf16(&occ[0], &occ[1]);
+    if (e == hipSuccess) e = afd::gemm_occupancy_f32(&occ[2], &occ[3]);
+    if (e != hipSuccess) {
+      release(h);
+      return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
+    }
+    for (int i = 0; i < 4; ++i) h->gemm_blocks[i] = (occ[i] > 0 ? occ[i] : 1) * h->num_cus;
+  }
 
   const size_t H = cfg->hidden, M = cfg->inter, Ms = cfg->shared_inter, E = cfg->num_experts;
   const size_t P = (size_t)cfg->max_tokens * cfg->top_k, T = cfg->max_tokens;
@@ -148,7 +158,6 @@ extern "C" int afd_ffn_create(const afd_ffn_config* cfg, const void* w_gate_up, 
       {&h->w_gu, E * H * 2 * M * es},  {&h->w_d, E * M * H * es},      {&h->ws_gu, H * 2 * Ms * es},
       {&h->ws_d, Ms * H * es},         {&h->h_routed, P * M * es},     {&h->h_shared, T * Ms * es},
       {(void**)&h->o_routed, P * H * 4}, {(void**)&h->o_shared, Ms ? T * H * 4 : 0},
-      {(void**)&h->counters, 8 * sizeof(unsigned)},
   };
   for (auto& a : allocs) {
     if (a.bytes == 0) continue;
@@ -179,7 +188,6 @@ extern "C" int afd_ffn_create(const afd_ffn_config* cfg, const void* w_gate_up, 
     if (e == hipSuccess && Ms) e = hipMemcpyAsync(h->ws_gu, ws_gate_up, H * 2 * Ms * es, hipMemcpyDeviceToDevice, st);
     if (e == hipSuccess && Ms) e = hipMemcpyAsync(h->ws_d, ws_down, Ms * H * es, hipMemcpyDeviceToDevice, st);
   }
-  if (e == hipSuccess) e = hipMemsetAsync(h->counters, 0, 8 * sizeof(unsigned), st);
   if (e == hipSuccess) e = hipStreamSynchronize(st);
   if (e != hipSuccess) {
     release(h);
@@ -253,7 +261,6 @@ extern "C" int afd_ffn_forward(afd_ffn_t h, const void* x, int32_t T, const afd_
   g1.out_shared = h->h_shared;
   g1.ldo_routed = M;
   g1.ldo_shared = Ms;
-  g1.work_counter = h->counters;
 
   afd::GroupedGemm g2 = g1;
   g2.gather_routed = 0;
@@ -272,7 +279,6 @@ extern "C" int afd_ffn_forward(afd_ffn_t h, const void* x, int32_t T, const afd_
   g2.out_shared = h->o_shared;
   g2.ldo_routed = H;
   g2.ldo_shared = H;
-  g2.work_counter = h->counters + 2;
 
   const long long items1 =
       afd::grouped_items_bound(P, E, g1.groups_routed, g1.shared_rows, g1.groups_shared, afd::kTileRows);
@@ -280,15 +286,15 @@ extern "C" int afd_ffn_forward(afd_ffn_t h, const void* x, int32_t T, const afd_
       afd::grouped_items_bound(P, E, g2.groups_routed, g2.shared_rows, g2.groups_shared, afd::kTileRows);
   {
     StageScope s(h, st, AFD_STAGE_GATE_UP);
-    hipError_t e = f32 ? afd::launch_gemm_f32(g1, true, items1, h->num_cus, st)
-                       : afd::launch_gemm_bf16(g1, true, items1, h->num_cus, st);
+    hipError_t e = f32 ? afd::launch_gemm_f32(g1, true, items1, h->gemm_blocks[2], st)
+                       : afd::launch_gemm_bf16(g1, true, items1, h->gemm_blocks[0], st);
     if (e != hipSuccess) return hip_fail(e, "gate/up GEMM launch");
     s.done();
   }
   {
     StageScope s(h, st, AFD_STAGE_DOWN);
-    hipError_t e = f32 ? afd::launch_gemm_f32(g2, false, items2, h->num_cus, st)
-                       : afd::launch_gemm_bf16(g2, false, items2, h->num_cus, st);
+    hipError_t e = f32 ? afd::launch_gemm_f32(g2, false, items2, h->gemm_blocks[3], st)
+                       : afd::launch_gemm_bf16(g2, false, items2, h->gemm_blocks[1], st);
     if (e != hipSuccess) return hip_fail(e, "down GEMM launch");
     s.done();
   }

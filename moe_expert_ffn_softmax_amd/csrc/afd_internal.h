@@ -49,8 +49,6 @@ struct GroupedGemm {
   float* outs_routed;           // fp8: per-row per-128 scales of the output, else null
   float* outs_shared;
   int ldo_routed, ldo_shared;   // output row stride (elements)
-  unsigned* work_counter;       // 2 zeroed words: item queue head, finished waves;
-                                // the last wave of a launch resets both to 0
 };
 
 hipError_t launch_router(const float* logits, int T, int E, int k, int32_t* ids, float* gates,
@@ -74,8 +72,13 @@ inline long long grouped_items_bound(int P, int E, int groups_routed, int shared
   return it;
 }
 
-hipError_t launch_gemm_bf16(const GroupedGemm& g, bool swiglu, long long max_items, int num_cus, hipStream_t st);
-hipError_t launch_gemm_f32(const GroupedGemm& g, bool swiglu, long long max_items, int num_cus, hipStream_t st);
+// Persistent grids: `max_items` bounds the work items, `max_blocks` is the number of
+// workgroups the device keeps resident at once (from the occupancy query at create).
+hipError_t launch_gemm_bf16(const GroupedGemm& g, bool swiglu, long long max_items, int max_blocks, hipStream_t st);
+hipError_t launch_gemm_f32(const GroupedGemm& g, bool swiglu, long long max_items, int max_blocks, hipStream_t st);
+// Resident workgroups per compute unit of the GEMM kernels.
+hipError_t gemm_occupancy_bf16(int* gate_up, int* down);
+hipError_t gemm_occupancy_f32(int* gate_up, int* down);
 
 // y[t] = sum_j gate[t,j] * O[pair_pos[t*k+j]] (+ Os[t]) -> y (bf16 or fp32).
 hipError_t launch_combine(const float* O, const float* Os, const float* gates, const int32_t* pair_pos,
@@ -98,7 +101,7 @@ struct afd_ffn {
   void* h_shared;   // [T_max, Ms]
   float* o_routed;  // [P_max, H]
   float* o_shared;  // [T_max, H]
-  unsigned* counters;  // [8] work-queue words of the GEMM launches (zeroed at create)
+  int gemm_blocks[4];  // resident workgroups of each GEMM kernel on the whole device
   size_t device_bytes;
   // profiling
   bool profiling;

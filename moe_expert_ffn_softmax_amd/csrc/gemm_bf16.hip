@@ -8,7 +8,7 @@
 // 32 output columns over the whole reduction, streaming that column group's
 // pre-packed weight fragments straight from HBM into registers: every lane issues
 // 16-byte loads that together cover contiguous 1 KiB fragments, two fragments per
-// 32-deep step, double-buffered four steps ahead, and each fragment feeds one
+// 32-deep step, loaded eight steps ahead of use (nontemporal), and each fragment feeds one
 // v_mfma_f32_16x16x32_bf16 directly (no LDS round trip: each weight byte is used by
 // exactly one wave).  The 16 activation rows of the tile are gathered through the
 // expert-sorted pair order (tokens of x for the gate/up projection, intermediate
@@ -27,7 +27,43 @@ namespace afd {
 
 constexpr int kGemmThreads = 256;
 constexpr int kGemmWaves = kGemmThreads / kWave;
-constexpr int kStepsAhead = 4;  // 32-deep reduction steps per prefetch batch
+
+// Weight fragments are read exactly once per launch: load them nontemporally so they
+// stream past the caches instead of evicting the activation rows every wave re-reads.
+__device__ __forceinline__ bf16x8 load_weight_frag(const i32x4* p) {
+  return __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(p));
+}
+
+// acc0/acc1 += A[16 x K] * B[K x 32] over K = 32 * KB, with the loads of step s + D
+// issued while step s computes (a rotating register pipeline; no branch inside, so
+// the compiler waits only for the oldest outstanding loads).  KB % D == 0, KB >= D.
+template <int D>
+__device__ __forceinline__ void stream_mfma(const bf16x8* __restrict__ A, const i32x4* __restrict__ B, int KB,
+                                            f32x4& acc0, f32x4& acc1) {
+  bf16x8 a[D], b0[D], b1[D];
+#pragma unroll
+  for (int u = 0; u < D; ++u) {
+    a[u] = A[u * 4];
+    b0[u] = load_weight_frag(B + (u * 2) * 64);
+    b1[u] = load_weight_frag(B + (u * 2 + 1) * 64);
+  }
+  for (int s0 = D; s0 < KB; s0 += D) {
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], b0[u], acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], b1[u], acc1, 0, 0, 0);
+      const int s = s0 + u;
+      a[u] = A[s * 4];
+      b0[u] = load_weight_frag(B + (s * 2) * 64);
+      b1[u] = load_weight_frag(B + (s * 2 + 1) * 64);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < D; ++u) {
+    acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], b0[u], acc0, 0, 0, 0);
+    acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], b1[u], acc1, 0, 0, 0);
+  }
+}
 
 template <bool SWIGLU>
 __global__ void __launch_bounds__(kGemmThreads) gemm_bf16_stream_kernel(GroupedGemm g) {
@@ -35,9 +71,10 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_bf16_stream_kernel(GroupedG
   __shared__ int scan_tmp[kGemmWaves + 1];
   const int total = build_item_prefix(g, kTileRows, prefix, scan_tmp);
   const int lane = lane_id();
-  const unsigned waves_in_launch = gridDim.x * kGemmWaves;
+  const int waves_in_launch = gridDim.x * kGemmWaves;
+  const int wave = blockIdx.x * kGemmWaves + threadIdx.x / kWave;
 
-  for (int item = queue_next(g.work_counter); item < total; item = queue_next(g.work_counter)) {
+  for (int item = wave; item < total; item += waves_in_launch) {
     const Item it = decode_item(g, kTileRows, prefix, item);
     const int K = it.shared ? g.K_shared : g.K_routed;
     const int KB = K / 32;
@@ -56,49 +93,13 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_bf16_stream_kernel(GroupedG
                       (lane >> 4);
     const __bf16* wbase = it.shared ? static_cast<const __bf16*>(g.w_shared)
                                     : static_cast<const __bf16*>(g.w_routed) + (size_t)it.seg * g.w_expert_elems;
-    const bf16x8* B = reinterpret_cast<const bf16x8*>(wbase) + (size_t)it.group * KB * 128 + lane;
+    const i32x4* B = reinterpret_cast<const i32x4*>(wbase) + (size_t)it.group * KB * 128 + lane;
 
     f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-    bf16x8 a_cur[kStepsAhead], b0_cur[kStepsAhead], b1_cur[kStepsAhead];
-    bf16x8 a_nxt[kStepsAhead], b0_nxt[kStepsAhead], b1_nxt[kStepsAhead];
-#pragma unroll
-    for (int u = 0; u < kStepsAhead; ++u) {
-      a_cur[u] = A[u * 4];
-      b0_cur[u] = B[(u * 2) * 64];
-      b1_cur[u] = B[(u * 2 + 1) * 64];
-    }
-    for (int kb = 0; kb < KB; kb += 2 * kStepsAhead) {
-      const int kn = kb + kStepsAhead;
-      if (kn < KB) {
-#pragma unroll
-        for (int u = 0; u < kStepsAhead; ++u) {
-          a_nxt[u] = A[(kn + u) * 4];
-          b0_nxt[u] = B[((kn + u) * 2) * 64];
-          b1_nxt[u] = B[((kn + u) * 2 + 1) * 64];
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < kStepsAhead; ++u) {
-        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_cur[u], b0_cur[u], acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_cur[u], b1_cur[u], acc1, 0, 0, 0);
-      }
-      if (kn < KB) {
-        const int kc = kn + kStepsAhead;
-        if (kc < KB) {
-#pragma unroll
-          for (int u = 0; u < kStepsAhead; ++u) {
-            a_cur[u] = A[(kc + u) * 4];
-            b0_cur[u] = B[((kc + u) * 2) * 64];
-            b1_cur[u] = B[((kc + u) * 2 + 1) * 64];
-          }
-        }
-#pragma unroll
-        for (int u = 0; u < kStepsAhead; ++u) {
-          acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_nxt[u], b0_nxt[u], acc0, 0, 0, 0);
-          acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_nxt[u], b1_nxt[u], acc1, 0, 0, 0);
-        }
-      }
-    }
+    if (KB % 8 == 0)
+      stream_mfma<8>(A, B, KB, acc0, acc1);
+    else
+      stream_mfma<4>(A, B, KB, acc0, acc1);
 
     const int col = lane & 15;
     const int rbase = (lane >> 4) * 4;
@@ -125,15 +126,14 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_bf16_stream_kernel(GroupedG
       }
     }
   }
-  queue_finish(g.work_counter, waves_in_launch);
 }
 
-hipError_t launch_gemm_bf16(const GroupedGemm& g, bool swiglu, long long max_items, int num_cus, hipStream_t st) {
+hipError_t launch_gemm_bf16(const GroupedGemm& g, bool swiglu, long long max_items, int max_blocks, hipStream_t st) {
   if (max_items <= 0) return hipSuccess;
-  // persistent grid: up to 4 workgroups (16 waves) per compute unit
+  // persistent grid of resident workgroups only: a workgroup that waits for a free
+  // slot would start its items a whole item late
   long long blocks = (max_items + kGemmWaves - 1) / kGemmWaves;
-  const long long cap = (long long)num_cus * 4;
-  if (blocks > cap) blocks = cap;
+  if (blocks > max_blocks) blocks = max_blocks;
   if (swiglu)
     gemm_bf16_stream_kernel<true><<<(unsigned)blocks, kGemmThreads, 0, st>>>(g);
   else
@@ -141,4 +141,13 @@ hipError_t launch_gemm_bf16(const GroupedGemm& g, bool swiglu, long long max_ite
   return hipGetLastError();
 }
 
+}  // namespace afd
+
+namespace afd {
+hipError_t gemm_occupancy_bf16(int* gate_up, int* down) {
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(gate_up, gemm_bf16_stream_kernel<true>, kGemmThreads, 0);
+  if (e == hipSuccess)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(down, gemm_bf16_stream_kernel<false>, kGemmThreads, 0);
+  return e;
+}
 }  // namespace afd

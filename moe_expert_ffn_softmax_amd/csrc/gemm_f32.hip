@@ -1,7 +1,7 @@
 // Grouped expert GEMMs in fp32 on the vector ALUs (the all-fp32 layer).
 //
 // Same work items as the bf16 kernels (16-row tile of one expert's rows times a
-// 32-column group, from the shared device-side queue), on weights in their natural
+// 32-column group, statically strided over the waves), on weights in their natural
 // row-major layout.  fp32 matrix-core throughput equals the fp32 vector peak on
 // gfx950, so plain FMAs lose nothing here.  Lane l owns column (l % 16) of each
 // 16-column block and rows (l / 16) * 4 .. + 3 of the tile.
@@ -18,9 +18,10 @@ __global__ void __launch_bounds__(kF32Threads) gemm_f32_kernel(GroupedGemm g) {
   __shared__ int scan_tmp[kF32Waves + 1];
   const int total = build_item_prefix(g, kTileRows, prefix, scan_tmp);
   const int lane = lane_id();
-  const unsigned waves_in_launch = gridDim.x * kF32Waves;
+  const int waves_in_launch = gridDim.x * kF32Waves;
+  const int wave = blockIdx.x * kF32Waves + threadIdx.x / kWave;
 
-  for (int item = queue_next(g.work_counter); item < total; item = queue_next(g.work_counter)) {
+  for (int item = wave; item < total; item += waves_in_launch) {
     const Item it = decode_item(g, kTileRows, prefix, item);
     const int K = it.shared ? g.K_shared : g.K_routed;
     const int lda = it.shared ? g.lda_shared : g.lda_routed;
@@ -71,14 +72,12 @@ __global__ void __launch_bounds__(kF32Threads) gemm_f32_kernel(GroupedGemm g) {
       }
     }
   }
-  queue_finish(g.work_counter, waves_in_launch);
 }
 
-hipError_t launch_gemm_f32(const GroupedGemm& g, bool swiglu, long long max_items, int num_cus, hipStream_t st) {
+hipError_t launch_gemm_f32(const GroupedGemm& g, bool swiglu, long long max_items, int max_blocks, hipStream_t st) {
   if (max_items <= 0) return hipSuccess;
   long long blocks = (max_items + kF32Waves - 1) / kF32Waves;
-  const long long cap = (long long)num_cus * 4;
-  if (blocks > cap) blocks = cap;
+  if (blocks > max_blocks) blocks = max_blocks;
   if (swiglu)
     gemm_f32_kernel<true><<<(unsigned)blocks, kF32Threads, 0, st>>>(g);
   else
@@ -86,4 +85,12 @@ hipError_t launch_gemm_f32(const GroupedGemm& g, bool swiglu, long long max_item
   return hipGetLastError();
 }
 
+}  // namespace afd
+
+namespace afd {
+hipError_t gemm_occupancy_f32(int* gate_up, int* down) {
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(gate_up, gemm_f32_kernel<true>, kF32Threads, 0);
+  if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(down, gemm_f32_kernel<false>, kF32Threads, 0);
+  return e;
+}
 }  // namespace afd

@@ -7,11 +7,11 @@
 // handed out one after another stream neighbouring weight groups.
 //
 // Every workgroup first turns the per-expert counts into a prefix of item counts
-// over the segments (in LDS); waves then take item numbers from a device-wide queue
-// head (one atomic per item) until the queue runs dry, so the launch balances
-// itself whatever the expert load skew.  The last wave to finish resets the queue
-// words to zero for the next launch on the same stream (no memset in the stream,
-// so the launch can sit in a captured graph).
+// over the segments (in LDS); wave w of the launch then takes items w, w + W,
+// w + 2W, ... (W waves in the grid, all resident).  Items of one launch stream
+// equal amounts of weights, so static striding balances them; a shared atomic
+// queue head was measured slower (thousands of waves contending for one word
+// cost more than the imbalance it removes).
 #pragma once
 #include "afd_device.h"
 #include "afd_internal.h"
@@ -72,24 +72,6 @@ __device__ __forceinline__ Item decode_item(const GroupedGemm& g, int tile_rows,
   it.row0 = (it.shared ? 0 : g.offsets[lo]) + tile * tile_rows;
   it.nrows = min(tile_rows, rows - tile * tile_rows);
   return it;
-}
-
-// Next item number for the calling wave (uniform across the wave).
-__device__ __forceinline__ int queue_next(unsigned* ctr) {
-  unsigned v = 0;
-  if (lane_id() == 0) v = atomicAdd(&ctr[0], 1u);
-  return __shfl(static_cast<int>(v), 0, kWave);
-}
-
-// Called once by every wave of the launch after its last item.
-__device__ __forceinline__ void queue_finish(unsigned* ctr, unsigned waves_in_launch) {
-  if (lane_id() == 0) {
-    const unsigned done = atomicAdd(&ctr[1], 1u);
-    if (done == waves_in_launch - 1) {
-      atomicExch(&ctr[0], 0u);
-      atomicExch(&ctr[1], 0u);
-    }
-  }
 }
 
 }  // namespace afd
