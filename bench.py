@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--workload", default=workloads.STARVED_DECODE.name)
     ap.add_argument("--batches", type=int, default=16, help="distinct resident batches cycled over the steps")
     ap.add_argument("--graph", action="store_true", help="replay route+forward from a captured HIP graph")
+    ap.add_argument("--gemm", default="auto", choices=["auto", "stream", "tiled"],
+                    help="grouped-GEMM kernel: automatic choice, 16-row streaming tiles or 128-row tiles")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true")
@@ -163,6 +165,7 @@ def main():
                          w_gate_up=weights["w_gu"], w_down=weights["w_d"], s_gate_up=weights["s_gu"],
                          s_down=weights["s_d"], shared_inter=w.Ms, ws_gate_up=weights["ws_gu"],
                          ws_down=weights["ws_d"], ss_gate_up=weights["ss_gu"], ss_down=weights["ss_d"])
+    layer.set_gemm_kernel(args.gemm)
     nb = max(1, args.batches)
     xs, lgs = [], []
     for b in range(nb):
@@ -256,7 +259,7 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "T": w.T, "H": w.H, "M": w.M, "E": w.E, "top_k": w.k, "shared_inter": w.Ms,
-                   "batches": nb, "launch": "hip_graph" if graphs is not None else "eager"},
+                   "batches": nb, "launch": "hip_graph" if graphs is not None else "eager", "gemm": args.gemm},
         "tflops": round(tflops, 3),
         "step_hbm": {"algorithmic_bytes": int(step_bytes), "touched_experts": round(float(touched), 2),
                      "achieved_GBps": round(step_bytes / (ms_per_step / 1e3) / 1e9, 1),

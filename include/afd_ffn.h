@@ -132,6 +132,14 @@ const char* afd_ffn_last_error(void);
 /* Device bytes the handle owns (repacked weights plus workspace). */
 size_t afd_ffn_device_bytes(afd_ffn_t h);
 
+/* Choice of grouped-GEMM kernel for bf16 layers.  AFD_GEMM_AUTO (the default)
+ * uses 16-row weight-streaming tiles while experts average at most 16 routed rows
+ * per batch (T * top_k <= 16 * E) and 128-row tiles above that; the other values
+ * force one kernel (results agree to rounding; a tuning and testing knob).  fp32
+ * layers always use their own kernel.  Takes effect for later forward calls. */
+typedef enum afd_gemm_kernel { AFD_GEMM_AUTO = 0, AFD_GEMM_STREAM = 1, AFD_GEMM_TILED = 2 } afd_gemm_kernel;
+int afd_ffn_set_gemm_kernel(afd_ffn_t h, int kernel);
+
 /* Per-kernel timing.  With profiling on, route and forward bracket each kernel
  * with HIP events on the launch stream.  afd_ffn_profile_read synchronises on the
  * recorded events, writes the summed milliseconds and launch counts of each stage

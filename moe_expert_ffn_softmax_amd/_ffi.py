@@ -12,6 +12,7 @@ LIB_PATH = os.path.join(_PKG, "libafd_ffn.so")
 
 AFD_OK, AFD_EINVAL, AFD_EUNSUPPORTED, AFD_ENOMEM, AFD_EHIP = 0, -1, -2, -3, -4
 AFD_F32, AFD_BF16, AFD_FP8_E4M3 = 0, 1, 2
+AFD_GEMM_AUTO, AFD_GEMM_STREAM, AFD_GEMM_TILED = 0, 1, 2
 STAGES = ("router", "permute", "quant_x", "gate_up", "down", "combine")
 AFD_NUM_STAGES = len(STAGES)
 
@@ -59,6 +60,8 @@ def load():
     lib.afd_ffn_last_error.restype = ctypes.c_char_p
     lib.afd_ffn_device_bytes.argtypes = [V]
     lib.afd_ffn_device_bytes.restype = ctypes.c_size_t
+    lib.afd_ffn_set_gemm_kernel.argtypes = [V, ctypes.c_int]
+    lib.afd_ffn_set_gemm_kernel.restype = ctypes.c_int
     lib.afd_ffn_set_profiling.argtypes = [V, ctypes.c_int]
     lib.afd_ffn_set_profiling.restype = ctypes.c_int
     lib.afd_ffn_profile_read.argtypes = [V, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64),
@@ -112,6 +115,10 @@ def afd_ffn_destroy(h: int) -> None:
 
 def afd_ffn_device_bytes(h: int) -> int:
     return int(load().afd_ffn_device_bytes(h))
+
+
+def afd_ffn_set_gemm_kernel(h: int, kernel: int) -> None:
+    _check(load().afd_ffn_set_gemm_kernel(h, int(kernel)))
 
 
 def afd_ffn_set_profiling(h: int, on: bool) -> None:

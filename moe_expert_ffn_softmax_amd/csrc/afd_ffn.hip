@@ -89,6 +89,14 @@ struct StageScope {
   }
 };
 
+// Kernel choice for a batch of P routed pairs: the 128-row tiled GEMM once experts
+// average more than 16 rows (one streaming tile), unless forced either way.
+bool use_tiled(const afd_ffn* h, int P) {
+  if (h->gemm_mode == 1) return false;
+  if (h->gemm_mode == 2) return true;
+  return (long long)P > 16ll * h->cfg.num_experts;
+}
+
 }  // namespace
 
 extern "C" const char* afd_ffn_strerror(int code) {
@@ -280,21 +288,33 @@ extern "C" int afd_ffn_forward(afd_ffn_t h, const void* x, int32_t T, const afd_
   g2.ldo_routed = H;
   g2.ldo_shared = H;
 
-  const long long items1 =
-      afd::grouped_items_bound(P, E, g1.groups_routed, g1.shared_rows, g1.groups_shared, afd::kTileRows);
-  const long long items2 =
-      afd::grouped_items_bound(P, E, g2.groups_routed, g2.shared_rows, g2.groups_shared, afd::kTileRows);
+  // Few rows per expert (decode batches): 16-row weight-streaming tiles.  Many rows:
+  // 128-row tiles, so each expert's weights are read once per 128 of its rows.
+  const bool tiled = !f32 && use_tiled(h, P);
+  long long items1, items2;
+  if (tiled) {
+    const int tr = afd::tiled_rows(), tg = afd::tiled_groups();
+    items1 = afd::grouped_items_bound(P, E, (g1.groups_routed + tg - 1) / tg, g1.shared_rows,
+                                      (g1.groups_shared + tg - 1) / tg, tr);
+    items2 = afd::grouped_items_bound(P, E, (g2.groups_routed + tg - 1) / tg, g2.shared_rows,
+                                      (g2.groups_shared + tg - 1) / tg, tr);
+  } else {
+    items1 = afd::grouped_items_bound(P, E, g1.groups_routed, g1.shared_rows, g1.groups_shared, afd::kTileRows);
+    items2 = afd::grouped_items_bound(P, E, g2.groups_routed, g2.shared_rows, g2.groups_shared, afd::kTileRows);
+  }
   {
     StageScope s(h, st, AFD_STAGE_GATE_UP);
-    hipError_t e = f32 ? afd::launch_gemm_f32(g1, true, items1, h->gemm_blocks[2], st)
-                       : afd::launch_gemm_bf16(g1, true, items1, h->gemm_blocks[0], st);
+    hipError_t e = f32     ? afd::launch_gemm_f32(g1, true, items1, h->gemm_blocks[2], st)
+                   : tiled ? afd::launch_gemm_bf16_tiled(g1, true, items1, h->num_cus, st)
+                           : afd::launch_gemm_bf16(g1, true, items1, h->gemm_blocks[0], st);
     if (e != hipSuccess) return hip_fail(e, "gate/up GEMM launch");
     s.done();
   }
   {
     StageScope s(h, st, AFD_STAGE_DOWN);
-    hipError_t e = f32 ? afd::launch_gemm_f32(g2, false, items2, h->gemm_blocks[3], st)
-                       : afd::launch_gemm_bf16(g2, false, items2, h->gemm_blocks[1], st);
+    hipError_t e = f32     ? afd::launch_gemm_f32(g2, false, items2, h->gemm_blocks[3], st)
+                   : tiled ? afd::launch_gemm_bf16_tiled(g2, false, items2, h->num_cus, st)
+                           : afd::launch_gemm_bf16(g2, false, items2, h->gemm_blocks[1], st);
     if (e != hipSuccess) return hip_fail(e, "down GEMM launch");
     s.done();
   }
@@ -305,6 +325,13 @@ extern "C" int afd_ffn_forward(afd_ffn_t h, const void* x, int32_t T, const afd_
     if (e != hipSuccess) return hip_fail(e, "combine launch");
     s.done();
   }
+  return AFD_OK;
+}
+
+extern "C" int afd_ffn_set_gemm_kernel(afd_ffn_t h, int kernel) {
+  if (!h) return fail(AFD_EINVAL, "handle is NULL");
+  if (kernel < AFD_GEMM_AUTO || kernel > AFD_GEMM_TILED) return fail(AFD_EINVAL, "unknown GEMM kernel %d", kernel);
+  h->gemm_mode = kernel;
   return AFD_OK;
 }
 

@@ -76,6 +76,13 @@ inline long long grouped_items_bound(int P, int E, int groups_routed, int shared
 // workgroups the device keeps resident at once (from the occupancy query at create).
 hipError_t launch_gemm_bf16(const GroupedGemm& g, bool swiglu, long long max_items, int max_blocks, hipStream_t st);
 hipError_t launch_gemm_f32(const GroupedGemm& g, bool swiglu, long long max_items, int max_blocks, hipStream_t st);
+// Large-tile variant (128-row tiles, 8 column groups per item) for experts with many
+// rows; `max_blocks` as above.
+hipError_t launch_gemm_bf16_tiled(const GroupedGemm& g, bool swiglu, long long max_items, int max_blocks,
+                                  hipStream_t st);
+int tiled_rows();
+int tiled_groups();
+
 // Resident workgroups per compute unit of the GEMM kernels.
 hipError_t gemm_occupancy_bf16(int* gate_up, int* down);
 hipError_t gemm_occupancy_f32(int* gate_up, int* down);
@@ -102,6 +109,7 @@ struct afd_ffn {
   float* o_routed;  // [P_max, H]
   float* o_shared;  // [T_max, H]
   int gemm_blocks[4];  // resident workgroups of each GEMM kernel on the whole device
+  int gemm_mode;       // 0 automatic, 1 always 16-row streaming, 2 always 128-row tiles
   size_t device_bytes;
   // profiling
   bool profiling;

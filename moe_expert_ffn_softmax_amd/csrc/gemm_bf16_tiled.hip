@@ -1,0 +1,232 @@
+// Grouped expert GEMMs in bf16 on the gfx950 matrix cores, large-tile form, for
+// batches where experts receive many tokens (an FFN instance aggregating several
+// attention instances' batches: "大模型推理的内存与计算解耦：AFD 架构解析与性能验证",
+// §2, and the MegaScale-Infer summary in "AF分离论文串讲").
+//
+// A workgroup of 4 waves computes a 128-row tile of one expert's rows times 8
+// 32-column groups; wave w owns groups 2w and 2w+1 (4 16-column blocks) for all 128
+// rows, i.e. 8 x 4 accumulators of v_mfma_f32_16x16x32_bf16.  Each weight fragment
+// is used by exactly one wave, so weights stream straight from HBM into registers
+// (fragment order, 4 reduction steps ahead, as in the weight-streaming kernel); the
+// 128 gathered activation rows are shared by the 4 waves and staged through LDS in
+// MFMA A-operand order, one K-chunk at a time, double-buffered: the next chunk's
+// global loads are issued before the current chunk is consumed.
+//
+// Items are (segment, column tile, row tile) with the row tile fastest, and the item
+// list is cut into 8 contiguous ranges, one per XCD (workgroup b runs on XCD b % 8):
+// the row tiles of a hot expert and the neighbouring column tiles run at the same
+// time on one XCD and share its L2 for the weights and the activation rows.
+#include "grouped.h"
+
+namespace afd {
+
+constexpr int kTiledThreads = 256;
+constexpr int kTiledWaves = 4;
+constexpr int kTiledRowBlocks = 8;                      // 16-row blocks per tile
+constexpr int kTiledRows = 16 * kTiledRowBlocks;        // 128
+constexpr int kTiledGroupsPerWave = 2;                  // 32-column groups per wave
+constexpr int kTiledGroups = kTiledWaves * kTiledGroupsPerWave;  // per item
+constexpr int kTiledBAhead = 4;                         // weight steps in flight per wave
+constexpr int kXcds = 8;
+
+template <int KC>
+struct TiledSmem {
+  // [buffer][step in chunk][row block][lane] 16-byte A fragments
+  bf16x8 a[2][KC][kTiledRowBlocks][kWave];
+};
+
+__device__ __forceinline__ bf16x8 tiled_load_b(const i32x4* p) {
+  return __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(p));
+}
+
+template <bool SWIGLU, int KC>
+__global__ void __launch_bounds__(kTiledThreads, 1) gemm_bf16_tiled_kernel(GroupedGemm g) {
+  __shared__ int prefix[kMaxSegments + 1];
+  __shared__ int scan_tmp[kTiledWaves + 1];
+  extern __shared__ __attribute__((aligned(16))) unsigned char dyn_smem[];
+  TiledSmem<KC>& sm = *reinterpret_cast<TiledSmem<KC>*>(dyn_smem);
+
+  const int total = build_item_prefix(g, kTiledRows, kTiledGroups, prefix, scan_tmp);
+  const int lane = lane_id();
+  const int w = threadIdx.x / kWave;
+
+  // XCD-aware striding: this workgroup's XCD owns a contiguous range of items
+  const int xcd = blockIdx.x % kXcds;
+  const int slot = blockIdx.x / kXcds;
+  const int slots = gridDim.x / kXcds;
+  const int begin = (int)((long long)total * xcd / kXcds);
+  const int end = (int)((long long)total * (xcd + 1) / kXcds);
+
+  for (int item = begin + slot; item < end; item += slots) {
+    const Item it = decode_item_tiled(g, kTiledRows, kTiledGroups, prefix, item);
+    const int K = it.shared ? g.K_shared : g.K_routed;
+    const int KB = K / 32;
+    const int NC = KB / KC;
+    const int groups = it.shared ? g.groups_shared : g.groups_routed;
+    const int group0 = it.group + w * kTiledGroupsPerWave;  // first group of this wave
+    const bool active = group0 < groups;                    // wave-uniform
+
+    // this lane's two A rows (row blocks 2w and 2w+1), clamped into the tile
+    const int lda = it.shared ? g.lda_shared : g.lda_routed;
+    const __bf16* abase = static_cast<const __bf16*>(it.shared ? g.a_shared : g.a_routed);
+    const bf16x8* arow[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      int r = (2 * w + j) * 16 + (lane & 15);
+      r = r < it.nrows ? r : 0;
+      int ar;
+      if (it.shared)
+        ar = it.row0 + r;
+      else
+        ar = g.gather_routed ? g.sorted_pair[it.row0 + r] / g.k : it.row0 + r;
+      arow[j] = reinterpret_cast<const bf16x8*>(abase + (size_t)ar * lda) + (lane >> 4);
+    }
+    // weights of this wave: groups group0, group0 + 1, each [KB][2 halves][64 lanes]
+    const __bf16* wbase = it.shared ? static_cast<const __bf16*>(g.w_shared)
+                                    : static_cast<const __bf16*>(g.w_routed) + (size_t)it.seg * g.w_expert_elems;
+    const i32x4* B = reinterpret_cast<const i32x4*>(wbase) + (size_t)(active ? group0 : 0) * KB * 128 + lane;
+    const size_t group_stride = (size_t)KB * 128;
+
+    f32x4 acc[kTiledRowBlocks][4];
+#pragma unroll
+    for (int rb = 0; rb < kTiledRowBlocks; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // weight ring: step s lives in slot s % kTiledBAhead
+    bf16x8 bring[kTiledBAhead][4];
+    if (active) {
+#pragma unroll
+      for (int u = 0; u < kTiledBAhead; ++u)
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+          bring[u][cb] = tiled_load_b(B + (cb >> 1) * group_stride + (u * 2 + (cb & 1)) * 64);
+    }
+
+    // A chunk 0 -> LDS buffer 0, chunk 1 -> staging registers
+    bf16x8 stage[2][KC];
+#pragma unroll
+    for (int u = 0; u < KC; ++u)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) stage[j][u] = arow[j][u * 4];
+#pragma unroll
+    for (int u = 0; u < KC; ++u)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) sm.a[0][u][2 * w + j][lane] = stage[j][u];
+    if (NC > 1) {
+#pragma unroll
+      for (int u = 0; u < KC; ++u)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) stage[j][u] = arow[j][(KC + u) * 4];
+    }
+    __syncthreads();
+
+    for (int c = 0; c < NC; ++c) {
+      const int buf = c & 1;
+      if (active) {
+#pragma unroll
+        for (int u = 0; u < KC; ++u) {
+          const int slotb = u % kTiledBAhead;
+          bf16x8 a[kTiledRowBlocks];
+#pragma unroll
+          for (int rb = 0; rb < kTiledRowBlocks; ++rb) a[rb] = sm.a[buf][u][rb][lane];
+#pragma unroll
+          for (int rb = 0; rb < kTiledRowBlocks; ++rb)
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb)
+              acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[rb], bring[slotb][cb], acc[rb][cb], 0, 0, 0);
+          // refill this ring slot with the step kTiledBAhead ahead (clamped to the last)
+          int s = c * KC + u + kTiledBAhead;
+          s = s < KB ? s : KB - 1;
+#pragma unroll
+          for (int cb = 0; cb < 4; ++cb)
+            bring[slotb][cb] = tiled_load_b(B + (cb >> 1) * group_stride + (s * 2 + (cb & 1)) * 64);
+        }
+      }
+      if (c + 1 < NC) {
+#pragma unroll
+        for (int u = 0; u < KC; ++u)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) sm.a[buf ^ 1][u][2 * w + j][lane] = stage[j][u];
+      }
+      __syncthreads();
+      if (c + 2 < NC) {
+#pragma unroll
+        for (int u = 0; u < KC; ++u)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) stage[j][u] = arow[j][((c + 2) * KC + u) * 4];
+      }
+    }
+
+    if (active) {
+      const int col = lane & 15;
+      const int rsub = (lane >> 4) * 4;
+      if (SWIGLU) {
+        __bf16* out = static_cast<__bf16*>(it.shared ? g.out_shared : g.out_routed);
+        const int ldo = it.shared ? g.ldo_shared : g.ldo_routed;
+#pragma unroll
+        for (int gi = 0; gi < kTiledGroupsPerWave; ++gi) {
+          if (group0 + gi >= groups) break;
+#pragma unroll
+          for (int rb = 0; rb < kTiledRowBlocks; ++rb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int row = rb * 16 + rsub + i;
+              if (row < it.nrows)
+                out[(size_t)(it.row0 + row) * ldo + (group0 + gi) * 16 + col] =
+                    f32_to_bf16(silu(acc[rb][2 * gi][i]) * acc[rb][2 * gi + 1][i]);
+            }
+        }
+      } else {
+        float* out = static_cast<float*>(it.shared ? g.out_shared : g.out_routed);
+        const int ldo = it.shared ? g.ldo_shared : g.ldo_routed;
+#pragma unroll
+        for (int gi = 0; gi < kTiledGroupsPerWave; ++gi) {
+          if (group0 + gi >= groups) break;
+#pragma unroll
+          for (int rb = 0; rb < kTiledRowBlocks; ++rb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int row = rb * 16 + rsub + i;
+              if (row < it.nrows) {
+                float* o = out + (size_t)(it.row0 + row) * ldo + (group0 + gi) * 32 + col;
+                o[0] = acc[rb][2 * gi][i];
+                o[16] = acc[rb][2 * gi + 1][i];
+              }
+            }
+        }
+      }
+    }
+    // the next item's first LDS writes must not overtake this item's last reads
+    __syncthreads();
+  }
+}
+
+template <bool SWIGLU, int KC>
+static hipError_t launch_tiled(const GroupedGemm& g, long long max_items, int max_blocks, hipStream_t st) {
+  const size_t smem = sizeof(TiledSmem<KC>);
+  static bool configured = false;  // raise the dynamic LDS limit once per process
+  if (!configured) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_bf16_tiled_kernel<SWIGLU, KC>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (e != hipSuccess) return e;
+    configured = true;
+  }
+  long long blocks = max_items < max_blocks ? max_items : max_blocks;
+  blocks = blocks < kXcds ? kXcds : blocks / kXcds * kXcds;
+  gemm_bf16_tiled_kernel<SWIGLU, KC><<<(unsigned)blocks, kTiledThreads, smem, st>>>(g);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_bf16_tiled(const GroupedGemm& g, bool swiglu, long long max_items, int max_blocks,
+                                  hipStream_t st) {
+  if (max_items <= 0) return hipSuccess;
+  // 4-step (128-deep) activation chunks: every K here is a multiple of 128, and an
+  // 8-step chunk's staging registers spill
+  return swiglu ? launch_tiled<true, 4>(g, max_items, max_blocks, st) : launch_tiled<false, 4>(g, max_items, max_blocks, st);
+}
+
+int tiled_rows() { return kTiledRows; }
+int tiled_groups() { return kTiledGroups; }
+
+}  // namespace afd

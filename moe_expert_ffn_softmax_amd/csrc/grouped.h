@@ -2,9 +2,7 @@
 //
 // A launch covers the routed experts (segments 0..E-1, rows in expert-sorted order)
 // and optionally the shared expert (segment E, one row per token).  A work item is
-// one row tile of one segment times one 32-column group of its output.  Items are
-// numbered segment by segment, row tile by row tile, column group fastest, so items
-// handed out one after another stream neighbouring weight groups.
+// one row tile of one segment times one or more 32-column groups of its output.
 //
 // Every workgroup first turns the per-expert counts into a prefix of item counts
 // over the segments (in LDS); wave w of the launch then takes items w, w + W,
@@ -29,8 +27,10 @@ struct Item {
 };
 
 // Fill prefix[0..S] (S = number of segments) with item-count prefixes; returns the
-// total.  Needs blockDim.x / 64 + 1 ints of `scan_tmp`.  Contains __syncthreads().
-__device__ __forceinline__ int build_item_prefix(const GroupedGemm& g, int tile_rows, int* prefix, int* scan_tmp) {
+// total.  An item covers `tile_rows` rows and `groups_per_item` 32-column groups.
+// Needs blockDim.x / 64 + 1 ints of `scan_tmp`.  Contains __syncthreads().
+__device__ __forceinline__ int build_item_prefix(const GroupedGemm& g, int tile_rows, int groups_per_item,
+                                                 int* prefix, int* scan_tmp) {
   const int S = g.E + (g.shared_rows > 0 ? 1 : 0);
   int carry = 0;
   for (int s0 = 0; s0 < S; s0 += blockDim.x) {
@@ -39,7 +39,8 @@ __device__ __forceinline__ int build_item_prefix(const GroupedGemm& g, int tile_
     if (s < S) {
       const bool sh = s >= g.E;
       const int rows = sh ? g.shared_rows : g.counts[s];
-      items = (rows + tile_rows - 1) / tile_rows * (sh ? g.groups_shared : g.groups_routed);
+      const int groups = sh ? g.groups_shared : g.groups_routed;
+      items = (rows + tile_rows - 1) / tile_rows * ((groups + groups_per_item - 1) / groups_per_item);
     }
     int tot = 0;
     const int ex = block_exclusive_scan(items, scan_tmp, &tot);
@@ -51,7 +52,11 @@ __device__ __forceinline__ int build_item_prefix(const GroupedGemm& g, int tile_
   return carry;
 }
 
-__device__ __forceinline__ Item decode_item(const GroupedGemm& g, int tile_rows, const int* prefix, int item) {
+__device__ __forceinline__ int build_item_prefix(const GroupedGemm& g, int tile_rows, int* prefix, int* scan_tmp) {
+  return build_item_prefix(g, tile_rows, 1, prefix, scan_tmp);
+}
+
+__device__ __forceinline__ int find_segment(const GroupedGemm& g, const int* prefix, int item) {
   const int S = g.E + (g.shared_rows > 0 ? 1 : 0);
   int lo = 0, hi = S;
   while (hi - lo > 1) {
@@ -61,16 +66,39 @@ __device__ __forceinline__ Item decode_item(const GroupedGemm& g, int tile_rows,
     else
       hi = mid;
   }
+  return lo;
+}
+
+// Item order: segment, row tile, column group fastest (one group per item).
+__device__ __forceinline__ Item decode_item(const GroupedGemm& g, int tile_rows, const int* prefix, int item) {
   Item it;
-  it.seg = lo;
-  it.shared = lo >= g.E;
-  const int local = item - prefix[lo];
+  it.seg = find_segment(g, prefix, item);
+  it.shared = it.seg >= g.E;
+  const int local = item - prefix[it.seg];
   const int groups = it.shared ? g.groups_shared : g.groups_routed;
   const int tile = local / groups;
   it.group = local - tile * groups;
-  const int rows = it.shared ? g.shared_rows : g.counts[lo];
-  it.row0 = (it.shared ? 0 : g.offsets[lo]) + tile * tile_rows;
+  const int rows = it.shared ? g.shared_rows : g.counts[it.seg];
+  it.row0 = (it.shared ? 0 : g.offsets[it.seg]) + tile * tile_rows;
   it.nrows = min(tile_rows, rows - tile * tile_rows);
+  return it;
+}
+
+// Item order: segment, column tile, row tile fastest, so the row tiles of one expert
+// that read the same weights are neighbours.  `group` is the first group of the item.
+__device__ __forceinline__ Item decode_item_tiled(const GroupedGemm& g, int tile_rows, int groups_per_item,
+                                                  const int* prefix, int item) {
+  Item it;
+  it.seg = find_segment(g, prefix, item);
+  it.shared = it.seg >= g.E;
+  const int local = item - prefix[it.seg];
+  const int rows = it.shared ? g.shared_rows : g.counts[it.seg];
+  const int rtiles = (rows + tile_rows - 1) / tile_rows;
+  const int nt = local / rtiles;
+  const int rt = local - nt * rtiles;
+  it.group = nt * groups_per_item;
+  it.row0 = (it.shared ? 0 : g.offsets[it.seg]) + rt * tile_rows;
+  it.nrows = min(tile_rows, rows - rt * tile_rows);
   return it;
 }
 

@@ -86,12 +86,13 @@ def oracle_rows(w, weights, x, logits_np, rows):
     return rows, yref
 
 
-def full_case(w, sample=None):
-    say(f"case {w.name}: T={w.T} H={w.H} M={w.M} E={w.E} k={w.k} Ms={w.Ms} {w.dtype}")
+def full_case(w, sample=None, kernel="auto"):
+    say(f"case {w.name}: T={w.T} H={w.H} M={w.M} E={w.E} k={w.k} Ms={w.Ms} {w.dtype} gemm={kernel}")
     weights = workloads.make_weights(w, device="cuda")
     x, logits = workloads.make_activations(w, device="cuda")
     logits_np = logits.cpu().numpy()
     layer = make_layer(w, weights)
+    layer.set_gemm_kernel(kernel)
     rb, y = run_layer(layer, x, logits)
     _, counts = check_route(rb, logits_np, w.E, w.k)
     if sample is None:
@@ -125,12 +126,18 @@ def test_starved_decode_full():
     full_case(workloads.STARVED_DECODE)
 
 
-def test_afd_aggregated_sampled():
-    full_case(workloads.AGGREGATED, sample=6)
+@pytest.mark.parametrize("kernel", ["auto", "stream"])
+def test_afd_aggregated_sampled(kernel):
+    full_case(workloads.AGGREGATED, sample=6, kernel=kernel)
 
 
 def test_coarse_experts_with_shared_sampled():
     full_case(workloads.COARSE, sample=3)
+
+
+def test_starved_decode_tiled_kernel():
+    """The 128-row kernel on a decode batch: one partial tile per touched expert."""
+    full_case(workloads.STARVED_DECODE, kernel="tiled")
 
 
 def test_fp8_blockscaled_sampled():
@@ -164,8 +171,20 @@ def test_route_full_size_every_workload(w):
     small("many_experts", T=9, E=1024, k=32, H=128, M=128),
     small("wide_f32", dtype="f32", T=17, H=384, M=128, E=6, k=3),
 ], ids=lambda w: w.name)
-def test_small_shapes(w):
-    full_case(w)
+@pytest.mark.parametrize("kernel", ["stream", "tiled"])
+def test_small_shapes(w, kernel):
+    full_case(w, kernel=kernel)
+
+
+@pytest.mark.parametrize("w", [
+    small("tiled_multi_tile", T=300, E=4, k=2, H=256, M=256, Ms=384),
+    small("tiled_odd_groups", T=200, E=3, k=2, H=384, M=128),
+    small("tiled_long_k", T=140, E=2, k=1, H=1024, M=640, Ms=128),
+], ids=lambda w: w.name)
+def test_tiled_shapes(w):
+    """Experts with several 128-row tiles (ragged last tile), a column count that
+    leaves half of the last column tile empty, and long reductions."""
+    full_case(w, kernel="tiled")
 
 
 def test_skewed_routing_multi_tile_expert():
