@@ -132,6 +132,16 @@ const char* afd_ffn_last_error(void);
 /* Device bytes the handle owns (repacked weights plus workspace). */
 size_t afd_ffn_device_bytes(afd_ffn_t h);
 
+/* The activation quantisation of the fp8 layer as a stand-alone call: rows x cols
+ * activations src (row-major; src_dtype AFD_BF16 or AFD_F32) -> e4m3 codes
+ * codes[rows, cols] and fp32 scales scales[rows, cols / 128], per row and per 128
+ * channels: scale = amax / 448 (1 for an all-zero group), code = e4m3 nearest to
+ * v / scale, ties to even, both divisions IEEE fp32 (the FP8/BF16 mixed precision of
+ * the omica.com.cn AFD article, §3.3; the forward call of an fp8 layer quantises x
+ * and h this way).  cols must be a multiple of 128.  Asynchronous on `stream`. */
+int afd_ffn_quantize_fp8(const void* src, int32_t rows, int32_t cols, int32_t src_dtype, uint8_t* codes,
+                         float* scales, void* stream);
+
 /* Choice of grouped-GEMM kernel for bf16 layers.  AFD_GEMM_AUTO (the default)
  * uses 16-row weight-streaming tiles while experts average at most 16 routed rows
  * per batch (T * top_k <= 16 * E) and 128-row tiles above that; the other values
@@ -148,7 +158,7 @@ int afd_ffn_set_gemm_kernel(afd_ffn_t h, int kernel);
 typedef enum afd_stage {
   AFD_STAGE_ROUTER = 0,  /* top-k softmax router */
   AFD_STAGE_PERMUTE = 1, /* histogram, prefix scan, scatter */
-  AFD_STAGE_QUANT_X = 2, /* fp8 quantisation of x */
+  AFD_STAGE_QUANT = 2,   /* fp8 quantisation of x and h */
   AFD_STAGE_GATE_UP = 3, /* grouped gate/up GEMM with SwiGLU epilogue */
   AFD_STAGE_DOWN = 4,    /* grouped down-projection GEMM */
   AFD_STAGE_COMBINE = 5, /* gate-weighted combine back to token order */

@@ -11,8 +11,8 @@ from __future__ import annotations
 from ._ffi import (AFD_BF16, AFD_F32, AFD_FP8_E4M3, AFD_GEMM_AUTO, AFD_GEMM_STREAM,  # noqa: F401
                    AFD_GEMM_TILED, STAGES, AfdError, afd_ffn_config, afd_ffn_create, afd_ffn_destroy,
                    afd_ffn_device_bytes, afd_ffn_forward, afd_ffn_last_error, afd_ffn_profile_read,
-                   afd_ffn_route, afd_ffn_set_gemm_kernel, afd_ffn_set_profiling, afd_ffn_strerror, afd_route,
-                   load)
+                   afd_ffn_quantize_fp8, afd_ffn_route, afd_ffn_set_gemm_kernel, afd_ffn_set_profiling,
+                   afd_ffn_strerror, afd_route, load)
 
 GEMM_KERNELS = {"auto": AFD_GEMM_AUTO, "stream": AFD_GEMM_STREAM, "tiled": AFD_GEMM_TILED}
 
@@ -22,6 +22,18 @@ DTYPES = {"f32": AFD_F32, "bf16": AFD_BF16, "fp8": AFD_FP8_E4M3}
 def _stream_handle(torch, stream=None):
     s = stream if stream is not None else torch.cuda.current_stream()
     return s.cuda_stream
+
+
+def quantize_fp8(x, stream=None):
+    """e4m3 codes (uint8 [rows, cols]) and fp32 scales ([rows, cols/128]) of a 2-D
+    bf16 or fp32 CUDA tensor, computed by the library's quantisation kernel."""
+    import torch
+    rows, cols = x.shape
+    codes = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((rows, cols // 128), dtype=torch.float32, device=x.device)
+    dt = AFD_BF16 if x.dtype == torch.bfloat16 else AFD_F32
+    afd_ffn_quantize_fp8(x.contiguous(), rows, cols, dt, codes, scales, _stream_handle(torch, stream))
+    return codes, scales
 
 
 class RouteBuffers:

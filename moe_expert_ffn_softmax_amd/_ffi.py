@@ -13,7 +13,7 @@ LIB_PATH = os.path.join(_PKG, "libafd_ffn.so")
 AFD_OK, AFD_EINVAL, AFD_EUNSUPPORTED, AFD_ENOMEM, AFD_EHIP = 0, -1, -2, -3, -4
 AFD_F32, AFD_BF16, AFD_FP8_E4M3 = 0, 1, 2
 AFD_GEMM_AUTO, AFD_GEMM_STREAM, AFD_GEMM_TILED = 0, 1, 2
-STAGES = ("router", "permute", "quant_x", "gate_up", "down", "combine")
+STAGES = ("router", "permute", "quant", "gate_up", "down", "combine")
 AFD_NUM_STAGES = len(STAGES)
 
 
@@ -60,6 +60,8 @@ def load():
     lib.afd_ffn_last_error.restype = ctypes.c_char_p
     lib.afd_ffn_device_bytes.argtypes = [V]
     lib.afd_ffn_device_bytes.restype = ctypes.c_size_t
+    lib.afd_ffn_quantize_fp8.argtypes = [P, I32, I32, I32, P, P, V]
+    lib.afd_ffn_quantize_fp8.restype = ctypes.c_int
     lib.afd_ffn_set_gemm_kernel.argtypes = [V, ctypes.c_int]
     lib.afd_ffn_set_gemm_kernel.restype = ctypes.c_int
     lib.afd_ffn_set_profiling.argtypes = [V, ctypes.c_int]
@@ -115,6 +117,11 @@ def afd_ffn_destroy(h: int) -> None:
 
 def afd_ffn_device_bytes(h: int) -> int:
     return int(load().afd_ffn_device_bytes(h))
+
+
+def afd_ffn_quantize_fp8(src, rows: int, cols: int, src_dtype: int, codes, scales, stream=None) -> None:
+    _check(load().afd_ffn_quantize_fp8(_ptr(src), int(rows), int(cols), int(src_dtype), _ptr(codes), _ptr(scales),
+                                       stream))
 
 
 def afd_ffn_set_gemm_kernel(h: int, kernel: int) -> None:

@@ -38,7 +38,6 @@ int check_config(const afd_ffn_config* c) {
   if ((long long)c->max_tokens * c->top_k >= (1ll << 31)) return fail(AFD_EINVAL, "max_tokens * top_k >= 2^31");
   if (c->dtype != AFD_F32 && c->dtype != AFD_BF16 && c->dtype != AFD_FP8_E4M3)
     return fail(AFD_EINVAL, "unknown dtype %d", c->dtype);
-  if (c->dtype == AFD_FP8_E4M3) return fail(AFD_EUNSUPPORTED, "fp8 weights are not implemented in this build");
   return AFD_OK;
 }
 
@@ -52,7 +51,9 @@ int check_route(const afd_ffn* h, const afd_route* r, int32_t T) {
 }
 
 void release(afd_ffn* h) {
-  void* bufs[] = {h->w_gu, h->w_d, h->ws_gu, h->ws_d, h->h_routed, h->h_shared, h->o_routed, h->o_shared};
+  void* bufs[] = {h->w_gu,      h->w_d,     h->ws_gu,    h->ws_d,      h->h_routed,  h->h_shared,
+                  h->o_routed,  h->o_shared, h->s_gu,    h->s_d,       h->ss_gu,     h->ss_d,
+                  h->xq,        h->xs,      h->hq_routed, h->hs_routed, h->hq_shared, h->hs_shared};
   for (void* b : bufs)
     if (b) (void)hipFree(b);
   for (hipEvent_t e : h->ev_pool) (void)hipEventDestroy(e);
@@ -97,7 +98,63 @@ bool use_tiled(const afd_ffn* h, int P) {
   return (long long)P > 16ll * h->cfg.num_experts;
 }
 
+// fp8 layer: quantise x -> gate/up GEMM (fp32 h) -> quantise h -> down GEMM -> combine.
+int forward_fp8(afd_ffn* h, const void* x, int T, const afd_route* r, void* y, hipStream_t st,
+                const afd::GroupedGemm& g1, const afd::GroupedGemm& g2) {
+  const afd_ffn_config& c = h->cfg;
+  const int H = c.hidden, M = c.inter, Ms = c.shared_inter, E = c.num_experts, k = c.top_k;
+  const int P = T * k;
+  {
+    StageScope s(h, st, AFD_STAGE_QUANT);
+    hipError_t e = afd::launch_quant_fp8(x, T, H, H, true, h->xq, h->xs, st);
+    if (e != hipSuccess) return hip_fail(e, "x quantisation launch");
+    s.done();
+  }
+  const long long items1 =
+      afd::grouped_items_bound(P, E, g1.groups_routed, g1.shared_rows, g1.groups_shared, afd::kTileRows);
+  const long long items2 =
+      afd::grouped_items_bound(P, E, g2.groups_routed, g2.shared_rows, g2.groups_shared, afd::kTileRows);
+  {
+    StageScope s(h, st, AFD_STAGE_GATE_UP);
+    hipError_t e = afd::launch_gemm_fp8(g1, true, items1, h->gemm_blocks[4], st);
+    if (e != hipSuccess) return hip_fail(e, "fp8 gate/up GEMM launch");
+    s.done();
+  }
+  {
+    StageScope s(h, st, AFD_STAGE_QUANT);
+    hipError_t e = afd::launch_quant_fp8(h->h_routed, P, M, M, false, h->hq_routed, h->hs_routed, st);
+    if (e == hipSuccess && Ms) e = afd::launch_quant_fp8(h->h_shared, T, Ms, Ms, false, h->hq_shared, h->hs_shared, st);
+    if (e != hipSuccess) return hip_fail(e, "h quantisation launch");
+    s.done();
+  }
+  {
+    StageScope s(h, st, AFD_STAGE_DOWN);
+    hipError_t e = afd::launch_gemm_fp8(g2, false, items2, h->gemm_blocks[5], st);
+    if (e != hipSuccess) return hip_fail(e, "fp8 down GEMM launch");
+    s.done();
+  }
+  {
+    StageScope s(h, st, AFD_STAGE_COMBINE);
+    hipError_t e = afd::launch_combine(h->o_routed, Ms ? h->o_shared : nullptr, r->topk_gates, r->pair_pos, T, k, H, y,
+                                       true, st);
+    if (e != hipSuccess) return hip_fail(e, "combine launch");
+    s.done();
+  }
+  return AFD_OK;
+}
+
 }  // namespace
+
+extern "C" int afd_ffn_quantize_fp8(const void* src, int32_t rows, int32_t cols, int32_t src_dtype, uint8_t* codes,
+                                    float* scales, void* stream) {
+  if (rows < 0 || cols <= 0 || cols % 128) return fail(AFD_EINVAL, "rows=%d cols=%d (cols must be a multiple of 128)", rows, cols);
+  if (src_dtype != AFD_F32 && src_dtype != AFD_BF16) return fail(AFD_EINVAL, "source dtype must be fp32 or bf16");
+  if (rows == 0) return AFD_OK;
+  if (!src || !codes || !scales) return fail(AFD_EINVAL, "a buffer is NULL");
+  hipError_t e = afd::launch_quant_fp8(src, rows, cols, cols, src_dtype == AFD_BF16, codes, scales,
+                                       static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? AFD_OK : hip_fail(e, "quantisation launch");
+}
 
 extern "C" const char* afd_ffn_strerror(int code) {
   switch (code) {
@@ -122,6 +179,11 @@ extern "C" int afd_ffn_create(const afd_ffn_config* cfg, const void* w_gate_up, 
   const bool fp8 = cfg->dtype == AFD_FP8_E4M3;
   if (!fp8 && (s_gate_up || s_down || ss_gate_up || ss_down))
     return fail(AFD_EINVAL, "block scales are only taken with fp8 weights");
+  if (fp8 && (!s_gate_up || !s_down)) return fail(AFD_EINVAL, "fp8 weights need their block scales");
+  if (fp8 && cfg->shared_inter > 0 && (!ss_gate_up || !ss_down))
+    return fail(AFD_EINVAL, "fp8 shared expert weights need their block scales");
+  if (fp8 && cfg->shared_inter == 0 && (ss_gate_up || ss_down))
+    return fail(AFD_EINVAL, "shared scales given without shared_inter");
   if (cfg->shared_inter > 0 && (!ws_gate_up || !ws_down)) return fail(AFD_EINVAL, "shared expert weights are NULL");
   if (cfg->shared_inter == 0 && (ws_gate_up || ws_down)) return fail(AFD_EINVAL, "shared weights given without shared_inter");
   *out = nullptr;
@@ -143,29 +205,48 @@ extern "C" int afd_ffn_create(const afd_ffn_config* cfg, const void* w_gate_up, 
   }
   h->num_cus = prop.multiProcessorCount;
   {
-    int occ[4] = {0, 0, 0, 0};
+    int occ[6] = {0, 0, 0, 0, 0, 0};
     e = afd::gemm_occupancy_bf16(&occ[0], &occ[1]);
     if (e == hipSuccess) e = afd::gemm_occupancy_f32(&occ[2], &occ[3]);
+    if (e == hipSuccess) e = afd::gemm_occupancy_fp8(&occ[4], &occ[5]);
     if (e != hipSuccess) {
       release(h);
       return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
     }
-    for (int i = 0; i < 4; ++i) h->gemm_blocks[i] = (occ[i] > 0 ? occ[i] : 1) * h->num_cus;
+    for (int i = 0; i < 6; ++i) h->gemm_blocks[i] = (occ[i] > 0 ? occ[i] : 1) * h->num_cus;
   }
 
   const size_t H = cfg->hidden, M = cfg->inter, Ms = cfg->shared_inter, E = cfg->num_experts;
   const size_t P = (size_t)cfg->max_tokens * cfg->top_k, T = cfg->max_tokens;
   const size_t es = elem_size(cfg->dtype);
+  const size_t hes = cfg->dtype == AFD_BF16 ? 2 : 4;  // intermediate h: bf16, or fp32 before fp8 quantisation
   h->w_gu_expert_elems = H * 2 * M;
   h->w_d_expert_elems = M * H;
+  const size_t sgu_n = (H / 128) * (2 * M / 128), sd_n = (M / 128) * (H / 128);
+  const size_t ssgu_n = (H / 128) * (2 * Ms / 128), ssd_n = (Ms / 128) * (H / 128);
 
   struct Alloc {
     void** dst;
     size_t bytes;
   } allocs[] = {
-      {&h->w_gu, E * H * 2 * M * es},  {&h->w_d, E * M * H * es},      {&h->ws_gu, H * 2 * Ms * es},
-      {&h->ws_d, Ms * H * es},         {&h->h_routed, P * M * es},     {&h->h_shared, T * Ms * es},
-      {(void**)&h->o_routed, P * H * 4}, {(void**)&h->o_shared, Ms ? T * H * 4 : 0},
+      {&h->w_gu, E * H * 2 * M * es},
+      {&h->w_d, E * M * H * es},
+      {&h->ws_gu, H * 2 * Ms * es},
+      {&h->ws_d, Ms * H * es},
+      {&h->h_routed, P * M * hes},
+      {&h->h_shared, T * Ms * hes},
+      {(void**)&h->o_routed, P * H * 4},
+      {(void**)&h->o_shared, Ms ? T * H * 4 : 0},
+      {(void**)&h->s_gu, fp8 ? E * sgu_n * 4 : 0},
+      {(void**)&h->s_d, fp8 ? E * sd_n * 4 : 0},
+      {(void**)&h->ss_gu, fp8 ? ssgu_n * 4 : 0},
+      {(void**)&h->ss_d, fp8 ? ssd_n * 4 : 0},
+      {(void**)&h->xq, fp8 ? T * H : 0},
+      {(void**)&h->xs, fp8 ? T * (H / 128) * 4 : 0},
+      {(void**)&h->hq_routed, fp8 ? P * M : 0},
+      {(void**)&h->hs_routed, fp8 ? P * (M / 128) * 4 : 0},
+      {(void**)&h->hq_shared, fp8 ? T * Ms : 0},
+      {(void**)&h->hs_shared, fp8 ? T * (Ms / 128) * 4 : 0},
   };
   for (auto& a : allocs) {
     if (a.bytes == 0) continue;
@@ -190,6 +271,22 @@ extern "C" int afd_ffn_create(const afd_ffn_config* cfg, const void* w_gate_up, 
     if (e == hipSuccess && Ms)
       e = afd::launch_pack_bf16(static_cast<const uint16_t*>(ws_down), static_cast<uint16_t*>(h->ws_d), 1, (int)Ms,
                                 (int)H, 0, st);
+  } else if (fp8) {
+    e = afd::launch_pack_fp8(static_cast<const uint8_t*>(w_gate_up), static_cast<uint8_t*>(h->w_gu), (int)E, (int)H,
+                             (int)(2 * M), 1, st);
+    if (e == hipSuccess)
+      e = afd::launch_pack_fp8(static_cast<const uint8_t*>(w_down), static_cast<uint8_t*>(h->w_d), (int)E, (int)M,
+                               (int)H, 0, st);
+    if (e == hipSuccess && Ms)
+      e = afd::launch_pack_fp8(static_cast<const uint8_t*>(ws_gate_up), static_cast<uint8_t*>(h->ws_gu), 1, (int)H,
+                               (int)(2 * Ms), 1, st);
+    if (e == hipSuccess && Ms)
+      e = afd::launch_pack_fp8(static_cast<const uint8_t*>(ws_down), static_cast<uint8_t*>(h->ws_d), 1, (int)Ms,
+                               (int)H, 0, st);
+    if (e == hipSuccess) e = hipMemcpyAsync(h->s_gu, s_gate_up, E * sgu_n * 4, hipMemcpyDeviceToDevice, st);
+    if (e == hipSuccess) e = hipMemcpyAsync(h->s_d, s_down, E * sd_n * 4, hipMemcpyDeviceToDevice, st);
+    if (e == hipSuccess && Ms) e = hipMemcpyAsync(h->ss_gu, ss_gate_up, ssgu_n * 4, hipMemcpyDeviceToDevice, st);
+    if (e == hipSuccess && Ms) e = hipMemcpyAsync(h->ss_d, ss_down, ssd_n * 4, hipMemcpyDeviceToDevice, st);
   } else {
     e = hipMemcpyAsync(h->w_gu, w_gate_up, E * H * 2 * M * es, hipMemcpyDeviceToDevice, st);
     if (e == hipSuccess) e = hipMemcpyAsync(h->w_d, w_down, E * M * H * es, hipMemcpyDeviceToDevice, st);
@@ -245,6 +342,7 @@ extern "C" int afd_ffn_forward(afd_ffn_t h, const void* x, int32_t T, const afd_
   const int H = c.hidden, M = c.inter, Ms = c.shared_inter, E = c.num_experts, k = c.top_k;
   const int P = T * k;
   const bool f32 = c.dtype == AFD_F32;
+  const bool fp8 = c.dtype == AFD_FP8_E4M3;
 
   afd::GroupedGemm g1 = {};
   g1.counts = r->expert_counts;
@@ -287,6 +385,24 @@ extern "C" int afd_ffn_forward(afd_ffn_t h, const void* x, int32_t T, const afd_
   g2.out_shared = h->o_shared;
   g2.ldo_routed = H;
   g2.ldo_shared = H;
+
+  if (fp8) {
+    g1.a_routed = h->xq;
+    g1.a_shared = h->xq;
+    g1.as_routed = h->xs;
+    g1.as_shared = h->xs;
+    g1.s_routed = h->s_gu;
+    g1.s_expert_elems = (size_t)(H / 128) * (2 * M / 128);
+    g1.s_shared = h->ss_gu;
+    g2.a_routed = h->hq_routed;
+    g2.a_shared = h->hq_shared;
+    g2.as_routed = h->hs_routed;
+    g2.as_shared = h->hs_shared;
+    g2.s_routed = h->s_d;
+    g2.s_expert_elems = (size_t)(M / 128) * (H / 128);
+    g2.s_shared = h->ss_d;
+    return forward_fp8(h, x, T, r, y, st, g1, g2);
+  }
 
   // Few rows per expert (decode batches): 16-row weight-streaming tiles.  Many rows:
   // 128-row tiles, so each expert's weights are read once per 128 of its rows.

@@ -83,9 +83,19 @@ hipError_t launch_gemm_bf16_tiled(const GroupedGemm& g, bool swiglu, long long m
 int tiled_rows();
 int tiled_groups();
 
+// fp8 (e4m3, fp32 block scales) streaming variant; weights packed by launch_pack_fp8,
+// A = fp8 codes with per-row per-128 scales `as_*`, weight scales `s_*`; writes fp32.
+hipError_t launch_gemm_fp8(const GroupedGemm& g, bool swiglu, long long max_items, int max_blocks, hipStream_t st);
+hipError_t launch_pack_fp8(const uint8_t* src, uint8_t* dst, int nmat, int R, int C, int gate_up, hipStream_t st);
+// rows x cols activations (bf16 or fp32, row stride ld) -> e4m3 codes [rows, cols]
+// and fp32 scales [rows, cols / 128].
+hipError_t launch_quant_fp8(const void* src, int rows, int cols, int ld, bool src_bf16, uint8_t* q, float* scales,
+                            hipStream_t st);
+
 // Resident workgroups per compute unit of the GEMM kernels.
 hipError_t gemm_occupancy_bf16(int* gate_up, int* down);
 hipError_t gemm_occupancy_f32(int* gate_up, int* down);
+hipError_t gemm_occupancy_fp8(int* gate_up, int* down);
 
 // y[t] = sum_j gate[t,j] * O[pair_pos[t*k+j]] (+ Os[t]) -> y (bf16 or fp32).
 hipError_t launch_combine(const float* O, const float* Os, const float* gates, const int32_t* pair_pos,
@@ -108,7 +118,19 @@ struct afd_ffn {
   void* h_shared;   // [T_max, Ms]
   float* o_routed;  // [P_max, H]
   float* o_shared;  // [T_max, H]
-  int gemm_blocks[4];  // resident workgroups of each GEMM kernel on the whole device
+  // fp8 layers only
+  float* s_gu;        // [E, H/128, 2M/128] weight block scales (copy)
+  float* s_d;         // [E, M/128, H/128]
+  float* ss_gu;       // shared expert scales
+  float* ss_d;
+  uint8_t* xq;        // [T_max, H] e4m3 codes of x
+  float* xs;          // [T_max, H/128]
+  uint8_t* hq_routed; // [P_max, M]
+  float* hs_routed;   // [P_max, M/128]
+  uint8_t* hq_shared; // [T_max, Ms]
+  float* hs_shared;   // [T_max, Ms/128]
+  int gemm_blocks[6];  // resident workgroups of each GEMM kernel on the whole device
+                       // (bf16 gate/up, down; fp32 gate/up, down; fp8 gate/up, down)
   int gemm_mode;       // 0 automatic, 1 always 16-row streaming, 2 always 128-row tiles
   size_t device_bytes;
   // profiling

@@ -26,7 +26,10 @@ constexpr int kTiledRowBlocks = 8;                      // 16-row blocks per til
 constexpr int kTiledRows = 16 * kTiledRowBlocks;        // 128
 constexpr int kTiledGroupsPerWave = 2;                  // 32-column groups per wave
 constexpr int kTiledGroups = kTiledWaves * kTiledGroupsPerWave;  // per item
-constexpr int kTiledBAhead = 4;                         // weight steps in flight per wave
+#ifndef AFD_TILED_B_AHEAD
+#define AFD_TILED_B_AHEAD 4
+#endif
+constexpr int kTiledBAhead = AFD_TILED_B_AHEAD;         // weight steps in flight per wave
 constexpr int kXcds = 8;
 
 template <int KC>
@@ -35,8 +38,15 @@ struct TiledSmem {
   bf16x8 a[2][KC][kTiledRowBlocks][kWave];
 };
 
+#ifndef AFD_TILED_B_NT
+#define AFD_TILED_B_NT 1
+#endif
 __device__ __forceinline__ bf16x8 tiled_load_b(const i32x4* p) {
+#if AFD_TILED_B_NT
   return __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(p));
+#else
+  return __builtin_bit_cast(bf16x8, *p);
+#endif
 }
 
 template <bool SWIGLU, int KC>

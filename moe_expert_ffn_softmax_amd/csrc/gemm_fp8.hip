@@ -1,0 +1,209 @@
+// Grouped expert GEMMs with fp8 (OCP e4m3) operands and fp32 block scales on the
+// gfx950 matrix cores (v_mfma_scale_f32_16x16x128_f8f6f4 with unit E8M0 scales).
+//
+// Weights carry one fp32 scale per 128x128 block and activations one per row per
+// 128 channels, so every 128-deep reduction block of an output element has exactly
+// one scale on each side: one MFMA instruction covers one such block, and its fp32
+// partial product is added to the accumulator times s_act[row][kb] * s_w[kb][nb]
+// (the FP8 DeepGEMM of "大模型推理的内存与计算解耦：AFD 架构解析与性能验证", §1, is
+// NVIDIA prior art with the same block structure; FP8/BF16 mixed precision is the
+// omica.com.cn AFD article's §3.3).
+//
+// Operand order.  A fragment is 64 lanes x 32 bytes: lane l supplies row (l % 16) of
+// A and column (l % 16) of B at reduction offsets (l / 16) * 32 .. + 31 of the
+// 128-deep block.  The instruction pairs A and B bytes held in the same (lane group,
+// register, byte) position, so any packing used identically on both sides gives the
+// exact block dot product; this one keeps each lane's 32 bytes contiguous in a row of
+// x (two 16-byte loads).  The result layout is that of the 16x16 fp32 MFMAs: lane l
+// holds rows (l / 16) * 4 .. + 3 of column (l % 16).
+//
+// Work items, weight streaming and item striding are those of the bf16 streaming
+// kernel: one wave per 16-row tile times one 32-column group, full reduction,
+// weight fragments loaded nontemporally several blocks ahead.
+#include "grouped.h"
+
+namespace afd {
+
+constexpr int kFp8Threads = 256;
+constexpr int kFp8Waves = kFp8Threads / kWave;
+
+__device__ __forceinline__ f32x4 mfma_fp8_block(const i32x8& a, const i32x8& b) {
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  // format codes 0 (fp8 e4m3) for both operands, E8M0 scale 127 = 2^0 on both sides
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 0, 0, 0, 0x7f7f7f7f, 0, 0x7f7f7f7f);
+}
+
+__device__ __forceinline__ i32x8 load32_nt(const uint8_t* p) {
+  const i32x4* q = reinterpret_cast<const i32x4*>(p);
+  const i32x4 lo = __builtin_nontemporal_load(q), hi = __builtin_nontemporal_load(q + 1);
+  return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+__device__ __forceinline__ i32x8 load32(const uint8_t* p) {
+  const i32x4* q = reinterpret_cast<const i32x4*>(p);
+  const i32x4 lo = q[0], hi = q[1];
+  return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// Column of the first element of packed 16-column block (group j, half) of a matrix
+// with N output columns.
+__device__ __forceinline__ int block_col(bool gate_up, int N, int j, int half) {
+  return gate_up ? half * (N / 2) + j * 16 : j * 32 + half * 16;
+}
+
+template <bool SWIGLU, int D>
+__global__ void __launch_bounds__(kFp8Threads) gemm_fp8_stream_kernel(GroupedGemm g) {
+  __shared__ int prefix[kMaxSegments + 1];
+  __shared__ int scan_tmp[kFp8Waves + 1];
+  const int total = build_item_prefix(g, kTileRows, prefix, scan_tmp);
+  const int lane = lane_id();
+  const int waves_in_launch = gridDim.x * kFp8Waves;
+  const int wave = blockIdx.x * kFp8Waves + threadIdx.x / kWave;
+
+  for (int item = wave; item < total; item += waves_in_launch) {
+    const Item it = decode_item(g, kTileRows, prefix, item);
+    const int K = it.shared ? g.K_shared : g.K_routed;
+    const int KB = K / 128;
+    const int groups = it.shared ? g.groups_shared : g.groups_routed;
+    const int N = groups * 32;
+    const int NB = N / 128;  // weight scale blocks per reduction block
+    // A row of this lane (rows past the tile end repeat its first row)
+    const int r = lane & 15;
+    const int rr = r < it.nrows ? r : 0;
+    int arow;
+    if (it.shared)
+      arow = it.row0 + rr;
+    else
+      arow = g.gather_routed ? g.sorted_pair[it.row0 + rr] / g.k : it.row0 + rr;
+    const int lda = it.shared ? g.lda_shared : g.lda_routed;
+    const uint8_t* A = static_cast<const uint8_t*>(it.shared ? g.a_shared : g.a_routed) + (size_t)arow * lda +
+                       (lane >> 4) * 32;
+    // activation scales of the 4 output rows this lane accumulates
+    const float* as_base = it.shared ? g.as_shared : g.as_routed;
+    const float* as_row[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int orow = (lane >> 4) * 4 + i;
+      const int orr = orow < it.nrows ? orow : 0;
+      int srow;
+      if (it.shared)
+        srow = it.row0 + orr;
+      else
+        srow = g.gather_routed ? g.sorted_pair[it.row0 + orr] / g.k : it.row0 + orr;
+      as_row[i] = as_base + (size_t)srow * KB;
+    }
+    const uint8_t* wbase = it.shared ? static_cast<const uint8_t*>(g.w_shared)
+                                     : static_cast<const uint8_t*>(g.w_routed) + (size_t)it.seg * g.w_expert_elems;
+    const uint8_t* B = wbase + (size_t)it.group * KB * 4096 + lane * 32;  // [kb][half][lane][32 B]
+    const float* ws = it.shared ? g.s_shared : g.s_routed + (size_t)it.seg * g.s_expert_elems;
+    const int nb0 = block_col(SWIGLU, N, it.group, 0) / 128, nb1 = block_col(SWIGLU, N, it.group, 1) / 128;
+
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    i32x8 a[D], b0[D], b1[D];
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+      if (u < KB) {
+        a[u] = load32(A + u * 128);
+        b0[u] = load32_nt(B + (u * 2) * 2048);
+        b1[u] = load32_nt(B + (u * 2 + 1) * 2048);
+      }
+    }
+    for (int kb0 = 0; kb0 < KB; kb0 += D) {
+#pragma unroll
+      for (int u = 0; u < D; ++u) {
+        const int kb = kb0 + u;
+        if (kb < KB) {
+          const f32x4 p0 = mfma_fp8_block(a[u], b0[u]);
+          const f32x4 p1 = mfma_fp8_block(a[u], b1[u]);
+          const float w0 = ws[(size_t)kb * NB + nb0], w1 = ws[(size_t)kb * NB + nb1];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float sa = as_row[i][kb];
+            acc0[i] = fmaf(p0[i], sa * w0, acc0[i]);
+            acc1[i] = fmaf(p1[i], sa * w1, acc1[i]);
+          }
+          const int kn = kb + D;
+          if (kn < KB) {
+            a[u] = load32(A + kn * 128);
+            b0[u] = load32_nt(B + (kn * 2) * 2048);
+            b1[u] = load32_nt(B + (kn * 2 + 1) * 2048);
+          }
+        }
+      }
+    }
+
+    const int col = lane & 15;
+    const int rbase = (lane >> 4) * 4;
+    float* out = static_cast<float*>(it.shared ? g.out_shared : g.out_routed);
+    const int ldo = it.shared ? g.ldo_shared : g.ldo_routed;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = rbase + i;
+      if (row >= it.nrows) continue;
+      float* o = out + (size_t)(it.row0 + row) * ldo;
+      if (SWIGLU) {
+        o[it.group * 16 + col] = silu(acc0[i]) * acc1[i];
+      } else {
+        o[it.group * 32 + col] = acc0[i];
+        o[it.group * 32 + 16 + col] = acc1[i];
+      }
+    }
+  }
+}
+
+hipError_t launch_gemm_fp8(const GroupedGemm& g, bool swiglu, long long max_items, int max_blocks, hipStream_t st) {
+  if (max_items <= 0) return hipSuccess;
+  long long blocks = (max_items + kFp8Waves - 1) / kFp8Waves;
+  if (blocks > max_blocks) blocks = max_blocks;
+  if (swiglu)
+    gemm_fp8_stream_kernel<true, 4><<<(unsigned)blocks, kFp8Threads, 0, st>>>(g);
+  else
+    gemm_fp8_stream_kernel<false, 4><<<(unsigned)blocks, kFp8Threads, 0, st>>>(g);
+  return hipGetLastError();
+}
+
+hipError_t gemm_occupancy_fp8(int* gate_up, int* down) {
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(gate_up, gemm_fp8_stream_kernel<true, 4>, kFp8Threads, 0);
+  if (e == hipSuccess)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(down, gemm_fp8_stream_kernel<false, 4>, kFp8Threads, 0);
+  return e;
+}
+
+// Repack fp8 weights [nmat][R][C] into [group][kb][half][lane][32 B] fragments
+// (group/half pairing as for bf16).
+__global__ void pack_fp8_kernel(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst, int nmat, int R, int C,
+                                int gate_up) {
+  const size_t slots_per_mat = (size_t)R * C / 32;
+  const size_t total = slots_per_mat * nmat;
+  const int KB = R / 128;
+  for (size_t s = blockIdx.x * (size_t)blockDim.x + threadIdx.x; s < total; s += (size_t)gridDim.x * blockDim.x) {
+    const size_t mat = s / slots_per_mat;
+    size_t rem = s % slots_per_mat;
+    const int lane = (int)(rem % 64);
+    rem /= 64;
+    const int half = (int)(rem % 2);
+    rem /= 2;
+    const int kb = (int)(rem % KB);
+    const int j = (int)(rem / KB);
+    const int c = lane % 16;
+    const int col = gate_up ? half * (C / 2) + j * 16 + c : j * 32 + half * 16 + c;
+    const int row0 = kb * 128 + (lane / 16) * 32;
+    const uint8_t* sp = src + mat * (size_t)R * C + (size_t)row0 * C + col;
+    uint32_t w[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      w[i] = (uint32_t)sp[(size_t)(4 * i) * C] | ((uint32_t)sp[(size_t)(4 * i + 1) * C] << 8) |
+             ((uint32_t)sp[(size_t)(4 * i + 2) * C] << 16) | ((uint32_t)sp[(size_t)(4 * i + 3) * C] << 24);
+    uint32_t* dp = reinterpret_cast<uint32_t*>(dst + s * 32);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dp[i] = w[i];
+  }
+}
+
+hipError_t launch_pack_fp8(const uint8_t* src, uint8_t* dst, int nmat, int R, int C, int gate_up, hipStream_t st) {
+  if (R % 128 || C % 32) return hipErrorInvalidValue;
+  pack_fp8_kernel<<<4096, 256, 0, st>>>(src, dst, nmat, R, C, gate_up);
+  return hipGetLastError();
+}
+
+}  // namespace afd

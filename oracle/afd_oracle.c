@@ -119,6 +119,20 @@ typedef struct {
   int rows, cols;
 } mat_t;
 
+/* Decoded value of every e4m3 code, filled once from afdo_fp8_decode. */
+static const double* fp8_table(void) {
+  static double table[256];
+  static int ready = 0;
+#pragma omp critical(afdo_fp8_table)
+  {
+    if (!ready) {
+      for (int c = 0; c < 256; ++c) table[c] = afdo_fp8_decode((uint8_t)c);
+      ready = 1;
+    }
+  }
+  return table;
+}
+
 /* Row r of a weight matrix, decoded to double (fp8: code times its block scale). */
 static void mat_row(const mat_t* w, int r, double* out) {
   if (w->dtype == AFDO_F32) {
@@ -130,7 +144,8 @@ static void mat_row(const mat_t* w, int r, double* out) {
   } else {
     const uint8_t* p = (const uint8_t*)w->data + (size_t)r * w->cols;
     const float* s = w->scales + (size_t)(r / QBLOCK) * (w->cols / QBLOCK);
-    for (int c = 0; c < w->cols; ++c) out[c] = afdo_fp8_decode(p[c]) * (double)s[c / QBLOCK];
+    const double* dec = fp8_table();
+    for (int c = 0; c < w->cols; ++c) out[c] = dec[p[c]] * (double)s[c / QBLOCK];
   }
 }
 

@@ -79,6 +79,20 @@ def test_create_rejects_bad_pointers():
                               ctypes.byref(h)) == _ffi.AFD_EINVAL          # shared weights w/o shared_inter
     assert lib.afd_ffn_create(ctypes.byref(cfg), 1, 1, None, None, None, None, None, None, None,
                               None) == _ffi.AFD_EINVAL
+    fp8 = _cfg(dtype=_ffi.AFD_FP8_E4M3)
+    assert lib.afd_ffn_create(ctypes.byref(fp8), 1, 1, None, None, None, None, None, None, None,
+                              ctypes.byref(h)) == _ffi.AFD_EINVAL          # fp8 without block scales
+    fp8s = _cfg(dtype=_ffi.AFD_FP8_E4M3, shared_inter=128)
+    assert lib.afd_ffn_create(ctypes.byref(fp8s), 1, 1, 1, 1, 1, 1, None, None, None,
+                              ctypes.byref(h)) == _ffi.AFD_EINVAL          # fp8 shared without scales
+
+
+def test_quantize_rejects_bad_arguments():
+    lib = _ffi.load()
+    assert lib.afd_ffn_quantize_fp8(1, 4, 100, _ffi.AFD_BF16, 1, 1, None) == _ffi.AFD_EINVAL   # cols % 128
+    assert lib.afd_ffn_quantize_fp8(1, 4, 128, _ffi.AFD_FP8_E4M3, 1, 1, None) == _ffi.AFD_EINVAL
+    assert lib.afd_ffn_quantize_fp8(None, 4, 128, _ffi.AFD_BF16, 1, 1, None) == _ffi.AFD_EINVAL
+    assert lib.afd_ffn_quantize_fp8(None, 0, 128, _ffi.AFD_BF16, None, None, None) == _ffi.AFD_OK  # empty
 
 
 def test_route_and_forward_reject_null_handle():

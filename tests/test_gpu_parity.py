@@ -141,7 +141,33 @@ def test_starved_decode_tiled_kernel():
 
 
 def test_fp8_blockscaled_sampled():
-    pytest.skip("fp8 block-scaled path not built yet (create returns AFD_EUNSUPPORTED)")
+    full_case(workloads.FP8_DSV3, sample=3)
+
+
+@pytest.mark.parametrize("src", ["bf16", "f32"])
+def test_fp8_quantisation_bit_exact(src):
+    """Step a0 alone: codes and scales equal the oracle's per-128 quantisation
+    bit for bit (both decide in fp32)."""
+    from moe_expert_ffn_softmax_amd import quantize_fp8
+    rng = np.random.default_rng(17)
+    rows, cols = 37, 640
+    v = rng.standard_normal((rows, cols)).astype(np.float32)
+    v *= rng.choice([1e-6, 1e-2, 1.0, 300.0], size=(rows, 1)).astype(np.float32)
+    v[3, :128] = 0.0                      # an all-zero group: scale 1
+    v[4, 128:256] = -0.0                  # negative zeros keep their sign bit
+    v[5, 5] = 1e-30                       # far below the group's amax: rounds to +-0
+    v[6, 256:384] = 7.0                   # constant group: every code 448
+    t = torch.from_numpy(v)
+    if src == "bf16":
+        t = t.to(torch.bfloat16)
+        v = t.float().numpy()
+    codes, scales = quantize_fp8(t.cuda())
+    torch.cuda.synchronize()
+    codes, scales = codes.cpu().numpy(), scales.cpu().numpy()
+    for r in range(rows):
+        c_ref, s_ref, _ = oracle.quant_row_fp8(v[r])
+        np.testing.assert_array_equal(scales[r], s_ref, err_msg=f"row {r}")
+        np.testing.assert_array_equal(codes[r], c_ref, err_msg=f"row {r}")
 
 
 @pytest.mark.parametrize("w", workloads.ORDERED, ids=lambda w: w.name)
@@ -174,6 +200,16 @@ def test_route_full_size_every_workload(w):
 @pytest.mark.parametrize("kernel", ["stream", "tiled"])
 def test_small_shapes(w, kernel):
     full_case(w, kernel=kernel)
+
+
+@pytest.mark.parametrize("w", [
+    small("fp8_ragged", dtype="fp8", T=37, H=256, M=384, E=16, k=4),
+    small("fp8_shared", dtype="fp8", T=50, H=384, M=256, E=6, k=2, Ms=256),
+    small("fp8_one_token", dtype="fp8", T=1, H=128, M=128, E=8, k=2, Ms=128),
+    small("fp8_skewed_long_k", dtype="fp8", T=90, H=1024, M=512, E=3, k=2),
+], ids=lambda w: w.name)
+def test_fp8_shapes(w):
+    full_case(w)
 
 
 @pytest.mark.parametrize("w", [
