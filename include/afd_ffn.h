@@ -142,7 +142,7 @@ size_t afd_ffn_device_bytes(afd_ffn_t h);
 int afd_ffn_quantize_fp8(const void* src, int32_t rows, int32_t cols, int32_t src_dtype, uint8_t* codes,
                          float* scales, void* stream);
 
-/* Choice of grouped-GEMM kernel for bf16 layers.  AFD_GEMM_AUTO (the default)
+/* Choice of grouped-GEMM kernel for bf16 and fp8 layers.  AFD_GEMM_AUTO (the default)
  * uses 16-row weight-streaming tiles while experts average at most 16 routed rows
  * per batch (T * top_k <= 16 * E) and 128-row tiles above that; the other values
  * force one kernel (results agree to rounding; a tuning and testing knob).  fp32

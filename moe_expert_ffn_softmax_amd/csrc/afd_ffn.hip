@@ -110,13 +110,22 @@ int forward_fp8(afd_ffn* h, const void* x, int T, const afd_route* r, void* y, h
     if (e != hipSuccess) return hip_fail(e, "x quantisation launch");
     s.done();
   }
-  const long long items1 =
-      afd::grouped_items_bound(P, E, g1.groups_routed, g1.shared_rows, g1.groups_shared, afd::kTileRows);
-  const long long items2 =
-      afd::grouped_items_bound(P, E, g2.groups_routed, g2.shared_rows, g2.groups_shared, afd::kTileRows);
+  const bool tiled = use_tiled(h, P);
+  long long items1, items2;
+  if (tiled) {
+    const int tr = afd::tiled_rows(), tg = afd::tiled_groups();
+    items1 = afd::grouped_items_bound(P, E, (g1.groups_routed + tg - 1) / tg, g1.shared_rows,
+                                      (g1.groups_shared + tg - 1) / tg, tr);
+    items2 = afd::grouped_items_bound(P, E, (g2.groups_routed + tg - 1) / tg, g2.shared_rows,
+                                      (g2.groups_shared + tg - 1) / tg, tr);
+  } else {
+    items1 = afd::grouped_items_bound(P, E, g1.groups_routed, g1.shared_rows, g1.groups_shared, afd::kTileRows);
+    items2 = afd::grouped_items_bound(P, E, g2.groups_routed, g2.shared_rows, g2.groups_shared, afd::kTileRows);
+  }
   {
     StageScope s(h, st, AFD_STAGE_GATE_UP);
-    hipError_t e = afd::launch_gemm_fp8(g1, true, items1, h->gemm_blocks[4], st);
+    hipError_t e = tiled ? afd::launch_gemm_fp8_tiled(g1, true, items1, h->num_cus, st)
+                         : afd::launch_gemm_fp8(g1, true, items1, h->gemm_blocks[4], st);
     if (e != hipSuccess) return hip_fail(e, "fp8 gate/up GEMM launch");
     s.done();
   }
@@ -129,7 +138,8 @@ int forward_fp8(afd_ffn* h, const void* x, int T, const afd_route* r, void* y, h
   }
   {
     StageScope s(h, st, AFD_STAGE_DOWN);
-    hipError_t e = afd::launch_gemm_fp8(g2, false, items2, h->gemm_blocks[5], st);
+    hipError_t e = tiled ? afd::launch_gemm_fp8_tiled(g2, false, items2, h->num_cus, st)
+                         : afd::launch_gemm_fp8(g2, false, items2, h->gemm_blocks[5], st);
     if (e != hipSuccess) return hip_fail(e, "fp8 down GEMM launch");
     s.done();
   }

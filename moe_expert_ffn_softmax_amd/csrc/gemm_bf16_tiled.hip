@@ -20,12 +20,19 @@
 
 namespace afd {
 
-constexpr int kTiledThreads = 256;
-constexpr int kTiledWaves = 4;
 constexpr int kTiledRowBlocks = 8;                      // 16-row blocks per tile
 constexpr int kTiledRows = 16 * kTiledRowBlocks;        // 128
 constexpr int kTiledGroupsPerWave = 2;                  // 32-column groups per wave
-constexpr int kTiledGroups = kTiledWaves * kTiledGroupsPerWave;  // per item
+constexpr int kTiledWavesN = 4;                         // waves across the columns
+constexpr int kTiledGroups = kTiledWavesN * kTiledGroupsPerWave;  // per item
+#ifndef AFD_TILED_WAVES_M
+#define AFD_TILED_WAVES_M 1
+#endif
+constexpr int kTiledWavesM = AFD_TILED_WAVES_M;         // waves across the rows (1 or 2)
+constexpr int kTiledWaves = kTiledWavesM * kTiledWavesN;
+constexpr int kTiledThreads = kTiledWaves * kWave;
+constexpr int kTiledWaveRowBlocks = kTiledRowBlocks / kTiledWavesM;  // row blocks per wave
+constexpr int kTiledStageBlocks = kTiledRowBlocks / kTiledWaves;     // row blocks each wave stages
 #ifndef AFD_TILED_B_AHEAD
 #define AFD_TILED_B_AHEAD 4
 #endif
@@ -39,7 +46,7 @@ struct TiledSmem {
 };
 
 #ifndef AFD_TILED_B_NT
-#define AFD_TILED_B_NT 1
+#define AFD_TILED_B_NT 0
 #endif
 __device__ __forceinline__ bf16x8 tiled_load_b(const i32x4* p) {
 #if AFD_TILED_B_NT
@@ -59,6 +66,8 @@ __global__ void __launch_bounds__(kTiledThreads, 1) gemm_bf16_tiled_kernel(Group
   const int total = build_item_prefix(g, kTiledRows, kTiledGroups, prefix, scan_tmp);
   const int lane = lane_id();
   const int w = threadIdx.x / kWave;
+  const int wm = w / kTiledWavesN;  // row half of this wave
+  const int wn = w % kTiledWavesN;  // column quarter of this wave
 
   // XCD-aware striding: this workgroup's XCD owns a contiguous range of items
   const int xcd = blockIdx.x % kXcds;
@@ -73,16 +82,21 @@ __global__ void __launch_bounds__(kTiledThreads, 1) gemm_bf16_tiled_kernel(Group
     const int KB = K / 32;
     const int NC = KB / KC;
     const int groups = it.shared ? g.groups_shared : g.groups_routed;
-    const int group0 = it.group + w * kTiledGroupsPerWave;  // first group of this wave
-    const bool active = group0 < groups;                    // wave-uniform
+    // First group of this wave.  A wave past the last group of a partial column tile
+    // recomputes the tile's last two groups and stores nothing: the main loop stays
+    // free of branches, which keeps the accumulators in place (a branch around the
+    // MFMAs made the compiler copy all of them through VGPRs every chunk).  Group
+    // counts are even (multiples of 128 columns), so group0 + 1 < groups.
+    const bool active = it.group + wn * kTiledGroupsPerWave < groups;  // wave-uniform
+    const int group0 = active ? it.group + wn * kTiledGroupsPerWave : groups - kTiledGroupsPerWave;
 
-    // this lane's two A rows (row blocks 2w and 2w+1), clamped into the tile
+    // this lane's staged A rows (row blocks w * kTiledStageBlocks + j), clamped
     const int lda = it.shared ? g.lda_shared : g.lda_routed;
     const __bf16* abase = static_cast<const __bf16*>(it.shared ? g.a_shared : g.a_routed);
-    const bf16x8* arow[2];
+    const bf16x8* arow[kTiledStageBlocks];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      int r = (2 * w + j) * 16 + (lane & 15);
+    for (int j = 0; j < kTiledStageBlocks; ++j) {
+      int r = (w * kTiledStageBlocks + j) * 16 + (lane & 15);
       r = r < it.nrows ? r : 0;
       int ar;
       if (it.shared)
@@ -94,117 +108,110 @@ __global__ void __launch_bounds__(kTiledThreads, 1) gemm_bf16_tiled_kernel(Group
     // weights of this wave: groups group0, group0 + 1, each [KB][2 halves][64 lanes]
     const __bf16* wbase = it.shared ? static_cast<const __bf16*>(g.w_shared)
                                     : static_cast<const __bf16*>(g.w_routed) + (size_t)it.seg * g.w_expert_elems;
-    const i32x4* B = reinterpret_cast<const i32x4*>(wbase) + (size_t)(active ? group0 : 0) * KB * 128 + lane;
+    const i32x4* B = reinterpret_cast<const i32x4*>(wbase) + (size_t)group0 * KB * 128 + lane;
     const size_t group_stride = (size_t)KB * 128;
 
-    f32x4 acc[kTiledRowBlocks][4];
+    f32x4 acc[kTiledWaveRowBlocks][4];
 #pragma unroll
-    for (int rb = 0; rb < kTiledRowBlocks; ++rb)
+    for (int rb = 0; rb < kTiledWaveRowBlocks; ++rb)
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // weight ring: step s lives in slot s % kTiledBAhead
     bf16x8 bring[kTiledBAhead][4];
-    if (active) {
 #pragma unroll
-      for (int u = 0; u < kTiledBAhead; ++u)
+    for (int u = 0; u < kTiledBAhead; ++u)
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb)
-          bring[u][cb] = tiled_load_b(B + (cb >> 1) * group_stride + (u * 2 + (cb & 1)) * 64);
-    }
+      for (int cb = 0; cb < 4; ++cb)
+        bring[u][cb] = tiled_load_b(B + (cb >> 1) * group_stride + (u * 2 + (cb & 1)) * 64);
 
     // A chunk 0 -> LDS buffer 0, chunk 1 -> staging registers
-    bf16x8 stage[2][KC];
+    bf16x8 stage[kTiledStageBlocks][KC];
 #pragma unroll
     for (int u = 0; u < KC; ++u)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) stage[j][u] = arow[j][u * 4];
+      for (int j = 0; j < kTiledStageBlocks; ++j) stage[j][u] = arow[j][u * 4];
 #pragma unroll
     for (int u = 0; u < KC; ++u)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) sm.a[0][u][2 * w + j][lane] = stage[j][u];
+      for (int j = 0; j < kTiledStageBlocks; ++j) sm.a[0][u][w * kTiledStageBlocks + j][lane] = stage[j][u];
     if (NC > 1) {
 #pragma unroll
       for (int u = 0; u < KC; ++u)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) stage[j][u] = arow[j][(KC + u) * 4];
+        for (int j = 0; j < kTiledStageBlocks; ++j) stage[j][u] = arow[j][(KC + u) * 4];
     }
     __syncthreads();
 
     for (int c = 0; c < NC; ++c) {
       const int buf = c & 1;
-      if (active) {
 #pragma unroll
-        for (int u = 0; u < KC; ++u) {
-          const int slotb = u % kTiledBAhead;
-          bf16x8 a[kTiledRowBlocks];
+      for (int u = 0; u < KC; ++u) {
+        const int slotb = u % kTiledBAhead;
+        bf16x8 a[kTiledWaveRowBlocks];
 #pragma unroll
-          for (int rb = 0; rb < kTiledRowBlocks; ++rb) a[rb] = sm.a[buf][u][rb][lane];
+        for (int rb = 0; rb < kTiledWaveRowBlocks; ++rb) a[rb] = sm.a[buf][u][wm * kTiledWaveRowBlocks + rb][lane];
 #pragma unroll
-          for (int rb = 0; rb < kTiledRowBlocks; ++rb)
-#pragma unroll
-            for (int cb = 0; cb < 4; ++cb)
-              acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[rb], bring[slotb][cb], acc[rb][cb], 0, 0, 0);
-          // refill this ring slot with the step kTiledBAhead ahead (clamped to the last)
-          int s = c * KC + u + kTiledBAhead;
-          s = s < KB ? s : KB - 1;
+        for (int rb = 0; rb < kTiledWaveRowBlocks; ++rb)
 #pragma unroll
           for (int cb = 0; cb < 4; ++cb)
-            bring[slotb][cb] = tiled_load_b(B + (cb >> 1) * group_stride + (s * 2 + (cb & 1)) * 64);
-        }
+            acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[rb], bring[slotb][cb], acc[rb][cb], 0, 0, 0);
+        // refill this ring slot with the step kTiledBAhead ahead (clamped to the last)
+        int s = c * KC + u + kTiledBAhead;
+        s = s < KB ? s : KB - 1;
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+          bring[slotb][cb] = tiled_load_b(B + (cb >> 1) * group_stride + (s * 2 + (cb & 1)) * 64);
       }
       if (c + 1 < NC) {
 #pragma unroll
         for (int u = 0; u < KC; ++u)
 #pragma unroll
-          for (int j = 0; j < 2; ++j) sm.a[buf ^ 1][u][2 * w + j][lane] = stage[j][u];
+          for (int j = 0; j < kTiledStageBlocks; ++j) sm.a[buf ^ 1][u][w * kTiledStageBlocks + j][lane] = stage[j][u];
       }
       __syncthreads();
       if (c + 2 < NC) {
 #pragma unroll
         for (int u = 0; u < KC; ++u)
 #pragma unroll
-          for (int j = 0; j < 2; ++j) stage[j][u] = arow[j][((c + 2) * KC + u) * 4];
+          for (int j = 0; j < kTiledStageBlocks; ++j) stage[j][u] = arow[j][((c + 2) * KC + u) * 4];
       }
     }
 
     if (active) {
       const int col = lane & 15;
       const int rsub = (lane >> 4) * 4;
+      const int rw0 = wm * kTiledWaveRowBlocks * 16;  // first tile row of this wave
       if (SWIGLU) {
         __bf16* out = static_cast<__bf16*>(it.shared ? g.out_shared : g.out_routed);
         const int ldo = it.shared ? g.ldo_shared : g.ldo_routed;
 #pragma unroll
-        for (int gi = 0; gi < kTiledGroupsPerWave; ++gi) {
-          if (group0 + gi >= groups) break;
+        for (int gi = 0; gi < kTiledGroupsPerWave; ++gi)
 #pragma unroll
-          for (int rb = 0; rb < kTiledRowBlocks; ++rb)
+          for (int rb = 0; rb < kTiledWaveRowBlocks; ++rb)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              const int row = rb * 16 + rsub + i;
+              const int row = rw0 + rb * 16 + rsub + i;
               if (row < it.nrows)
                 out[(size_t)(it.row0 + row) * ldo + (group0 + gi) * 16 + col] =
                     f32_to_bf16(silu(acc[rb][2 * gi][i]) * acc[rb][2 * gi + 1][i]);
             }
-        }
       } else {
         float* out = static_cast<float*>(it.shared ? g.out_shared : g.out_routed);
         const int ldo = it.shared ? g.ldo_shared : g.ldo_routed;
 #pragma unroll
-        for (int gi = 0; gi < kTiledGroupsPerWave; ++gi) {
-          if (group0 + gi >= groups) break;
+        for (int gi = 0; gi < kTiledGroupsPerWave; ++gi)
 #pragma unroll
-          for (int rb = 0; rb < kTiledRowBlocks; ++rb)
+          for (int rb = 0; rb < kTiledWaveRowBlocks; ++rb)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              const int row = rb * 16 + rsub + i;
+              const int row = rw0 + rb * 16 + rsub + i;
               if (row < it.nrows) {
                 float* o = out + (size_t)(it.row0 + row) * ldo + (group0 + gi) * 32 + col;
                 o[0] = acc[rb][2 * gi][i];
                 o[16] = acc[rb][2 * gi + 1][i];
               }
             }
-        }
       }
     }
     // the next item's first LDS writes must not overtake this item's last reads
