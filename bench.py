@@ -50,6 +50,10 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="one JSON line per workload: every layer shape plus the 256/512/1024 tokens-per-expert "
+                         "bf16 and fp8 sweeps (HBM and MFMA fractions); not the benchmark line")
+    ap.add_argument("--only", default="", help="with --sweep: run the workloads whose name contains this text")
     return ap.parse_args()
 
 
@@ -145,6 +149,66 @@ def cpu_baseline(w, weights, batches, seconds):
                       f"{spent:.1f} s of oracle time on the host, double precision"}
 
 
+def run_workload(w, steps, warmup, batches, gemm, torch):
+    """Time `steps` route+forward steps of workload `w`; returns a dict of figures."""
+    from moe_expert_ffn_softmax_amd import MoeExpertFFN, afd_ffn_profile_read, afd_ffn_set_profiling
+    weights = workloads.make_weights(w, device="cuda")
+    layer = MoeExpertFFN(hidden=w.H, inter=w.M, num_experts=w.E, top_k=w.k, max_tokens=w.T, dtype=w.dtype,
+                         w_gate_up=weights["w_gu"], w_down=weights["w_d"], s_gate_up=weights["s_gu"],
+                         s_down=weights["s_d"], shared_inter=w.Ms, ws_gate_up=weights["ws_gu"],
+                         ws_down=weights["ws_d"], ss_gate_up=weights["ss_gu"], ss_down=weights["ss_d"])
+    layer.set_gemm_kernel(gemm)
+    del weights
+    ydt = torch.float32 if w.dtype == "f32" else torch.bfloat16
+    xs, lgs, ys, rbs = [], [], [], []
+    for b in range(batches):
+        x, lg = workloads.make_activations(w, device="cuda", batch=b)
+        xs.append(x)
+        lgs.append(lg)
+        ys.append(torch.empty((w.T, w.H), dtype=ydt, device="cuda"))
+        rbs.append(layer.new_route())
+
+    def step(i):
+        b = i % batches
+        layer.route(lgs[b], w.T, rbs[b])
+        layer.forward(xs[b], w.T, rbs[b], ys[b])
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    afd_ffn_set_profiling(layer.handle, True)
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    prof = afd_ffn_profile_read(layer.handle)
+    counts = [rb.expert_counts.cpu().numpy() for rb in rbs]
+    layer.close()
+    step_bytes = float(np.mean([algorithmic_bytes(w, c)[0] for c in counts]))
+    tflops = w.flops() / (ms / 1e3) / 1e12
+    gbs = step_bytes / (ms / 1e3) / 1e9
+    return {"workload": w.name, "dtype": w.dtype, "tokens_per_expert": round(w.tokens_per_expert, 2),
+            "ms_per_step": round(ms, 4), "tokens_per_s": round(w.T / (ms / 1e3), 1), "tflops": round(tflops, 2),
+            "hbm_GBps": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+            "mfma_frac": round(tflops / MFMA_PEAK_TFLOPS[w.dtype], 4),
+            "kernels_us": {k: round(v[0] / max(v[1], 1) * 1e3, 2) for k, v in prof.items() if v[1]}}
+
+
+def sweep(args, torch):
+    wls = list(workloads.ORDERED) + workloads.mfma_sweep("bf16") + workloads.mfma_sweep("fp8")
+    for w in wls:
+        if args.only and not any(o in w.name for o in args.only.split(",")):
+            continue
+        steps = args.steps if w.T <= 64 else max(3, min(args.steps, 20))
+        r = run_workload(w, steps, min(args.warmup, 3), min(args.batches, 4 if w.T <= 64 else 2), args.gemm, torch)
+        print(json.dumps(r), flush=True)
+        torch.cuda.empty_cache()
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -154,6 +218,10 @@ def main():
     import torch
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.sweep:
+        torch.cuda.set_device(0)
+        sweep(args, torch)
         return
     from moe_expert_ffn_softmax_amd import MoeExpertFFN, afd_ffn_profile_read, afd_ffn_set_profiling
 
