@@ -45,7 +45,7 @@ def parse():
     ap.add_argument("--workload", default=workloads.STARVED_DECODE.name)
     ap.add_argument("--batches", type=int, default=16, help="distinct resident batches cycled over the steps")
     ap.add_argument("--graph", action="store_true", help="replay route+forward from a captured HIP graph")
-    ap.add_argument("--gemm", default="auto", choices=["auto", "stream", "tiled"],
+    ap.add_argument("--gemm", default="auto", choices=["auto", "stream", "tiled", "wide"],
                     help="grouped-GEMM kernel: automatic choice, 16-row streaming tiles or 128-row tiles")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)

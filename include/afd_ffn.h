@@ -145,9 +145,17 @@ int afd_ffn_quantize_fp8(const void* src, int32_t rows, int32_t cols, int32_t sr
 /* Choice of grouped-GEMM kernel for bf16 and fp8 layers.  AFD_GEMM_AUTO (the default)
  * uses 16-row weight-streaming tiles while experts average at most 16 routed rows
  * per batch (T * top_k <= 16 * E) and 128-row tiles above that; the other values
- * force one kernel (results agree to rounding; a tuning and testing knob).  fp32
- * layers always use their own kernel.  Takes effect for later forward calls. */
-typedef enum afd_gemm_kernel { AFD_GEMM_AUTO = 0, AFD_GEMM_STREAM = 1, AFD_GEMM_TILED = 2 } afd_gemm_kernel;
+ * force one kernel (results agree to rounding; a tuning and testing knob).
+ * AFD_GEMM_WIDE (256x256 tiles, both operands staged in LDS) is never chosen
+ * automatically and applies to bf16 layers only (fp8 layers take the 128-row kernel
+ * instead).  fp32 layers always use their own kernel.  Takes effect for later
+ * forward calls. */
+typedef enum afd_gemm_kernel {
+  AFD_GEMM_AUTO = 0,
+  AFD_GEMM_STREAM = 1,
+  AFD_GEMM_TILED = 2,
+  AFD_GEMM_WIDE = 3
+} afd_gemm_kernel;
 int afd_ffn_set_gemm_kernel(afd_ffn_t h, int kernel);
 
 /* Per-kernel timing.  With profiling on, route and forward bracket each kernel

@@ -9,12 +9,13 @@ PyTorch fallback: if libafd_ffn.so is missing, constructing a layer raises.
 from __future__ import annotations
 
 from ._ffi import (AFD_BF16, AFD_F32, AFD_FP8_E4M3, AFD_GEMM_AUTO, AFD_GEMM_STREAM,  # noqa: F401
-                   AFD_GEMM_TILED, STAGES, AfdError, afd_ffn_config, afd_ffn_create, afd_ffn_destroy,
+                   AFD_GEMM_TILED, AFD_GEMM_WIDE, STAGES, AfdError, afd_ffn_config, afd_ffn_create, afd_ffn_destroy,
                    afd_ffn_device_bytes, afd_ffn_forward, afd_ffn_last_error, afd_ffn_profile_read,
                    afd_ffn_quantize_fp8, afd_ffn_route, afd_ffn_set_gemm_kernel, afd_ffn_set_profiling,
                    afd_ffn_strerror, afd_route, load)
 
-GEMM_KERNELS = {"auto": AFD_GEMM_AUTO, "stream": AFD_GEMM_STREAM, "tiled": AFD_GEMM_TILED}
+GEMM_KERNELS = {"auto": AFD_GEMM_AUTO, "stream": AFD_GEMM_STREAM, "tiled": AFD_GEMM_TILED,
+                "wide": AFD_GEMM_WIDE}
 
 DTYPES = {"f32": AFD_F32, "bf16": AFD_BF16, "fp8": AFD_FP8_E4M3}
 
@@ -72,7 +73,8 @@ class MoeExpertFFN:
                                      ss_gate_up, ss_down, _stream_handle(torch))
 
     def set_gemm_kernel(self, name: str) -> None:
-        """'auto', 'stream' (16-row weight-streaming tiles) or 'tiled' (128-row tiles)."""
+        """'auto', 'stream' (16-row weight-streaming tiles), 'tiled' (128-row tiles) or
+        'wide' (256x256 tiles, bf16 layers)."""
         afd_ffn_set_gemm_kernel(self.handle, GEMM_KERNELS[name])
 
     def new_route(self) -> RouteBuffers:

@@ -93,9 +93,17 @@ struct StageScope {
 // Kernel choice for a batch of P routed pairs: the 128-row tiled GEMM once experts
 // average more than 16 rows (one streaming tile), unless forced either way.
 bool use_tiled(const afd_ffn* h, int P) {
-  if (h->gemm_mode == 1) return false;
-  if (h->gemm_mode == 2) return true;
+  if (h->gemm_mode == AFD_GEMM_STREAM) return false;
+  if (h->gemm_mode == AFD_GEMM_TILED || h->gemm_mode == AFD_GEMM_WIDE) return true;
   return (long long)P > 16ll * h->cfg.num_experts;
+}
+
+// bf16 layers: the 256x256-tile GEMM only when forced.  It moves a third less operand
+// traffic per FLOP through L1/L2, but twice the LDS traffic, and measured no faster
+// than the 128-row kernel at 512 and 1024 rows per expert.
+bool use_wide(const afd_ffn* h, int P) {
+  (void)P;
+  return h->gemm_mode == AFD_GEMM_WIDE;
 }
 
 // fp8 layer: quantise x -> gate/up GEMM (fp32 h) -> quantise h -> down GEMM -> combine.
@@ -415,10 +423,18 @@ extern "C" int afd_ffn_forward(afd_ffn_t h, const void* x, int32_t T, const afd_
   }
 
   // Few rows per expert (decode batches): 16-row weight-streaming tiles.  Many rows:
-  // 128-row tiles, so each expert's weights are read once per 128 of its rows.
+  // 128-row tiles, so each expert's weights are read once per 128 of its rows; several
+  // hundred rows: 256x256 tiles.
   const bool tiled = !f32 && use_tiled(h, P);
+  const bool wide = tiled && use_wide(h, P);
   long long items1, items2;
-  if (tiled) {
+  if (wide) {
+    const int tr = afd::wide_rows(), tg = afd::wide_groups();
+    items1 = afd::grouped_items_bound(P, E, (g1.groups_routed + tg - 1) / tg, g1.shared_rows,
+                                      (g1.groups_shared + tg - 1) / tg, tr);
+    items2 = afd::grouped_items_bound(P, E, (g2.groups_routed + tg - 1) / tg, g2.shared_rows,
+                                      (g2.groups_shared + tg - 1) / tg, tr);
+  } else if (tiled) {
     const int tr = afd::tiled_rows(), tg = afd::tiled_groups();
     items1 = afd::grouped_items_bound(P, E, (g1.groups_routed + tg - 1) / tg, g1.shared_rows,
                                       (g1.groups_shared + tg - 1) / tg, tr);
@@ -431,6 +447,7 @@ extern "C" int afd_ffn_forward(afd_ffn_t h, const void* x, int32_t T, const afd_
   {
     StageScope s(h, st, AFD_STAGE_GATE_UP);
     hipError_t e = f32     ? afd::launch_gemm_f32(g1, true, items1, h->gemm_blocks[2], st)
+                   : wide  ? afd::launch_gemm_bf16_wide(g1, true, items1, h->num_cus, st)
                    : tiled ? afd::launch_gemm_bf16_tiled(g1, true, items1, h->num_cus, st)
                            : afd::launch_gemm_bf16(g1, true, items1, h->gemm_blocks[0], st);
     if (e != hipSuccess) return hip_fail(e, "gate/up GEMM launch");
@@ -439,6 +456,7 @@ extern "C" int afd_ffn_forward(afd_ffn_t h, const void* x, int32_t T, const afd_
   {
     StageScope s(h, st, AFD_STAGE_DOWN);
     hipError_t e = f32     ? afd::launch_gemm_f32(g2, false, items2, h->gemm_blocks[3], st)
+                   : wide  ? afd::launch_gemm_bf16_wide(g2, false, items2, h->num_cus, st)
                    : tiled ? afd::launch_gemm_bf16_tiled(g2, false, items2, h->num_cus, st)
                            : afd::launch_gemm_bf16(g2, false, items2, h->gemm_blocks[1], st);
     if (e != hipSuccess) return hip_fail(e, "down GEMM launch");
@@ -456,7 +474,7 @@ extern "C" int afd_ffn_forward(afd_ffn_t h, const void* x, int32_t T, const afd_
 
 extern "C" int afd_ffn_set_gemm_kernel(afd_ffn_t h, int kernel) {
   if (!h) return fail(AFD_EINVAL, "handle is NULL");
-  if (kernel < AFD_GEMM_AUTO || kernel > AFD_GEMM_TILED) return fail(AFD_EINVAL, "unknown GEMM kernel %d", kernel);
+  if (kernel < AFD_GEMM_AUTO || kernel > AFD_GEMM_WIDE) return fail(AFD_EINVAL, "unknown GEMM kernel %d", kernel);
   h->gemm_mode = kernel;
   return AFD_OK;
 }

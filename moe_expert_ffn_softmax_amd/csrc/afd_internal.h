@@ -82,6 +82,11 @@ hipError_t launch_gemm_bf16_tiled(const GroupedGemm& g, bool swiglu, long long m
                                   hipStream_t st);
 int tiled_rows();
 int tiled_groups();
+// 256x256-tile variant (both operands through LDS) for experts with hundreds of rows.
+hipError_t launch_gemm_bf16_wide(const GroupedGemm& g, bool swiglu, long long max_items, int max_blocks,
+                                 hipStream_t st);
+int wide_rows();
+int wide_groups();
 
 // fp8 (e4m3, fp32 block scales) streaming variant; weights packed by launch_pack_fp8,
 // A = fp8 codes with per-row per-128 scales `as_*`, weight scales `s_*`; writes fp32.
@@ -133,7 +138,7 @@ struct afd_ffn {
   float* hs_shared;   // [T_max, Ms/128]
   int gemm_blocks[6];  // resident workgroups of each GEMM kernel on the whole device
                        // (bf16 gate/up, down; fp32 gate/up, down; fp8 gate/up, down)
-  int gemm_mode;       // 0 automatic, 1 always 16-row streaming, 2 always 128-row tiles
+  int gemm_mode;       // afd_gemm_kernel: automatic, or always 16-row, 128-row or 256x256 tiles
   size_t device_bytes;
   // profiling
   bool profiling;

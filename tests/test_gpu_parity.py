@@ -197,7 +197,7 @@ def test_route_full_size_every_workload(w):
     small("many_experts", T=9, E=1024, k=32, H=128, M=128),
     small("wide_f32", dtype="f32", T=17, H=384, M=128, E=6, k=3),
 ], ids=lambda w: w.name)
-@pytest.mark.parametrize("kernel", ["stream", "tiled"])
+@pytest.mark.parametrize("kernel", ["stream", "tiled", "wide"])
 def test_small_shapes(w, kernel):
     full_case(w, kernel=kernel)
 
@@ -221,6 +221,18 @@ def test_tiled_shapes(w):
     """Experts with several 128-row tiles (ragged last tile), a column count that
     leaves half of the last column tile empty, and long reductions."""
     full_case(w, kernel="tiled")
+
+
+@pytest.mark.parametrize("w", [
+    small("wide_multi_tile", T=700, E=2, k=1, H=256, M=256, Ms=384),
+    small("wide_half_column_tile", T=300, E=3, k=2, H=128, M=128),
+    small("wide_long_k", T=600, E=2, k=2, H=1024, M=640, Ms=128),
+], ids=lambda w: w.name)
+def test_wide_shapes(w):
+    """256x256 tiles: experts with two or more row tiles (the last ragged), a column
+    count of 4 groups (the second wave column of every tile idle), long reductions
+    and a shared expert segment."""
+    full_case(w, kernel="wide")
 
 
 def test_skewed_routing_multi_tile_expert():
