@@ -25,13 +25,23 @@ HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
              "-I", INCLUDE, "-I", CSRC]
 
 
+# Per-file code-generation options.  The fp8 tiled GEMM rescales every MFMA result
+# with VALU FMAs; asking for the VGPR form of the MFMA destination keeps the results
+# out of the accumulator registers (no copy back per value).
+FILE_FLAGS = {"gemm_fp8_tiled.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
+def flags_for(src: str):
+    return [*HIP_FLAGS, *FILE_FLAGS.get(os.path.basename(src), [])]
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *HIP_FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *flags_for(src), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)
     if r.returncode != 0:

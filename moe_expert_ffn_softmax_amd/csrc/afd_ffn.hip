@@ -121,7 +121,7 @@ int forward_fp8(afd_ffn* h, const void* x, int T, const afd_route* r, void* y, h
   const bool tiled = use_tiled(h, P);
   long long items1, items2;
   if (tiled) {
-    const int tr = afd::tiled_rows(), tg = afd::tiled_groups();
+    const int tr = afd::fp8_tiled_rows(), tg = afd::fp8_tiled_groups();
     items1 = afd::grouped_items_bound(P, E, (g1.groups_routed + tg - 1) / tg, g1.shared_rows,
                                       (g1.groups_shared + tg - 1) / tg, tr);
     items2 = afd::grouped_items_bound(P, E, (g2.groups_routed + tg - 1) / tg, g2.shared_rows,

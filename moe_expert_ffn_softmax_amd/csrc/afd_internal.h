@@ -93,6 +93,8 @@ int wide_groups();
 hipError_t launch_gemm_fp8(const GroupedGemm& g, bool swiglu, long long max_items, int max_blocks, hipStream_t st);
 hipError_t launch_gemm_fp8_tiled(const GroupedGemm& g, bool swiglu, long long max_items, int max_blocks,
                                  hipStream_t st);
+int fp8_tiled_rows();
+int fp8_tiled_groups();
 hipError_t launch_pack_fp8(const uint8_t* src, uint8_t* dst, int nmat, int R, int C, int gate_up, hipStream_t st);
 // rows x cols activations (bf16 or fp32, row stride ld) -> e4m3 codes [rows, cols]
 // and fp32 scales [rows, cols / 128].

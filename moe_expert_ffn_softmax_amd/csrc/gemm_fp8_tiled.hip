@@ -3,41 +3,52 @@
 // receive many rows (the DeepSeek-V3-like layer of an FFN instance aggregating
 // attention batches; FP8/BF16 mixed precision: the omica.com.cn AFD article, §3.3).
 //
-// A workgroup of kFp8TiledWavesM x 4 waves computes a 128-row tile of one expert
-// times 8 32-column groups; wave (m, n) owns rows m * 128 / WM .. and groups 2n, 2n+1.
-// One reduction step is one 128-deep scale block, i.e. one
-// v_mfma_scale_f32_16x16x128_f8f6f4 per 16x16 block; its fp32 partial product is
-// added times s_act[row][kb] * s_w[kb][nb].  Weight fragments (2 KiB: 64 lanes x 32
-// bytes) stream from HBM straight into registers a few steps ahead; the 128 gathered
-// activation rows (fp8 codes) and their per-row scales are staged through
-// double-buffered LDS, chunk by chunk, shared by all waves.  Items and XCD ranges as
-// in the bf16 tiled kernel.
+// A workgroup of 4 waves computes a 128-token tile of one expert times 8 32-column
+// groups; wave w owns groups 2w and 2w+1 for all 128 tokens.  The matrix-core
+// instruction is v_mfma_scale_f32_16x16x128_f8f6f4 (unit E8M0 scales): one
+// instruction covers one 128-deep scale block of a 16 x 16 output block, and its fp32
+// partial product is added to the accumulator times s_act[token][kb] * s_w[kb][nb].
+//
+// Operand roles.  The weights are the instruction's first operand and the tokens its
+// second, so the 16 x 16 result is (weight column) x (token): lane l holds columns
+// (l / 16) * 4 .. + 3 of token l % 16.  Each lane then needs one activation scale per
+// token block and scale block, and the weight scale is uniform over a 16-column
+// block: rescaling a partial product is one multiply and four FMAs.  Lane l supplies
+// column (or token) l % 16 at reduction offsets (l / 16) * 32 .. + 31 of the 128-deep
+// block; the packed weight layout (see gemm_fp8.hip) is exactly that order, so a
+// fragment is one contiguous 2 KiB run.
+//
+// Activation staging.  A 256-deep chunk (two scale blocks) of the 128 gathered token
+// rows is loaded as 4 rows x 256 contiguous bytes per instruction (lane l: row l / 16,
+// 16-byte piece l % 16) and written to LDS in operand order: token block b (16 rows)
+// has 16 slots of 272 bytes, slot q holding piece q of its 16 rows at (row % 16) * 16.
+// Piece q of a chunk is (scale block q / 8, reduction group (q % 8) / 2, 16-byte half
+// q % 2) of the operand.  The 16 lanes writing one row hit 16 different bank groups;
+// a 16-lane quarter of an operand read is one slot, contiguous.  The tokens' scales of
+// the chunk are staged beside them.  Double-buffered; the next chunk is loaded into
+// registers while the current one is multiplied.
+//
+// Items and XCD ranges as in the bf16 tiled kernel.
 #include "grouped.h"
 
 namespace afd {
 
-constexpr int kF8RowBlocks = 8;
-constexpr int kF8Rows = 16 * kF8RowBlocks;  // 128
-constexpr int kF8GroupsPerWave = 2;
-constexpr int kF8WavesN = 4;
-constexpr int kF8Groups = kF8WavesN * kF8GroupsPerWave;
-#ifndef AFD_FP8_TILED_WAVES_M
-#define AFD_FP8_TILED_WAVES_M 2
-#endif
-constexpr int kF8WavesM = AFD_FP8_TILED_WAVES_M;
-constexpr int kF8Waves = kF8WavesM * kF8WavesN;
+constexpr int kF8Waves = 4;
 constexpr int kF8Threads = kF8Waves * kWave;
-constexpr int kF8WaveRowBlocks = kF8RowBlocks / kF8WavesM;
-constexpr int kF8StageBlocks = kF8RowBlocks / kF8Waves;
-constexpr int kF8BAhead = 2;  // 128-deep weight steps in flight per wave (8 KiB each); the
-                              // even/odd step loop below relies on this being 2
-constexpr int kF8Chunk = 1;   // 128-deep steps per staged activation chunk
+constexpr int kF8RowBlocks = 8;                 // 16-token blocks per tile
+constexpr int kF8Rows = 16 * kF8RowBlocks;      // 128
+#ifndef AFD_FP8_TILED_GPW
+#define AFD_FP8_TILED_GPW 2
+#endif
+constexpr int kF8GroupsPerWave = AFD_FP8_TILED_GPW;  // 32-column groups per wave (1 or 2)
+constexpr int kF8Groups = kF8Waves * kF8GroupsPerWave;
+constexpr int kF8CB = 2 * kF8GroupsPerWave;     // 16-column blocks per wave
+constexpr int kF8Slot = 272;                    // bytes per staging slot (16 rows x 16 B + padding)
+constexpr int kF8A = kF8RowBlocks * 16 * kF8Slot;  // activation bytes per buffer
+constexpr int kF8Buf = kF8A + 2 * kF8Rows * 4;  // + the chunk's two scale columns
+constexpr int kF8Loads = 8;                     // staging loads per thread per chunk (4 rows each)
+constexpr int kF8BAhead = 2;                    // scale blocks of weights in flight per wave
 constexpr int kF8Xcds = 8;
-
-struct Fp8TiledSmem {
-  i32x8 a[2][kF8Chunk][kF8RowBlocks][kWave];  // [buffer][step][row block][lane] 32-byte fragments
-  float s[2][kF8Chunk][kF8Rows];              // activation scales of the staged rows
-};
 
 __device__ __forceinline__ f32x4 f8_mfma(const i32x8& a, const i32x8& b) {
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
@@ -50,17 +61,21 @@ __device__ __forceinline__ i32x8 f8_load32(const uint8_t* p) {
   return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
+#ifndef AFD_FP8_TILED_MIN_BLOCKS
+#define AFD_FP8_TILED_MIN_BLOCKS 1
+#endif
+constexpr int kF8MinBlocks = AFD_FP8_TILED_MIN_BLOCKS;  // workgroups per CU the registers must allow
+
 template <bool SWIGLU>
-__global__ void __launch_bounds__(kF8Threads, 1) gemm_fp8_tiled_kernel(GroupedGemm g) {
+__global__ void __launch_bounds__(kF8Threads, kF8MinBlocks) gemm_fp8_tiled_kernel(GroupedGemm g) {
   __shared__ int prefix[kMaxSegments + 1];
   __shared__ int scan_tmp[kF8Waves + 1];
-  extern __shared__ __attribute__((aligned(16))) unsigned char dyn_smem[];
-  Fp8TiledSmem& sm = *reinterpret_cast<Fp8TiledSmem*>(dyn_smem);
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
 
   const int total = build_item_prefix(g, kF8Rows, kF8Groups, prefix, scan_tmp);
-  const int w = threadIdx.x / kWave;
-  const int wm = w / kF8WavesN;
-  const int wn = w % kF8WavesN;
+  // wave index, made visibly uniform so that per-wave values (group, scale indices,
+  // weight bases) live in scalar registers and use scalar loads
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
 
   const int xcd = blockIdx.x % kF8Xcds;
   const int slot = blockIdx.x / kF8Xcds;
@@ -69,42 +84,45 @@ __global__ void __launch_bounds__(kF8Threads, 1) gemm_fp8_tiled_kernel(GroupedGe
   const int end = (int)((long long)total * (xcd + 1) / kF8Xcds);
 
   for (int item = begin + slot; item < end; item += slots) {
-    // Lane-derived indices are recomputed per item: hoisted out of the item loop they
-    // (row indices and addresses of the epilogue) no longer fit the register budget.
+    // lane-derived indices are recomputed per item (hoisted out of the item loop they
+    // do not fit the register budget)
     int lane = lane_id();
     asm volatile("" : "+v"(lane));
     const Item it = decode_item_tiled(g, kF8Rows, kF8Groups, prefix, item);
     const int K = it.shared ? g.K_shared : g.K_routed;
     const int KB = K / 128;
-    const int NC = (KB + kF8Chunk - 1) / kF8Chunk;
+    const int NC = (KB + 1) / 2;  // 256-deep chunks; an odd KB leaves the last chunk half live
     const int groups = it.shared ? g.groups_shared : g.groups_routed;
     const int N = groups * 32;
     const int NB = N / 128;
-    // waves past the last group recompute valid groups and store nothing (even group
-    // counts: group0 + 1 < groups)
-    const bool active = it.group + wn * kF8GroupsPerWave < groups;
-    const int group0 = active ? it.group + wn * kF8GroupsPerWave : groups - kF8GroupsPerWave;
+    // A wave past the last group of a partial column tile recomputes the tile's last
+    // two groups and stores nothing (group counts are multiples of 4).
+    const bool active = it.group + w * kF8GroupsPerWave < groups;  // wave-uniform
+    const int group0 = active ? it.group + w * kF8GroupsPerWave : groups - kF8GroupsPerWave;
 
-    // staged rows of this lane (row blocks w * kF8StageBlocks + j), clamped into the tile
+    // staged rows: w*32 + i*4 + lane/16 (i = 0..7); the lane loads piece lane % 16 of
+    // each row's chunk
     const int lda = it.shared ? g.lda_shared : g.lda_routed;
     const uint8_t* abase = static_cast<const uint8_t*>(it.shared ? g.a_shared : g.a_routed);
-    const float* asbase = it.shared ? g.as_shared : g.as_routed;
-    const uint8_t* arow[kF8StageBlocks];
+    const int piece = lane & 15;
+    const uint8_t* arow[kF8Loads];
 #pragma unroll
-    for (int j = 0; j < kF8StageBlocks; ++j) {
-      int r = (w * kF8StageBlocks + j) * 16 + (lane & 15);
+    for (int i = 0; i < kF8Loads; ++i) {
+      int r = w * 32 + i * 4 + (lane >> 4);
       r = r < it.nrows ? r : 0;
       int ar;
       if (it.shared)
         ar = it.row0 + r;
       else
         ar = g.gather_routed ? g.sorted_pair[it.row0 + r] / g.k : it.row0 + r;
-      arow[j] = abase + (size_t)ar * lda + (lane >> 4) * 32;
+      arow[i] = abase + (size_t)ar * lda;
     }
-    // activation-scale row staged by this thread (threads 0..127: one tile row each)
-    const float* srow = nullptr;
-    if (threadIdx.x < kF8Rows) {
-      int r = threadIdx.x < it.nrows ? threadIdx.x : 0;
+    // token scales of the chunk: thread t < 128 stages row t's two scale-block values
+    const float* asbase = it.shared ? g.as_shared : g.as_routed;
+    const float* srow;
+    {
+      const int t = threadIdx.x < kF8Rows ? threadIdx.x : 0;
+      const int r = t < it.nrows ? t : 0;
       int ar;
       if (it.shared)
         ar = it.row0 + r;
@@ -112,143 +130,156 @@ __global__ void __launch_bounds__(kF8Threads, 1) gemm_fp8_tiled_kernel(GroupedGe
         ar = g.gather_routed ? g.sorted_pair[it.row0 + r] / g.k : it.row0 + r;
       srow = asbase + (size_t)ar * KB;
     }
+    // byte offset in the row of chunk c's piece for this lane (clamped past the end of
+    // K: that scale block is multiplied with weight scale 0)
+    auto a_off = [&](int c) {
+      const int o = c * 256 + piece * 16;
+      return o < K ? o : o - 128;
+    };
+    // LDS: write slot of load i (token block (w*32 + i*4 + lane/16) / 16 = w*2 + i/4,
+    // slot = piece, row in block (i % 4) * 4 + lane / 16)
+    const int wr_off = ((w * 2) * 16 + piece) * kF8Slot + (lane >> 4) * 16;
+    // read: slot (lane / 16) * 2 (+1 for the upper 16 bytes) of the scale block's 8
+    const int rd_off = ((lane >> 4) * 2) * kF8Slot + (lane & 15) * 16;
 
     const uint8_t* wbase = it.shared ? static_cast<const uint8_t*>(g.w_shared)
                                      : static_cast<const uint8_t*>(g.w_routed) + (size_t)it.seg * g.w_expert_elems;
     const size_t group_stride = (size_t)KB * 4096;  // bytes per 32-column group
+    // 16-column block cb = (group group0 + cb / 2, half cb % 2): 2 KiB per scale block
     const uint8_t* B = wbase + (size_t)group0 * group_stride + lane * 32;
     const float* ws = it.shared ? g.s_shared : g.s_routed + (size_t)it.seg * g.s_expert_elems;
-    int nbc[4];
+    int nbc[kF8CB];
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
+    for (int cb = 0; cb < kF8CB; ++cb) {
       const int j = group0 + (cb >> 1), half = cb & 1;
       nbc[cb] = (SWIGLU ? half * (N / 2) + j * 16 : j * 32 + half * 16) / 128;
     }
 
-    f32x4 acc[kF8WaveRowBlocks][4];
+    f32x4 acc[kF8RowBlocks][kF8CB];
 #pragma unroll
-    for (int rb = 0; rb < kF8WaveRowBlocks; ++rb)
+    for (int rb = 0; rb < kF8RowBlocks; ++rb)
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int cb = 0; cb < kF8CB; ++cb) acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    i32x8 bring[kF8BAhead][4];
+    i32x8 bring[kF8BAhead][kF8CB];
 #pragma unroll
     for (int u = 0; u < kF8BAhead; ++u) {
       const int s = u < KB ? u : KB - 1;
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) bring[u][cb] = f8_load32(B + (cb >> 1) * group_stride + (s * 2 + (cb & 1)) * 2048);
+      for (int cb = 0; cb < kF8CB; ++cb) bring[u][cb] = f8_load32(B + (cb >> 1) * group_stride + (s * 2 + (cb & 1)) * 2048);
     }
 
-    // activation chunk 0 -> LDS buffer 0, chunk 1 -> staging registers (steps past
-    // the end of K repeat the last step; they are never consumed)
-    i32x8 stage[kF8StageBlocks][kF8Chunk];
-    float sstage[kF8Chunk];
+    // chunk 0 -> LDS buffer 0, chunk 1 (or 0 again) -> staging registers
+    bf16x8 stage[kF8Loads];
+    float sstage0 = 0.f, sstage1 = 0.f;
+    auto load_stage = [&](int c) {
 #pragma unroll
-    for (int u = 0; u < kF8Chunk; ++u) {
-      const int s = u < KB ? u : KB - 1;
-#pragma unroll
-      for (int j = 0; j < kF8StageBlocks; ++j) stage[j][u] = f8_load32(arow[j] + s * 128);
-      sstage[u] = srow ? srow[s] : 0.f;
-    }
-#pragma unroll
-    for (int u = 0; u < kF8Chunk; ++u) {
-#pragma unroll
-      for (int j = 0; j < kF8StageBlocks; ++j) sm.a[0][u][w * kF8StageBlocks + j][lane] = stage[j][u];
-      if (srow) sm.s[0][u][threadIdx.x] = sstage[u];
-    }
-    if (NC > 1) {
-#pragma unroll
-      for (int u = 0; u < kF8Chunk; ++u) {
-        int s = kF8Chunk + u;
-        s = s < KB ? s : KB - 1;
-#pragma unroll
-        for (int j = 0; j < kF8StageBlocks; ++j) stage[j][u] = f8_load32(arow[j] + s * 128);
-        sstage[u] = srow ? srow[s] : 0.f;
-      }
-    }
-    __syncthreads();
-
-    const int rsub = (lane >> 4) * 4;
-    // One 128-deep step per LDS buffer and per weight-ring slot; the loop handles an
-    // even and an odd step per iteration so that both indices are compile-time
-    // constants (a runtime ring index put the ring in scratch memory).  A step past
-    // the end of K recomputes the last step with weight scale 0 (no branch around the
-    // MFMAs: see the bf16 tiled kernel).
-    auto step = [&](const int c, const int par) {
-      const int kbc = c < KB ? c : KB - 1;
-      const float live = c < KB ? 1.f : 0.f;
-      const i32x8* abuf = &sm.a[par][0][wm * kF8WaveRowBlocks][lane];
-      const float* sbuf = &sm.s[par][0][wm * kF8WaveRowBlocks * 16 + rsub];
-      float wsc[4];
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb) wsc[cb] = ws[(size_t)kbc * NB + nbc[cb]] * live;
-#pragma unroll
-      for (int rb = 0; rb < kF8WaveRowBlocks; ++rb) {
-        const i32x8 a = abuf[rb * kWave];
-        const f32x4 sa = *reinterpret_cast<const f32x4*>(sbuf + rb * 16);
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
-          const f32x4 p = f8_mfma(a, bring[par][cb]);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[rb][cb][i] = fmaf(p[i], sa[i] * wsc[cb], acc[rb][cb][i]);
-        }
-        // consume each row block's partial products before the next block's MFMAs
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      int sn = c + kF8BAhead;
-      sn = sn < KB ? sn : KB - 1;
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb)
-        bring[par][cb] = f8_load32(B + (cb >> 1) * group_stride + (sn * 2 + (cb & 1)) * 2048);
-      // stage the next step into the other buffer, then fetch the one after it
-      if (c + 1 < NC) {
-#pragma unroll
-        for (int j = 0; j < kF8StageBlocks; ++j) sm.a[par ^ 1][0][w * kF8StageBlocks + j][lane] = stage[j][0];
-        if (srow) sm.s[par ^ 1][0][threadIdx.x] = sstage[0];
-      }
-      __syncthreads();
-      if (c + 2 < NC) {
-        int s2 = c + 2;
-        s2 = s2 < KB ? s2 : KB - 1;
-#pragma unroll
-        for (int j = 0; j < kF8StageBlocks; ++j) stage[j][0] = f8_load32(arow[j] + s2 * 128);
-        sstage[0] = srow ? srow[s2] : 0.f;
+      for (int i = 0; i < kF8Loads; ++i) stage[i] = *reinterpret_cast<const bf16x8*>(arow[i] + a_off(c));
+      if (threadIdx.x < kF8Rows) {
+        const int k1 = 2 * c + 1 < KB ? 2 * c + 1 : KB - 1;
+        sstage0 = srow[2 * c];
+        sstage1 = srow[k1];
       }
     };
-    for (int c = 0; c < NC; c += 2) {
-      step(c, 0);
-      if (c + 1 < NC) step(c + 1, 1);
+    auto write_stage = [&](int buf) {
+#pragma unroll
+      for (int i = 0; i < kF8Loads; ++i)
+        *reinterpret_cast<bf16x8*>(lds + buf + wr_off + (i >> 2) * 16 * kF8Slot + (i & 3) * 64) = stage[i];
+      if (threadIdx.x < kF8Rows) {
+        float* s = reinterpret_cast<float*>(lds + buf + kF8A);
+        s[threadIdx.x] = sstage0;
+        s[kF8Rows + threadIdx.x] = sstage1;
+      }
+    };
+    load_stage(0);
+    write_stage(0);
+    load_stage(NC > 1 ? 1 : 0);
+    __syncthreads();
+
+    // Weight scales of scale block kb (0 past the end of K), loaded one block ahead.
+    auto load_wsc = [&](int kb, float* dst) {
+      const float live = kb < KB ? 1.f : 0.f;
+      const int kbc = kb < KB ? kb : KB - 1;
+#pragma unroll
+      for (int cb = 0; cb < kF8CB; ++cb) dst[cb] = ws[(size_t)kbc * NB + nbc[cb]] * live;
+    };
+    float wsn[kF8CB];
+    load_wsc(0, wsn);
+
+    // One 128-deep scale block: h is the block within the chunk and also the weight-ring
+    // slot (scale blocks alternate slots; a chunk holds one of each).
+    auto block = [&](const int c, const int h, const int buf) {
+      const int kb = 2 * c + h;
+      float wsc[kF8CB];
+#pragma unroll
+      for (int cb = 0; cb < kF8CB; ++cb) wsc[cb] = wsn[cb];
+      load_wsc(kb + 1, wsn);
+      const float* sbuf = reinterpret_cast<const float*>(lds + buf + kF8A) + h * kF8Rows + (lane & 15);
+#pragma unroll
+      for (int rb = 0; rb < kF8RowBlocks; ++rb) {
+        const unsigned char* ap = lds + buf + (rb * 16 + h * 8) * kF8Slot + rd_off;
+        const i32x4 l4 = *reinterpret_cast<const i32x4*>(ap);
+        const i32x4 h4 = *reinterpret_cast<const i32x4*>(ap + kF8Slot);
+        const i32x8 a = {l4[0], l4[1], l4[2], l4[3], h4[0], h4[1], h4[2], h4[3]};
+        const float sa = sbuf[rb * 16];
+#pragma unroll
+        for (int cb = 0; cb < kF8CB; ++cb) {
+          const f32x4 p = f8_mfma(bring[h][cb], a);
+          const float sc = sa * wsc[cb];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[rb][cb][i] = fmaf(p[i], sc, acc[rb][cb][i]);
+        }
+      }
+      // refill this ring slot with the block kF8BAhead ahead (clamped to the last)
+      int sn = kb + kF8BAhead;
+      sn = sn < KB ? sn : KB - 1;
+#pragma unroll
+      for (int cb = 0; cb < kF8CB; ++cb)
+        bring[h][cb] = f8_load32(B + (cb >> 1) * group_stride + (sn * 2 + (cb & 1)) * 2048);
+    };
+
+    for (int c = 0; c < NC; ++c) {
+      const int buf = (c & 1) * kF8Buf;
+      block(c, 0, buf);
+      block(c, 1, buf);
+      // chunk boundary: the next chunk (in registers) goes to the other buffer, then
+      // the one after it is loaded (clamped past the end; never consumed there)
+      write_stage(kF8Buf - buf);
+      __syncthreads();
+      load_stage(c + 2 < NC ? c + 2 : NC - 1);
     }
 
     if (active) {
-      const int col = lane & 15;
-      const int rw0 = wm * kF8WaveRowBlocks * 16;
+      const int tok = lane & 15;
+      const int n0 = (lane >> 4) * 4;
       float* out = static_cast<float*>(it.shared ? g.out_shared : g.out_routed);
       const int ldo = it.shared ? g.ldo_shared : g.ldo_routed;
 #pragma unroll
-      for (int gi = 0; gi < kF8GroupsPerWave; ++gi)
+      for (int rb = 0; rb < kF8RowBlocks; ++rb) {
+        const int t = rb * 16 + tok;
+        if (t >= it.nrows) continue;
+        float* o = out + (size_t)(it.row0 + t) * ldo;
 #pragma unroll
-        for (int rb = 0; rb < kF8WaveRowBlocks; ++rb)
+        for (int j = 0; j < kF8GroupsPerWave; ++j) {
+          if (SWIGLU) {
+            f32x4 v;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int row = rw0 + rb * 16 + rsub + i;
-            if (row >= it.nrows) continue;
-            float* o = out + (size_t)(it.row0 + row) * ldo;
-            if (SWIGLU) {
-              o[(group0 + gi) * 16 + col] = silu(acc[rb][2 * gi][i]) * acc[rb][2 * gi + 1][i];
-            } else {
-              o[(group0 + gi) * 32 + col] = acc[rb][2 * gi][i];
-              o[(group0 + gi) * 32 + 16 + col] = acc[rb][2 * gi + 1][i];
-            }
+            for (int i = 0; i < 4; ++i) v[i] = silu(acc[rb][2 * j][i]) * acc[rb][2 * j + 1][i];
+            *reinterpret_cast<f32x4*>(o + (group0 + j) * 16 + n0) = v;
+          } else {
+            *reinterpret_cast<f32x4*>(o + (group0 + j) * 32 + n0) = acc[rb][2 * j];
+            *reinterpret_cast<f32x4*>(o + (group0 + j) * 32 + 16 + n0) = acc[rb][2 * j + 1];
           }
+        }
+      }
     }
-    __syncthreads();
+    // every LDS read of this item happened before its last chunk's barrier
   }
 }
 
 template <bool SWIGLU>
 static hipError_t launch_fp8_tiled(const GroupedGemm& g, long long max_items, int max_blocks, hipStream_t st) {
-  const size_t smem = sizeof(Fp8TiledSmem);
+  const size_t smem = 2 * kF8Buf;
   static bool configured = false;
   if (!configured) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_fp8_tiled_kernel<SWIGLU>),
@@ -256,16 +287,27 @@ static hipError_t launch_fp8_tiled(const GroupedGemm& g, long long max_items, in
     if (e != hipSuccess) return e;
     configured = true;
   }
-  long long blocks = max_items < max_blocks ? max_items : max_blocks;
+  // max_blocks counts compute units; the kernel is built for kF8MinBlocks workgroups
+  // on each
+  const long long resident = (long long)max_blocks * kF8MinBlocks;
+  long long blocks = max_items < resident ? max_items : resident;
   blocks = blocks < kF8Xcds ? kF8Xcds : blocks / kF8Xcds * kF8Xcds;
   gemm_fp8_tiled_kernel<SWIGLU><<<(unsigned)blocks, kF8Threads, smem, st>>>(g);
   return hipGetLastError();
 }
 
+// Reduction lengths are multiples of 128 and group counts multiples of 4 (the layer's
+// dimensions are multiples of 128); output rows are 16-byte aligned (ldo % 4 == 0).
 hipError_t launch_gemm_fp8_tiled(const GroupedGemm& g, bool swiglu, long long max_items, int max_blocks,
                                  hipStream_t st) {
   if (max_items <= 0) return hipSuccess;
+  if (g.K_routed % 128 || g.groups_routed % 4 || g.ldo_routed % 4 ||
+      (g.shared_rows > 0 && (g.K_shared % 128 || g.groups_shared % 4 || g.ldo_shared % 4)))
+    return hipErrorInvalidValue;
   return swiglu ? launch_fp8_tiled<true>(g, max_items, max_blocks, st) : launch_fp8_tiled<false>(g, max_items, max_blocks, st);
 }
+
+int fp8_tiled_rows() { return kF8Rows; }
+int fp8_tiled_groups() { return kF8Groups; }
 
 }  // namespace afd

@@ -208,8 +208,9 @@ def test_small_shapes(w, kernel):
     small("fp8_one_token", dtype="fp8", T=1, H=128, M=128, E=8, k=2, Ms=128),
     small("fp8_skewed_long_k", dtype="fp8", T=90, H=1024, M=512, E=3, k=2),
 ], ids=lambda w: w.name)
-def test_fp8_shapes(w):
-    full_case(w)
+@pytest.mark.parametrize("kernel", ["stream", "tiled"])
+def test_fp8_shapes(w, kernel):
+    full_case(w, kernel=kernel)
 
 
 @pytest.mark.parametrize("w", [
