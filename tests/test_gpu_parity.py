@@ -185,6 +185,28 @@ def test_route_full_size_every_workload(w):
     check_route(rb, logits.cpu().numpy(), w.E, w.k)
 
 
+@pytest.mark.parametrize("T,E,k,ties", [
+    (16384 + 37, 128, 8, False),   # 32 full blocks of pairs and a ragged last one
+    (16384, 256, 8, True),         # integer logits: many ties, decided by expert index
+    (300, 1024, 32, False),        # E = 1024 and k = 32: 9600 pairs, three blocks
+    (1025, 8, 8, False),           # k = E: every expert gets every token
+], ids=["ragged_last_block", "ties_large", "many_experts_k32", "k_equals_E"])
+def test_route_large_batches(T, E, k, ties):
+    """The multi-block permute (used above 8192 pairs) is bit-identical to the
+    stable counting sort of the oracle."""
+    say(f"route case T={T} E={E} k={k} ties={ties}")
+    w = workloads.Workload(name="route_large", index=200, T=T, H=128, M=128, E=E, k=k, Ms=0, dtype="bf16")
+    weights = workloads.make_weights(w, device="cuda")
+    layer = make_layer(w, weights, max_tokens=T)
+    rng = np.random.default_rng(T + E)
+    lg = (rng.integers(-2, 3, size=(T, E)) if ties else rng.standard_normal((T, E))).astype(np.float32)
+    logits = torch.from_numpy(lg).cuda()
+    rb = layer.new_route()
+    layer.route(logits, T, rb)
+    torch.cuda.synchronize()
+    check_route(rb, lg, E, k)
+
+
 # ----------------------------------------------------------------------------- shapes and edges
 @pytest.mark.parametrize("w", [
     small("ragged_bf16"),
