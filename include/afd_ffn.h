@@ -164,8 +164,8 @@ int afd_ffn_set_gemm_kernel(afd_ffn_t h, int kernel);
  * (index = afd_stage) into ms[n_stages] and launches[n_stages], and clears them.
  * Timing adds an event pair per kernel; leave it off for throughput runs. */
 typedef enum afd_stage {
-  AFD_STAGE_ROUTER = 0,  /* top-k softmax router */
-  AFD_STAGE_PERMUTE = 1, /* histogram, prefix scan, scatter */
+  AFD_STAGE_ROUTER = 0,  /* top-k softmax router (for T <= 64 also the permute: one launch) */
+  AFD_STAGE_PERMUTE = 1, /* histogram, prefix scan, scatter (T > 64) */
   AFD_STAGE_QUANT = 2,   /* fp8 quantisation of x and h */
   AFD_STAGE_GATE_UP = 3, /* grouped gate/up GEMM with SwiGLU epilogue */
   AFD_STAGE_DOWN = 4,    /* grouped down-projection GEMM */

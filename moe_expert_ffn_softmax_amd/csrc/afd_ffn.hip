@@ -334,6 +334,15 @@ extern "C" int afd_ffn_route(afd_ffn_t h, const float* logits, int32_t T, const 
   if (T == 0) return AFD_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int E = h->cfg.num_experts, k = h->cfg.top_k;
+  if (T <= afd::route_small_tokens()) {
+    // decode batches: router and permute in one launch (timed as the router stage)
+    StageScope s(h, st, AFD_STAGE_ROUTER);
+    hipError_t e = afd::launch_route_small(logits, T, E, k, r->topk_ids, r->topk_gates, r->expert_counts,
+                                           r->expert_offsets, r->sorted_pair, r->pair_pos, st);
+    if (e != hipSuccess) return hip_fail(e, "route launch");
+    s.done();
+    return AFD_OK;
+  }
   {
     StageScope s(h, st, AFD_STAGE_ROUTER);
     hipError_t e = afd::launch_router(logits, T, E, k, r->topk_ids, r->topk_gates, st);

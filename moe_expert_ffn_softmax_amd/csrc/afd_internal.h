@@ -53,6 +53,10 @@ struct GroupedGemm {
 
 hipError_t launch_router(const float* logits, int T, int E, int k, int32_t* ids, float* gates,
                          hipStream_t st);
+// Router and permute as one launch for batches of at most route_small_tokens() tokens.
+hipError_t launch_route_small(const float* logits, int T, int E, int k, int32_t* ids, float* gates, int32_t* counts,
+                              int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos, hipStream_t st);
+int route_small_tokens();
 hipError_t launch_permute(const int32_t* ids, int P, int E, int32_t* counts, int32_t* offsets,
                           int32_t* sorted_pair, int32_t* pair_pos, hipStream_t st);
 

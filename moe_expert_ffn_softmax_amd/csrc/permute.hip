@@ -17,6 +17,7 @@
 // segment pairs are ordered by token.
 #include "afd_device.h"
 #include "afd_internal.h"
+#include "route.h"
 
 namespace afd {
 
@@ -35,11 +36,12 @@ __device__ __forceinline__ uint64_t match_lanes(int id, int nbits, uint64_t vali
   return m;
 }
 
-__global__ void __launch_bounds__(kPermuteThreads) permute_kernel(const int32_t* __restrict__ ids, int P, int E,
-                                                                  int32_t* __restrict__ counts,
-                                                                  int32_t* __restrict__ offsets,
-                                                                  int32_t* __restrict__ sorted_pair,
-                                                                  int32_t* __restrict__ pair_pos) {
+// The whole sort in one workgroup of kPermuteThreads threads; `ids` may point to
+// global memory or to LDS.
+__device__ __forceinline__ void permute_one_workgroup(const int32_t* ids, int P, int E, int32_t* __restrict__ counts,
+                                                      int32_t* __restrict__ offsets,
+                                                      int32_t* __restrict__ sorted_pair,
+                                                      int32_t* __restrict__ pair_pos) {
   __shared__ int base[kPermuteWaves][kPermuteMaxE];
   __shared__ int scan_tmp[kPermuteWaves + 1];
   const int lane = lane_id();
@@ -103,6 +105,65 @@ __global__ void __launch_bounds__(kPermuteThreads) permute_kernel(const int32_t*
     }
   }
 }
+
+__global__ void __launch_bounds__(kPermuteThreads) permute_kernel(const int32_t* __restrict__ ids, int P, int E,
+                                                                  int32_t* __restrict__ counts,
+                                                                  int32_t* __restrict__ offsets,
+                                                                  int32_t* __restrict__ sorted_pair,
+                                                                  int32_t* __restrict__ pair_pos) {
+  permute_one_workgroup(ids, P, E, counts, offsets, sorted_pair, pair_pos);
+}
+
+// Decode batches (at most kRouteSmallTokens tokens): routing and the sort in one
+// workgroup, so the route call is a single launch.  Wave w routes tokens w, w + 16,
+// ...; the experts go to LDS as well as to ids, and the sort reads them from there.
+constexpr int kRouteSmallTokens = 64;
+
+template <int PER_LANE>
+__global__ void __launch_bounds__(kPermuteThreads) route_small_kernel(const float* __restrict__ logits, int T, int E,
+                                                                      int k, int32_t* __restrict__ ids,
+                                                                      float* __restrict__ gates,
+                                                                      int32_t* __restrict__ counts,
+                                                                      int32_t* __restrict__ offsets,
+                                                                      int32_t* __restrict__ sorted_pair,
+                                                                      int32_t* __restrict__ pair_pos) {
+  __shared__ int32_t ids_s[kRouteSmallTokens * kRouterMaxSlots];
+  const int lane = lane_id();
+  for (int t = threadIdx.x / kWave; t < T; t += kPermuteWaves) {
+    int id;
+    float gate;
+    route_token<PER_LANE>(logits + (size_t)t * E, E, k, &id, &gate);
+    if (lane < k) {
+      ids[(size_t)t * k + lane] = id;
+      gates[(size_t)t * k + lane] = gate;
+      ids_s[t * k + lane] = id;
+    }
+  }
+  __syncthreads();
+  permute_one_workgroup(ids_s, T * k, E, counts, offsets, sorted_pair, pair_pos);
+}
+
+hipError_t launch_route_small(const float* logits, int T, int E, int k, int32_t* ids, float* gates, int32_t* counts,
+                              int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos, hipStream_t st) {
+  if (T <= 0) return hipSuccess;
+  if (T > kRouteSmallTokens || k > kRouterMaxSlots || E > kPermuteMaxE) return hipErrorInvalidValue;
+#define AFD_ROUTE_SMALL(PL) \
+  route_small_kernel<PL><<<1, kPermuteThreads, 0, st>>>(logits, T, E, k, ids, gates, counts, offsets, sorted_pair, pair_pos)
+  if (E <= 64)
+    AFD_ROUTE_SMALL(1);
+  else if (E <= 128)
+    AFD_ROUTE_SMALL(2);
+  else if (E <= 256)
+    AFD_ROUTE_SMALL(4);
+  else if (E <= 512)
+    AFD_ROUTE_SMALL(8);
+  else
+    AFD_ROUTE_SMALL(kRouterMaxPerLane);
+#undef AFD_ROUTE_SMALL
+  return hipGetLastError();
+}
+
+int route_small_tokens() { return kRouteSmallTokens; }
 
 // ---------------------------------------------------------------------------------
 // Large batches: the same three steps spread over blocks of kPermuteBlock pairs.

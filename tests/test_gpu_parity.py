@@ -325,8 +325,11 @@ def test_smaller_batch_after_larger_and_determinism():
     assert torch.equal(y5[:5], y1[:5])
 
 
-def test_profiling_counts_launches():
-    w = small("profiled", T=32)
+@pytest.mark.parametrize("T", [100, 32])
+def test_profiling_counts_launches(T):
+    """Every stage is timed once per call; batches of at most 64 tokens route and
+    permute in one launch, timed as the router stage."""
+    w = small("profiled", T=T)
     weights = workloads.make_weights(w, device="cuda")
     x, logits = workloads.make_activations(w, device="cuda")
     layer = make_layer(w, weights)
@@ -336,6 +339,10 @@ def test_profiling_counts_launches():
         run_layer(layer, x, logits)
     prof = afd_ffn_profile_read(layer.handle)
     afd_ffn_set_profiling(layer.handle, False)
+    fused = T <= 64
     for st in ("router", "permute", "gate_up", "down", "combine"):
-        assert prof[st][1] == 3 and prof[st][0] > 0
+        if st == "permute" and fused:
+            assert prof[st][1] == 0
+        else:
+            assert prof[st][1] == 3 and prof[st][0] > 0
     assert afd_ffn_profile_read(layer.handle)["gate_up"][1] == 0
