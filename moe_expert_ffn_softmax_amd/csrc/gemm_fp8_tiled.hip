@@ -222,13 +222,22 @@ __global__ void __launch_bounds__(kF8Threads, kF8MinBlocks) gemm_fp8_tiled_kerne
         const i32x4 h4 = *reinterpret_cast<const i32x4*>(ap + kF8Slot);
         const i32x8 a = {l4[0], l4[1], l4[2], l4[3], h4[0], h4[1], h4[2], h4[3]};
         const float sa = sbuf[rb * 16];
+        // the block's MFMAs first (each product in its own registers), then their
+        // rescaling; the group barriers keep one token block's reads, MFMAs and FMAs
+        // together so products do not all share one register (which serialises every
+        // MFMA with its FMAs)
+        f32x4 p[kF8CB];
+#pragma unroll
+        for (int cb = 0; cb < kF8CB; ++cb) p[cb] = f8_mfma(bring[h][cb], a);
 #pragma unroll
         for (int cb = 0; cb < kF8CB; ++cb) {
-          const f32x4 p = f8_mfma(bring[h][cb], a);
           const float sc = sa * wsc[cb];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[rb][cb][i] = fmaf(p[i], sc, acc[rb][cb][i]);
+          for (int i = 0; i < 4; ++i) acc[rb][cb][i] = fmaf(p[cb][i], sc, acc[rb][cb][i]);
         }
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);             // the block's two LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, kF8CB, 0);         // its MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x002, 5 * kF8CB, 0);     // its multiplies and FMAs
       }
       // refill this ring slot with the block kF8BAhead ahead (clamped to the last)
       int sn = kb + kF8BAhead;
