@@ -293,6 +293,44 @@ def test_integer_logits_ties():
     check_y(y, yref, TOL[w.dtype], w.name)
 
 
+@pytest.mark.parametrize("w,kernel", [
+    (small("graph_decode", T=6, E=16, k=4, Ms=128), "auto"),        # one-launch route, streaming GEMMs
+    (small("graph_tiled", T=200, E=4, k=2, H=256, M=256), "tiled"),  # two-kernel route, 128-row tiles
+    (small("graph_fp8", dtype="fp8", T=50, H=384, M=256, E=6, k=2, Ms=256), "tiled"),
+], ids=lambda v: v if isinstance(v, str) else v.name)
+def test_hip_graph_replays_match_eager(w, kernel):
+    """route + forward captured in a HIP graph: every replay, with eager work and
+    synchronisations between replays, reproduces the eager result bit for bit."""
+    say(f"case {w.name} graph gemm={kernel}")
+    weights = workloads.make_weights(w, device="cuda")
+    x, logits = workloads.make_activations(w, device="cuda")
+    layer = make_layer(w, weights)
+    layer.set_gemm_kernel(kernel)
+    rb_e, y_e = run_layer(layer, x, logits)
+    rb = layer.new_route()
+    y = torch.zeros_like(y_e)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        layer.route(logits, w.T, rb, stream=s)       # warm-up on the capture stream
+        layer.forward(x, w.T, rb, y, stream=s)
+        s.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            layer.route(logits, w.T, rb, stream=s)
+            layer.forward(x, w.T, rb, y, stream=s)
+    torch.cuda.current_stream().wait_stream(s)
+    for rep in range(4):
+        y.zero_()
+        rb.sorted_pair.fill_(-1)
+        run_layer(layer, x.flip(0), logits.flip(0))  # unrelated eager work in between
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_e), f"replay {rep}: output differs from the eager run"
+        assert torch.equal(rb.sorted_pair, rb_e.sorted_pair), f"replay {rep}: permutation differs"
+
+
 def test_zero_tokens_is_a_no_op():
     w = small("empty", T=8)
     weights = workloads.make_weights(w, device="cuda")
