@@ -26,6 +26,19 @@ __device__ __forceinline__ __bf16 f32_to_bf16(float f) { return static_cast<__bf
 
 __device__ __forceinline__ uint16_t bf16_bits(__bf16 v) { return __builtin_bit_cast(uint16_t, v); }
 
+// e4m3 codes of four values already divided by their scale, |v| clamped to 448
+// (values between 448 and the next binade would otherwise leave the e4m3 range);
+// the hardware conversion rounds to nearest even.  Byte i holds value i.
+__device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float d) {
+  a = fminf(fmaxf(a, -448.f), 448.f);
+  b = fminf(fmaxf(b, -448.f), 448.f);
+  c = fminf(fmaxf(c, -448.f), 448.f);
+  d = fminf(fmaxf(d, -448.f), 448.f);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return static_cast<uint32_t>(w);
+}
+
 // SiLU(z) = z * sigmoid(z).
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 

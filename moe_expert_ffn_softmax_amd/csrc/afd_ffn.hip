@@ -106,7 +106,8 @@ bool use_wide(const afd_ffn* h, int P) {
   return h->gemm_mode == AFD_GEMM_WIDE;
 }
 
-// fp8 layer: quantise x -> gate/up GEMM (fp32 h) -> quantise h -> down GEMM -> combine.
+// fp8 layer: quantise x -> gate/up GEMM -> quantise h (in the tiled GEMM's epilogue, else a
+// separate pass over fp32 h) -> down GEMM -> combine.
 int forward_fp8(afd_ffn* h, const void* x, int T, const afd_route* r, void* y, hipStream_t st,
                 const afd::GroupedGemm& g1, const afd::GroupedGemm& g2) {
   const afd_ffn_config& c = h->cfg;
@@ -130,14 +131,24 @@ int forward_fp8(afd_ffn* h, const void* x, int T, const afd_route* r, void* y, h
     items1 = afd::grouped_items_bound(P, E, g1.groups_routed, g1.shared_rows, g1.groups_shared, afd::kTileRows);
     items2 = afd::grouped_items_bound(P, E, g2.groups_routed, g2.shared_rows, g2.groups_shared, afd::kTileRows);
   }
-  {
+  if (tiled) {
+    // the tiled gate/up GEMM quantises h in its epilogue (no fp32 h round trip)
+    afd::GroupedGemm gq = g1;
+    gq.out_routed = h->hq_routed;
+    gq.outs_routed = h->hs_routed;
+    gq.out_shared = h->hq_shared;
+    gq.outs_shared = h->hs_shared;
     StageScope s(h, st, AFD_STAGE_GATE_UP);
-    hipError_t e = tiled ? afd::launch_gemm_fp8_tiled(g1, true, items1, h->num_cus, st)
-                         : afd::launch_gemm_fp8(g1, true, items1, h->gemm_blocks[4], st);
+    hipError_t e = afd::launch_gemm_fp8_tiled(gq, true, items1, h->num_cus, st);
     if (e != hipSuccess) return hip_fail(e, "fp8 gate/up GEMM launch");
     s.done();
-  }
-  {
+  } else {
+    {
+      StageScope s(h, st, AFD_STAGE_GATE_UP);
+      hipError_t e = afd::launch_gemm_fp8(g1, true, items1, h->gemm_blocks[4], st);
+      if (e != hipSuccess) return hip_fail(e, "fp8 gate/up GEMM launch");
+      s.done();
+    }
     StageScope s(h, st, AFD_STAGE_QUANT);
     hipError_t e = afd::launch_quant_fp8(h->h_routed, P, M, M, false, h->hq_routed, h->hs_routed, st);
     if (e == hipSuccess && Ms) e = afd::launch_quant_fp8(h->h_shared, T, Ms, Ms, false, h->hq_shared, h->hs_shared, st);

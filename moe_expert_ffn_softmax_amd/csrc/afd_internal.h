@@ -46,8 +46,8 @@ struct GroupedGemm {
   int lda_routed, lda_shared;   // A row stride (elements)
   void* out_routed;             // output rows in sorted order
   void* out_shared;
-  float* outs_routed;           // fp8: per-row per-128 scales of the output, else null
-  float* outs_shared;
+  float* outs_routed;           // set: the fp8 tiled gate/up GEMM writes e4m3 codes to
+  float* outs_shared;           // out_* and per-row per-128 scales here, else fp32 h
   int ldo_routed, ldo_shared;   // output row stride (elements)
 };
 

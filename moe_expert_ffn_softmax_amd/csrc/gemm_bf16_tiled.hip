@@ -77,8 +77,13 @@ __device__ __forceinline__ bf16x8 tiled_load_b(const bf16x8* p) { return *p; }
 #define AFD_TILED_SCHED 1
 #endif
 
+#ifndef AFD_TILED_MIN_BLOCKS
+#define AFD_TILED_MIN_BLOCKS 1
+#endif
+constexpr int kTiledMinBlocks = AFD_TILED_MIN_BLOCKS;  // workgroups per CU the registers must allow
+
 template <bool SWIGLU>
-__global__ void __launch_bounds__(kTiledThreads, 1) gemm_bf16_tiled_kernel(GroupedGemm g) {
+__global__ void __launch_bounds__(kTiledThreads, kTiledMinBlocks) gemm_bf16_tiled_kernel(GroupedGemm g) {
   __shared__ int prefix[kMaxSegments + 1];
   __shared__ int scan_tmp[kTiledWaves + 1];
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
@@ -286,8 +291,10 @@ static hipError_t launch_tiled(const GroupedGemm& g, long long max_items, int ma
     if (e != hipSuccess) return e;
     configured = true;
   }
-  // max_blocks counts compute units: one resident workgroup on each
-  long long blocks = max_items < max_blocks ? max_items : max_blocks;
+  // max_blocks counts compute units; the kernel is built for kTiledMinBlocks
+  // resident workgroups on each
+  const long long resident = (long long)max_blocks * kTiledMinBlocks;
+  long long blocks = max_items < resident ? max_items : resident;
   blocks = blocks < kXcds ? kXcds : blocks / kXcds * kXcds;
   gemm_bf16_tiled_kernel<SWIGLU><<<(unsigned)blocks, kTiledThreads, smem, st>>>(g);
   return hipGetLastError();

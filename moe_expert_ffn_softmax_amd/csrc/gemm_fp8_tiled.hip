@@ -28,6 +28,9 @@
 // the chunk are staged beside them.  Double-buffered; the next chunk is loaded into
 // registers while the current one is multiplied.
 //
+// For the gate/up projection the epilogue can write h already quantised (e4m3 codes
+// and per-token per-128 scales; see below) instead of fp32 h.
+//
 // Items and XCD ranges as in the bf16 tiled kernel.
 #include "grouped.h"
 
@@ -70,6 +73,7 @@ template <bool SWIGLU>
 __global__ void __launch_bounds__(kF8Threads, kF8MinBlocks) gemm_fp8_tiled_kernel(GroupedGemm g) {
   __shared__ int prefix[kMaxSegments + 1];
   __shared__ int scan_tmp[kF8Waves + 1];
+  __shared__ float qamax[kF8Waves][kF8Rows];  // per-wave token amax of the quantising epilogue
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
 
   const int total = build_item_prefix(g, kF8Rows, kF8Groups, prefix, scan_tmp);
@@ -258,7 +262,51 @@ __global__ void __launch_bounds__(kF8Threads, kF8MinBlocks) gemm_fp8_tiled_kerne
       load_stage(c + 2 < NC ? c + 2 : NC - 1);
     }
 
-    if (active) {
+    float* qscale = it.shared ? g.outs_shared : g.outs_routed;
+    if (SWIGLU && qscale) {
+      // h quantised in place of the separate pass: the tile's 8 groups are exactly one
+      // 128-channel quantisation group of each of its tokens (gate/up column tiles are
+      // whole, as 2M/32 is a multiple of 8).  Per token: amax over the 4 lanes of
+      // each wave holding it, then over the 4 waves through LDS; scale = amax / 448
+      // (1 for an all-zero group); codes = e4m3(v / scale) as the quantisation kernel.
+      const int tok = lane & 15;
+      const int n0 = (lane >> 4) * 4;
+      f32x4 hv[kF8RowBlocks][kF8GroupsPerWave];
+#pragma unroll
+      for (int rb = 0; rb < kF8RowBlocks; ++rb) {
+        float m = 0.f;
+#pragma unroll
+        for (int j = 0; j < kF8GroupsPerWave; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            hv[rb][j][i] = silu(acc[rb][2 * j][i]) * acc[rb][2 * j + 1][i];
+            m = fmaxf(m, fabsf(hv[rb][j][i]));
+          }
+        m = fmaxf(m, __shfl_xor(m, 16, kWave));
+        m = fmaxf(m, __shfl_xor(m, 32, kWave));
+        if (lane < 16) qamax[w][rb * 16 + tok] = m;
+      }
+      __syncthreads();
+      uint8_t* q = static_cast<uint8_t*>(it.shared ? g.out_shared : g.out_routed);
+      const int ldo = it.shared ? g.ldo_shared : g.ldo_routed;
+      const int qgroups = ldo / 128;
+#pragma unroll
+      for (int rb = 0; rb < kF8RowBlocks; ++rb) {
+        const int t = rb * 16 + tok;
+        float amax = qamax[0][t];
+#pragma unroll
+        for (int v = 1; v < kF8Waves; ++v) amax = fmaxf(amax, qamax[v][t]);
+        const float sc = amax > 0.f ? amax / 448.f : 1.f;
+        if (t < it.nrows) {
+          const size_t row = (size_t)(it.row0 + t);
+#pragma unroll
+          for (int j = 0; j < kF8GroupsPerWave; ++j)
+            *reinterpret_cast<uint32_t*>(q + row * ldo + (group0 + j) * 16 + n0) =
+                e4m3_pack4(hv[rb][j][0] / sc, hv[rb][j][1] / sc, hv[rb][j][2] / sc, hv[rb][j][3] / sc);
+          if (w == 0 && lane < 16) qscale[row * qgroups + it.group / 8] = sc;
+        }
+      }
+    } else if (active) {
       const int tok = lane & 15;
       const int n0 = (lane >> 4) * 4;
       float* out = static_cast<float*>(it.shared ? g.out_shared : g.out_routed);
@@ -312,6 +360,10 @@ hipError_t launch_gemm_fp8_tiled(const GroupedGemm& g, bool swiglu, long long ma
   if (max_items <= 0) return hipSuccess;
   if (g.K_routed % 128 || g.groups_routed % 4 || g.ldo_routed % 4 ||
       (g.shared_rows > 0 && (g.K_shared % 128 || g.groups_shared % 4 || g.ldo_shared % 4)))
+    return hipErrorInvalidValue;
+  // the quantising epilogue needs whole column tiles (every wave active)
+  if (swiglu && g.outs_routed &&
+      (g.groups_routed % kF8Groups || (g.shared_rows > 0 && g.groups_shared % kF8Groups)))
     return hipErrorInvalidValue;
   return swiglu ? launch_fp8_tiled<true>(g, max_items, max_blocks, st) : launch_fp8_tiled<false>(g, max_items, max_blocks, st);
 }

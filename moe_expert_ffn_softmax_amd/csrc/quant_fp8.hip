@@ -20,19 +20,6 @@ __device__ __forceinline__ float load_act(const void* p, size_t i, bool bf16) {
   return static_cast<const float*>(p)[i];
 }
 
-// e4m3 code of v / s with |v / s| clamped to 448 (values between 448 and the next
-// binade would otherwise leave the e4m3 range); hardware conversion rounds to
-// nearest even.
-__device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float d) {
-  a = fminf(fmaxf(a, -448.f), 448.f);
-  b = fminf(fmaxf(b, -448.f), 448.f);
-  c = fminf(fmaxf(c, -448.f), 448.f);
-  d = fminf(fmaxf(d, -448.f), 448.f);
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
-  return static_cast<uint32_t>(w);
-}
-
 // rows x cols activations (bf16 or fp32, row stride ld) -> codes [rows, cols] and
 // scales [rows, cols / 128].  `row_index` (optional) gathers source rows.
 __global__ void __launch_bounds__(kQuantThreads) quant_fp8_kernel(const void* __restrict__ src, int rows, int cols,
