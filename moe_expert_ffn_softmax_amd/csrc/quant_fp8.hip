@@ -6,8 +6,7 @@
 // 128-deep block of a product has one scale on each side.  FP8/BF16 mixed precision
 // is the omica.com.cn AFD article's §3.3 ("FP8BF16混合精度").
 //
-// One wave per (row, 2 groups): lane l handles 4 consecutive channels of group
-// (l / 32); the group amax is a 32-lane max.
+// One wave per (row, 64 * VPL channels), 16 bytes per lane.
 #include "afd_device.h"
 #include "afd_internal.h"
 
@@ -15,39 +14,60 @@ namespace afd {
 
 constexpr int kQuantThreads = 256;
 
-__device__ __forceinline__ float load_act(const void* p, size_t i, bool bf16) {
-  if (bf16) return bf16_bits_to_f32(static_cast<const uint16_t*>(p)[i]);
-  return static_cast<const float*>(p)[i];
-}
-
-// rows x cols activations (bf16 or fp32, row stride ld) -> codes [rows, cols] and
-// scales [rows, cols / 128].  `row_index` (optional) gathers source rows.
+// Each lane loads 16 bytes: 8 bf16 or 4 fp32 values (VPL), so a 128-channel group
+// spans 128 / VPL lanes and a wave covers 64 * VPL channels of one row; the group
+// amax is a max over those lanes.
+template <bool BF16>
 __global__ void __launch_bounds__(kQuantThreads) quant_fp8_kernel(const void* __restrict__ src, int rows, int cols,
-                                                                  int ld, bool src_bf16, uint8_t* __restrict__ q,
+                                                                  int ld, uint8_t* __restrict__ q,
                                                                   float* __restrict__ scales) {
+  constexpr int VPL = BF16 ? 8 : 4;       // values per lane
+  constexpr int LPG = 128 / VPL;          // lanes per 128-channel group
+  constexpr int CPW = kWave * VPL;        // channels per wave
   const int lane = lane_id();
   const int groups = cols / 128;
-  const int pairs = (groups + 1) / 2;
+  const int chunks = (cols + CPW - 1) / CPW;
   const long long wave = (long long)blockIdx.x * (kQuantThreads / kWave) + threadIdx.x / kWave;
   const long long waves = (long long)gridDim.x * (kQuantThreads / kWave);
-  for (long long wi = wave; wi < (long long)rows * pairs; wi += waves) {
-    const int r = (int)(wi / pairs);
-    const int g = (int)(wi % pairs) * 2 + lane / 32;
-    const bool ok = g < groups;
-    const int c0 = g * 128 + (lane & 31) * 4;
-    float v[4] = {0.f, 0.f, 0.f, 0.f};
+  for (long long wi = wave; wi < (long long)rows * chunks; wi += waves) {
+    const int r = (int)(wi / chunks);
+    const int c0 = (int)(wi % chunks) * CPW + lane * VPL;
+    const bool ok = c0 < cols;  // cols is a multiple of 128, so a group is all in or all out
+    float v[VPL];
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) v[i] = 0.f;
     if (ok) {
+      if (BF16) {
+        const uint4 raw = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(src) + (size_t)r * ld + c0);
+        const uint32_t wds[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = load_act(src, (size_t)r * ld + c0 + i, src_bf16);
+        for (int i = 0; i < 4; ++i) {
+          v[2 * i] = bf16_bits_to_f32((uint16_t)(wds[i] & 0xffffu));
+          v[2 * i + 1] = bf16_bits_to_f32((uint16_t)(wds[i] >> 16));
+        }
+      } else {
+        const float4 f = *reinterpret_cast<const float4*>(static_cast<const float*>(src) + (size_t)r * ld + c0);
+        v[0] = f.x;
+        v[1] = f.y;
+        v[2] = f.z;
+        v[3] = f.w;
+      }
     }
-    float amax = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+    float amax = 0.f;
 #pragma unroll
-    for (int off = 16; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, kWave));
+    for (int i = 0; i < VPL; ++i) amax = fmaxf(amax, fabsf(v[i]));
+#pragma unroll
+    for (int off = LPG / 2; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, kWave));
     const float s = amax > 0.f ? amax / 448.f : 1.f;
     if (ok) {
-      const uint32_t pk = e4m3_pack4(v[0] / s, v[1] / s, v[2] / s, v[3] / s);
-      *reinterpret_cast<uint32_t*>(q + (size_t)r * cols + c0) = pk;
-      if ((lane & 31) == 0) scales[(size_t)r * groups + g] = s;
+      uint32_t pk[VPL / 4];
+#pragma unroll
+      for (int i = 0; i < VPL / 4; ++i) pk[i] = e4m3_pack4(v[4 * i] / s, v[4 * i + 1] / s, v[4 * i + 2] / s, v[4 * i + 3] / s);
+      if (BF16)
+        *reinterpret_cast<uint2*>(q + (size_t)r * cols + c0) = make_uint2(pk[0], pk[VPL / 4 - 1]);
+      else
+        *reinterpret_cast<uint32_t*>(q + (size_t)r * cols + c0) = pk[0];
+      if (lane % LPG == 0) scales[(size_t)r * groups + c0 / 128] = s;
     }
   }
 }
@@ -55,11 +75,15 @@ __global__ void __launch_bounds__(kQuantThreads) quant_fp8_kernel(const void* __
 hipError_t launch_quant_fp8(const void* src, int rows, int cols, int ld, bool src_bf16, uint8_t* q, float* scales,
                             hipStream_t st) {
   if (rows <= 0) return hipSuccess;
-  if (cols % 128) return hipErrorInvalidValue;
-  const long long work = (long long)rows * ((cols / 128 + 1) / 2);
+  if (cols % 128 || ld % 8) return hipErrorInvalidValue;
+  const int cpw = kWave * (src_bf16 ? 8 : 4);
+  const long long work = (long long)rows * ((cols + cpw - 1) / cpw);
   long long blocks = (work + 3) / 4;
-  if (blocks > 4096) blocks = 4096;
-  quant_fp8_kernel<<<(unsigned)blocks, kQuantThreads, 0, st>>>(src, rows, cols, ld, src_bf16, q, scales);
+  if (blocks > 8192) blocks = 8192;
+  if (src_bf16)
+    quant_fp8_kernel<true><<<(unsigned)blocks, kQuantThreads, 0, st>>>(src, rows, cols, ld, q, scales);
+  else
+    quant_fp8_kernel<false><<<(unsigned)blocks, kQuantThreads, 0, st>>>(src, rows, cols, ld, q, scales);
   return hipGetLastError();
 }
 
