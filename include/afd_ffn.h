@@ -30,7 +30,9 @@
  *                block; x and y are bfloat16; x and h are quantised to e4m3 per
  *                token and per 128 channels (scale amax/448) inside forward (the
  *                FP8/BF16 mixed precision of the omica.com.cn AFD article, §3.3).
- * All accumulation is float32.
+ * All accumulation is float32.  In the bf16 and fp8 layers each expert's output
+ * row o_tj is rounded to bf16 before the combine (which sums in float32 and rounds
+ * y once); the fp32 layer keeps o_tj in float32.
  *
  * Memory.  Every pointer argument is a device pointer (HIP, same device as the
  * handle), except `cfg`, `out` and the route struct itself, which are host

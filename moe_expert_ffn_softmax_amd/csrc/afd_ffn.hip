@@ -249,6 +249,7 @@ extern "C" int afd_ffn_create(const afd_ffn_config* cfg, const void* w_gate_up, 
   const size_t P = (size_t)cfg->max_tokens * cfg->top_k, T = cfg->max_tokens;
   const size_t es = elem_size(cfg->dtype);
   const size_t hes = cfg->dtype == AFD_BF16 ? 2 : 4;  // intermediate h: bf16, or fp32 before fp8 quantisation
+  const size_t oes = cfg->dtype == AFD_F32 ? 4 : 2;    // expert outputs O: bf16 except in the fp32 layer
   h->w_gu_expert_elems = H * 2 * M;
   h->w_d_expert_elems = M * H;
   const size_t sgu_n = (H / 128) * (2 * M / 128), sd_n = (M / 128) * (H / 128);
@@ -264,8 +265,8 @@ extern "C" int afd_ffn_create(const afd_ffn_config* cfg, const void* w_gate_up, 
       {&h->ws_d, Ms * H * es},
       {&h->h_routed, P * M * hes},
       {&h->h_shared, T * Ms * hes},
-      {(void**)&h->o_routed, P * H * 4},
-      {(void**)&h->o_shared, Ms ? T * H * 4 : 0},
+      {&h->o_routed, P * H * oes},
+      {&h->o_shared, Ms ? T * H * oes : 0},
       {(void**)&h->s_gu, fp8 ? E * sgu_n * 4 : 0},
       {(void**)&h->s_d, fp8 ? E * sd_n * 4 : 0},
       {(void**)&h->ss_gu, fp8 ? ssgu_n * 4 : 0},

@@ -44,7 +44,8 @@ struct GroupedGemm {
   const float* as_routed;       // fp8 activation scales [rows, K/128], else null
   const float* as_shared;
   int lda_routed, lda_shared;   // A row stride (elements)
-  void* out_routed;             // output rows in sorted order
+  void* out_routed;             // output rows in sorted order: h (bf16 layer: bf16, fp8
+                                //   layer: fp32 or e4m3 codes), or O (bf16; fp32 layer fp32)
   void* out_shared;
   float* outs_routed;           // set: the fp8 tiled gate/up GEMM writes e4m3 codes to
   float* outs_shared;           // out_* and per-row per-128 scales here, else fp32 h
@@ -110,9 +111,10 @@ hipError_t gemm_occupancy_bf16(int* gate_up, int* down);
 hipError_t gemm_occupancy_f32(int* gate_up, int* down);
 hipError_t gemm_occupancy_fp8(int* gate_up, int* down);
 
-// y[t] = sum_j gate[t,j] * O[pair_pos[t*k+j]] (+ Os[t]) -> y (bf16 or fp32).
-hipError_t launch_combine(const float* O, const float* Os, const float* gates, const int32_t* pair_pos,
-                          int T, int k, int H, void* y, bool y_bf16, hipStream_t st);
+// y[t] = sum_j gate[t,j] * O[pair_pos[t*k+j]] (+ Os[t]); O, Os and y all bf16
+// (bf16 = true) or all fp32.
+hipError_t launch_combine(const void* O, const void* Os, const float* gates, const int32_t* pair_pos,
+                          int T, int k, int H, void* y, bool bf16, hipStream_t st);
 
 }  // namespace afd
 
@@ -129,8 +131,8 @@ struct afd_ffn {
   // workspace (owned)
   void* h_routed;   // [P_max, M]
   void* h_shared;   // [T_max, Ms]
-  float* o_routed;  // [P_max, H]
-  float* o_shared;  // [T_max, H]
+  void* o_routed;   // [P_max, H], bf16 (fp32 for the fp32 layer)
+  void* o_shared;   // [T_max, H], likewise
   // fp8 layers only
   float* s_gu;        // [E, H/128, 2M/128] weight block scales (copy)
   float* s_d;         // [E, M/128, H/128]

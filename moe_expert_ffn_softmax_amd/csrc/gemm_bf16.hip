@@ -17,7 +17,7 @@
 //   gate/up (SWIGLU = true): the column group holds gate block j and up block j, so
 //     the epilogue forms h = SiLU(gate) * up in registers and stores bf16 h;
 //   down    (SWIGLU = false): the group holds output blocks 2j and 2j+1, stored as
-//     fp32 rows for the combine.
+//     bf16 rows for the combine (which sums them in fp32).
 // MFMA operand order (16x16x32 bf16): lane l supplies row (l % 16) of A and column
 // (l % 16) of B at reduction offsets (l / 16) * 8 .. + 7; it receives rows
 // (l / 16) * 4 .. + 3 of column (l % 16) of the 16x16 fp32 result.
@@ -113,15 +113,15 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_bf16_stream_kernel(GroupedG
           out[(size_t)(it.row0 + row) * ldo + it.group * 16 + col] = f32_to_bf16(silu(acc0[i]) * acc1[i]);
       }
     } else {
-      float* out = static_cast<float*>(it.shared ? g.out_shared : g.out_routed);
+      __bf16* out = static_cast<__bf16*>(it.shared ? g.out_shared : g.out_routed);
       const int ldo = it.shared ? g.ldo_shared : g.ldo_routed;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = rbase + i;
         if (row < it.nrows) {
-          float* o = out + (size_t)(it.row0 + row) * ldo + it.group * 32 + col;
-          o[0] = acc0[i];
-          o[16] = acc1[i];
+          __bf16* o = out + (size_t)(it.row0 + row) * ldo + it.group * 32 + col;
+          o[0] = f32_to_bf16(acc0[i]);
+          o[16] = f32_to_bf16(acc1[i]);
         }
       }
     }

@@ -244,7 +244,7 @@ __global__ void __launch_bounds__(kWideThreads, 1) gemm_bf16_wide_kernel(Grouped
             }
           }
       } else {
-        float* out = static_cast<float*>(it.shared ? g.out_shared : g.out_routed);
+        __bf16* out = static_cast<__bf16*>(it.shared ? g.out_shared : g.out_routed);
         const int ldo = it.shared ? g.ldo_shared : g.ldo_routed;
 #pragma unroll
         for (int rb = 0; rb < kWideRB; ++rb)
@@ -252,9 +252,9 @@ __global__ void __launch_bounds__(kWideThreads, 1) gemm_bf16_wide_kernel(Grouped
           for (int i = 0; i < 16; ++i) {
             const int row = rsub + rb * 32 + (i / 4) * 8 + (i % 4);
             if (row < it.nrows) {
-              float* o = out + (size_t)(it.row0 + row) * ldo + g0 * 32 + col;
+              __bf16* o = out + (size_t)(it.row0 + row) * ldo + g0 * 32 + col;
 #pragma unroll
-              for (int cb = 0; cb < kWideCB; ++cb) o[cb * 32] = acc[rb][cb][i];
+              for (int cb = 0; cb < kWideCB; ++cb) o[cb * 32] = f32_to_bf16(acc[rb][cb][i]);
             }
           }
       }

@@ -134,18 +134,19 @@ __global__ void __launch_bounds__(kFp8Threads) gemm_fp8_stream_kernel(GroupedGem
 
     const int col = lane & 15;
     const int rbase = (lane >> 4) * 4;
-    float* out = static_cast<float*>(it.shared ? g.out_shared : g.out_routed);
     const int ldo = it.shared ? g.ldo_shared : g.ldo_routed;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = rbase + i;
       if (row >= it.nrows) continue;
-      float* o = out + (size_t)(it.row0 + row) * ldo;
       if (SWIGLU) {
+        // fp32 h, quantised by the next pass
+        float* o = static_cast<float*>(it.shared ? g.out_shared : g.out_routed) + (size_t)(it.row0 + row) * ldo;
         o[it.group * 16 + col] = silu(acc0[i]) * acc1[i];
       } else {
-        o[it.group * 32 + col] = acc0[i];
-        o[it.group * 32 + 16 + col] = acc1[i];
+        __bf16* o = static_cast<__bf16*>(it.shared ? g.out_shared : g.out_routed) + (size_t)(it.row0 + row) * ldo;
+        o[it.group * 32 + col] = f32_to_bf16(acc0[i]);
+        o[it.group * 32 + 16 + col] = f32_to_bf16(acc1[i]);
       }
     }
   }

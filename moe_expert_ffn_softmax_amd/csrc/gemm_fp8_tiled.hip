@@ -324,8 +324,17 @@ __global__ void __launch_bounds__(kF8Threads, kF8MinBlocks) gemm_fp8_tiled_kerne
             for (int i = 0; i < 4; ++i) v[i] = silu(acc[rb][2 * j][i]) * acc[rb][2 * j + 1][i];
             *reinterpret_cast<f32x4*>(o + (group0 + j) * 16 + n0) = v;
           } else {
-            *reinterpret_cast<f32x4*>(o + (group0 + j) * 32 + n0) = acc[rb][2 * j];
-            *reinterpret_cast<f32x4*>(o + (group0 + j) * 32 + 16 + n0) = acc[rb][2 * j + 1];
+            // bf16 output rows for the combine: 4 consecutive channels, one 8-byte store
+            __bf16* orow = static_cast<__bf16*>(it.shared ? g.out_shared : g.out_routed) +
+                           (size_t)(it.row0 + t) * ldo;
+#pragma unroll
+            for (int hlf = 0; hlf < 2; ++hlf) {
+              const f32x4 v = acc[rb][2 * j + hlf];
+              uint2 pk;
+              pk.x = (uint32_t)bf16_bits(f32_to_bf16(v[0])) | ((uint32_t)bf16_bits(f32_to_bf16(v[1])) << 16);
+              pk.y = (uint32_t)bf16_bits(f32_to_bf16(v[2])) | ((uint32_t)bf16_bits(f32_to_bf16(v[3])) << 16);
+              *reinterpret_cast<uint2*>(orow + (group0 + j) * 32 + hlf * 16 + n0) = pk;
+            }
           }
         }
       }
