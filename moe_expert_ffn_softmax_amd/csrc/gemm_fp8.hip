@@ -33,9 +33,11 @@ __device__ __forceinline__ f32x4 mfma_fp8_block(const i32x8& a, const i32x8& b) 
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 0, 0, 0, 0x7f7f7f7f, 0, 0x7f7f7f7f);
 }
 
-__device__ __forceinline__ i32x8 load32_nt(const uint8_t* p) {
+// A lane's 32 weight bytes of a packed fragment: 16 at p, 16 at p + 1 KiB (see the
+// packing below).
+__device__ __forceinline__ i32x8 load_frag_nt(const uint8_t* p) {
   const i32x4* q = reinterpret_cast<const i32x4*>(p);
-  const i32x4 lo = __builtin_nontemporal_load(q), hi = __builtin_nontemporal_load(q + 1);
+  const i32x4 lo = __builtin_nontemporal_load(q), hi = __builtin_nontemporal_load(q + 64);
   return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
@@ -94,7 +96,7 @@ __global__ void __launch_bounds__(kFp8Threads) gemm_fp8_stream_kernel(GroupedGem
     }
     const uint8_t* wbase = it.shared ? static_cast<const uint8_t*>(g.w_shared)
                                      : static_cast<const uint8_t*>(g.w_routed) + (size_t)it.seg * g.w_expert_elems;
-    const uint8_t* B = wbase + (size_t)it.group * KB * 4096 + lane * 32;  // [kb][half][lane][32 B]
+    const uint8_t* B = wbase + (size_t)it.group * KB * 4096 + lane * 16;  // [kb][half][2][lane][16 B]
     const float* ws = it.shared ? g.s_shared : g.s_routed + (size_t)it.seg * g.s_expert_elems;
     const int nb0 = block_col(SWIGLU, N, it.group, 0) / 128, nb1 = block_col(SWIGLU, N, it.group, 1) / 128;
 
@@ -104,8 +106,8 @@ __global__ void __launch_bounds__(kFp8Threads) gemm_fp8_stream_kernel(GroupedGem
     for (int u = 0; u < D; ++u) {
       if (u < KB) {
         a[u] = load32(A + u * 128);
-        b0[u] = load32_nt(B + (u * 2) * 2048);
-        b1[u] = load32_nt(B + (u * 2 + 1) * 2048);
+        b0[u] = load_frag_nt(B + (u * 2) * 2048);
+        b1[u] = load_frag_nt(B + (u * 2 + 1) * 2048);
       }
     }
     for (int kb0 = 0; kb0 < KB; kb0 += D) {
@@ -125,8 +127,8 @@ __global__ void __launch_bounds__(kFp8Threads) gemm_fp8_stream_kernel(GroupedGem
           const int kn = kb + D;
           if (kn < KB) {
             a[u] = load32(A + kn * 128);
-            b0[u] = load32_nt(B + (kn * 2) * 2048);
-            b1[u] = load32_nt(B + (kn * 2 + 1) * 2048);
+            b0[u] = load_frag_nt(B + (kn * 2) * 2048);
+            b1[u] = load_frag_nt(B + (kn * 2 + 1) * 2048);
           }
         }
       }
@@ -170,8 +172,10 @@ hipError_t gemm_occupancy_fp8(int* gate_up, int* down) {
   return e;
 }
 
-// Repack fp8 weights [nmat][R][C] into [group][kb][half][lane][32 B] fragments
-// (group/half pairing as for bf16).
+// Repack fp8 weights [nmat][R][C] into 2 KiB fragments [group][kb][half], each
+// holding lane l's 32 reduction bytes as two 16-byte halves at l * 16 and 1024 + l * 16,
+// so that each of the two loads of a fragment reads 1 KiB contiguously (group/half
+// pairing as for bf16).
 __global__ void pack_fp8_kernel(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst, int nmat, int R, int C,
                                 int gate_up) {
   const size_t slots_per_mat = (size_t)R * C / 32;
@@ -195,9 +199,14 @@ __global__ void pack_fp8_kernel(const uint8_t* __restrict__ src, uint8_t* __rest
     for (int i = 0; i < 8; ++i)
       w[i] = (uint32_t)sp[(size_t)(4 * i) * C] | ((uint32_t)sp[(size_t)(4 * i + 1) * C] << 8) |
              ((uint32_t)sp[(size_t)(4 * i + 2) * C] << 16) | ((uint32_t)sp[(size_t)(4 * i + 3) * C] << 24);
-    uint32_t* dp = reinterpret_cast<uint32_t*>(dst + s * 32);
+    uint8_t* frag = dst + (s / 64) * 2048 + lane * 16;
+    uint32_t* lo = reinterpret_cast<uint32_t*>(frag);
+    uint32_t* hi = reinterpret_cast<uint32_t*>(frag + 1024);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) dp[i] = w[i];
+    for (int i = 0; i < 4; ++i) {
+      lo[i] = w[i];
+      hi[i] = w[4 + i];
+    }
   }
 }
 

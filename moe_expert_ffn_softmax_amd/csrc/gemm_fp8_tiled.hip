@@ -15,8 +15,9 @@
 // token block and scale block, and the weight scale is uniform over a 16-column
 // block: rescaling a partial product is one multiply and four FMAs.  Lane l supplies
 // column (or token) l % 16 at reduction offsets (l / 16) * 32 .. + 31 of the 128-deep
-// block; the packed weight layout (see gemm_fp8.hip) is exactly that order, so a
-// fragment is one contiguous 2 KiB run.
+// block; the packed weight layout (see gemm_fp8.hip) keeps a fragment in one 2 KiB
+// run whose two halves each give every lane 16 of its bytes, so each of a fragment's
+// two loads reads 1 KiB contiguously.
 //
 // Activation staging.  A 256-deep chunk (two scale blocks) of the 128 gathered token
 // rows is loaded as 4 rows x 256 contiguous bytes per instruction (lane l: row l / 16,
@@ -27,6 +28,18 @@
 // a 16-lane quarter of an operand read is one slot, contiguous.  The tokens' scales of
 // the chunk are staged beside them.  Double-buffered; the next chunk is loaded into
 // registers while the current one is multiplied.
+//
+// The weight scales of a chunk's two blocks are staged through LDS beside the token
+// scales, so inside a block the only memory waits are for the weight ring.
+//
+// Schedule of a block.  Rescaling costs one multiply and four FMAs per MFMA, about
+// half the MFMA time, and with one wave per SIMD it only overlaps the matrix core when
+// the instruction order interleaves them.  Each step rb of a block reads token block
+// rb + 1's operand from LDS, then alternates block rb's MFMAs with the rescaling of
+// block rb - 1's products (kept in a second register set).  The compiler would
+// otherwise gather the pure arithmetic of the whole unrolled block in one place, so
+// empty asm statements that consume a step's products and accumulators keep each step
+// between scheduling barriers.
 //
 // For the gate/up projection the epilogue can write h already quantised (e4m3 codes
 // and per-token per-128 scales; see below) instead of fp32 h.
@@ -43,12 +56,14 @@ constexpr int kF8Rows = 16 * kF8RowBlocks;      // 128
 #ifndef AFD_FP8_TILED_GPW
 #define AFD_FP8_TILED_GPW 2
 #endif
-constexpr int kF8GroupsPerWave = AFD_FP8_TILED_GPW;  // 32-column groups per wave (1 or 2)
+constexpr int kF8GroupsPerWave = AFD_FP8_TILED_GPW;  // 32-column groups per wave
 constexpr int kF8Groups = kF8Waves * kF8GroupsPerWave;
 constexpr int kF8CB = 2 * kF8GroupsPerWave;     // 16-column blocks per wave
+static_assert(kF8CB == 4, "the step anchors below name four 16-column blocks");
 constexpr int kF8Slot = 272;                    // bytes per staging slot (16 rows x 16 B + padding)
 constexpr int kF8A = kF8RowBlocks * 16 * kF8Slot;  // activation bytes per buffer
-constexpr int kF8Buf = kF8A + 2 * kF8Rows * 4;  // + the chunk's two scale columns
+constexpr int kF8WScales = 2 * kF8Waves * 2 * AFD_FP8_TILED_GPW;  // weight scales per chunk (2 blocks)
+constexpr int kF8Buf = kF8A + 2 * kF8Rows * 4 + kF8WScales * 4;  // + the chunk's token and weight scales
 constexpr int kF8Loads = 8;                     // staging loads per thread per chunk (4 rows each)
 constexpr int kF8BAhead = 2;                    // scale blocks of weights in flight per wave
 constexpr int kF8Xcds = 8;
@@ -58,9 +73,10 @@ __device__ __forceinline__ f32x4 f8_mfma(const i32x8& a, const i32x8& b) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 0, 0, 0, 0x7f7f7f7f, 0, 0x7f7f7f7f);
 }
 
+// A lane's 32 weight bytes of a packed fragment: 16 at p, 16 at p + 1 KiB.
 __device__ __forceinline__ i32x8 f8_load32(const uint8_t* p) {
   const i32x4* q = reinterpret_cast<const i32x4*>(p);
-  const i32x4 lo = q[0], hi = q[1];
+  const i32x4 lo = q[0], hi = q[64];
   return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
@@ -150,13 +166,19 @@ __global__ void __launch_bounds__(kF8Threads, kF8MinBlocks) gemm_fp8_tiled_kerne
                                      : static_cast<const uint8_t*>(g.w_routed) + (size_t)it.seg * g.w_expert_elems;
     const size_t group_stride = (size_t)KB * 4096;  // bytes per 32-column group
     // 16-column block cb = (group group0 + cb / 2, half cb % 2): 2 KiB per scale block
-    const uint8_t* B = wbase + (size_t)group0 * group_stride + lane * 32;
+    const uint8_t* B = wbase + (size_t)group0 * group_stride + lane * 16;
     const float* ws = it.shared ? g.s_shared : g.s_routed + (size_t)it.seg * g.s_expert_elems;
-    int nbc[kF8CB];
-#pragma unroll
-    for (int cb = 0; cb < kF8CB; ++cb) {
-      const int j = group0 + (cb >> 1), half = cb & 1;
-      nbc[cb] = (SWIGLU ? half * (N / 2) + j * 16 : j * 32 + half * 16) / 128;
+    // Weight scales are staged through LDS with the activations: thread t <
+    // kF8WScales loads, for block t / (kF8WScales / 2) of a chunk, the scale of wave
+    // (t / kF8CB) % kF8Waves's 16-column block t % kF8CB.
+    int wnb;
+    {
+      const int t = threadIdx.x % (kF8WScales / 2);
+      const int w2 = t / kF8CB, cb = t % kF8CB;
+      const int g0 = it.group + w2 * kF8GroupsPerWave < groups ? it.group + w2 * kF8GroupsPerWave
+                                                               : groups - kF8GroupsPerWave;
+      const int j = g0 + (cb >> 1), half = cb & 1;
+      wnb = (SWIGLU ? half * (N / 2) + j * 16 : j * 32 + half * 16) / 128;
     }
 
     f32x4 acc[kF8RowBlocks][kF8CB];
@@ -175,7 +197,7 @@ __global__ void __launch_bounds__(kF8Threads, kF8MinBlocks) gemm_fp8_tiled_kerne
 
     // chunk 0 -> LDS buffer 0, chunk 1 (or 0 again) -> staging registers
     bf16x8 stage[kF8Loads];
-    float sstage0 = 0.f, sstage1 = 0.f;
+    float sstage0 = 0.f, sstage1 = 0.f, wstage = 0.f;
     auto load_stage = [&](int c) {
 #pragma unroll
       for (int i = 0; i < kF8Loads; ++i) stage[i] = *reinterpret_cast<const bf16x8*>(arow[i] + a_off(c));
@@ -183,6 +205,12 @@ __global__ void __launch_bounds__(kF8Threads, kF8MinBlocks) gemm_fp8_tiled_kerne
         const int k1 = 2 * c + 1 < KB ? 2 * c + 1 : KB - 1;
         sstage0 = srow[2 * c];
         sstage1 = srow[k1];
+      }
+      if (threadIdx.x < kF8WScales) {
+        // a scale block past the end of K (odd K / 128) gets weight scale 0
+        const int kb = 2 * c + threadIdx.x / (kF8WScales / 2);
+        const int kbc = kb < KB ? kb : KB - 1;
+        wstage = ws[(size_t)kbc * NB + wnb] * (kb < KB ? 1.f : 0.f);
       }
     };
     auto write_stage = [&](int buf) {
@@ -194,55 +222,69 @@ __global__ void __launch_bounds__(kF8Threads, kF8MinBlocks) gemm_fp8_tiled_kerne
         s[threadIdx.x] = sstage0;
         s[kF8Rows + threadIdx.x] = sstage1;
       }
+      if (threadIdx.x < kF8WScales) reinterpret_cast<float*>(lds + buf + kF8A)[2 * kF8Rows + threadIdx.x] = wstage;
     };
     load_stage(0);
     write_stage(0);
     load_stage(NC > 1 ? 1 : 0);
     __syncthreads();
 
-    // Weight scales of scale block kb (0 past the end of K), loaded one block ahead.
-    auto load_wsc = [&](int kb, float* dst) {
-      const float live = kb < KB ? 1.f : 0.f;
-      const int kbc = kb < KB ? kb : KB - 1;
-#pragma unroll
-      for (int cb = 0; cb < kF8CB; ++cb) dst[cb] = ws[(size_t)kbc * NB + nbc[cb]] * live;
-    };
-    float wsn[kF8CB];
-    load_wsc(0, wsn);
-
     // One 128-deep scale block: h is the block within the chunk and also the weight-ring
     // slot (scale blocks alternate slots; a chunk holds one of each).
     auto block = [&](const int c, const int h, const int buf) {
       const int kb = 2 * c + h;
+      const float* swl = reinterpret_cast<const float*>(lds + buf + kF8A) + 2 * kF8Rows +
+                         h * (kF8WScales / 2) + w * kF8CB;
       float wsc[kF8CB];
 #pragma unroll
-      for (int cb = 0; cb < kF8CB; ++cb) wsc[cb] = wsn[cb];
-      load_wsc(kb + 1, wsn);
+      for (int cb = 0; cb < kF8CB; ++cb) wsc[cb] = swl[cb];
       const float* sbuf = reinterpret_cast<const float*>(lds + buf + kF8A) + h * kF8Rows + (lane & 15);
-#pragma unroll
-      for (int rb = 0; rb < kF8RowBlocks; ++rb) {
+      // Software pipeline over token blocks: block rb + 1's operand is read from LDS
+      // and block rb - 1's products are rescaled while block rb's MFMAs run.  The
+      // products alternate between two register sets; the token scales rotate over
+      // three slots, as step rb reads block rb + 1's while block rb - 1's is in use.
+      f32x4 p[2][kF8CB];
+      i32x8 av[2];
+      float sa[3];
+      auto rd = [&](const int rb) {
         const unsigned char* ap = lds + buf + (rb * 16 + h * 8) * kF8Slot + rd_off;
         const i32x4 l4 = *reinterpret_cast<const i32x4*>(ap);
         const i32x4 h4 = *reinterpret_cast<const i32x4*>(ap + kF8Slot);
-        const i32x8 a = {l4[0], l4[1], l4[2], l4[3], h4[0], h4[1], h4[2], h4[3]};
-        const float sa = sbuf[rb * 16];
-        // the block's MFMAs first (each product in its own registers), then their
-        // rescaling; the group barriers keep one token block's reads, MFMAs and FMAs
-        // together so products do not all share one register (which serialises every
-        // MFMA with its FMAs)
-        f32x4 p[kF8CB];
-#pragma unroll
-        for (int cb = 0; cb < kF8CB; ++cb) p[cb] = f8_mfma(bring[h][cb], a);
+        av[rb & 1] = i32x8{l4[0], l4[1], l4[2], l4[3], h4[0], h4[1], h4[2], h4[3]};
+        sa[rb % 3] = sbuf[rb * 16];
+      };
+      auto fm = [&](const int rb) {
 #pragma unroll
         for (int cb = 0; cb < kF8CB; ++cb) {
-          const float sc = sa * wsc[cb];
+          const float sc = sa[rb % 3] * wsc[cb];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[rb][cb][i] = fmaf(p[cb][i], sc, acc[rb][cb][i]);
+          for (int i = 0; i < 4; ++i) acc[rb][cb][i] = fmaf(p[rb & 1][cb][i], sc, acc[rb][cb][i]);
         }
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);             // the block's two LDS reads
-        __builtin_amdgcn_sched_group_barrier(0x008, kF8CB, 0);         // its MFMAs
-        __builtin_amdgcn_sched_group_barrier(0x002, 5 * kF8CB, 0);     // its multiplies and FMAs
+      };
+      rd(0);
+#pragma unroll
+      for (int rb = 0; rb < kF8RowBlocks; ++rb) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (rb + 1 < kF8RowBlocks) rd(rb + 1);
+        f32x4* pc = p[rb & 1];
+#pragma unroll
+        for (int cb = 0; cb < kF8CB; ++cb) pc[cb] = f8_mfma(bring[h][cb], av[rb & 1]);
+        if (rb > 0) fm(rb - 1);
+        if (rb + 1 < kF8RowBlocks) __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+#pragma unroll
+        for (int cb = 0; cb < kF8CB; ++cb) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (rb > 0) __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+        }
+        // keep this step's MFMAs and the previous step's rescaling inside the step
+        asm volatile("" ::"v"(pc[0]), "v"(pc[1]), "v"(pc[2]), "v"(pc[3]));
+        if (rb > 0) {
+          f32x4* ac = acc[rb - 1];
+          asm volatile("" : "+v"(ac[0]), "+v"(ac[1]), "+v"(ac[2]), "+v"(ac[3]));
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
+      fm(kF8RowBlocks - 1);
       // refill this ring slot with the block kF8BAhead ahead (clamped to the last)
       int sn = kb + kF8BAhead;
       sn = sn < KB ? sn : KB - 1;
