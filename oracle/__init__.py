@@ -9,6 +9,9 @@ marshals numpy arrays into it.
 Function-by-function pins (tests/test_oracle.py):
   route      -- numpy stable argsort; rank-count brute force; closed-form gates;
                 the top-k-then-softmax form of the router on the MoE engineering page.
+  router_scores -- a hand-computed integer example; one-hot gate vectors pick x's
+                columns; exact integer sums against brute force; bias shift invariance
+                of the routing and a dominant bias forcing an expert.
   permute    -- numpy stable argsort of the flattened ids; bijection; count sums.
   layer      -- numpy float64 matmuls for one expert; a diagonal-weight closed form;
                 the k = E dense mixture; token-order equivariance; MAC count 3*H*M per
@@ -63,6 +66,8 @@ def _load():
         P = ctypes.c_void_p
         lib.afdo_route.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, P]
         lib.afdo_route.restype = None
+        lib.afdo_router_scores.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, P, P]
+        lib.afdo_router_scores.restype = None
         lib.afdo_permute.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, P, P, P]
         lib.afdo_permute.restype = None
         lib.afdo_layer.argtypes = [ctypes.POINTER(_Problem), ctypes.c_int, P, P, P, P, P,
@@ -96,6 +101,20 @@ def route(logits: np.ndarray, k: int):
     gates = np.zeros((T, k), np.float64)
     _load().afdo_route(T, E, k, _p(logits), _p(ids), _p(gates))
     return ids, gates
+
+
+def router_scores(x: np.ndarray, w: np.ndarray, bias: Optional[np.ndarray] = None) -> np.ndarray:
+    """scores [T,E] float64 = x [T,H] w [E,H]^T + bias [E] (the router projection)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    T, H = x.shape
+    E = w.shape[0]
+    if w.shape[1] != H:
+        raise ValueError("x and w disagree on H")
+    b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+    out = np.zeros((T, E), np.float64)
+    _load().afdo_router_scores(T, E, H, _p(x), _p(w), None if b is None else _p(b), _p(out))
+    return out
 
 
 def permute(ids: np.ndarray, E: int):

@@ -151,6 +151,23 @@ static void mat_row(const mat_t* w, int r, double* out) {
 
 /* ------------------------------------------------------------------ routing */
 
+/* Router projection of the MoE engineering page (§4.1): a bias-free linear map from
+ * the hidden size to the experts, plus a per-expert dynamic bias, gives the scores
+ * the top-k selects on.  scores[t, e] = sum_h x[t, h] * w[e, h] + bias[e] in double
+ * (bias may be NULL: none); x [T, H] and w [E, H] hold fp32 (or bf16-valued) inputs. */
+void afdo_router_scores(int T, int E, int H, const float* x, const float* w, const float* bias, double* scores) {
+#pragma omp parallel for schedule(static)
+  for (int t = 0; t < T; ++t) {
+    const float* xr = x + (size_t)t * H;
+    for (int e = 0; e < E; ++e) {
+      const float* wr = w + (size_t)e * H;
+      double s = 0.0;
+      for (int h = 0; h < H; ++h) s += (double)xr[h] * (double)wr[h];
+      scores[(size_t)t * E + e] = s + (bias ? (double)bias[e] : 0.0);
+    }
+  }
+}
+
 /* Per token: softmax over all E logits (double), then the k experts ranked by
  * (logit descending, expert index ascending) compared on the raw fp32 logits, then
  * gates = selected probabilities / their sum.  The rank of expert e is the number of

@@ -83,6 +83,67 @@ def test_gates_renormalised_and_equal_to_softmax_of_selected(E, k):
     np.testing.assert_allclose(gates, p / p.sum(axis=1, keepdims=True), rtol=1e-13, atol=1e-15)
 
 
+# ----------------------------------------------------------------------------- router projection
+def _mat(text):
+    return np.array([[float(v) for v in row.split(",")] for row in text.split(";")], np.float32)
+
+
+def test_router_scores_golden_cases():
+    for name, k, x, w, bias, scores, ids, gates, tol in _rows("router_proj_cases.txt"):
+        b = None if bias == "-" else _mat(bias)[0]
+        got = oracle.router_scores(_mat(x), _mat(w), b)
+        np.testing.assert_array_equal(got, _mat(scores).astype(np.float64), err_msg=name)
+        got_ids, got_g = oracle.route(got.astype(np.float32), int(k))
+        np.testing.assert_array_equal(got_ids, _mat(ids).astype(np.int32), err_msg=name)
+        np.testing.assert_allclose(got_g, _mat(gates).astype(np.float64), rtol=0, atol=float(tol), err_msg=name)
+
+
+def test_router_scores_one_hot_gate_vectors_pick_columns():
+    """Gate vector of expert e = unit vector of channel perm[e]: the score is that
+    channel of x plus the bias, exactly."""
+    rng = np.random.default_rng(11)
+    T, H, E = 9, 40, 24
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    perm = rng.permutation(H)[:E]
+    w = np.zeros((E, H), np.float32)
+    w[np.arange(E), perm] = 1.0
+    bias = rng.standard_normal(E).astype(np.float32)
+    got = oracle.router_scores(x, w, bias)
+    np.testing.assert_array_equal(got, x[:, perm].astype(np.float64) + bias.astype(np.float64))
+
+
+def test_router_scores_integer_inputs_exact():
+    """Small integers: every sum is exact in double, so the scores equal numpy's int64
+    matrix product (a library routine) plus the bias."""
+    rng = np.random.default_rng(12)
+    for T, H, E in ((1, 128, 8), (7, 384, 20), (33, 1024, 256)):
+        x = rng.integers(-8, 9, size=(T, H))
+        w = rng.integers(-8, 9, size=(E, H))
+        bias = rng.integers(-50, 51, size=E)
+        got = oracle.router_scores(x.astype(np.float32), w.astype(np.float32), bias.astype(np.float32))
+        np.testing.assert_array_equal(got, (x @ w.T + bias[None, :]).astype(np.float64))
+
+
+def test_router_bias_shift_invariance_and_dominant_bias():
+    """Adding one constant to every expert's bias changes neither the selection nor the
+    gates (softmax over the selected scores); a dominant bias puts its expert in slot 0
+    of every token with a gate of 1 to double precision."""
+    rng = np.random.default_rng(13)
+    T, H, E, k = 20, 64, 16, 4
+    x = rng.integers(-4, 5, size=(T, H)).astype(np.float32)
+    w = rng.integers(-4, 5, size=(E, H)).astype(np.float32)
+    bias = rng.integers(-3, 4, size=E).astype(np.float32)
+    ids0, g0 = oracle.route(oracle.router_scores(x, w, bias).astype(np.float32), k)
+    ids1, g1 = oracle.route(oracle.router_scores(x, w, bias + 64.0).astype(np.float32), k)
+    np.testing.assert_array_equal(ids0, ids1)
+    np.testing.assert_allclose(g0, g1, rtol=0, atol=1e-12)
+    forced = bias.copy()
+    forced[5] = 1e4
+    ids2, g2 = oracle.route(oracle.router_scores(x, w, forced).astype(np.float32), k)
+    assert np.all(ids2[:, 0] == 5)
+    np.testing.assert_allclose(g2[:, 0], 1.0, rtol=0, atol=1e-12)
+
+
 # ----------------------------------------------------------------------------- permute
 @pytest.mark.parametrize("T,E,k,seed", [(64, 8, 2, 0), (6, 128, 8, 1), (300, 256, 8, 2), (1, 4, 4, 3), (0, 8, 2, 4)])
 def test_permute_is_stable_counting_sort(T, E, k, seed):
