@@ -54,6 +54,9 @@ def parse():
                     help="one JSON line per workload: every layer shape plus the 256/512/1024 tokens-per-expert "
                          "bf16 and fp8 sweeps (HBM and MFMA fractions); not the benchmark line")
     ap.add_argument("--only", default="", help="with --sweep: run the workloads whose name contains this text")
+    ap.add_argument("--router-proj", action="store_true",
+                    help="one JSON line per workload shape: the router projection of afd_ffn_route_hidden "
+                         "(logits = x W_r^T + bias) timed alone, with its roofline; not the benchmark line")
     return ap.parse_args()
 
 
@@ -242,6 +245,57 @@ def sweep(args, torch):
         torch.cuda.empty_cache()
 
 
+def router_proj(args, torch):
+    """Time the router projection (the first kernel of afd_ffn_route_hidden) on each
+    workload's (T, H, E) with seeded synthetic x, gate vectors ~ N(0, 1/H) and bias.
+    Algorithmic bytes: W_r and x read once, logits written once; FLOPs 2 T H E."""
+    from moe_expert_ffn_softmax_amd import MoeExpertFFN, afd_ffn_profile_read, afd_ffn_set_profiling
+    wls = list(workloads.ORDERED) + workloads.mfma_sweep("bf16") + workloads.mfma_sweep("fp8")
+    for w in wls:
+        if args.only and not any(o in w.name for o in args.only.split(",")):
+            continue
+        dt = "f32" if w.dtype == "f32" else "bf16"
+        tdt = torch.float32 if dt == "f32" else torch.bfloat16
+        a = 4 if dt == "f32" else 2
+        M = 128
+        layer = MoeExpertFFN(hidden=w.H, inter=M, num_experts=w.E, top_k=w.k, max_tokens=w.T, dtype=dt,
+                             w_gate_up=torch.zeros((w.E, w.H, 2 * M), dtype=tdt, device="cuda"),
+                             w_down=torch.zeros((w.E, M, w.H), dtype=tdt, device="cuda"))
+        g = torch.Generator(device="cuda").manual_seed(1000 + w.index)
+        x = torch.randn((w.T, w.H), generator=g, device="cuda").to(tdt)
+        wr = (torch.randn((w.E, w.H), generator=g, device="cuda") / float(np.sqrt(w.H))).to(tdt)
+        bias = torch.randn(w.E, generator=g, device="cuda") * 0.01
+        logits = torch.empty((w.T, w.E), dtype=torch.float32, device="cuda")
+        rb = layer.new_route()
+        steps = args.steps if w.T <= 64 else max(5, min(args.steps, 50))
+        for _ in range(min(args.warmup, 5)):
+            layer.route_hidden(x, wr, logits, w.T, rb, bias=bias)
+        torch.cuda.synchronize()
+        afd_ffn_set_profiling(layer.handle, True)
+        for _ in range(steps):
+            layer.route_hidden(x, wr, logits, w.T, rb, bias=bias)
+        torch.cuda.synchronize()
+        prof = afd_ffn_profile_read(layer.handle)
+        layer.close()
+        us = prof["router_proj"][0] / max(prof["router_proj"][1], 1) * 1e3
+        nbytes = (w.E * w.H + w.T * w.H) * a + w.T * w.E * 4 + w.E * 4
+        flops = 2.0 * w.T * w.H * w.E
+        peak_tf = MFMA_PEAK_TFLOPS[dt]
+        mfma_bound = flops / (peak_tf * 1e12) > nbytes / (HBM_PEAK_GBS * 1e9)
+        if mfma_bound:
+            ach, peak, unit = flops / (us * 1e-6) / 1e12, peak_tf, "TFLOP/s"
+        else:
+            ach, peak, unit = nbytes / (us * 1e-6) / 1e9, HBM_PEAK_GBS, "GB/s"
+        route_us = {k: round(v[0] / max(v[1], 1) * 1e3, 2) for k, v in prof.items() if v[1] and k != "router_proj"}
+        print(json.dumps({"workload": w.name, "T": w.T, "H": w.H, "E": w.E, "dtype": dt,
+                          "router_proj_us": round(us, 2), "bytes": nbytes, "flops": flops,
+                          "roofline": {"bound": "mfma" if mfma_bound else "hbm", "achieved": round(ach, 1),
+                                       "peak": peak, "unit": unit, "frac": round(ach / peak, 4)},
+                          "route_us": route_us}), flush=True)
+        del x, wr, logits, rb
+        torch.cuda.empty_cache()
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -255,6 +309,10 @@ def main():
     if args.sweep:
         torch.cuda.set_device(0)
         sweep(args, torch)
+        return
+    if args.router_proj:
+        torch.cuda.set_device(0)
+        router_proj(args, torch)
         return
     from moe_expert_ffn_softmax_amd import MoeExpertFFN, afd_ffn_profile_read, afd_ffn_set_profiling
 

@@ -116,6 +116,20 @@ int afd_ffn_create(const afd_ffn_config* cfg, const void* w_gate_up, const void*
  * 0 <= T <= max_tokens. */
 int afd_ffn_route(afd_ffn_t h, const float* logits, int32_t T, const afd_route* r, void* stream);
 
+/* Route T tokens from their hidden states: the router projection of "MoE 大规模分布式
+ * 推理工程实战：从 All-to-All 通信到动态专家放置" (§4.1), a bias-free linear map from
+ * the hidden size to the experts plus a per-expert dynamic bias, followed by the
+ * routing of afd_ffn_route.
+ *   logits[t, e] = sum_h x[t, h] * w_router[e, h] + bias[e]   (fp32 accumulation)
+ * x [T, H] and w_router [E, H] (row e is expert e's gate vector) are fp32 for AFD_F32
+ * and bf16 otherwise; bias [E] is fp32, or NULL for none.  The bias takes part in the
+ * selection and in the gates, which are the softmax of the selected biased logits, as
+ * in that router.  logits [T, E] fp32 (caller-owned device memory, not overlapping
+ * the inputs) receives the biased logits and is then routed exactly as
+ * afd_ffn_route(h, logits, T, r, stream) would route it.  0 <= T <= max_tokens. */
+int afd_ffn_route_hidden(afd_ffn_t h, const void* x, const void* w_router, const float* bias, float* logits,
+                         int32_t T, const afd_route* r, void* stream);
+
 /* Expert FFN of T routed tokens: x [T, H] (fp32 for AFD_F32, else bf16) and the
  * result of afd_ffn_route for the same T -> y [T, H] (fp32 for AFD_F32, else bf16).
  * x and y must not overlap. */
@@ -172,7 +186,8 @@ typedef enum afd_stage {
   AFD_STAGE_GATE_UP = 3, /* grouped gate/up GEMM with SwiGLU epilogue */
   AFD_STAGE_DOWN = 4,    /* grouped down-projection GEMM */
   AFD_STAGE_COMBINE = 5, /* gate-weighted combine back to token order */
-  AFD_NUM_STAGES = 6
+  AFD_STAGE_ROUTER_PROJ = 6, /* router projection of afd_ffn_route_hidden */
+  AFD_NUM_STAGES = 7
 } afd_stage;
 int afd_ffn_set_profiling(afd_ffn_t h, int on);
 int afd_ffn_profile_read(afd_ffn_t h, double* ms, int64_t* launches, int n_stages);

@@ -11,7 +11,8 @@ from __future__ import annotations
 from ._ffi import (AFD_BF16, AFD_F32, AFD_FP8_E4M3, AFD_GEMM_AUTO, AFD_GEMM_STREAM,  # noqa: F401
                    AFD_GEMM_TILED, AFD_GEMM_WIDE, STAGES, AfdError, afd_ffn_config, afd_ffn_create, afd_ffn_destroy,
                    afd_ffn_device_bytes, afd_ffn_forward, afd_ffn_last_error, afd_ffn_profile_read,
-                   afd_ffn_quantize_fp8, afd_ffn_route, afd_ffn_set_gemm_kernel, afd_ffn_set_profiling,
+                   afd_ffn_quantize_fp8, afd_ffn_route, afd_ffn_route_hidden, afd_ffn_set_gemm_kernel,
+                   afd_ffn_set_profiling,
                    afd_ffn_strerror, afd_route, load)
 
 GEMM_KERNELS = {"auto": AFD_GEMM_AUTO, "stream": AFD_GEMM_STREAM, "tiled": AFD_GEMM_TILED,
@@ -83,6 +84,12 @@ class MoeExpertFFN:
     def route(self, logits, T: int, rb: RouteBuffers, stream=None) -> None:
         import torch
         afd_ffn_route(self.handle, logits, T, rb.c, _stream_handle(torch, stream))
+
+    def route_hidden(self, x, w_router, logits, T: int, rb: RouteBuffers, bias=None, stream=None) -> None:
+        """Route from hidden states: logits [T, E] (fp32, written) = x w_router^T + bias,
+        then the routing of route()."""
+        import torch
+        afd_ffn_route_hidden(self.handle, x, w_router, bias, logits, T, rb.c, _stream_handle(torch, stream))
 
     def forward(self, x, T: int, rb: RouteBuffers, y, stream=None) -> None:
         import torch

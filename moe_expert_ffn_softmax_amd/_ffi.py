@@ -13,7 +13,7 @@ LIB_PATH = os.path.join(_PKG, "libafd_ffn.so")
 AFD_OK, AFD_EINVAL, AFD_EUNSUPPORTED, AFD_ENOMEM, AFD_EHIP = 0, -1, -2, -3, -4
 AFD_F32, AFD_BF16, AFD_FP8_E4M3 = 0, 1, 2
 AFD_GEMM_AUTO, AFD_GEMM_STREAM, AFD_GEMM_TILED, AFD_GEMM_WIDE = 0, 1, 2, 3
-STAGES = ("router", "permute", "quant", "gate_up", "down", "combine")
+STAGES = ("router", "permute", "quant", "gate_up", "down", "combine", "router_proj")
 AFD_NUM_STAGES = len(STAGES)
 
 
@@ -50,6 +50,8 @@ def load():
     lib.afd_ffn_create.restype = ctypes.c_int
     lib.afd_ffn_route.argtypes = [V, P, I32, ctypes.POINTER(afd_route), V]
     lib.afd_ffn_route.restype = ctypes.c_int
+    lib.afd_ffn_route_hidden.argtypes = [V, P, P, P, P, I32, ctypes.POINTER(afd_route), V]
+    lib.afd_ffn_route_hidden.restype = ctypes.c_int
     lib.afd_ffn_forward.argtypes = [V, P, I32, ctypes.POINTER(afd_route), P, V]
     lib.afd_ffn_forward.restype = ctypes.c_int
     lib.afd_ffn_destroy.argtypes = [V]
@@ -105,6 +107,11 @@ def afd_ffn_create(cfg: afd_ffn_config, w_gate_up, w_down, s_gate_up=None, s_dow
 
 def afd_ffn_route(h: int, logits, T: int, route: afd_route, stream=None) -> None:
     _check(load().afd_ffn_route(h, _ptr(logits), int(T), ctypes.byref(route), stream))
+
+
+def afd_ffn_route_hidden(h: int, x, w_router, bias, logits, T: int, route: afd_route, stream=None) -> None:
+    _check(load().afd_ffn_route_hidden(h, _ptr(x), _ptr(w_router), _ptr(bias), _ptr(logits), int(T),
+                                       ctypes.byref(route), stream))
 
 
 def afd_ffn_forward(h: int, x, T: int, route: afd_route, y, stream=None) -> None:

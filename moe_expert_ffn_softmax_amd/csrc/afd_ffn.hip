@@ -371,6 +371,24 @@ extern "C" int afd_ffn_route(afd_ffn_t h, const float* logits, int32_t T, const 
   return AFD_OK;
 }
 
+extern "C" int afd_ffn_route_hidden(afd_ffn_t h, const void* x, const void* w_router, const float* bias,
+                                    float* logits, int32_t T, const afd_route* r, void* stream) {
+  int rc = check_route(h, r, T);
+  if (rc) return rc;
+  if (!x || !w_router || !logits) return fail(AFD_EINVAL, "x, w_router or logits is NULL");
+  if (T == 0) return AFD_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const afd_ffn_config& c = h->cfg;
+  {
+    StageScope s(h, st, AFD_STAGE_ROUTER_PROJ);
+    hipError_t e = afd::launch_router_proj(x, w_router, bias, T, c.hidden, c.num_experts, c.dtype == AFD_F32,
+                                           logits, st);
+    if (e != hipSuccess) return hip_fail(e, "router projection launch");
+    s.done();
+  }
+  return afd_ffn_route(h, logits, T, r, stream);
+}
+
 extern "C" int afd_ffn_forward(afd_ffn_t h, const void* x, int32_t T, const afd_route* r, void* y, void* stream) {
   int rc = check_route(h, r, T);
   if (rc) return rc;

@@ -54,6 +54,9 @@ struct GroupedGemm {
 
 hipError_t launch_router(const float* logits, int T, int E, int k, int32_t* ids, float* gates,
                          hipStream_t st);
+// logits [T, E] = x [T, H] * w [E, H]^T (+ bias [E]); x and w bf16, or fp32 when f32.
+hipError_t launch_router_proj(const void* x, const void* w, const float* bias, int T, int H, int E, bool f32,
+                              float* logits, hipStream_t st);
 // Router and permute as one launch for batches of at most route_small_tokens() tokens.
 hipError_t launch_route_small(const float* logits, int T, int E, int k, int32_t* ids, float* gates, int32_t* counts,
                               int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos, hipStream_t st);
