@@ -73,6 +73,11 @@ static_assert(kTiledLoads * 4 == 32, "a wave stages 32 rows, 4 per load");
 
 __device__ __forceinline__ bf16x8 tiled_load_b(const bf16x8* p) { return *p; }
 
+template <int N>
+struct IntC {
+  static constexpr int value = N;
+};
+
 #ifndef AFD_TILED_SCHED
 #define AFD_TILED_SCHED 1
 #endif
@@ -166,81 +171,107 @@ __global__ void __launch_bounds__(kTiledThreads, kTiledMinBlocks) gemm_bf16_tile
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh) bring[u][cb][kh] = tiled_load_b(bbase[cb] + u * 128 + kh * 32);
 
-    // A chunk 0 -> LDS buffer 0, chunk 1 (or chunk 0 again) -> staging registers;
-    // a chunk is 16 pieces of 16 bytes per row
-    bf16x8 stage[kTiledLoads];
+    // The main loop is instantiated for RB = 1..4 row blocks holding rows, so a tile
+    // with few rows does only the MFMAs, LDS reads and activation staging its rows
+    // need (waves w >= RB stage nothing; every wave still takes the barriers).  RB is
+    // uniform over the workgroup.
+    auto main_loop = [&](auto rbc) {
+      constexpr int RB = decltype(rbc)::value;
+      // A chunk 0 -> LDS buffer 0, chunk 1 (or chunk 0 again) -> staging registers;
+      // a chunk is 16 pieces of 16 bytes per row
+      bf16x8 stage[kTiledLoads];
+      if (w < RB) {
 #pragma unroll
-    for (int i = 0; i < kTiledLoads; ++i) stage[i] = arow[i][0];
+        for (int i = 0; i < kTiledLoads; ++i) stage[i] = arow[i][0];
 #pragma unroll
-    for (int i = 0; i < kTiledLoads; ++i) *reinterpret_cast<bf16x8*>(lds + wr_off + i * 64) = stage[i];
-    {
-      const int cn = NC > 1 ? 1 : 0;
+        for (int i = 0; i < kTiledLoads; ++i) *reinterpret_cast<bf16x8*>(lds + wr_off + i * 64) = stage[i];
+        const int cn = NC > 1 ? 1 : 0;
 #pragma unroll
-      for (int i = 0; i < kTiledLoads; ++i) stage[i] = arow[i][cn * 16];
-    }
-    __syncthreads();
-
-    // The reduction runs as 16-deep half-steps (u, kh).  The A fragments of the next
-    // half-step are read from LDS while the current half-step's MFMAs run; in the
-    // chunk's last half-step the next chunk (already in registers) is written to the
-    // other LDS buffer and the barrier is taken before its first fragments are read,
-    // so that read is covered by the last MFMAs of this chunk too.
-    bf16x8 a[2][kTiledRowBlocks];
-#pragma unroll
-    for (int rb = 0; rb < kTiledRowBlocks; ++rb)
-      a[0][rb] = *reinterpret_cast<const bf16x8*>(lds + rb * kTiledFrags * kTiledSlot + rd_off);
-
-    for (int c = 0; c < NC; ++c) {
-      const int buf = (c & 1) * kTiledBuf;
-      const int nbuf = kTiledBuf - buf;
-#pragma unroll
-      for (int hs = 0; hs < kTiledFrags; ++hs) {
-        const int u = hs >> 1, kh = hs & 1;
-        const int cur = hs & 1, nxt = cur ^ 1;
-        if (hs + 1 < kTiledFrags) {
-#pragma unroll
-          for (int rb = 0; rb < kTiledRowBlocks; ++rb)
-            a[nxt][rb] =
-                *reinterpret_cast<const bf16x8*>(lds + buf + (rb * kTiledFrags + hs + 1) * kTiledSlot + rd_off);
-        } else {
-          // branch-free chunk boundary: past the last chunk these write, load and read
-          // data nobody uses (the loads are clamped to the last chunk)
-#pragma unroll
-          for (int i = 0; i < kTiledLoads; ++i) *reinterpret_cast<bf16x8*>(lds + nbuf + wr_off + i * 64) = stage[i];
-          __syncthreads();
-          const int cn = c + 2 < NC ? c + 2 : NC - 1;
-#pragma unroll
-          for (int i = 0; i < kTiledLoads; ++i) stage[i] = arow[i][cn * 16];
-#pragma unroll
-          for (int rb = 0; rb < kTiledRowBlocks; ++rb)
-            a[nxt][rb] = *reinterpret_cast<const bf16x8*>(lds + nbuf + rb * kTiledFrags * kTiledSlot + rd_off);
-        }
-        const int slotb = u % kTiledBAhead;
-#pragma unroll
-        for (int rb = 0; rb < kTiledRowBlocks; ++rb)
-#pragma unroll
-          for (int cb = 0; cb < kTiledGroupsPerWave; ++cb)
-            acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cur][rb], bring[slotb][cb][kh], acc[rb][cb], 0, 0, 0);
-        if (kh == 1) {
-          // refill this ring slot with the step kTiledBAhead ahead (clamped to the last)
-          int s = c * kTiledKC + u + kTiledBAhead;
-          s = s < KB ? s : KB - 1;
-#pragma unroll
-          for (int cb = 0; cb < kTiledGroupsPerWave; ++cb)
-#pragma unroll
-            for (int k2 = 0; k2 < 2; ++k2) bring[slotb][cb][k2] = tiled_load_b(bbase[cb] + s * 128 + k2 * 32);
-        }
-#if AFD_TILED_SCHED
-        // keep the next half-step's LDS reads spread between this half-step's MFMAs
-        // (left alone, the scheduler sinks each read to just before its first use)
-#pragma unroll
-        for (int rb = 0; rb < kTiledRowBlocks; ++rb) {
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                    // one LDS read
-          __builtin_amdgcn_sched_group_barrier(0x008, kTiledGroupsPerWave, 0);  // one row block's MFMAs
-        }
-#endif
+        for (int i = 0; i < kTiledLoads; ++i) stage[i] = arow[i][cn * 16];
       }
-    }
+      __syncthreads();
+
+      // The reduction runs as 16-deep half-steps (u, kh).  The A fragments of the next
+      // half-step are read from LDS while the current half-step's MFMAs run; in the
+      // chunk's last half-step the next chunk (already in registers) is written to the
+      // other LDS buffer and the barrier is taken before its first fragments are read,
+      // so that read is covered by the last MFMAs of this chunk too.
+      bf16x8 a[2][kTiledRowBlocks];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+        a[0][rb] = *reinterpret_cast<const bf16x8*>(lds + rb * kTiledFrags * kTiledSlot + rd_off);
+
+      for (int c = 0; c < NC; ++c) {
+        const int buf = (c & 1) * kTiledBuf;
+        const int nbuf = kTiledBuf - buf;
+#pragma unroll
+        for (int hs = 0; hs < kTiledFrags; ++hs) {
+          const int u = hs >> 1, kh = hs & 1;
+          const int cur = hs & 1, nxt = cur ^ 1;
+          if (hs + 1 < kTiledFrags) {
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+              a[nxt][rb] =
+                  *reinterpret_cast<const bf16x8*>(lds + buf + (rb * kTiledFrags + hs + 1) * kTiledSlot + rd_off);
+          } else {
+            // branch-free chunk boundary: past the last chunk these write, load and read
+            // data nobody uses (the loads are clamped to the last chunk)
+            if (w < RB) {
+#pragma unroll
+              for (int i = 0; i < kTiledLoads; ++i)
+                *reinterpret_cast<bf16x8*>(lds + nbuf + wr_off + i * 64) = stage[i];
+            }
+            __syncthreads();
+            if (w < RB) {
+              const int cn = c + 2 < NC ? c + 2 : NC - 1;
+#pragma unroll
+              for (int i = 0; i < kTiledLoads; ++i) stage[i] = arow[i][cn * 16];
+            }
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+              a[nxt][rb] = *reinterpret_cast<const bf16x8*>(lds + nbuf + rb * kTiledFrags * kTiledSlot + rd_off);
+          }
+          const int slotb = u % kTiledBAhead;
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int cb = 0; cb < kTiledGroupsPerWave; ++cb)
+              acc[rb][cb] =
+                  __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cur][rb], bring[slotb][cb][kh], acc[rb][cb], 0, 0, 0);
+          if (kh == 1) {
+            // refill this ring slot with the step kTiledBAhead ahead (clamped to the last)
+            int s = c * kTiledKC + u + kTiledBAhead;
+            s = s < KB ? s : KB - 1;
+#pragma unroll
+            for (int cb = 0; cb < kTiledGroupsPerWave; ++cb)
+#pragma unroll
+              for (int k2 = 0; k2 < 2; ++k2) bring[slotb][cb][k2] = tiled_load_b(bbase[cb] + s * 128 + k2 * 32);
+          }
+#if AFD_TILED_SCHED
+          // keep the next half-step's LDS reads spread between this half-step's MFMAs
+          // (left alone, the scheduler sinks each read to just before its first use)
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                    // one LDS read
+            __builtin_amdgcn_sched_group_barrier(0x008, kTiledGroupsPerWave, 0);  // one row block's MFMAs
+          }
+#endif
+        }
+      }
+    };
+    // Only an expert's single row tile is shortened: the row tiles of a larger
+    // expert stream the same weights at the same time through one XCD's L2, and a
+    // shortened last tile running ahead of its siblings measured slower.
+    const int seg_rows = it.shared ? g.shared_rows : g.counts[it.seg];
+    const int nrb = seg_rows > kTiledRows ? kTiledRowBlocks : (it.nrows + 31) / 32;
+    if (nrb >= 4)
+      main_loop(IntC<4>{});
+    else if (nrb == 3)
+      main_loop(IntC<3>{});
+    else if (nrb == 2)
+      main_loop(IntC<2>{});
+    else
+      main_loop(IntC<1>{});
 
     if (active) {
       const int col = lane & 31;
