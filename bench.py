@@ -54,6 +54,10 @@ def parse():
                     help="one JSON line per workload: every layer shape plus the 256/512/1024 tokens-per-expert "
                          "bf16 and fp8 sweeps (HBM and MFMA fractions); not the benchmark line")
     ap.add_argument("--only", default="", help="with --sweep: run the workloads whose name contains this text")
+    ap.add_argument("--ubatches", action="store_true",
+                    help="one JSON line per workload: the batch as one call vs split in two micro-batches, "
+                         "serial or with the second's routing on a second stream under the first's forward; "
+                         "not the benchmark line")
     ap.add_argument("--router-proj", action="store_true",
                     help="one JSON line per workload shape: the router projection of afd_ffn_route_hidden "
                          "(logits = x W_r^T + bias) timed alone, with its roofline; not the benchmark line")
@@ -296,6 +300,84 @@ def router_proj(args, torch):
         torch.cuda.empty_cache()
 
 
+def ubatches(args, torch):
+    """Two micro-batches in flight on one handle (the two-micro-batch overlap of the
+    AFD blog's section 4, on the FFN side): micro-batch 2's route runs on a second stream
+    while micro-batch 1's forward runs; both forwards stay on the first stream, which
+    owns the handle's workspace.  Compared with the whole batch as one call and with
+    the two micro-batches run back to back on one stream."""
+    from moe_expert_ffn_softmax_amd import MoeExpertFFN
+    wls = list(workloads.ORDERED) + workloads.mfma_sweep("bf16") + workloads.mfma_sweep("fp8")
+    for w in wls:
+        if args.only and not any(o in w.name for o in args.only.split(",")):
+            continue
+        weights = workloads.make_weights(w, device="cuda")
+        layer = MoeExpertFFN(hidden=w.H, inter=w.M, num_experts=w.E, top_k=w.k, max_tokens=w.T, dtype=w.dtype,
+                             w_gate_up=weights["w_gu"], w_down=weights["w_d"], s_gate_up=weights["s_gu"],
+                             s_down=weights["s_d"], shared_inter=w.Ms, ws_gate_up=weights["ws_gu"],
+                             ws_down=weights["ws_d"], ss_gate_up=weights["ss_gu"], ss_down=weights["ss_d"])
+        del weights
+        nb = 2
+        T1 = (w.T + 1) // 2
+        T2 = w.T - T1
+        ydt = torch.float32 if w.dtype == "f32" else torch.bfloat16
+        xs, lgs, ys = [], [], []
+        for b in range(nb):
+            x, lg = workloads.make_activations(w, device="cuda", batch=b)
+            xs.append(x)
+            lgs.append(lg)
+            ys.append(torch.empty((w.T, w.H), dtype=ydt, device="cuda"))
+        rb0 = [layer.new_route() for _ in range(nb)]
+        rb1 = [layer.new_route() for _ in range(nb)]
+        rb2 = [layer.new_route() for _ in range(nb)]
+        sa = torch.cuda.current_stream()
+        sb = torch.cuda.Stream()
+        ev_route = [torch.cuda.Event() for _ in range(nb)]
+        ev_free = [torch.cuda.Event() for _ in range(nb)]
+        for e in ev_free:
+            e.record(sa)
+
+        def whole(i):
+            b = i % nb
+            layer.route(lgs[b], w.T, rb0[b])
+            layer.forward(xs[b], w.T, rb0[b], ys[b])
+
+        def serial(i):
+            b = i % nb
+            layer.route(lgs[b], T1, rb1[b])
+            layer.forward(xs[b], T1, rb1[b], ys[b])
+            layer.route(lgs[b][T1:], T2, rb2[b])
+            layer.forward(xs[b][T1:], T2, rb2[b], ys[b][T1:])
+
+        def overlapped(i):
+            b = i % nb
+            sb.wait_event(ev_free[b])  # the last forward that read rb2[b] is done
+            layer.route(lgs[b][T1:], T2, rb2[b], stream=sb)
+            ev_route[b].record(sb)
+            layer.route(lgs[b], T1, rb1[b])
+            layer.forward(xs[b], T1, rb1[b], ys[b])
+            sa.wait_event(ev_route[b])
+            layer.forward(xs[b][T1:], T2, rb2[b], ys[b][T1:])
+            ev_free[b].record(sa)
+
+        steps = args.steps if w.T <= 64 else max(5, min(args.steps, 20))
+        out = {"workload": w.name, "T": w.T, "micro_batches": [T1, T2]}
+        for name, fn in (("whole_ms", whole), ("serial_ms", serial), ("overlapped_ms", overlapped),
+                         ("whole_ms_again", whole)):
+            for i in range(min(args.warmup, 5)):
+                fn(i)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for i in range(steps):
+                fn(i)
+            torch.cuda.synchronize()
+            out[name] = round((time.perf_counter() - t0) * 1e3 / steps, 4)
+        layer.close()
+        print(json.dumps(out), flush=True)
+        del xs, lgs, ys, rb0, rb1, rb2
+        torch.cuda.empty_cache()
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -313,6 +395,10 @@ def main():
     if args.router_proj:
         torch.cuda.set_device(0)
         router_proj(args, torch)
+        return
+    if args.ubatches:
+        torch.cuda.set_device(0)
+        ubatches(args, torch)
         return
     from moe_expert_ffn_softmax_amd import MoeExpertFFN, afd_ffn_profile_read, afd_ffn_set_profiling
 

@@ -331,6 +331,54 @@ def test_hip_graph_replays_match_eager(w, kernel):
         assert torch.equal(rb.sorted_pair, rb_e.sorted_pair), f"replay {rep}: permutation differs"
 
 
+@pytest.mark.parametrize("w", [
+    small("ubatch_bf16", T=100, H=256, M=384, E=16, k=4),
+    small("ubatch_decode", T=6, H=512, M=256, E=32, k=4),
+    small("ubatch_fp8_shared", dtype="fp8", T=90, H=384, M=256, E=6, k=2, Ms=256),
+], ids=lambda w: w.name)
+def test_two_micro_batches_on_two_streams(w):
+    """Two micro-batches in flight on one handle (the AFD blog's two-micro-batch
+    overlap, FFN side): micro-batch 2 is routed on a second stream while micro-batch
+    1's forward runs; both forwards run on the first stream.  Each micro-batch's
+    output equals that micro-batch run alone, bit for bit, over several rounds."""
+    weights = workloads.make_weights(w, device="cuda")
+    x, logits = workloads.make_activations(w, device="cuda")
+    layer = make_layer(w, weights)
+    T1 = (w.T + 1) // 2
+    T2 = w.T - T1
+    ydt = torch.float32 if w.dtype == "f32" else torch.bfloat16
+    # each micro-batch alone, on the default stream
+    ref = torch.empty((w.T, w.H), dtype=ydt, device="cuda")
+    ra, rb_ = layer.new_route(), layer.new_route()
+    layer.route(logits, T1, ra)
+    layer.forward(x, T1, ra, ref)
+    layer.route(logits[T1:], T2, rb_)
+    layer.forward(x[T1:], T2, rb_, ref[T1:])
+    torch.cuda.synchronize()
+    # overlapped, three rounds reusing the route buffers
+    sa = torch.cuda.current_stream()
+    sb = torch.cuda.Stream()
+    r1, r2 = layer.new_route(), layer.new_route()
+    ev_route, ev_free = torch.cuda.Event(), torch.cuda.Event()
+    ev_free.record(sa)
+    for rnd in range(3):
+        y = torch.full((w.T, w.H), float("nan"), dtype=ydt, device="cuda")
+        sb.wait_event(ev_free)
+        layer.route(logits[T1:], T2, r2, stream=sb)
+        ev_route.record(sb)
+        layer.route(logits, T1, r1)
+        layer.forward(x, T1, r1, y)
+        sa.wait_event(ev_route)
+        layer.forward(x[T1:], T2, r2, y[T1:])
+        ev_free.record(sa)
+        torch.cuda.synchronize()
+        assert torch.equal(y, ref), f"round {rnd}: overlapped micro-batches differ from the runs alone"
+    # and the whole output against the oracle
+    rows, yref = oracle_rows(w, weights, x, logits.cpu().numpy(), np.arange(w.T))
+    check_y(y, yref, TOL[w.dtype], w.name)
+    layer.close()
+
+
 def test_zero_tokens_is_a_no_op():
     w = small("empty", T=8)
     weights = workloads.make_weights(w, device="cuda")
