@@ -233,6 +233,13 @@ extern "C" int afd_ffn_create(const afd_ffn_config* cfg, const void* w_gate_up, 
     return hip_fail(e, "hipGetDeviceProperties");
   }
   h->num_cus = prop.multiProcessorCount;
+  e = afd::configure_gemm_bf16_tiled();
+  if (e == hipSuccess) e = afd::configure_gemm_bf16_wide();
+  if (e == hipSuccess) e = afd::configure_gemm_fp8_tiled();
+  if (e != hipSuccess) {
+    release(h);
+    return hip_fail(e, "hipFuncSetAttribute (dynamic LDS limit)");
+  }
   {
     int occ[6] = {0, 0, 0, 0, 0, 0};
     e = afd::gemm_occupancy_bf16(&occ[0], &occ[1]);

@@ -86,6 +86,11 @@ hipError_t launch_gemm_bf16(const GroupedGemm& g, bool swiglu, long long max_ite
 hipError_t launch_gemm_f32(const GroupedGemm& g, bool swiglu, long long max_items, int max_blocks, hipStream_t st);
 // Large-tile variant (128-row tiles, 8 column groups per item) for experts with many
 // rows; `max_blocks` as above.
+// The 128-row and 256x256 GEMM kernels use more than the default dynamic LDS; these
+// raise the limit for the current device (called once per handle at creation).
+hipError_t configure_gemm_bf16_tiled();
+hipError_t configure_gemm_bf16_wide();
+hipError_t configure_gemm_fp8_tiled();
 hipError_t launch_gemm_bf16_tiled(const GroupedGemm& g, bool swiglu, long long max_items, int max_blocks,
                                   hipStream_t st);
 int tiled_rows();

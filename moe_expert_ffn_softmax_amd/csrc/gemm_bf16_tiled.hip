@@ -314,14 +314,7 @@ __global__ void __launch_bounds__(kTiledThreads, kTiledMinBlocks) gemm_bf16_tile
 
 template <bool SWIGLU>
 static hipError_t launch_tiled(const GroupedGemm& g, long long max_items, int max_blocks, hipStream_t st) {
-  const size_t smem = 2 * kTiledBuf;
-  static bool configured = false;  // raise the dynamic LDS limit once per process
-  if (!configured) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_bf16_tiled_kernel<SWIGLU>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-    if (e != hipSuccess) return e;
-    configured = true;
-  }
+  const size_t smem = 2 * kTiledBuf;  // above the default limit: see configure_gemm_bf16_tiled
   // max_blocks counts compute units; the kernel is built for kTiledMinBlocks
   // resident workgroups on each
   const long long resident = (long long)max_blocks * kTiledMinBlocks;
@@ -333,6 +326,17 @@ static hipError_t launch_tiled(const GroupedGemm& g, long long max_items, int ma
 
 // Every reduction length here is a multiple of 128 (the layer's dimensions are), so
 // whole 128-deep chunks cover it.
+// Raise the kernels' dynamic LDS limit on the current device (handle creation).
+hipError_t configure_gemm_bf16_tiled() {
+  const int smem = 2 * kTiledBuf;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_bf16_tiled_kernel<true>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, smem);
+  if (e == hipSuccess)
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_bf16_tiled_kernel<false>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, smem);
+  return e;
+}
+
 hipError_t launch_gemm_bf16_tiled(const GroupedGemm& g, bool swiglu, long long max_items, int max_blocks,
                                   hipStream_t st) {
   if (max_items <= 0) return hipSuccess;

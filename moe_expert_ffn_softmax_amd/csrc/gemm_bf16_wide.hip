@@ -265,14 +265,7 @@ __global__ void __launch_bounds__(kWideThreads, 1) gemm_bf16_wide_kernel(Grouped
 
 template <bool SWIGLU>
 static hipError_t launch_wide(const GroupedGemm& g, long long max_items, int max_blocks, hipStream_t st) {
-  const size_t smem = 2 * kWideBuf;
-  static bool configured = false;  // raise the dynamic LDS limit once per process
-  if (!configured) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_bf16_wide_kernel<SWIGLU>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-    if (e != hipSuccess) return e;
-    configured = true;
-  }
+  const size_t smem = 2 * kWideBuf;  // above the default limit: see configure_gemm_bf16_wide
   long long blocks = max_items < max_blocks ? max_items : max_blocks;
   blocks = blocks < kWideXcds ? kWideXcds : blocks / kWideXcds * kWideXcds;
   gemm_bf16_wide_kernel<SWIGLU><<<(unsigned)blocks, kWideThreads, smem, st>>>(g);
@@ -281,6 +274,17 @@ static hipError_t launch_wide(const GroupedGemm& g, long long max_items, int max
 
 // Reduction lengths are multiples of 128 and group counts multiples of 4 (the layer's
 // dimensions are multiples of 128); `max_blocks` counts compute units.
+// Raise the kernels' dynamic LDS limit on the current device (handle creation).
+hipError_t configure_gemm_bf16_wide() {
+  const int smem = 2 * kWideBuf;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_bf16_wide_kernel<true>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, smem);
+  if (e == hipSuccess)
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_bf16_wide_kernel<false>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, smem);
+  return e;
+}
+
 hipError_t launch_gemm_bf16_wide(const GroupedGemm& g, bool swiglu, long long max_items, int max_blocks,
                                  hipStream_t st) {
   if (max_items <= 0) return hipSuccess;

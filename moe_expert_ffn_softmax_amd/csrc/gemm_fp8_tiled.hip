@@ -387,14 +387,7 @@ __global__ void __launch_bounds__(kF8Threads, kF8MinBlocks) gemm_fp8_tiled_kerne
 
 template <bool SWIGLU>
 static hipError_t launch_fp8_tiled(const GroupedGemm& g, long long max_items, int max_blocks, hipStream_t st) {
-  const size_t smem = 2 * kF8Buf;
-  static bool configured = false;
-  if (!configured) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_fp8_tiled_kernel<SWIGLU>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-    if (e != hipSuccess) return e;
-    configured = true;
-  }
+  const size_t smem = 2 * kF8Buf;  // above the default limit: see configure_gemm_fp8_tiled
   // max_blocks counts compute units; the kernel is built for kF8MinBlocks workgroups
   // on each
   const long long resident = (long long)max_blocks * kF8MinBlocks;
@@ -406,6 +399,17 @@ static hipError_t launch_fp8_tiled(const GroupedGemm& g, long long max_items, in
 
 // Reduction lengths are multiples of 128 and group counts multiples of 4 (the layer's
 // dimensions are multiples of 128); output rows are 16-byte aligned (ldo % 4 == 0).
+// Raise the kernels' dynamic LDS limit on the current device (handle creation).
+hipError_t configure_gemm_fp8_tiled() {
+  const int smem = 2 * kF8Buf;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_fp8_tiled_kernel<true>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, smem);
+  if (e == hipSuccess)
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_fp8_tiled_kernel<false>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, smem);
+  return e;
+}
+
 hipError_t launch_gemm_fp8_tiled(const GroupedGemm& g, bool swiglu, long long max_items, int max_blocks,
                                  hipStream_t st) {
   if (max_items <= 0) return hipSuccess;
