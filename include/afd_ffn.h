@@ -125,14 +125,14 @@ int afd_ffn_route(afd_ffn_t h, const float* logits, int32_t T, const afd_route* 
  * and bf16 otherwise; bias [E] is fp32, or NULL for none.  The bias takes part in the
  * selection and in the gates, which are the softmax of the selected biased logits, as
  * in that router.  logits [T, E] fp32 (caller-owned device memory, not overlapping
- * the inputs) receives the biased logits and is then routed exactly as
+ * the inputs; checked: AFD_EINVAL) receives the biased logits and is then routed exactly as
  * afd_ffn_route(h, logits, T, r, stream) would route it.  0 <= T <= max_tokens. */
 int afd_ffn_route_hidden(afd_ffn_t h, const void* x, const void* w_router, const float* bias, float* logits,
                          int32_t T, const afd_route* r, void* stream);
 
 /* Expert FFN of T routed tokens: x [T, H] (fp32 for AFD_F32, else bf16) and the
  * result of afd_ffn_route for the same T -> y [T, H] (fp32 for AFD_F32, else bf16).
- * x and y must not overlap. */
+ * x and y must not overlap (checked: AFD_EINVAL). */
 int afd_ffn_forward(afd_ffn_t h, const void* x, int32_t T, const afd_route* r, void* y, void* stream);
 
 /* Release the handle's weights and workspace.  The caller must have synchronised

@@ -2,6 +2,7 @@
 // launch sequence of route (router -> permute) and forward (gate/up GEMM + SwiGLU
 // -> down GEMM -> combine), all asynchronous on the caller's stream.
 #include <stdarg.h>
+#include <stdint.h>
 #include <stdio.h>
 #include <string.h>
 
@@ -48,6 +49,12 @@ int check_route(const afd_ffn* h, const afd_route* r, int32_t T) {
   if (!r->topk_ids || !r->topk_gates || !r->expert_counts || !r->expert_offsets || !r->sorted_pair || !r->pair_pos)
     return fail(AFD_EINVAL, "a route buffer is NULL");
   return AFD_OK;
+}
+
+// Do the byte ranges [a, a + na) and [b, b + nb) intersect?
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return na && nb && x < y + nb && y < x + na;
 }
 
 void release(afd_ffn* h) {
@@ -384,6 +391,14 @@ extern "C" int afd_ffn_route_hidden(afd_ffn_t h, const void* x, const void* w_ro
   if (rc) return rc;
   if (!x || !w_router || !logits) return fail(AFD_EINVAL, "x, w_router or logits is NULL");
   if (T == 0) return AFD_OK;
+  {
+    const afd_ffn_config& c = h->cfg;
+    const size_t a = c.dtype == AFD_F32 ? 4 : 2;
+    const size_t lb = (size_t)T * c.num_experts * 4;
+    if (overlaps(logits, lb, x, (size_t)T * c.hidden * a) ||
+        overlaps(logits, lb, w_router, (size_t)c.num_experts * c.hidden * a))
+      return fail(AFD_EINVAL, "logits overlaps x or w_router");
+  }
   hipStream_t st = static_cast<hipStream_t>(stream);
   const afd_ffn_config& c = h->cfg;
   {
@@ -401,6 +416,10 @@ extern "C" int afd_ffn_forward(afd_ffn_t h, const void* x, int32_t T, const afd_
   if (rc) return rc;
   if (!x || !y) return fail(AFD_EINVAL, "x or y is NULL");
   if (T == 0) return AFD_OK;
+  {
+    const size_t rowb = (size_t)h->cfg.hidden * (h->cfg.dtype == AFD_F32 ? 4 : 2);
+    if (overlaps(x, (size_t)T * rowb, y, (size_t)T * rowb)) return fail(AFD_EINVAL, "x and y overlap");
+  }
   hipStream_t st = static_cast<hipStream_t>(stream);
   const afd_ffn_config& c = h->cfg;
   const int H = c.hidden, M = c.inter, Ms = c.shared_inter, E = c.num_experts, k = c.top_k;

@@ -379,6 +379,28 @@ def test_two_micro_batches_on_two_streams(w):
     layer.close()
 
 
+def test_overlapping_buffers_are_rejected():
+    """forward's x and y, and route_hidden's logits and inputs, must not overlap: the
+    host checks return AFD_EINVAL and enqueue nothing."""
+    from moe_expert_ffn_softmax_amd._ffi import AFD_EINVAL, AfdError
+    w = small("overlap", T=8, H=128, M=128, E=4, k=2)
+    weights = workloads.make_weights(w, device="cuda")
+    x, logits = workloads.make_activations(w, device="cuda")
+    layer = make_layer(w, weights)
+    rb = layer.new_route()
+    layer.route(logits, w.T, rb)
+    with pytest.raises(AfdError) as e:
+        layer.forward(x, w.T, rb, x[1:])
+    assert e.value.code == AFD_EINVAL
+    wr = torch.zeros((w.E, w.H), dtype=torch.bfloat16, device="cuda")
+    buf = torch.zeros(w.T * w.H, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(AfdError) as e:
+        layer.route_hidden(buf.view(w.T, w.H), wr, buf.view(torch.float32), w.T, rb)
+    assert e.value.code == AFD_EINVAL
+    torch.cuda.synchronize()
+    layer.close()
+
+
 def test_zero_tokens_is_a_no_op():
     w = small("empty", T=8)
     weights = workloads.make_weights(w, device="cuda")
