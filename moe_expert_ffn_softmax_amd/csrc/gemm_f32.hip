@@ -11,6 +11,7 @@ namespace afd {
 
 constexpr int kF32Threads = 256;
 constexpr int kF32Waves = kF32Threads / kWave;
+constexpr int kF32Ahead = 8;  // reduction steps in flight
 
 template <bool SWIGLU>
 __global__ void __launch_bounds__(kF32Threads) gemm_f32_kernel(GroupedGemm g) {
@@ -46,15 +47,28 @@ __global__ void __launch_bounds__(kF32Threads) gemm_f32_kernel(GroupedGemm g) {
                                : static_cast<const float*>(g.w_routed) + (size_t)it.seg * g.w_expert_elems;
     const int col0 = SWIGLU ? it.group * 16 + c : it.group * 32 + c;
     const int col1 = SWIGLU ? N / 2 + it.group * 16 + c : it.group * 32 + 16 + c;
+    // loads run kF32Ahead reduction steps ahead in a rotating register ring (K is a
+    // multiple of 128); the FMAs keep ascending k order
     float acc0[4] = {0.f, 0.f, 0.f, 0.f}, acc1[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int kk = 0; kk < K; ++kk) {
-      const float w0 = W[(size_t)kk * N + col0];
-      const float w1 = W[(size_t)kk * N + col1];
+    float w0r[kF32Ahead], w1r[kF32Ahead], ar[kF32Ahead][4];
+    auto load = [&](int kk, int u) {
+      w0r[u] = W[(size_t)kk * N + col0];
+      w1r[u] = W[(size_t)kk * N + col1];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float a = arow[i][kk];
-        acc0[i] = fmaf(a, w0, acc0[i]);
-        acc1[i] = fmaf(a, w1, acc1[i]);
+      for (int i = 0; i < 4; ++i) ar[u][i] = arow[i][kk];
+    };
+#pragma unroll
+    for (int u = 0; u < kF32Ahead; ++u) load(u, u);
+    for (int k0 = 0; k0 < K; k0 += kF32Ahead) {
+#pragma unroll
+      for (int u = 0; u < kF32Ahead; ++u) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc0[i] = fmaf(ar[u][i], w0r[u], acc0[i]);
+          acc1[i] = fmaf(ar[u][i], w1r[u], acc1[i]);
+        }
+        const int kn = k0 + kF32Ahead + u;
+        load(kn < K ? kn : K - 1, u);  // past the end: reload the last step, unused
       }
     }
     float* out = static_cast<float*>(it.shared ? g.out_shared : g.out_routed);
