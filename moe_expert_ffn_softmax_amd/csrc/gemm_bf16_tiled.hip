@@ -40,6 +40,11 @@
 // list is cut into 8 contiguous ranges, one per XCD (workgroup b runs on XCD b % 8):
 // the row tiles of a hot expert and the neighbouring column tiles run at the same
 // time on one XCD and share its L2 for the weights and the activation rows.
+//
+// A workgroup's items run as one stream: during an item's last chunks the activation
+// staging and the weight ring already load the next item's first chunks and steps,
+// so the next item starts without waiting for its first loads (measured: the start-up
+// latency of an item was 5-9% of the launch at 128 to 1024 rows per expert).
 #include "grouped.h"
 
 namespace afd {
@@ -87,6 +92,72 @@ struct IntC {
 #endif
 constexpr int kTiledMinBlocks = AFD_TILED_MIN_BLOCKS;  // workgroups per CU the registers must allow
 
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Addressing of one work item for one wave: the rows it stages and the weight streams
+// of its groups.  Item-level values are wave-uniform (scalar registers); per lane
+// there are only 32-bit offsets.
+struct TiledCtx {
+  int seg, shared, row0, nrows;
+  int KB, NC;      // 32-deep steps and 128-deep chunks of the reduction
+  int active;      // the wave's groups exist (else it recomputes the last ones, stores nothing)
+  int group0;      // first group of the wave
+  const bf16x8* abase;                    // the A matrix
+  uint32_t aoff[kTiledLoads];             // this lane's piece of each staged row (bf16x8 units)
+  const bf16x8* wbase;                    // the expert's packed weights
+  uint32_t boff[kTiledGroupsPerWave];     // this lane's weight stream of each block (bf16x8 units)
+};
+
+template <bool SWIGLU>
+__device__ __forceinline__ void tiled_ctx(const GroupedGemm& g, const int* prefix, int item, int w, int lane,
+                                          TiledCtx& x) {
+  const Item it = decode_item_tiled(g, kTiledRows, kTiledGroups, prefix, item);
+  x.seg = uni(it.seg);
+  x.shared = uni(it.shared ? 1 : 0);
+  x.row0 = uni(it.row0);
+  x.nrows = uni(it.nrows);
+  const int K = x.shared ? g.K_shared : g.K_routed;
+  x.KB = K / 32;
+  x.NC = x.KB / kTiledKC;
+  const int groups = x.shared ? g.groups_shared : g.groups_routed;
+  const int group = uni(it.group);
+  // A wave past the last group of a partial column tile recomputes the tile's last
+  // groups and stores nothing: the main loop stays free of branches around the MFMAs
+  // (such a branch made the compiler copy every accumulator through VGPRs).  Group
+  // counts are multiples of 4, so a wave's groups are all valid or all past the end.
+  x.active = group + w * kTiledGroupsPerWave < groups;
+  x.group0 = x.active ? group + w * kTiledGroupsPerWave : groups - kTiledGroupsPerWave;
+  // Rows this wave stages: w * 32 + i * 4 + lane / 16 (i = 0..7), clamped into the
+  // tile; the lane carries the 16-byte piece lane % 16 of each row's 256-byte chunk.
+  const int lda = x.shared ? g.lda_shared : g.lda_routed;
+  x.abase = static_cast<const bf16x8*>(x.shared ? g.a_shared : g.a_routed);
+#pragma unroll
+  for (int i = 0; i < kTiledLoads; ++i) {
+    int r = w * 32 + i * 4 + (lane >> 4);
+    r = r < x.nrows ? r : 0;
+    int ar;
+    if (x.shared)
+      ar = x.row0 + r;
+    else
+      ar = g.gather_routed ? g.sorted_pair[x.row0 + r] / g.k : x.row0 + r;
+    x.aoff[i] = (uint32_t)ar * (uint32_t)(lda / 8) + (uint32_t)(lane & 15);
+  }
+  // weights: 16-byte chunk of (step s, half kh) of block cb at boff[cb] + s*128 + kh*32
+  x.wbase = x.shared ? static_cast<const bf16x8*>(g.w_shared)
+                     : static_cast<const bf16x8*>(g.w_routed) + (size_t)x.seg * (g.w_expert_elems / 8);
+#pragma unroll
+  for (int cb = 0; cb < kTiledGroupsPerWave; ++cb) {
+    const int grp = SWIGLU ? x.group0 + (cb >> 1) * 2 + ((lane & 31) >> 4) : x.group0 + cb;
+    const int half = SWIGLU ? (cb & 1) : ((lane & 31) >> 4);
+    x.boff[cb] = (uint32_t)grp * (uint32_t)(x.KB * 128) + half * 64 + (lane >> 5) * 16 + (lane & 15);
+  }
+}
+
+// The work items of a workgroup run as one stream: during an item's last chunks the
+// staging loads and the weight ring already fetch the next item's first chunk and
+// steps (when both items have at least two chunks), so the next item starts without
+// the latency of its first loads.  The next item's addresses (which need its rows'
+// sorted_pair entries) are computed at the start of the current one.
 template <bool SWIGLU>
 __global__ void __launch_bounds__(kTiledThreads, kTiledMinBlocks) gemm_bf16_tiled_kernel(GroupedGemm g) {
   __shared__ int prefix[kMaxSegments + 1];
@@ -102,95 +173,69 @@ __global__ void __launch_bounds__(kTiledThreads, kTiledMinBlocks) gemm_bf16_tile
   const int slots = gridDim.x / kXcds;
   const int begin = (int)((long long)total * xcd / kXcds);
   const int end = (int)((long long)total * (xcd + 1) / kXcds);
+  int item = begin + slot;
+  if (item >= end) return;  // uniform over the workgroup
 
-  for (int item = begin + slot; item < end; item += slots) {
-    // lane-derived indices are recomputed per item (hoisted out of the item loop
-    // they do not fit the register budget)
-    int lane = lane_id();
-    asm volatile("" : "+v"(lane));
-    const Item it = decode_item_tiled(g, kTiledRows, kTiledGroups, prefix, item);
-    const int K = it.shared ? g.K_shared : g.K_routed;
-    const int KB = K / 32;
-    const int NC = KB / kTiledKC;
-    const int groups = it.shared ? g.groups_shared : g.groups_routed;
-    // First group of this wave.  A wave past the last group of a partial column tile
-    // recomputes the tile's last groups and stores nothing: the main loop stays free
-    // of branches around the MFMAs (such a branch made the compiler copy every
-    // accumulator through VGPRs).  Group counts are multiples of 4, so a wave's groups
-    // are all valid or all past the end.
-    const bool active = it.group + w * kTiledGroupsPerWave < groups;  // wave-uniform
-    const int group0 = active ? it.group + w * kTiledGroupsPerWave : groups - kTiledGroupsPerWave;
+  const int lane = lane_id();
+  const int piece = lane & 15;
+  // LDS byte offsets: where this lane's staged piece goes (row block w, fragment
+  // piece / 2, reduction half piece % 2; + i * 64 for load i), and where it reads
+  // its A operand (fragment slot base + lane position)
+  const int wr_off = (w * kTiledFrags + (piece >> 1)) * kTiledSlot + (lane >> 4) * 16 + (piece & 1) * kTiledHalfOff;
+  const int rd_off = (lane & 31) * 16 + (lane >> 5) * kTiledHalfOff;
 
-    // Rows this wave stages: w * 32 + i * 4 + lane / 16 (i = 0..7), clamped into the
-    // tile; the lane carries the 16-byte piece lane % 16 of each row's 256-byte chunk.
-    const int lda = it.shared ? g.lda_shared : g.lda_routed;
-    const __bf16* abase = static_cast<const __bf16*>(it.shared ? g.a_shared : g.a_routed);
-    const int piece = lane & 15;
-    const bf16x8* arow[kTiledLoads];
+  TiledCtx cur;
+  tiled_ctx<SWIGLU>(g, prefix, item, w, lane, cur);
+
+  f32x16v acc[kTiledRowBlocks][kTiledGroupsPerWave];
 #pragma unroll
-    for (int i = 0; i < kTiledLoads; ++i) {
-      int r = w * 32 + i * 4 + (lane >> 4);
-      r = r < it.nrows ? r : 0;
-      int ar;
-      if (it.shared)
-        ar = it.row0 + r;
-      else
-        ar = g.gather_routed ? g.sorted_pair[it.row0 + r] / g.k : it.row0 + r;
-      arow[i] = reinterpret_cast<const bf16x8*>(abase + (size_t)ar * lda) + piece;
+  for (int rb = 0; rb < kTiledRowBlocks; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < kTiledGroupsPerWave; ++cb) acc[rb][cb] = f32x16v{};
+  // weight ring: step s lives in slot s % kTiledBAhead ([cb][kh])
+  bf16x8 bring[kTiledBAhead][kTiledGroupsPerWave][2];
+  bf16x8 stage[kTiledLoads];  // the staged chunk after the one in LDS
+  int base = 0;               // LDS buffer of the current item's chunk 0
+  bool primed = false;        // ring, LDS chunk 0 and stage already hold this item's data
+
+  for (;;) {
+    const int item_n = item + slots;
+    const bool has_next = item_n < end;
+    TiledCtx nxt;
+    if (has_next)
+      tiled_ctx<SWIGLU>(g, prefix, item_n, w, lane, nxt);
+    else
+      nxt = cur;
+    // chaining needs two chunks on both sides (the staging runs two chunks ahead) and
+    // ring slots that line up across the item boundary
+    const bool chain = has_next && cur.NC >= 2 && nxt.NC >= 2 && cur.KB % kTiledBAhead == 0;
+
+    if (!primed) {
+#pragma unroll
+      for (int u = 0; u < kTiledBAhead; ++u)
+#pragma unroll
+        for (int cb = 0; cb < kTiledGroupsPerWave; ++cb)
+#pragma unroll
+          for (int kh = 0; kh < 2; ++kh) bring[u][cb][kh] = tiled_load_b(cur.wbase + cur.boff[cb] + u * 128 + kh * 32);
+      // chunk 0 -> LDS buffer `base`, chunk 1 (or chunk 0 again) -> staging registers;
+      // a chunk is 16 pieces of 16 bytes per row
+#pragma unroll
+      for (int i = 0; i < kTiledLoads; ++i) stage[i] = cur.abase[cur.aoff[i]];
+#pragma unroll
+      for (int i = 0; i < kTiledLoads; ++i)
+        *reinterpret_cast<bf16x8*>(lds + base * kTiledBuf + wr_off + i * 64) = stage[i];
+      const int cn = cur.NC > 1 ? 1 : 0;
+#pragma unroll
+      for (int i = 0; i < kTiledLoads; ++i) stage[i] = cur.abase[cur.aoff[i] + cn * 16];
+      __syncthreads();
     }
-    // LDS byte offsets: where this lane's staged piece goes (row block w, fragment
-    // piece / 2, reduction half piece % 2; + i * 64 for load i), and where it reads
-    // its A operand (fragment slot base + lane position)
-    const int wr_off = (w * kTiledFrags + (piece >> 1)) * kTiledSlot + (lane >> 4) * 16 + (piece & 1) * kTiledHalfOff;
-    const int rd_off = (lane & 31) * 16 + (lane >> 5) * kTiledHalfOff;
 
-    // weights: 16-byte chunk of (step s, half kh) for block cb at bbase[cb] + s*128 + kh*32
-    const __bf16* wbase = it.shared ? static_cast<const __bf16*>(g.w_shared)
-                                    : static_cast<const __bf16*>(g.w_routed) + (size_t)it.seg * g.w_expert_elems;
-    const bf16x8* bbase[kTiledGroupsPerWave];
-#pragma unroll
-    for (int cb = 0; cb < kTiledGroupsPerWave; ++cb) {
-      const int grp = SWIGLU ? group0 + (cb >> 1) * 2 + ((lane & 31) >> 4) : group0 + cb;
-      const int half = SWIGLU ? (cb & 1) : ((lane & 31) >> 4);
-      bbase[cb] = reinterpret_cast<const bf16x8*>(wbase) + (size_t)grp * KB * 128 + half * 64 + (lane >> 5) * 16 +
-                  (lane & 15);
-    }
-
-    f32x16v acc[kTiledRowBlocks][kTiledGroupsPerWave];
-#pragma unroll
-    for (int rb = 0; rb < kTiledRowBlocks; ++rb)
-#pragma unroll
-      for (int cb = 0; cb < kTiledGroupsPerWave; ++cb) acc[rb][cb] = f32x16v{};
-
-    // weight ring: step s lives in slot s % kTiledBAhead ([cb][kh])
-    bf16x8 bring[kTiledBAhead][kTiledGroupsPerWave][2];
-#pragma unroll
-    for (int u = 0; u < kTiledBAhead; ++u)
-#pragma unroll
-      for (int cb = 0; cb < kTiledGroupsPerWave; ++cb)
-#pragma unroll
-        for (int kh = 0; kh < 2; ++kh) bring[u][cb][kh] = tiled_load_b(bbase[cb] + u * 128 + kh * 32);
-
-    // The main loop is instantiated for RB = 1..4 row blocks holding rows, so a tile
-    // with few rows does only the MFMAs, LDS reads and activation staging its rows
-    // need (waves w >= RB stage nothing; every wave still takes the barriers).  RB is
-    // uniform over the workgroup.
+    // The chunk loop runs inside a generic lambda over the row-block count (always
+    // all four here): written inline, the compiler schedules it worse (measured 6%
+    // slower at 1024 rows per expert).
     auto main_loop = [&](auto rbc) {
       constexpr int RB = decltype(rbc)::value;
-      // A chunk 0 -> LDS buffer 0, chunk 1 (or chunk 0 again) -> staging registers;
-      // a chunk is 16 pieces of 16 bytes per row
-      bf16x8 stage[kTiledLoads];
-      if (w < RB) {
-#pragma unroll
-        for (int i = 0; i < kTiledLoads; ++i) stage[i] = arow[i][0];
-#pragma unroll
-        for (int i = 0; i < kTiledLoads; ++i) *reinterpret_cast<bf16x8*>(lds + wr_off + i * 64) = stage[i];
-        const int cn = NC > 1 ? 1 : 0;
-#pragma unroll
-        for (int i = 0; i < kTiledLoads; ++i) stage[i] = arow[i][cn * 16];
-      }
-      __syncthreads();
-
+      const int NC = cur.NC, KB = cur.KB;
       // The reduction runs as 16-deep half-steps (u, kh).  The A fragments of the next
       // half-step are read from LDS while the current half-step's MFMAs run; in the
       // chunk's last half-step the next chunk (already in registers) is written to the
@@ -199,37 +244,39 @@ __global__ void __launch_bounds__(kTiledThreads, kTiledMinBlocks) gemm_bf16_tile
       bf16x8 a[2][kTiledRowBlocks];
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb)
-        a[0][rb] = *reinterpret_cast<const bf16x8*>(lds + rb * kTiledFrags * kTiledSlot + rd_off);
+        a[0][rb] = *reinterpret_cast<const bf16x8*>(lds + base * kTiledBuf + rb * kTiledFrags * kTiledSlot + rd_off);
 
       for (int c = 0; c < NC; ++c) {
-        const int buf = (c & 1) * kTiledBuf;
+        const int buf = ((base + c) & 1) * kTiledBuf;
         const int nbuf = kTiledBuf - buf;
 #pragma unroll
         for (int hs = 0; hs < kTiledFrags; ++hs) {
           const int u = hs >> 1, kh = hs & 1;
-          const int cur = hs & 1, nxt = cur ^ 1;
+          const int cur_a = hs & 1, nxt_a = cur_a ^ 1;
           if (hs + 1 < kTiledFrags) {
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
-              a[nxt][rb] =
+              a[nxt_a][rb] =
                   *reinterpret_cast<const bf16x8*>(lds + buf + (rb * kTiledFrags + hs + 1) * kTiledSlot + rd_off);
           } else {
-            // branch-free chunk boundary: past the last chunk these write, load and read
-            // data nobody uses (the loads are clamped to the last chunk)
-            if (w < RB) {
+            // chunk boundary: the staged chunk goes to the other buffer, then the chunk
+            // two ahead is staged: this item's, the next item's first ones when
+            // chaining, else a clamped load nobody uses
 #pragma unroll
-              for (int i = 0; i < kTiledLoads; ++i)
-                *reinterpret_cast<bf16x8*>(lds + nbuf + wr_off + i * 64) = stage[i];
-            }
+            for (int i = 0; i < kTiledLoads; ++i)
+              *reinterpret_cast<bf16x8*>(lds + nbuf + wr_off + i * 64) = stage[i];
             __syncthreads();
-            if (w < RB) {
-              const int cn = c + 2 < NC ? c + 2 : NC - 1;
+            const int c2 = c + 2;
+            const bool own = c2 < NC;
+            const bool take_next = !own && chain;  // uniform
+            const int cc = own ? c2 : take_next ? c2 - NC : NC - 1;
+            const bf16x8* ab = take_next ? nxt.abase : cur.abase;
 #pragma unroll
-              for (int i = 0; i < kTiledLoads; ++i) stage[i] = arow[i][cn * 16];
-            }
+            for (int i = 0; i < kTiledLoads; ++i)
+              stage[i] = ab[(take_next ? nxt.aoff[i] : cur.aoff[i]) + cc * 16];
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
-              a[nxt][rb] = *reinterpret_cast<const bf16x8*>(lds + nbuf + rb * kTiledFrags * kTiledSlot + rd_off);
+              a[nxt_a][rb] = *reinterpret_cast<const bf16x8*>(lds + nbuf + rb * kTiledFrags * kTiledSlot + rd_off);
           }
           const int slotb = u % kTiledBAhead;
 #pragma unroll
@@ -237,15 +284,21 @@ __global__ void __launch_bounds__(kTiledThreads, kTiledMinBlocks) gemm_bf16_tile
 #pragma unroll
             for (int cb = 0; cb < kTiledGroupsPerWave; ++cb)
               acc[rb][cb] =
-                  __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cur][rb], bring[slotb][cb][kh], acc[rb][cb], 0, 0, 0);
+                  __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[cur_a][rb], bring[slotb][cb][kh], acc[rb][cb], 0, 0, 0);
           if (kh == 1) {
-            // refill this ring slot with the step kTiledBAhead ahead (clamped to the last)
-            int s = c * kTiledKC + u + kTiledBAhead;
-            s = s < KB ? s : KB - 1;
+            // refill this ring slot with the step kTiledBAhead ahead: this item's, the
+            // next item's first steps when chaining, else the last step again
+            const int s = c * kTiledKC + u + kTiledBAhead;
+            const bool own = s < KB;
+            const bool take_next = !own && chain;  // uniform
+            const int ss = own ? s : take_next ? s - KB : KB - 1;
+            const bf16x8* wb = take_next ? nxt.wbase : cur.wbase;
 #pragma unroll
-            for (int cb = 0; cb < kTiledGroupsPerWave; ++cb)
+            for (int cb = 0; cb < kTiledGroupsPerWave; ++cb) {
+              const bf16x8* bp = wb + (take_next ? nxt.boff[cb] : cur.boff[cb]) + ss * 128;
 #pragma unroll
-              for (int k2 = 0; k2 < 2; ++k2) bring[slotb][cb][k2] = tiled_load_b(bbase[cb] + s * 128 + k2 * 32);
+              for (int k2 = 0; k2 < 2; ++k2) bring[slotb][cb][k2] = tiled_load_b(bp + k2 * 32);
+            }
           }
 #if AFD_TILED_SCHED
           // keep the next half-step's LDS reads spread between this half-step's MFMAs
@@ -259,56 +312,52 @@ __global__ void __launch_bounds__(kTiledThreads, kTiledMinBlocks) gemm_bf16_tile
         }
       }
     };
-    // Only an expert's single row tile is shortened: the row tiles of a larger
-    // expert stream the same weights at the same time through one XCD's L2, and a
-    // shortened last tile running ahead of its siblings measured slower.
-    const int seg_rows = it.shared ? g.shared_rows : g.counts[it.seg];
-    const int nrb = seg_rows > kTiledRows ? kTiledRowBlocks : (it.nrows + 31) / 32;
-    if (nrb >= 4)
-      main_loop(IntC<4>{});
-    else if (nrb == 3)
-      main_loop(IntC<3>{});
-    else if (nrb == 2)
-      main_loop(IntC<2>{});
-    else
-      main_loop(IntC<1>{});
+    main_loop(IntC<4>{});
 
-    if (active) {
+    if (cur.active) {
       const int col = lane & 31;
       const int rsub = (lane >> 5) * 4;
+      __bf16* out = static_cast<__bf16*>(cur.shared ? g.out_shared : g.out_routed);
+      const int ldo = cur.shared ? g.ldo_shared : g.ldo_routed;
       if (SWIGLU) {
-        __bf16* out = static_cast<__bf16*>(it.shared ? g.out_shared : g.out_routed);
-        const int ldo = it.shared ? g.ldo_shared : g.ldo_routed;
 #pragma unroll
         for (int rb = 0; rb < kTiledRowBlocks; ++rb)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int row = rb * 32 + (i / 4) * 8 + rsub + (i % 4);
-            if (row < it.nrows) {
-              __bf16* o = out + (size_t)(it.row0 + row) * ldo + group0 * 16 + col;
+            if (row < cur.nrows) {
+              __bf16* o = out + (size_t)(cur.row0 + row) * ldo + cur.group0 * 16 + col;
 #pragma unroll
               for (int p = 0; p < kTiledGroupsPerWave / 2; ++p)
                 o[p * 32] = f32_to_bf16(silu(acc[rb][2 * p][i]) * acc[rb][2 * p + 1][i]);
             }
           }
       } else {
-        __bf16* out = static_cast<__bf16*>(it.shared ? g.out_shared : g.out_routed);
-        const int ldo = it.shared ? g.ldo_shared : g.ldo_routed;
 #pragma unroll
         for (int rb = 0; rb < kTiledRowBlocks; ++rb)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int row = rb * 32 + (i / 4) * 8 + rsub + (i % 4);
-            if (row < it.nrows) {
-              __bf16* o = out + (size_t)(it.row0 + row) * ldo + group0 * 32 + col;
+            if (row < cur.nrows) {
+              __bf16* o = out + (size_t)(cur.row0 + row) * ldo + cur.group0 * 32 + col;
 #pragma unroll
               for (int cb = 0; cb < kTiledGroupsPerWave; ++cb) o[cb * 32] = f32_to_bf16(acc[rb][cb][i]);
             }
           }
       }
     }
-    // every LDS read of this item was issued before the barrier of its last half-step,
-    // so the next item's first LDS writes need no further barrier
+    if (!has_next) break;
+#pragma unroll
+    for (int rb = 0; rb < kTiledRowBlocks; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < kTiledGroupsPerWave; ++cb) acc[rb][cb] = f32x16v{};
+    // the last chunk boundary wrote the next item's chunk 0 (or, unchained, a chunk
+    // nobody reads) to buffer (base + NC) % 2 and took a barrier after every read of
+    // this item's data
+    base = (base + cur.NC) & 1;
+    primed = chain;
+    cur = nxt;
+    item = item_n;
   }
 }
 
