@@ -9,6 +9,10 @@ marshals numpy arrays into it.
 Function-by-function pins (tests/test_oracle.py):
   route      -- numpy stable argsort; rank-count brute force; closed-form gates;
                 the top-k-then-softmax form of the router on the MoE engineering page.
+  route_select_bias -- closed-form gates of hand-made cases; a key tie that exists only
+                after fp32 rounding of score + bias; zero bias reproduces route; a
+                dominant bias forces the chosen set while the gates stay those of
+                the unbiased scores.
   router_scores -- a hand-computed integer example; one-hot gate vectors pick x's
                 columns; exact integer sums against brute force; bias shift invariance
                 of the routing and a dominant bias forcing an expert.
@@ -66,6 +70,8 @@ def _load():
         P = ctypes.c_void_p
         lib.afdo_route.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, P]
         lib.afdo_route.restype = None
+        lib.afdo_route_select_bias.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, P, P]
+        lib.afdo_route_select_bias.restype = None
         lib.afdo_router_scores.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, P, P]
         lib.afdo_router_scores.restype = None
         lib.afdo_permute.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, P, P, P]
@@ -100,6 +106,20 @@ def route(logits: np.ndarray, k: int):
     ids = np.zeros((T, k), np.int32)
     gates = np.zeros((T, k), np.float64)
     _load().afdo_route(T, E, k, _p(logits), _p(ids), _p(gates))
+    return ids, gates
+
+
+def route_select_bias(scores: np.ndarray, bias: np.ndarray, k: int):
+    """ids [T,k] int32 and gates [T,k] float64: experts chosen on fp32(scores + bias),
+    gates from the unbiased fp32 scores [T,E] (the selection-only bias router)."""
+    scores = np.ascontiguousarray(scores, dtype=np.float32)
+    T, E = scores.shape
+    bias = np.ascontiguousarray(bias, dtype=np.float32)
+    if bias.shape != (E,):
+        raise ValueError("bias must have shape [E]")
+    ids = np.zeros((T, k), np.int32)
+    gates = np.zeros((T, k), np.float64)
+    _load().afdo_route_select_bias(T, E, k, _p(scores), _p(bias), _p(ids), _p(gates))
     return ids, gates
 
 

@@ -191,6 +191,39 @@ void afdo_route(int T, int E, int k, const float* logits, int32_t* ids, double* 
   }
 }
 
+/* Router with a selection-only bias.  [MoE-eng] §4.1 steers expert load with a
+ * per-expert dynamic bias and names DeepSeek-V3's dynamic bias adjustment; in the
+ * variant built here the bias only decides which experts are chosen, while the gate
+ * weights come from the unbiased scores.  Per token: key[e] = scores[e] + bias[e]
+ * rounded to fp32 (the precision the selection is decided in); the k experts ranked
+ * by (key descending, expert index ascending); gates = the softmax probabilities of
+ * the unbiased scores (double) of the chosen experts, renormalised to sum to 1. */
+void afdo_route_select_bias(int T, int E, int k, const float* scores, const float* bias, int32_t* ids,
+                            double* gates) {
+  float* key = (float*)malloc(sizeof(float) * (size_t)(E > 0 ? E : 1));
+  for (int t = 0; t < T; ++t) {
+    const float* s = scores + (size_t)t * E;
+    double m = -INFINITY, z = 0.0, sel = 0.0;
+    for (int e = 0; e < E; ++e) {
+      volatile float v = s[e] + bias[e];
+      key[e] = v;
+    }
+    for (int e = 0; e < E; ++e)
+      if ((double)s[e] > m) m = (double)s[e];
+    for (int e = 0; e < E; ++e) z += exp((double)s[e] - m);
+    for (int e = 0; e < E; ++e) {
+      int rank = 0;
+      for (int i = 0; i < E; ++i)
+        if (key[i] > key[e] || (key[i] == key[e] && i < e)) ++rank;
+      if (rank < k) ids[(size_t)t * k + rank] = e;
+    }
+    for (int j = 0; j < k; ++j) sel += exp((double)s[ids[(size_t)t * k + j]] - m) / z;
+    for (int j = 0; j < k; ++j)
+      gates[(size_t)t * k + j] = (exp((double)s[ids[(size_t)t * k + j]] - m) / z) / sel;
+  }
+  free(key);
+}
+
 /* Counting sort of pair ids p = t*k + j by expert: counts, exclusive prefix sum
  * (offsets[E] = T*k), then each pair placed at its expert's cursor in ascending p.
  * pair_pos is the inverse permutation of sorted_pair. */

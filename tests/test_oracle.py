@@ -144,6 +144,71 @@ def test_router_bias_shift_invariance_and_dominant_bias():
     np.testing.assert_allclose(g2[:, 0], 1.0, rtol=0, atol=1e-12)
 
 
+def test_route_select_bias_closed_form_cases():
+    """Selection on score + bias, gates from the unbiased scores, against values worked
+    out by hand: the bias of expert 0 lifts it into the chosen pair, but its gate is
+    that of its own score 0 against expert 3's score 3."""
+    s = np.array([[0.0, 1.0, 2.0, 3.0]], np.float32)
+    b = np.array([5.0, 0.0, 0.0, 0.0], np.float32)
+    ids, g = oracle.route_select_bias(s, b, 2)
+    np.testing.assert_array_equal(ids, [[0, 3]])
+    e3 = math.exp(3.0)
+    np.testing.assert_allclose(g, [[1.0 / (1.0 + e3), e3 / (1.0 + e3)]], rtol=0, atol=1e-15)
+    # the same choice with the bias inside the gates gives other weights: softmax(5, 3)
+    ids_in, g_in = oracle.route((s + b).astype(np.float32), 2)
+    np.testing.assert_array_equal(ids_in, ids)
+    e2 = math.exp(2.0)
+    np.testing.assert_allclose(g_in, [[e2 / (1.0 + e2), 1.0 / (1.0 + e2)]], rtol=0, atol=1e-15)
+    # equal keys (1.0 + 0.0 and 0.5 + 0.5): the lower expert takes slot 0; gates from 1.0 and 0.5
+    ids, g = oracle.route_select_bias(np.array([[1.0, 0.5]], np.float32), np.array([0.0, 0.5], np.float32), 2)
+    np.testing.assert_array_equal(ids, [[0, 1]])
+    q = math.exp(0.5)
+    np.testing.assert_allclose(g, [[q / (q + 1.0), 1.0 / (q + 1.0)]], rtol=0, atol=1e-15)
+    # k = 1: the gate is exactly 1 whatever the scores
+    ids, g = oracle.route_select_bias(s, b, 1)
+    assert ids[0, 0] == 0 and g[0, 0] == 1.0
+
+
+def test_route_select_bias_key_is_decided_in_fp32():
+    """1 + 2^-25 is 1 in fp32: the two keys tie after rounding and the lower expert
+    wins, although the exact sums would put expert 1 first."""
+    s = np.array([[1.0, 1.0, -1.0]], np.float32)
+    b = np.array([0.0, 2.0 ** -25, 0.0], np.float32)
+    assert np.float32(s[0, 1]) + np.float32(b[1]) == np.float32(1.0)
+    ids, _ = oracle.route_select_bias(s, b, 2)
+    np.testing.assert_array_equal(ids, [[0, 1]])
+    b[1] = 2.0 ** -22  # now representable above 1: expert 1 first
+    ids, _ = oracle.route_select_bias(s, b, 2)
+    np.testing.assert_array_equal(ids, [[1, 0]])
+
+
+@pytest.mark.parametrize("E,k,seed", [(8, 2, 0), (128, 8, 1), (256, 8, 2)])
+def test_route_select_bias_reductions_and_forced_set(E, k, seed):
+    """Zero bias reproduces the plain router; a bias of +16 on k chosen experts (scores
+    are N(0, 1)) forces exactly that set, with the gates the plain router gives when
+    only those k experts exist; gates are positive and sum to one.  Rounding is
+    monotone, so with no two chosen keys equal the key order is the score order."""
+    rng = np.random.default_rng(seed)
+    T = 40
+    s = rng.standard_normal((T, E)).astype(np.float32)
+    ids0, g0 = oracle.route(s, k)
+    ids1, g1 = oracle.route_select_bias(s, np.zeros(E, np.float32), k)
+    np.testing.assert_array_equal(ids0, ids1)
+    np.testing.assert_allclose(g0, g1, rtol=0, atol=1e-15)
+    chosen = rng.choice(E, size=k, replace=False)
+    b = np.zeros(E, np.float32)
+    b[chosen] = 16.0
+    keys = (s[:, chosen] + np.float32(16.0)).astype(np.float32)
+    assert all(len(set(r.tolist())) == k for r in keys)
+    assert keys.min() > (s + b).max(initial=-np.inf, where=(b == 0)[None, :])
+    ids, g = oracle.route_select_bias(s, b, k)
+    sub_ids, sub_g = oracle.route(np.ascontiguousarray(s[:, chosen]), k)
+    np.testing.assert_array_equal(ids, chosen[sub_ids])
+    np.testing.assert_allclose(g, sub_g, rtol=0, atol=1e-12)
+    assert np.all(g > 0)
+    np.testing.assert_allclose(g.sum(axis=1), 1.0, rtol=0, atol=1e-12)
+
+
 # ----------------------------------------------------------------------------- permute
 @pytest.mark.parametrize("T,E,k,seed", [(64, 8, 2, 0), (6, 128, 8, 1), (300, 256, 8, 2), (1, 4, 4, 3), (0, 8, 2, 4)])
 def test_permute_is_stable_counting_sort(T, E, k, seed):
