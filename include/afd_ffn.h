@@ -116,6 +116,21 @@ int afd_ffn_create(const afd_ffn_config* cfg, const void* w_gate_up, const void*
  * 0 <= T <= max_tokens. */
 int afd_ffn_route(afd_ffn_t h, const float* logits, int32_t T, const afd_route* r, void* stream);
 
+/* Route T tokens with a bias that steers only the choice of experts: the dynamic
+ * per-expert bias of "MoE 大规模分布式推理工程实战：从 All-to-All 通信到动态专家放置"
+ * (§4.1, load balancing by a bias on the router scores, as in DeepSeek-V3's
+ * bias-based balancing), in the form where the bias decides which experts a token
+ * goes to while the gate weights follow the router's own scores.
+ *   key[t, e]  = scores[t, e] + bias[e], rounded to fp32;
+ *   ids[t, :]  = the top_k experts by (key descending, expert index ascending);
+ *   gates[t, j]= softmax of the unbiased scores of the chosen experts (renormalised
+ *                over them, fp32).
+ * scores [T, E] and bias [E] are fp32 device buffers (neither may be NULL); every
+ * field of *r is filled as by afd_ffn_route, whose result this equals when bias is
+ * all zeros.  0 <= T <= max_tokens. */
+int afd_ffn_route_select_bias(afd_ffn_t h, const float* scores, const float* bias, int32_t T, const afd_route* r,
+                              void* stream);
+
 /* Route T tokens from their hidden states: the router projection of "MoE 大规模分布式
  * 推理工程实战：从 All-to-All 通信到动态专家放置" (§4.1), a bias-free linear map from
  * the hidden size to the experts plus a per-expert dynamic bias, followed by the

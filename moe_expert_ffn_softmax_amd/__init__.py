@@ -11,7 +11,8 @@ from __future__ import annotations
 from ._ffi import (AFD_BF16, AFD_F32, AFD_FP8_E4M3, AFD_GEMM_AUTO, AFD_GEMM_STREAM,  # noqa: F401
                    AFD_GEMM_TILED, AFD_GEMM_WIDE, STAGES, AfdError, afd_ffn_config, afd_ffn_create, afd_ffn_destroy,
                    afd_ffn_device_bytes, afd_ffn_forward, afd_ffn_last_error, afd_ffn_profile_read,
-                   afd_ffn_quantize_fp8, afd_ffn_route, afd_ffn_route_hidden, afd_ffn_set_gemm_kernel,
+                   afd_ffn_quantize_fp8, afd_ffn_route, afd_ffn_route_hidden, afd_ffn_route_select_bias,
+                   afd_ffn_set_gemm_kernel,
                    afd_ffn_set_profiling,
                    afd_ffn_strerror, afd_route, load)
 
@@ -84,6 +85,12 @@ class MoeExpertFFN:
     def route(self, logits, T: int, rb: RouteBuffers, stream=None) -> None:
         import torch
         afd_ffn_route(self.handle, logits, T, rb.c, _stream_handle(torch, stream))
+
+    def route_select_bias(self, scores, bias, T: int, rb: RouteBuffers, stream=None) -> None:
+        """Route with a bias that only steers the choice: experts ranked on scores + bias,
+        gates = softmax of the chosen experts' unbiased scores."""
+        import torch
+        afd_ffn_route_select_bias(self.handle, scores, bias, T, rb.c, _stream_handle(torch, stream))
 
     def route_hidden(self, x, w_router, logits, T: int, rb: RouteBuffers, bias=None, stream=None) -> None:
         """Route from hidden states: logits [T, E] (fp32, written) = x w_router^T + bias,

@@ -52,6 +52,8 @@ def load():
     lib.afd_ffn_route.restype = ctypes.c_int
     lib.afd_ffn_route_hidden.argtypes = [V, P, P, P, P, I32, ctypes.POINTER(afd_route), V]
     lib.afd_ffn_route_hidden.restype = ctypes.c_int
+    lib.afd_ffn_route_select_bias.argtypes = [V, P, P, I32, ctypes.POINTER(afd_route), V]
+    lib.afd_ffn_route_select_bias.restype = ctypes.c_int
     lib.afd_ffn_forward.argtypes = [V, P, I32, ctypes.POINTER(afd_route), P, V]
     lib.afd_ffn_forward.restype = ctypes.c_int
     lib.afd_ffn_destroy.argtypes = [V]
@@ -107,6 +109,10 @@ def afd_ffn_create(cfg: afd_ffn_config, w_gate_up, w_down, s_gate_up=None, s_dow
 
 def afd_ffn_route(h: int, logits, T: int, route: afd_route, stream=None) -> None:
     _check(load().afd_ffn_route(h, _ptr(logits), int(T), ctypes.byref(route), stream))
+
+
+def afd_ffn_route_select_bias(h: int, scores, bias, T: int, route: afd_route, stream=None) -> None:
+    _check(load().afd_ffn_route_select_bias(h, _ptr(scores), _ptr(bias), int(T), ctypes.byref(route), stream))
 
 
 def afd_ffn_route_hidden(h: int, x, w_router, bias, logits, T: int, route: afd_route, stream=None) -> None:

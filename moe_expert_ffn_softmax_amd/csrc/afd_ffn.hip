@@ -353,17 +353,15 @@ extern "C" int afd_ffn_destroy(afd_ffn_t h) {
 
 extern "C" size_t afd_ffn_device_bytes(afd_ffn_t h) { return h ? h->device_bytes : 0; }
 
-extern "C" int afd_ffn_route(afd_ffn_t h, const float* logits, int32_t T, const afd_route* r, void* stream) {
-  int rc = check_route(h, r, T);
-  if (rc) return rc;
-  if (!logits) return fail(AFD_EINVAL, "logits is NULL");
-  if (T == 0) return AFD_OK;
-  hipStream_t st = static_cast<hipStream_t>(stream);
+// Steps a1-a4 on logits already checked by the caller: router (with an optional
+// selection-only bias) and the permute; one launch for decode batches.
+static int route_checked(afd_ffn_t h, const float* logits, const float* sel_bias, int32_t T, const afd_route* r,
+                         hipStream_t st) {
   const int E = h->cfg.num_experts, k = h->cfg.top_k;
   if (T <= afd::route_small_tokens()) {
     // decode batches: router and permute in one launch (timed as the router stage)
     StageScope s(h, st, AFD_STAGE_ROUTER);
-    hipError_t e = afd::launch_route_small(logits, T, E, k, r->topk_ids, r->topk_gates, r->expert_counts,
+    hipError_t e = afd::launch_route_small(logits, sel_bias, T, E, k, r->topk_ids, r->topk_gates, r->expert_counts,
                                            r->expert_offsets, r->sorted_pair, r->pair_pos, st);
     if (e != hipSuccess) return hip_fail(e, "route launch");
     s.done();
@@ -371,7 +369,7 @@ extern "C" int afd_ffn_route(afd_ffn_t h, const float* logits, int32_t T, const 
   }
   {
     StageScope s(h, st, AFD_STAGE_ROUTER);
-    hipError_t e = afd::launch_router(logits, T, E, k, r->topk_ids, r->topk_gates, st);
+    hipError_t e = afd::launch_router(logits, sel_bias, T, E, k, r->topk_ids, r->topk_gates, st);
     if (e != hipSuccess) return hip_fail(e, "router launch");
     s.done();
   }
@@ -383,6 +381,23 @@ extern "C" int afd_ffn_route(afd_ffn_t h, const float* logits, int32_t T, const 
     s.done();
   }
   return AFD_OK;
+}
+
+extern "C" int afd_ffn_route(afd_ffn_t h, const float* logits, int32_t T, const afd_route* r, void* stream) {
+  int rc = check_route(h, r, T);
+  if (rc) return rc;
+  if (!logits) return fail(AFD_EINVAL, "logits is NULL");
+  if (T == 0) return AFD_OK;
+  return route_checked(h, logits, nullptr, T, r, static_cast<hipStream_t>(stream));
+}
+
+extern "C" int afd_ffn_route_select_bias(afd_ffn_t h, const float* scores, const float* bias, int32_t T,
+                                         const afd_route* r, void* stream) {
+  int rc = check_route(h, r, T);
+  if (rc) return rc;
+  if (!scores || !bias) return fail(AFD_EINVAL, "scores or bias is NULL");
+  if (T == 0) return AFD_OK;
+  return route_checked(h, scores, bias, T, r, static_cast<hipStream_t>(stream));
 }
 
 extern "C" int afd_ffn_route_hidden(afd_ffn_t h, const void* x, const void* w_router, const float* bias,

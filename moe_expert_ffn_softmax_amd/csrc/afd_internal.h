@@ -52,14 +52,16 @@ struct GroupedGemm {
   int ldo_routed, ldo_shared;   // output row stride (elements)
 };
 
-hipError_t launch_router(const float* logits, int T, int E, int k, int32_t* ids, float* gates,
-                         hipStream_t st);
+// sel_bias [E] (or NULL): a bias added to the logits for the choice of experts only.
+hipError_t launch_router(const float* logits, const float* sel_bias, int T, int E, int k, int32_t* ids,
+                         float* gates, hipStream_t st);
 // logits [T, E] = x [T, H] * w [E, H]^T (+ bias [E]); x and w bf16, or fp32 when f32.
 hipError_t launch_router_proj(const void* x, const void* w, const float* bias, int T, int H, int E, bool f32,
                               float* logits, hipStream_t st);
 // Router and permute as one launch for batches of at most route_small_tokens() tokens.
-hipError_t launch_route_small(const float* logits, int T, int E, int k, int32_t* ids, float* gates, int32_t* counts,
-                              int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos, hipStream_t st);
+hipError_t launch_route_small(const float* logits, const float* sel_bias, int T, int E, int k, int32_t* ids,
+                              float* gates, int32_t* counts, int32_t* offsets, int32_t* sorted_pair,
+                              int32_t* pair_pos, hipStream_t st);
 int route_small_tokens();
 hipError_t launch_permute(const int32_t* ids, int P, int E, int32_t* counts, int32_t* offsets,
                           int32_t* sorted_pair, int32_t* pair_pos, hipStream_t st);

@@ -120,7 +120,8 @@ __global__ void __launch_bounds__(kPermuteThreads) permute_kernel(const int32_t*
 constexpr int kRouteSmallTokens = 64;
 
 template <int PER_LANE>
-__global__ void __launch_bounds__(kPermuteThreads) route_small_kernel(const float* __restrict__ logits, int T, int E,
+__global__ void __launch_bounds__(kPermuteThreads) route_small_kernel(const float* __restrict__ logits,
+                                                                      const float* __restrict__ sel_bias, int T, int E,
                                                                       int k, int32_t* __restrict__ ids,
                                                                       float* __restrict__ gates,
                                                                       int32_t* __restrict__ counts,
@@ -132,7 +133,7 @@ __global__ void __launch_bounds__(kPermuteThreads) route_small_kernel(const floa
   for (int t = threadIdx.x / kWave; t < T; t += kPermuteWaves) {
     int id;
     float gate;
-    route_token<PER_LANE>(logits + (size_t)t * E, E, k, &id, &gate);
+    route_token<PER_LANE>(logits + (size_t)t * E, sel_bias, E, k, &id, &gate);
     if (lane < k) {
       ids[(size_t)t * k + lane] = id;
       gates[(size_t)t * k + lane] = gate;
@@ -143,12 +144,13 @@ __global__ void __launch_bounds__(kPermuteThreads) route_small_kernel(const floa
   permute_one_workgroup(ids_s, T * k, E, counts, offsets, sorted_pair, pair_pos);
 }
 
-hipError_t launch_route_small(const float* logits, int T, int E, int k, int32_t* ids, float* gates, int32_t* counts,
-                              int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos, hipStream_t st) {
+hipError_t launch_route_small(const float* logits, const float* sel_bias, int T, int E, int k, int32_t* ids,
+                              float* gates, int32_t* counts, int32_t* offsets, int32_t* sorted_pair,
+                              int32_t* pair_pos, hipStream_t st) {
   if (T <= 0) return hipSuccess;
   if (T > kRouteSmallTokens || k > kRouterMaxSlots || E > kPermuteMaxE) return hipErrorInvalidValue;
 #define AFD_ROUTE_SMALL(PL) \
-  route_small_kernel<PL><<<1, kPermuteThreads, 0, st>>>(logits, T, E, k, ids, gates, counts, offsets, sorted_pair, pair_pos)
+  route_small_kernel<PL><<<1, kPermuteThreads, 0, st>>>(logits, sel_bias, T, E, k, ids, gates, counts, offsets, sorted_pair, pair_pos)
   if (E <= 64)
     AFD_ROUTE_SMALL(1);
   else if (E <= 128)

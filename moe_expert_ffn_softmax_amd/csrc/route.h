@@ -20,14 +20,24 @@ __device__ __forceinline__ float unordered_bits(uint32_t o) {
 
 // Route one token with one wave: lane j < k returns the expert of slot j in *id and
 // its gate in *gate (other lanes: unspecified).
+//
+// sel_bias == NULL: the experts are ranked on the logits themselves and the gates are
+// the softmax of the selected logits.  sel_bias != NULL (a per-expert bias that only
+// steers the choice, the dynamic-bias load balancing of "MoE 大规模分布式推理工程实战：
+// 从 All-to-All 通信到动态专家放置", §4.1, in its selection-only form): the experts are
+// ranked on the fp32 sum row[e] + sel_bias[e], and the gates are the softmax of the
+// unbiased row values of the chosen experts, renormalised over them.
 template <int PER_LANE>
-__device__ __forceinline__ void route_token(const float* __restrict__ row, int E, int k, int* id, float* gate) {
+__device__ __forceinline__ void route_token(const float* __restrict__ row, const float* __restrict__ sel_bias,
+                                            int E, int k, int* id, float* gate) {
   const int lane = lane_id();
   uint64_t key[PER_LANE];
 #pragma unroll
   for (int i = 0; i < PER_LANE; ++i) {
     const int e = lane + i * kWave;
-    key[i] = e < E ? ((uint64_t)ordered_bits(row[e]) << 32) | (uint32_t)(~(uint32_t)e) : 0ull;
+    float v = 0.0f;
+    if (e < E) v = sel_bias ? row[e] + sel_bias[e] : row[e];
+    key[i] = e < E ? ((uint64_t)ordered_bits(v) << 32) | (uint32_t)(~(uint32_t)e) : 0ull;
   }
   float sel_val = 0.0f;  // lane j keeps the logit of slot j
   int sel_id = 0;
@@ -49,6 +59,11 @@ __device__ __forceinline__ void route_token(const float* __restrict__ row, int E
       for (int i = 0; i < PER_LANE; ++i)
         if (i == e / kWave) key[i] = 0;
     }
+  }
+  if (sel_bias) {
+    // the keys held score + bias: take the chosen experts' unbiased scores instead
+    sel_val = lane < k ? row[sel_id] : -INFINITY;
+    top = wave_max_f32(sel_val);
   }
   const float ex = lane < k ? expf(sel_val - top) : 0.0f;
   const float sum = wave_sum_f32(ex);

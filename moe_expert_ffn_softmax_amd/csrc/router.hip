@@ -11,7 +11,8 @@
 // high word = the float's bits mapped to unsigned order (-0 folded onto +0, so the
 // two compare equal as in IEEE), low word = ~expert, so the larger key is the larger
 // logit and, on a tie, the lower expert.  k rounds of a wave-wide max pick the
-// experts in slot order; the lane that owns the winner retires it.
+// experts in slot order; the lane that owns the winner retires it.  With a
+// selection-only bias the keys are built from logit + bias (see route.h).
 #include "afd_device.h"
 #include "afd_internal.h"
 #include "route.h"
@@ -19,34 +20,36 @@
 namespace afd {
 
 template <int PER_LANE>
-__global__ void __launch_bounds__(256) router_topk_kernel(const float* __restrict__ logits, int T, int E, int k,
+__global__ void __launch_bounds__(256) router_topk_kernel(const float* __restrict__ logits,
+                                                          const float* __restrict__ sel_bias, int T, int E, int k,
                                                           int32_t* __restrict__ ids, float* __restrict__ gates) {
   const int lane = lane_id();
   const int t = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
   if (t >= T) return;
   int id;
   float gate;
-  route_token<PER_LANE>(logits + (size_t)t * E, E, k, &id, &gate);
+  route_token<PER_LANE>(logits + (size_t)t * E, sel_bias, E, k, &id, &gate);
   if (lane < k) {
     ids[(size_t)t * k + lane] = id;
     gates[(size_t)t * k + lane] = gate;
   }
 }
 
-hipError_t launch_router(const float* logits, int T, int E, int k, int32_t* ids, float* gates, hipStream_t st) {
+hipError_t launch_router(const float* logits, const float* sel_bias, int T, int E, int k, int32_t* ids, float* gates,
+                         hipStream_t st) {
   if (T <= 0) return hipSuccess;
   const int waves_per_block = 4;
   dim3 grid((T + waves_per_block - 1) / waves_per_block), block(waves_per_block * kWave);
   if (E <= 64)
-    router_topk_kernel<1><<<grid, block, 0, st>>>(logits, T, E, k, ids, gates);
+    router_topk_kernel<1><<<grid, block, 0, st>>>(logits, sel_bias, T, E, k, ids, gates);
   else if (E <= 128)
-    router_topk_kernel<2><<<grid, block, 0, st>>>(logits, T, E, k, ids, gates);
+    router_topk_kernel<2><<<grid, block, 0, st>>>(logits, sel_bias, T, E, k, ids, gates);
   else if (E <= 256)
-    router_topk_kernel<4><<<grid, block, 0, st>>>(logits, T, E, k, ids, gates);
+    router_topk_kernel<4><<<grid, block, 0, st>>>(logits, sel_bias, T, E, k, ids, gates);
   else if (E <= 512)
-    router_topk_kernel<8><<<grid, block, 0, st>>>(logits, T, E, k, ids, gates);
+    router_topk_kernel<8><<<grid, block, 0, st>>>(logits, sel_bias, T, E, k, ids, gates);
   else
-    router_topk_kernel<kRouterMaxPerLane><<<grid, block, 0, st>>>(logits, T, E, k, ids, gates);
+    router_topk_kernel<kRouterMaxPerLane><<<grid, block, 0, st>>>(logits, sel_bias, T, E, k, ids, gates);
   return hipGetLastError();
 }
 
