@@ -150,6 +150,18 @@ int afd_ffn_route_hidden(afd_ffn_t h, const void* x, const void* w_router, const
  * x and y must not overlap (checked: AFD_EINVAL). */
 int afd_ffn_forward(afd_ffn_t h, const void* x, int32_t T, const afd_route* r, void* y, void* stream);
 
+/* Expert FFN of an AFD_FP8_E4M3 layer on activations that arrive already quantised
+ * (the attention side sends fp8 activations with per-token, per-128-channel scales,
+ * the FP8/BF16 mixed precision of the omica.com.cn AFD article, §3.3, which halves
+ * the bytes of the attention-to-FFN transfer).  xq [T, H] e4m3 codes and xs
+ * [T, H/128] fp32 scales (activation = code * scale), row-major: the layout
+ * afd_ffn_quantize_fp8 writes.  y [T, H] bf16.  Identical to afd_ffn_forward on the
+ * bf16 activations those codes and scales were quantised from, without its
+ * quantisation launch.  Other layer types: AFD_EUNSUPPORTED.  xq, xs and y must not
+ * overlap (checked: AFD_EINVAL). */
+int afd_ffn_forward_fp8_input(afd_ffn_t h, const uint8_t* xq, const float* xs, int32_t T, const afd_route* r,
+                              void* y, void* stream);
+
 /* Release the handle's weights and workspace.  The caller must have synchronised
  * every stream with work of this handle.  NULL is a no-op. */
 int afd_ffn_destroy(afd_ffn_t h);

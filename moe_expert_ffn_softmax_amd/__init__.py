@@ -10,10 +10,9 @@ from __future__ import annotations
 
 from ._ffi import (AFD_BF16, AFD_F32, AFD_FP8_E4M3, AFD_GEMM_AUTO, AFD_GEMM_STREAM,  # noqa: F401
                    AFD_GEMM_TILED, AFD_GEMM_WIDE, STAGES, AfdError, afd_ffn_config, afd_ffn_create, afd_ffn_destroy,
-                   afd_ffn_device_bytes, afd_ffn_forward, afd_ffn_last_error, afd_ffn_profile_read,
-                   afd_ffn_quantize_fp8, afd_ffn_route, afd_ffn_route_hidden, afd_ffn_route_select_bias,
-                   afd_ffn_set_gemm_kernel,
-                   afd_ffn_set_profiling,
+                   afd_ffn_device_bytes, afd_ffn_forward, afd_ffn_forward_fp8_input, afd_ffn_last_error,
+                   afd_ffn_profile_read, afd_ffn_quantize_fp8, afd_ffn_route, afd_ffn_route_hidden,
+                   afd_ffn_route_select_bias, afd_ffn_set_gemm_kernel, afd_ffn_set_profiling,
                    afd_ffn_strerror, afd_route, load)
 
 GEMM_KERNELS = {"auto": AFD_GEMM_AUTO, "stream": AFD_GEMM_STREAM, "tiled": AFD_GEMM_TILED,
@@ -101,6 +100,11 @@ class MoeExpertFFN:
     def forward(self, x, T: int, rb: RouteBuffers, y, stream=None) -> None:
         import torch
         afd_ffn_forward(self.handle, x, T, rb.c, y, _stream_handle(torch, stream))
+
+    def forward_fp8_input(self, xq, xs, T: int, rb: RouteBuffers, y, stream=None) -> None:
+        """fp8 layers: forward on e4m3 codes xq [T, H] (uint8) and fp32 scales xs [T, H/128]."""
+        import torch
+        afd_ffn_forward_fp8_input(self.handle, xq, xs, T, rb.c, y, _stream_handle(torch, stream))
 
     def __call__(self, x, logits, rb: RouteBuffers = None, y=None):
         """route + forward of a whole batch; returns y (allocated if not given)."""

@@ -115,12 +115,13 @@ bool use_wide(const afd_ffn* h, int P) {
 
 // fp8 layer: quantise x -> gate/up GEMM -> quantise h (in the tiled GEMM's epilogue, else a
 // separate pass over fp32 h) -> down GEMM -> combine.
+// x == NULL: g1 already points at caller-quantised activations (no quantisation launch).
 int forward_fp8(afd_ffn* h, const void* x, int T, const afd_route* r, void* y, hipStream_t st,
                 const afd::GroupedGemm& g1, const afd::GroupedGemm& g2) {
   const afd_ffn_config& c = h->cfg;
   const int H = c.hidden, M = c.inter, Ms = c.shared_inter, E = c.num_experts, k = c.top_k;
   const int P = T * k;
-  {
+  if (x) {
     StageScope s(h, st, AFD_STAGE_QUANT);
     hipError_t e = afd::launch_quant_fp8(x, T, H, H, true, h->xq, h->xs, st);
     if (e != hipSuccess) return hip_fail(e, "x quantisation launch");
@@ -426,16 +427,10 @@ extern "C" int afd_ffn_route_hidden(afd_ffn_t h, const void* x, const void* w_ro
   return afd_ffn_route(h, logits, T, r, stream);
 }
 
-extern "C" int afd_ffn_forward(afd_ffn_t h, const void* x, int32_t T, const afd_route* r, void* y, void* stream) {
-  int rc = check_route(h, r, T);
-  if (rc) return rc;
-  if (!x || !y) return fail(AFD_EINVAL, "x or y is NULL");
-  if (T == 0) return AFD_OK;
-  {
-    const size_t rowb = (size_t)h->cfg.hidden * (h->cfg.dtype == AFD_F32 ? 4 : 2);
-    if (overlaps(x, (size_t)T * rowb, y, (size_t)T * rowb)) return fail(AFD_EINVAL, "x and y overlap");
-  }
-  hipStream_t st = static_cast<hipStream_t>(stream);
+// Steps a0 and a5-a8 on checked arguments.  fp8 layers: x (bf16) is quantised here,
+// or, when x is NULL, xq / xs are the caller's e4m3 codes and scales of it.
+static int forward_checked(afd_ffn_t h, const void* x, const uint8_t* xq, const float* xs, int32_t T,
+                           const afd_route* r, void* y, hipStream_t st) {
   const afd_ffn_config& c = h->cfg;
   const int H = c.hidden, M = c.inter, Ms = c.shared_inter, E = c.num_experts, k = c.top_k;
   const int P = T * k;
@@ -485,10 +480,10 @@ extern "C" int afd_ffn_forward(afd_ffn_t h, const void* x, int32_t T, const afd_
   g2.ldo_shared = H;
 
   if (fp8) {
-    g1.a_routed = h->xq;
-    g1.a_shared = h->xq;
-    g1.as_routed = h->xs;
-    g1.as_shared = h->xs;
+    g1.a_routed = x ? h->xq : xq;
+    g1.a_shared = g1.a_routed;
+    g1.as_routed = x ? h->xs : xs;
+    g1.as_shared = g1.as_routed;
     g1.s_routed = h->s_gu;
     g1.s_expert_elems = (size_t)(H / 128) * (2 * M / 128);
     g1.s_shared = h->ss_gu;
@@ -550,6 +545,29 @@ extern "C" int afd_ffn_forward(afd_ffn_t h, const void* x, int32_t T, const afd_
     s.done();
   }
   return AFD_OK;
+}
+
+extern "C" int afd_ffn_forward(afd_ffn_t h, const void* x, int32_t T, const afd_route* r, void* y, void* stream) {
+  int rc = check_route(h, r, T);
+  if (rc) return rc;
+  if (!x || !y) return fail(AFD_EINVAL, "x or y is NULL");
+  if (T == 0) return AFD_OK;
+  const size_t rowb = (size_t)h->cfg.hidden * (h->cfg.dtype == AFD_F32 ? 4 : 2);
+  if (overlaps(x, (size_t)T * rowb, y, (size_t)T * rowb)) return fail(AFD_EINVAL, "x and y overlap");
+  return forward_checked(h, x, nullptr, nullptr, T, r, y, static_cast<hipStream_t>(stream));
+}
+
+extern "C" int afd_ffn_forward_fp8_input(afd_ffn_t h, const uint8_t* xq, const float* xs, int32_t T,
+                                         const afd_route* r, void* y, void* stream) {
+  int rc = check_route(h, r, T);
+  if (rc) return rc;
+  if (h->cfg.dtype != AFD_FP8_E4M3) return fail(AFD_EUNSUPPORTED, "pre-quantised input needs an fp8 layer");
+  if (!xq || !xs || !y) return fail(AFD_EINVAL, "xq, xs or y is NULL");
+  if (T == 0) return AFD_OK;
+  const size_t H = h->cfg.hidden, yb = (size_t)T * H * 2, qb = (size_t)T * H, sb = (size_t)T * (H / 128) * 4;
+  if (overlaps(xq, qb, y, yb) || overlaps(xs, sb, y, yb) || overlaps(xq, qb, xs, sb))
+    return fail(AFD_EINVAL, "xq, xs and y overlap");
+  return forward_checked(h, nullptr, xq, xs, T, r, y, static_cast<hipStream_t>(stream));
 }
 
 extern "C" int afd_ffn_set_gemm_kernel(afd_ffn_t h, int kernel) {

@@ -18,6 +18,12 @@ __device__ __forceinline__ float unordered_bits(uint32_t o) {
   return __uint_as_float(b);
 }
 
+__device__ __forceinline__ float wave_max_f32(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+  return v;
+}
+
 // Route one token with one wave: lane j < k returns the expert of slot j in *id and
 // its gate in *gate (other lanes: unspecified).
 //

@@ -144,6 +144,15 @@ def test_fp8_blockscaled_sampled():
     full_case(workloads.FP8_DSV3, sample=3)
 
 
+@pytest.mark.parametrize("w", [workloads.mfma_sweep("bf16")[0], workloads.mfma_sweep("bf16")[-1],
+                               workloads.mfma_sweep("fp8")[-1]], ids=lambda w: w.name)
+def test_mfma_sweep_sampled(w):
+    """The 256 / 1024 tokens-per-expert batches on which the matrix-core rate is
+    measured, at full size and in the launch configuration timed there (automatic
+    kernel choice: the 128-row tiled GEMMs), on sampled tokens."""
+    full_case(w, sample=3)
+
+
 @pytest.mark.parametrize("src", ["bf16", "f32"])
 def test_fp8_quantisation_bit_exact(src):
     """Step a0 alone: codes and scales equal the oracle's per-128 quantisation
