@@ -130,9 +130,10 @@ def traffic_from_counters(w, kernel):
     return e.get("bytes_per_launch")
 
 
-def cpu_baseline(w, weights, batches, seconds):
+def cpu_baseline(w, weights, batches, seconds, single_seconds=3.0):
     """The oracle (as it stands) on whole batches of the timed workload, cycling over
-    the timed ring of batches until about `seconds` of oracle time have passed.
+    the timed ring of batches until about `seconds` of oracle time have passed, on
+    every host core; then the same on one thread for about `single_seconds`.
     Copying experts to host memory (once per expert) is not timed."""
     import torch
 
@@ -142,9 +143,8 @@ def cpu_baseline(w, weights, batches, seconds):
     for k in ("w_gu", "w_d", "s_gu", "s_d"):
         host[k] = {} if weights[k] is not None else None
     inputs = {}
-    spent, done = 0.0, 0
-    while spent < seconds:
-        b = done % batches
+
+    def batch(b):
         if b not in inputs:
             x = workloads.tokens_f32(w, batch=b)
             if w.dtype != "f32":
@@ -157,15 +157,28 @@ def cpu_baseline(w, weights, batches, seconds):
                         if int(e) not in host[k]:
                             host[k][int(e)] = weights[k][int(e)].cpu()
             inputs[b] = (x, logits, need)
-        x, logits, need = inputs[b]
-        t0 = time.perf_counter()
-        oracle.layer_from_weights(x, logits, w, host, experts_needed=need)
-        spent += time.perf_counter() - t0
-        done += 1
-    return {"value": round(done * w.T / spent, 3), "unit": "tokens/s", "cores": oracle.max_threads(),
-            "kind": "oracle",
-            "sample": f"{done} whole batches of {w.T} tokens (the timed ring of {min(done, batches)} batches, "
-                      f"cycled), {spent:.1f} s of oracle time on the host, double precision"}
+        return inputs[b]
+
+    def timed(limit, nthreads):
+        spent, done = 0.0, 0
+        while spent < limit:
+            x, logits, need = batch(done % batches)
+            t0 = time.perf_counter()
+            oracle.layer_from_weights(x, logits, w, host, experts_needed=need, nthreads=nthreads)
+            spent += time.perf_counter() - t0
+            done += 1
+        return spent, done
+
+    spent, done = timed(seconds, 0)
+    spent1, done1 = timed(single_seconds, 1) if single_seconds > 0 else (0.0, 0)
+    out = {"value": round(done * w.T / spent, 3), "unit": "tokens/s", "cores": oracle.max_threads(),
+           "kind": "oracle",
+           "sample": f"{done} whole batches of {w.T} tokens (the timed ring of {min(done, batches)} batches, "
+                     f"cycled), {spent:.1f} s of oracle time on the host, double precision"}
+    if done1:
+        out["single_thread"] = {"value": round(done1 * w.T / spent1, 3), "unit": "tokens/s", "cores": 1,
+                                "sample": f"{done1} whole batches, {spent1:.1f} s on one thread"}
+    return out
 
 
 def cold_steps(run, n, torch):
