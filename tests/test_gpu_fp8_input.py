@@ -123,3 +123,48 @@ def test_fp8_input_rejects_other_layers_and_overlap():
     layer.forward_fp8_input(buf, xs, 0, rb, buf)  # T = 0: no-op, nothing checked past the route
     torch.cuda.synchronize()
     layer.close()
+
+
+def test_select_bias_route_and_fp8_input_forward_in_a_hip_graph():
+    """The selection-only-bias route and the pre-quantised fp8 forward captured in one
+    HIP graph: every replay, with eager work and synchronisations in between, equals
+    the eager calls bit for bit."""
+    w = _case("fp8_input_graph", T=70, H=256, M=256, E=16, k=4, Ms=128)
+    print(f"case {w.name}: graph of route_select_bias + forward_fp8_input", flush=True)
+    weights = workloads.make_weights(w, device="cuda")
+    x, logits = workloads.make_activations(w, device="cuda")
+    bias = torch.linspace(-1.0, 1.0, w.E, device="cuda")
+    xq, xs = quantize_fp8(x)
+    layer = _layer(w, weights)
+    rb_e = layer.new_route()
+    y_e = torch.zeros((w.T, w.H), dtype=torch.bfloat16, device="cuda")
+    layer.route_select_bias(logits, bias, w.T, rb_e)
+    layer.forward_fp8_input(xq, xs, w.T, rb_e, y_e)
+    torch.cuda.synchronize()
+    rb = layer.new_route()
+    y = torch.zeros_like(y_e)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        layer.route_select_bias(logits, bias, w.T, rb, stream=s)  # warm-up on the capture stream
+        layer.forward_fp8_input(xq, xs, w.T, rb, y, stream=s)
+        s.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            layer.route_select_bias(logits, bias, w.T, rb, stream=s)
+            layer.forward_fp8_input(xq, xs, w.T, rb, y, stream=s)
+    torch.cuda.current_stream().wait_stream(s)
+    other = torch.zeros_like(y_e)
+    for rep in range(3):
+        y.zero_()
+        rb.sorted_pair.fill_(-1)
+        rb2 = layer.new_route()
+        layer.route_select_bias(logits.flip(0), bias.flip(0), w.T, rb2)  # unrelated eager work
+        layer.forward_fp8_input(xq.flip(0).contiguous(), xs.flip(0).contiguous(), w.T, rb2, other)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), y_e.view(torch.int16)), f"replay {rep}: output differs"
+        assert torch.equal(rb.sorted_pair, rb_e.sorted_pair), f"replay {rep}: permutation differs"
+        assert torch.equal(rb.topk_gates, rb_e.topk_gates), f"replay {rep}: gates differ"
+    layer.close()
