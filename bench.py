@@ -19,6 +19,7 @@ traffic, used to scale rocprofv3's FETCH_SIZE / WRITE_SIZE counters).
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -43,6 +44,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=workloads.STARVED_DECODE.name)
+    ap.add_argument("--tokens", type=int, default=0,
+                    help="override the workload's batch size T (same layer, same input distributions)")
     ap.add_argument("--batches", type=int, default=16, help="distinct resident batches cycled over the steps")
     ap.add_argument("--graph", action="store_true", help="replay route+forward from a captured HIP graph")
     ap.add_argument("--gemm", default="auto", choices=["auto", "stream", "tiled", "wide"],
@@ -416,6 +419,8 @@ def main():
     from moe_expert_ffn_softmax_amd import MoeExpertFFN, afd_ffn_profile_read, afd_ffn_set_profiling
 
     w = workloads.get(args.workload)
+    if args.tokens > 0 and args.tokens != w.T:
+        w = dataclasses.replace(w, T=args.tokens, name=f"{w.name}_at_T{args.tokens}")
     torch.cuda.set_device(0)
     dev = "cuda"
     weights = workloads.make_weights(w, device=dev)

@@ -97,12 +97,19 @@ struct StageScope {
   }
 };
 
-// Kernel choice for a batch of P routed pairs: the 128-row tiled GEMM once experts
-// average more than 16 rows (one streaming tile), unless forced either way.
+// Kernel choice for a batch of P routed pairs, unless forced either way, from whole-layer
+// times of both kernels on MI355X over batch sizes:
+//   bf16: the 16-row streaming GEMM up to 8 routed rows per expert on average, the
+//     128-row tiled GEMM above (E=128, H=4096: streaming 4% faster at 8 rows, tiled 1%
+//     faster at 9, 7% at 11, 20% at 16; E=48, H=7168 with a shared expert: streaming
+//     3% faster at 8, tiled 45% faster at 16);
+//   fp8: always the tiled GEMM (E=256, H=7168: 11% faster at 6 tokens, 21% at 1 row per
+//     expert, 29% at 8, 82% at 16; with a 2048-wide shared expert 22% faster at 4 rows).
 bool use_tiled(const afd_ffn* h, int P) {
   if (h->gemm_mode == AFD_GEMM_STREAM) return false;
   if (h->gemm_mode == AFD_GEMM_TILED || h->gemm_mode == AFD_GEMM_WIDE) return true;
-  return (long long)P > 16ll * h->cfg.num_experts;
+  if (h->cfg.dtype == AFD_FP8_E4M3) return true;
+  return (long long)P > 8ll * h->cfg.num_experts;
 }
 
 // bf16 layers: the 256x256-tile GEMM only when forced.  It moves a third less operand
