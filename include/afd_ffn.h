@@ -186,11 +186,10 @@ int afd_ffn_quantize_fp8(const void* src, int32_t rows, int32_t cols, int32_t sr
                          float* scales, void* stream);
 
 /* Choice of grouped-GEMM kernel for bf16 and fp8 layers.  AFD_GEMM_AUTO (the default)
- * uses, for bf16 layers, 16-row weight-streaming tiles while experts average at most
- * 8 routed rows per batch (T * top_k <= 8 * E) and 128-row tiles above that, and for
- * fp8 layers always the 128-row tiles (the faster kernel at every batch size measured);
- * the other values force one kernel (results agree to rounding; a tuning and testing
- * knob).
+ * uses 16-row weight-streaming tiles while experts average at most 8 (bf16) or 12
+ * (fp8) routed rows per batch (T * top_k <= 8 * E, resp. 12 * E) and 128-row tiles
+ * above that (the measured crossovers); the other values force one kernel (results
+ * agree to rounding; a tuning and testing knob).
  * AFD_GEMM_WIDE (256x256 tiles, both operands staged in LDS) is never chosen
  * automatically and applies to bf16 layers only (fp8 layers take the 128-row kernel
  * instead).  fp32 layers always use their own kernel.  Takes effect for later

@@ -98,18 +98,19 @@ struct StageScope {
 };
 
 // Kernel choice for a batch of P routed pairs, unless forced either way, from whole-layer
-// times of both kernels on MI355X over batch sizes:
-//   bf16: the 16-row streaming GEMM up to 8 routed rows per expert on average, the
-//     128-row tiled GEMM above (E=128, H=4096: streaming 4% faster at 8 rows, tiled 1%
-//     faster at 9, 7% at 11, 20% at 16; E=48, H=7168 with a shared expert: streaming
-//     3% faster at 8, tiled 45% faster at 16);
-//   fp8: always the tiled GEMM (E=256, H=7168: 11% faster at 6 tokens, 21% at 1 row per
-//     expert, 29% at 8, 82% at 16; with a 2048-wide shared expert 22% faster at 4 rows).
+// times of both kernels on MI355X over batch sizes: the 16-row streaming GEMM while
+// experts average at most a few routed rows, the 128-row tiled GEMM above.
+//   bf16: streaming up to 8 rows per expert (E=128, H=4096: streaming 4% faster at 8
+//     rows, tiled 1% faster at 9, 7% at 11, 20% at 16; E=48, H=7168 with a shared
+//     expert: streaming 3% faster at 8, tiled 45% faster at 16);
+//   fp8: streaming up to 12 rows per expert (E=256, H=7168: streaming 33% faster at 6
+//     tokens, 10% at 12 rows; tiled 15% faster at 16; with a 2048-wide shared expert
+//     streaming 2% faster at 12 rows, tiled 18% faster at 16).
 bool use_tiled(const afd_ffn* h, int P) {
   if (h->gemm_mode == AFD_GEMM_STREAM) return false;
   if (h->gemm_mode == AFD_GEMM_TILED || h->gemm_mode == AFD_GEMM_WIDE) return true;
-  if (h->cfg.dtype == AFD_FP8_E4M3) return true;
-  return (long long)P > 8ll * h->cfg.num_experts;
+  const long long rows_per_expert = h->cfg.dtype == AFD_FP8_E4M3 ? 12 : 8;
+  return (long long)P > rows_per_expert * h->cfg.num_experts;
 }
 
 // bf16 layers: the 256x256-tile GEMM only when forced.  It moves a third less operand

@@ -19,7 +19,7 @@
 //
 // Work items, weight streaming and item striding are those of the bf16 streaming
 // kernel: one wave per 16-row tile times one 32-column group, full reduction,
-// weight fragments loaded nontemporally several blocks ahead.
+// weight fragments (and the blocks' scales) loaded nontemporally four blocks ahead.
 #include "grouped.h"
 
 namespace afd {
@@ -53,7 +53,50 @@ __device__ __forceinline__ int block_col(bool gate_up, int N, int j, int half) {
   return gate_up ? half * (N / 2) + j * 16 : j * 32 + half * 16;
 }
 
-template <bool SWIGLU, int D>
+// acc0/acc1 += the 128-deep blocks 0..KB-1 of one 16-row tile and two 16-column weight
+// blocks, each block's fp32 product rescaled by s_act[row][kb] * s_w[kb][nb].  A ring of
+// D blocks in flight holds the operands and the block's scales (two weight scales,
+// the activation scales of the lane's four rows), so a block waits on no load issued
+// in its own iteration; no branch inside (KB % D == 0, KB >= D), so the compiler
+// waits only for the oldest loads.
+template <int D>
+__device__ __forceinline__ void stream_fp8(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B,
+                                           const float* __restrict__ ws, int NB, int nb0, int nb1,
+                                           const float* const (&as_row)[4], int KB, f32x4& acc0, f32x4& acc1) {
+  i32x8 a[D], b0[D], b1[D];
+  float w0r[D], w1r[D], sar[D][4];
+  auto fetch = [&](const int u, const int kb) {
+    a[u] = load32(A + kb * 128);
+    b0[u] = load_frag_nt(B + (kb * 2) * 2048);
+    b1[u] = load_frag_nt(B + (kb * 2 + 1) * 2048);
+    w0r[u] = ws[(size_t)kb * NB + nb0];
+    w1r[u] = ws[(size_t)kb * NB + nb1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sar[u][i] = as_row[i][kb];
+  };
+  auto compute = [&](const int u) {
+    const f32x4 p0 = mfma_fp8_block(a[u], b0[u]);
+    const f32x4 p1 = mfma_fp8_block(a[u], b1[u]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc0[i] = fmaf(p0[i], sar[u][i] * w0r[u], acc0[i]);
+      acc1[i] = fmaf(p1[i], sar[u][i] * w1r[u], acc1[i]);
+    }
+  };
+#pragma unroll
+  for (int u = 0; u < D; ++u) fetch(u, u);
+  for (int kb0 = D; kb0 < KB; kb0 += D) {
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+      compute(u);
+      fetch(u, kb0 + u);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < D; ++u) compute(u);
+}
+
+template <bool SWIGLU>
 __global__ void __launch_bounds__(kFp8Threads) gemm_fp8_stream_kernel(GroupedGemm g) {
   __shared__ int prefix[kMaxSegments + 1];
   __shared__ int scan_tmp[kFp8Waves + 1];
@@ -101,38 +144,12 @@ __global__ void __launch_bounds__(kFp8Threads) gemm_fp8_stream_kernel(GroupedGem
     const int nb0 = block_col(SWIGLU, N, it.group, 0) / 128, nb1 = block_col(SWIGLU, N, it.group, 1) / 128;
 
     f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-    i32x8 a[D], b0[D], b1[D];
-#pragma unroll
-    for (int u = 0; u < D; ++u) {
-      if (u < KB) {
-        a[u] = load32(A + u * 128);
-        b0[u] = load_frag_nt(B + (u * 2) * 2048);
-        b1[u] = load_frag_nt(B + (u * 2 + 1) * 2048);
-      }
-    }
-    for (int kb0 = 0; kb0 < KB; kb0 += D) {
-#pragma unroll
-      for (int u = 0; u < D; ++u) {
-        const int kb = kb0 + u;
-        if (kb < KB) {
-          const f32x4 p0 = mfma_fp8_block(a[u], b0[u]);
-          const f32x4 p1 = mfma_fp8_block(a[u], b1[u]);
-          const float w0 = ws[(size_t)kb * NB + nb0], w1 = ws[(size_t)kb * NB + nb1];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float sa = as_row[i][kb];
-            acc0[i] = fmaf(p0[i], sa * w0, acc0[i]);
-            acc1[i] = fmaf(p1[i], sa * w1, acc1[i]);
-          }
-          const int kn = kb + D;
-          if (kn < KB) {
-            a[u] = load32(A + kn * 128);
-            b0[u] = load_frag_nt(B + (kn * 2) * 2048);
-            b1[u] = load_frag_nt(B + (kn * 2 + 1) * 2048);
-          }
-        }
-      }
-    }
+    if (KB % 4 == 0)
+      stream_fp8<4>(A, B, ws, NB, nb0, nb1, as_row, KB, acc0, acc1);
+    else if (KB % 2 == 0)
+      stream_fp8<2>(A, B, ws, NB, nb0, nb1, as_row, KB, acc0, acc1);
+    else
+      stream_fp8<1>(A, B, ws, NB, nb0, nb1, as_row, KB, acc0, acc1);
 
     const int col = lane & 15;
     const int rbase = (lane >> 4) * 4;
@@ -159,16 +176,16 @@ hipError_t launch_gemm_fp8(const GroupedGemm& g, bool swiglu, long long max_item
   long long blocks = (max_items + kFp8Waves - 1) / kFp8Waves;
   if (blocks > max_blocks) blocks = max_blocks;
   if (swiglu)
-    gemm_fp8_stream_kernel<true, 4><<<(unsigned)blocks, kFp8Threads, 0, st>>>(g);
+    gemm_fp8_stream_kernel<true><<<(unsigned)blocks, kFp8Threads, 0, st>>>(g);
   else
-    gemm_fp8_stream_kernel<false, 4><<<(unsigned)blocks, kFp8Threads, 0, st>>>(g);
+    gemm_fp8_stream_kernel<false><<<(unsigned)blocks, kFp8Threads, 0, st>>>(g);
   return hipGetLastError();
 }
 
 hipError_t gemm_occupancy_fp8(int* gate_up, int* down) {
-  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(gate_up, gemm_fp8_stream_kernel<true, 4>, kFp8Threads, 0);
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(gate_up, gemm_fp8_stream_kernel<true>, kFp8Threads, 0);
   if (e == hipSuccess)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(down, gemm_fp8_stream_kernel<false, 4>, kFp8Threads, 0);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(down, gemm_fp8_stream_kernel<false>, kFp8Threads, 0);
   return e;
 }
 
