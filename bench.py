@@ -255,7 +255,8 @@ def run_workload(w, steps, warmup, batches, gemm, torch):
 
 
 def sweep(args, torch):
-    wls = list(workloads.ORDERED) + workloads.mfma_sweep("bf16") + workloads.mfma_sweep("fp8")
+    wls = (list(workloads.ORDERED) + list(workloads.CONTEXT) + workloads.mfma_sweep("bf16") +
+           workloads.mfma_sweep("fp8"))
     for w in wls:
         if args.only and not any(o in w.name for o in args.only.split(",")):
             continue

@@ -135,6 +135,11 @@ def test_coarse_experts_with_shared_sampled():
     full_case(workloads.COARSE, sample=3)
 
 
+def test_fp8_decode_full():
+    """The fp8 layer at a decode batch of 6 tokens (streaming GEMMs), every token."""
+    full_case(workloads.FP8_DECODE)
+
+
 def test_starved_decode_tiled_kernel():
     """The 128-row kernel on a decode batch: one partial tile per touched expert."""
     full_case(workloads.STARVED_DECODE, kernel="tiled")

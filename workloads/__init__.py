@@ -113,6 +113,16 @@ FP8_DSV3 = _add(Workload(
 
 ORDERED = [TINY, STARVED_DECODE, AGGREGATED, COARSE, FP8_DSV3]
 
+# The fp8 DeepSeek-V3-like layer at a starved decode batch (the fp8 end of the MFU
+# collapse the AFD lecture notes describe in their first section), with the decode
+# layer's per-expert logit bias N(0, 0.5).  A measured context case, not one of the
+# five layer configurations above.
+FP8_DECODE = _add(Workload(
+    "fp8_decode_T6_H7168_M2048_E256_k8_shared2048", 5, T=6, H=7168, M=2048, E=256, k=8, Ms=2048,
+    dtype="fp8", bias="normal", bias_param=0.5,
+    note="DeepSeek-V3-like fp8 layer at a decode batch of 6: weight streaming"))
+CONTEXT = [FP8_DECODE]
+
 
 def mfma_sweep(dtype: str = "bf16"):
     """Token-count sweep at 256/512/1024 routed tokens per expert (the regime where the
