@@ -175,6 +175,12 @@ const char* afd_ffn_last_error(void);
 /* Device bytes the handle owns (repacked weights plus workspace). */
 size_t afd_ffn_device_bytes(afd_ffn_t h);
 
+/* Device bytes of one set of route buffers for this layer (the six afd_route arrays
+ * at their sizes for max_tokens: 4 * (4 * max_tokens * top_k + 2 * num_experts + 1)),
+ * for callers that carve them out of one allocation; each array must be 4-byte
+ * aligned.  One set per batch in flight.  0 for a NULL handle. */
+size_t afd_ffn_route_bytes(afd_ffn_t h);
+
 /* The activation quantisation of the fp8 layer as a stand-alone call: rows x cols
  * activations src (row-major; src_dtype AFD_BF16 or AFD_F32) -> e4m3 codes
  * codes[rows, cols] and fp32 scales scales[rows, cols / 128], per row and per 128

@@ -66,6 +66,8 @@ def load():
     lib.afd_ffn_last_error.restype = ctypes.c_char_p
     lib.afd_ffn_device_bytes.argtypes = [V]
     lib.afd_ffn_device_bytes.restype = ctypes.c_size_t
+    lib.afd_ffn_route_bytes.argtypes = [V]
+    lib.afd_ffn_route_bytes.restype = ctypes.c_size_t
     lib.afd_ffn_quantize_fp8.argtypes = [P, I32, I32, I32, P, P, V]
     lib.afd_ffn_quantize_fp8.restype = ctypes.c_int
     lib.afd_ffn_set_gemm_kernel.argtypes = [V, ctypes.c_int]
@@ -136,6 +138,10 @@ def afd_ffn_destroy(h: int) -> None:
 
 def afd_ffn_device_bytes(h: int) -> int:
     return int(load().afd_ffn_device_bytes(h))
+
+
+def afd_ffn_route_bytes(h: int) -> int:
+    return int(load().afd_ffn_route_bytes(h))
 
 
 def afd_ffn_quantize_fp8(src, rows: int, cols: int, src_dtype: int, codes, scales, stream=None) -> None:

@@ -362,6 +362,12 @@ extern "C" int afd_ffn_destroy(afd_ffn_t h) {
 
 extern "C" size_t afd_ffn_device_bytes(afd_ffn_t h) { return h ? h->device_bytes : 0; }
 
+extern "C" size_t afd_ffn_route_bytes(afd_ffn_t h) {
+  if (!h) return 0;
+  const size_t P = (size_t)h->cfg.max_tokens * h->cfg.top_k, E = h->cfg.num_experts;
+  return 4 * (4 * P + 2 * E + 1);  // ids, gates, sorted_pair, pair_pos [P]; counts [E]; offsets [E + 1]
+}
+
 // Steps a1-a4 on logits already checked by the caller: router (with an optional
 // selection-only bias) and the permute; one launch for decode batches.
 static int route_checked(afd_ffn_t h, const float* logits, const float* sel_bias, int32_t T, const afd_route* r,

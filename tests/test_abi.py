@@ -107,6 +107,7 @@ def test_route_and_forward_reject_null_handle():
     assert lib.afd_ffn_set_profiling(None, 1) == _ffi.AFD_EINVAL
     assert lib.afd_ffn_set_gemm_kernel(None, 0) == _ffi.AFD_EINVAL
     assert lib.afd_ffn_device_bytes(None) == 0
+    assert lib.afd_ffn_route_bytes(None) == 0
 
 
 def test_strerror_names_every_code():

@@ -415,6 +415,17 @@ def test_overlapping_buffers_are_rejected():
     layer.close()
 
 
+def test_route_bytes_matches_the_route_buffers():
+    from moe_expert_ffn_softmax_amd import afd_ffn_route_bytes
+    w = small("route_bytes", T=37, E=20, k=3)
+    weights = workloads.make_weights(w, device="cuda")
+    layer = make_layer(w, weights)
+    rb = layer.new_route()
+    arrays = [rb.topk_ids, rb.topk_gates, rb.expert_counts, rb.expert_offsets, rb.sorted_pair, rb.pair_pos]
+    assert afd_ffn_route_bytes(layer.handle) == sum(a.numel() * a.element_size() for a in arrays)
+    layer.close()
+
+
 def test_zero_tokens_is_a_no_op():
     w = small("empty", T=8)
     weights = workloads.make_weights(w, device="cuda")
