@@ -3,15 +3,19 @@
 // Same work items as the bf16 kernels (16-row tile of one expert's rows times a
 // 32-column group, statically strided over the waves), on weights in their natural
 // row-major layout.  fp32 matrix-core throughput equals the fp32 vector peak on
-// gfx950, so plain FMAs lose nothing here.  Lane l owns column (l % 16) of each
-// 16-column block and rows (l / 16) * 4 .. + 3 of the tile.
+// gfx950, so plain FMAs lose nothing here.  The reduction is split over the wave's
+// four 16-lane groups: lane l owns column (l % 16) of each 16-column block and the
+// reduction quarter l / 16, accumulating all 16 rows of the tile over its quarter (a
+// quarter of the dependent steps of a whole-K walk, four times the work per step).
+// The four partial sums are then added across the lane groups in a fixed order,
+// (q0 + q1) + (q2 + q3), and lanes 0..15 store the tile.
 #include "grouped.h"
 
 namespace afd {
 
 constexpr int kF32Threads = 256;
 constexpr int kF32Waves = kF32Threads / kWave;
-constexpr int kF32Ahead = 8;  // reduction steps in flight
+constexpr int kF32Ahead = 2;  // 4-step groups of the reduction in flight per lane
 
 template <bool SWIGLU>
 __global__ void __launch_bounds__(kF32Threads) gemm_f32_kernel(GroupedGemm g) {
@@ -28,61 +32,84 @@ __global__ void __launch_bounds__(kF32Threads) gemm_f32_kernel(GroupedGemm g) {
     const int lda = it.shared ? g.lda_shared : g.lda_routed;
     const float* Abase = static_cast<const float*>(it.shared ? g.a_shared : g.a_routed);
     const int c = lane & 15;
-    const int rbase = (lane >> 4) * 4;
-    const float* arow[4];
+    const int q = lane >> 4;            // reduction quarter
+    const int KQ = K / 4;               // K is a multiple of 128
+    const int k0 = q * KQ;
+    // the tile's 16 rows (rows past the tile end repeat its first row; not stored)
+    const float* arow[kTileRows];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = rbase + i < it.nrows ? rbase + i : 0;
+    for (int r = 0; r < kTileRows; ++r) {
+      const int rr = r < it.nrows ? r : 0;
       int ar;
       if (it.shared)
-        ar = it.row0 + r;
+        ar = it.row0 + rr;
       else
-        ar = g.gather_routed ? g.sorted_pair[it.row0 + r] / g.k : it.row0 + r;
-      arow[i] = Abase + (size_t)ar * lda;
+        ar = g.gather_routed ? g.sorted_pair[it.row0 + rr] / g.k : it.row0 + rr;
+      arow[r] = Abase + (size_t)ar * lda + k0;
     }
     // weights [K][N] row-major; N = 2 * (groups * 16) for gate/up, groups * 32 for down
     const int groups = it.shared ? g.groups_shared : g.groups_routed;
     const int N = groups * 32;
-    const float* W = it.shared ? static_cast<const float*>(g.w_shared)
-                               : static_cast<const float*>(g.w_routed) + (size_t)it.seg * g.w_expert_elems;
+    const float* W = (it.shared ? static_cast<const float*>(g.w_shared)
+                                : static_cast<const float*>(g.w_routed) + (size_t)it.seg * g.w_expert_elems) +
+                     (size_t)k0 * N;
     const int col0 = SWIGLU ? it.group * 16 + c : it.group * 32 + c;
     const int col1 = SWIGLU ? N / 2 + it.group * 16 + c : it.group * 32 + 16 + c;
-    // loads run kF32Ahead reduction steps ahead in a rotating register ring (K is a
-    // multiple of 128); the FMAs keep ascending k order
-    float acc0[4] = {0.f, 0.f, 0.f, 0.f}, acc1[4] = {0.f, 0.f, 0.f, 0.f};
-    float w0r[kF32Ahead], w1r[kF32Ahead], ar[kF32Ahead][4];
-    auto load = [&](int kk, int u) {
-      w0r[u] = W[(size_t)kk * N + col0];
-      w1r[u] = W[(size_t)kk * N + col1];
+    // loads run two 4-step groups ahead in a rotating register ring (each row's 4
+    // activations of a group in one 16-byte load); the FMAs of each quarter keep
+    // ascending k order
+    float acc0[kTileRows], acc1[kTileRows];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) ar[u][i] = arow[i][kk];
+    for (int r = 0; r < kTileRows; ++r) acc0[r] = acc1[r] = 0.f;
+    float w0r[kF32Ahead][4], w1r[kF32Ahead][4];
+    float4 ar[kF32Ahead][kTileRows];
+    auto load = [&](int kk, int u) {  // steps kk .. kk + 3
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        w0r[u][i] = W[(size_t)(kk + i) * N + col0];
+        w1r[u][i] = W[(size_t)(kk + i) * N + col1];
+      }
+#pragma unroll
+      for (int r = 0; r < kTileRows; ++r) ar[u][r] = *reinterpret_cast<const float4*>(arow[r] + kk);
     };
 #pragma unroll
-    for (int u = 0; u < kF32Ahead; ++u) load(u, u);
-    for (int k0 = 0; k0 < K; k0 += kF32Ahead) {
+    for (int u = 0; u < kF32Ahead; ++u) load(4 * u, u);
+    for (int kb = 0; kb < KQ; kb += 4 * kF32Ahead) {
 #pragma unroll
       for (int u = 0; u < kF32Ahead; ++u) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          acc0[i] = fmaf(ar[u][i], w0r[u], acc0[i]);
-          acc1[i] = fmaf(ar[u][i], w1r[u], acc1[i]);
-        }
-        const int kn = k0 + kF32Ahead + u;
-        load(kn < K ? kn : K - 1, u);  // past the end: reload the last step, unused
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int r = 0; r < kTileRows; ++r) {
+            const float av = i == 0 ? ar[u][r].x : i == 1 ? ar[u][r].y : i == 2 ? ar[u][r].z : ar[u][r].w;
+            acc0[r] = fmaf(av, w0r[u][i], acc0[r]);
+            acc1[r] = fmaf(av, w1r[u][i], acc1[r]);
+          }
+        const int kn = kb + 4 * (kF32Ahead + u);
+        load(kn < KQ ? kn : KQ - 4, u);  // past the end: reload the last group, unused
       }
     }
-    float* out = static_cast<float*>(it.shared ? g.out_shared : g.out_routed);
-    const int ldo = it.shared ? g.ldo_shared : g.ldo_routed;
+    // (q0 + q1) + (q2 + q3): the same sum, bit for bit, in every lane of the column
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = rbase + i;
-      if (row >= it.nrows) continue;
-      float* o = out + (size_t)(it.row0 + row) * ldo;
-      if (SWIGLU) {
-        o[it.group * 16 + c] = silu(acc0[i]) * acc1[i];
-      } else {
-        o[it.group * 32 + c] = acc0[i];
-        o[it.group * 32 + 16 + c] = acc1[i];
+    for (int r = 0; r < kTileRows; ++r) {
+      acc0[r] += __shfl_xor(acc0[r], 16, kWave);
+      acc1[r] += __shfl_xor(acc1[r], 16, kWave);
+      acc0[r] += __shfl_xor(acc0[r], 32, kWave);
+      acc1[r] += __shfl_xor(acc1[r], 32, kWave);
+    }
+    if (q == 0) {
+      float* out = static_cast<float*>(it.shared ? g.out_shared : g.out_routed);
+      const int ldo = it.shared ? g.ldo_shared : g.ldo_routed;
+#pragma unroll
+      for (int r = 0; r < kTileRows; ++r) {
+        if (r >= it.nrows) continue;
+        float* o = out + (size_t)(it.row0 + r) * ldo;
+        if (SWIGLU) {
+          o[it.group * 16 + c] = silu(acc0[r]) * acc1[r];
+        } else {
+          o[it.group * 32 + c] = acc0[r];
+          o[it.group * 32 + 16 + c] = acc1[r];
+        }
       }
     }
   }
