@@ -166,8 +166,10 @@ int forward_fp8(afd_ffn* h, const void* x, int T, const afd_route* r, void* y, h
       s.done();
     }
     StageScope s(h, st, AFD_STAGE_QUANT);
-    hipError_t e = afd::launch_quant_fp8(h->h_routed, P, M, M, false, h->hq_routed, h->hs_routed, st);
-    if (e == hipSuccess && Ms) e = afd::launch_quant_fp8(h->h_shared, T, Ms, Ms, false, h->hq_shared, h->hs_shared, st);
+    // routed and shared h in one launch
+    const afd::QuantSeg routed = {h->h_routed, P, M, M, h->hq_routed, h->hs_routed};
+    const afd::QuantSeg shared = {h->h_shared, Ms ? T : 0, Ms ? Ms : 128, Ms ? Ms : 128, h->hq_shared, h->hs_shared};
+    hipError_t e = afd::launch_quant_fp8_segments(routed, shared, false, st);
     if (e != hipSuccess) return hip_fail(e, "h quantisation launch");
     s.done();
   }

@@ -113,8 +113,18 @@ int fp8_tiled_groups();
 hipError_t launch_pack_fp8(const uint8_t* src, uint8_t* dst, int nmat, int R, int C, int gate_up, hipStream_t st);
 // rows x cols activations (bf16 or fp32, row stride ld) -> e4m3 codes [rows, cols]
 // and fp32 scales [rows, cols / 128].
+// One row segment of the fp8 activation quantisation: rows x cols values at src (row
+// stride ld) -> e4m3 codes q [rows, cols] and scales [rows, cols / 128].
+struct QuantSeg {
+  const void* src;
+  int rows, cols, ld;
+  uint8_t* q;
+  float* scales;
+};
 hipError_t launch_quant_fp8(const void* src, int rows, int cols, int ld, bool src_bf16, uint8_t* q, float* scales,
                             hipStream_t st);
+// Two segments of the same source type in one launch (s1.rows may be 0).
+hipError_t launch_quant_fp8_segments(const QuantSeg& s0, const QuantSeg& s1, bool src_bf16, hipStream_t st);
 
 // Resident workgroups per compute unit of the GEMM kernels.
 hipError_t gemm_occupancy_bf16(int* gate_up, int* down);

@@ -16,20 +16,25 @@ constexpr int kQuantThreads = 256;
 
 // Each lane loads 16 bytes: 8 bf16 or 4 fp32 values (VPL), so a 128-channel group
 // spans 128 / VPL lanes and a wave covers 64 * VPL channels of one row; the group
-// amax is a max over those lanes.
+// amax is a max over those lanes.  One launch covers up to two row segments (the
+// routed and the shared expert's h of the fp8 layer); a wave's rows all belong to one.
 template <bool BF16>
-__global__ void __launch_bounds__(kQuantThreads) quant_fp8_kernel(const void* __restrict__ src, int rows, int cols,
-                                                                  int ld, uint8_t* __restrict__ q,
-                                                                  float* __restrict__ scales) {
+__global__ void __launch_bounds__(kQuantThreads) quant_fp8_kernel(QuantSeg s0, QuantSeg s1) {
   constexpr int VPL = BF16 ? 8 : 4;       // values per lane
   constexpr int LPG = 128 / VPL;          // lanes per 128-channel group
   constexpr int CPW = kWave * VPL;        // channels per wave
   const int lane = lane_id();
-  const int groups = cols / 128;
-  const int chunks = (cols + CPW - 1) / CPW;
+  const long long work0 = (long long)s0.rows * ((s0.cols + CPW - 1) / CPW);
+  const long long work = work0 + (long long)s1.rows * ((s1.cols + CPW - 1) / CPW);
   const long long wave = (long long)blockIdx.x * (kQuantThreads / kWave) + threadIdx.x / kWave;
   const long long waves = (long long)gridDim.x * (kQuantThreads / kWave);
-  for (long long wi = wave; wi < (long long)rows * chunks; wi += waves) {
+  for (long long wj = wave; wj < work; wj += waves) {
+    const bool first = wj < work0;  // uniform over the wave
+    const QuantSeg& sg = first ? s0 : s1;
+    const long long wi = first ? wj : wj - work0;
+    const int cols = sg.cols, ld = sg.ld;
+    const int groups = cols / 128;
+    const int chunks = (cols + CPW - 1) / CPW;
     const int r = (int)(wi / chunks);
     const int c0 = (int)(wi % chunks) * CPW + lane * VPL;
     const bool ok = c0 < cols;  // cols is a multiple of 128, so a group is all in or all out
@@ -38,7 +43,7 @@ __global__ void __launch_bounds__(kQuantThreads) quant_fp8_kernel(const void* __
     for (int i = 0; i < VPL; ++i) v[i] = 0.f;
     if (ok) {
       if (BF16) {
-        const uint4 raw = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(src) + (size_t)r * ld + c0);
+        const uint4 raw = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(sg.src) + (size_t)r * ld + c0);
         const uint32_t wds[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -46,7 +51,7 @@ __global__ void __launch_bounds__(kQuantThreads) quant_fp8_kernel(const void* __
           v[2 * i + 1] = bf16_bits_to_f32((uint16_t)(wds[i] >> 16));
         }
       } else {
-        const float4 f = *reinterpret_cast<const float4*>(static_cast<const float*>(src) + (size_t)r * ld + c0);
+        const float4 f = *reinterpret_cast<const float4*>(static_cast<const float*>(sg.src) + (size_t)r * ld + c0);
         v[0] = f.x;
         v[1] = f.y;
         v[2] = f.z;
@@ -64,27 +69,36 @@ __global__ void __launch_bounds__(kQuantThreads) quant_fp8_kernel(const void* __
 #pragma unroll
       for (int i = 0; i < VPL / 4; ++i) pk[i] = e4m3_pack4(v[4 * i] / s, v[4 * i + 1] / s, v[4 * i + 2] / s, v[4 * i + 3] / s);
       if (BF16)
-        *reinterpret_cast<uint2*>(q + (size_t)r * cols + c0) = make_uint2(pk[0], pk[VPL / 4 - 1]);
+        *reinterpret_cast<uint2*>(sg.q + (size_t)r * cols + c0) = make_uint2(pk[0], pk[VPL / 4 - 1]);
       else
-        *reinterpret_cast<uint32_t*>(q + (size_t)r * cols + c0) = pk[0];
-      if (lane % LPG == 0) scales[(size_t)r * groups + c0 / 128] = s;
+        *reinterpret_cast<uint32_t*>(sg.q + (size_t)r * cols + c0) = pk[0];
+      if (lane % LPG == 0) sg.scales[(size_t)r * groups + c0 / 128] = s;
     }
   }
+}
+
+hipError_t launch_quant_fp8_segments(const QuantSeg& s0, const QuantSeg& s1, bool src_bf16, hipStream_t st) {
+  if (s0.rows < 0 || s1.rows < 0) return hipErrorInvalidValue;
+  if (s0.rows == 0 && s1.rows == 0) return hipSuccess;
+  for (const QuantSeg* sg : {&s0, &s1})
+    if (sg->rows > 0 && (sg->cols % 128 || sg->ld % 8)) return hipErrorInvalidValue;
+  const int cpw = kWave * (src_bf16 ? 8 : 4);
+  const long long work = (long long)s0.rows * ((s0.cols + cpw - 1) / cpw) + (long long)s1.rows * ((s1.cols + cpw - 1) / cpw);
+  long long blocks = (work + 3) / 4;
+  if (blocks > 8192) blocks = 8192;
+  if (src_bf16)
+    quant_fp8_kernel<true><<<(unsigned)blocks, kQuantThreads, 0, st>>>(s0, s1);
+  else
+    quant_fp8_kernel<false><<<(unsigned)blocks, kQuantThreads, 0, st>>>(s0, s1);
+  return hipGetLastError();
 }
 
 hipError_t launch_quant_fp8(const void* src, int rows, int cols, int ld, bool src_bf16, uint8_t* q, float* scales,
                             hipStream_t st) {
   if (rows <= 0) return hipSuccess;
-  if (cols % 128 || ld % 8) return hipErrorInvalidValue;
-  const int cpw = kWave * (src_bf16 ? 8 : 4);
-  const long long work = (long long)rows * ((cols + cpw - 1) / cpw);
-  long long blocks = (work + 3) / 4;
-  if (blocks > 8192) blocks = 8192;
-  if (src_bf16)
-    quant_fp8_kernel<true><<<(unsigned)blocks, kQuantThreads, 0, st>>>(src, rows, cols, ld, q, scales);
-  else
-    quant_fp8_kernel<false><<<(unsigned)blocks, kQuantThreads, 0, st>>>(src, rows, cols, ld, q, scales);
-  return hipGetLastError();
+  const QuantSeg s0 = {src, rows, cols, ld, q, scales};
+  const QuantSeg none = {nullptr, 0, 128, 128, nullptr, nullptr};
+  return launch_quant_fp8_segments(s0, none, src_bf16, st);
 }
 
 }  // namespace afd
