@@ -138,6 +138,8 @@ def _check_exact(T, H, E, k, dtype="bf16", seed=0):
     (3, 128, 8, 2, "bf16"),
     (45, 384, 20, 4, "bf16"),
     (130, 1024, 128, 8, "bf16"),
+    (100, 128, 16, 2, "bf16"),      # one 128-deep stage: the second reduction half is empty
+    (200, 384, 40, 4, "bf16"),      # three stages: halves of 2 and 1
     (4096, 7168, 256, 8, "bf16"),   # the fp8 layer's router shape
     (64, 256, 8, 2, "f32"),
 ])
