@@ -61,6 +61,9 @@ def parse():
                     help="one JSON line per workload: the batch as one call vs split in two micro-batches, "
                          "serial or with the second's routing on a second stream under the first's forward; "
                          "not the benchmark line")
+    ap.add_argument("--batch-sweep", action="store_true",
+                    help="the starved-decode layer shape (Qwen3-235B-A22B-like) in bf16 and fp8 at batch sizes "
+                         "6..1580: tokens/s, matrix-core utilisation (MFU) and HBM fraction per batch size")
     ap.add_argument("--router-proj", action="store_true",
                     help="one JSON line per workload shape: the router projection of afd_ffn_route_hidden "
                          "(logits = x W_r^T + bias) timed alone, with its roofline; not the benchmark line")
@@ -266,6 +269,23 @@ def sweep(args, torch):
         torch.cuda.empty_cache()
 
 
+BATCH_SWEEP_T = (6, 25, 100, 197, 395, 788, 1580)
+
+
+def batch_sweep(args, torch):
+    """One JSON line per (dtype, T): the starved-decode layer's shape at decode batch sizes
+    from 6 to 1580 tokens (one attention instance's batch up to four aggregated), with its
+    utilisation of the dense matrix-core peak and of HBM."""
+    base = workloads.STARVED_DECODE
+    for dt in ("bf16", "fp8"):
+        for T in BATCH_SWEEP_T:
+            w = dataclasses.replace(base, T=T, dtype=dt, name=f"decode_layer_{dt}_T{T}_H4096_M1536_E128_k8")
+            steps = args.steps if T <= 64 else max(3, min(args.steps, 50))
+            r = run_workload(w, steps, min(args.warmup, 5), min(args.batches, 8), args.gemm, torch)
+            print(json.dumps(r), flush=True)
+            torch.cuda.empty_cache()
+
+
 def router_proj(args, torch):
     """Time the router projection (the first kernel of afd_ffn_route_hidden) on each
     workload's (T, H, E) with seeded synthetic x, gate vectors ~ N(0, 1/H) and bias.
@@ -412,6 +432,10 @@ def main():
     if args.router_proj:
         torch.cuda.set_device(0)
         router_proj(args, torch)
+        return
+    if args.batch_sweep:
+        torch.cuda.set_device(0)
+        batch_sweep(args, torch)
         return
     if args.ubatches:
         torch.cuda.set_device(0)
