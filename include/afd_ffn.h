@@ -36,7 +36,9 @@
  *
  * Memory.  Every pointer argument is a device pointer (HIP, same device as the
  * handle), except `cfg`, `out` and the route struct itself, which are host
- * pointers.  Row-major layouts throughout.  The caller owns all buffers it passes;
+ * pointers.  Row-major layouts throughout.  Alignment (checked: AFD_EINVAL): the
+ * weights, x, y, w_router, the fp8 codes xq and the quantiser's source 16 bytes, the
+ * quantiser's codes 8 bytes, every other buffer 4 bytes.  The caller owns all buffers it passes;
  * the library never frees them.  afd_ffn_create copies the weights into a layout
  * of its own (tiles ordered for the matrix cores) and owns that copy and a
  * workspace sized from max_tokens until afd_ffn_destroy; the caller's weight

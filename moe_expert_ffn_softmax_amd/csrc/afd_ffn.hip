@@ -42,12 +42,19 @@ int check_config(const afd_ffn_config* c) {
   return AFD_OK;
 }
 
+// Is a non-null pointer off an `a`-byte boundary?  Buffers the kernels read or write
+// in 16-byte vectors must be 16-byte aligned, the others 4-byte aligned.
+bool misaligned(const void* p, size_t a) { return p && reinterpret_cast<uintptr_t>(p) % a != 0; }
+
 int check_route(const afd_ffn* h, const afd_route* r, int32_t T) {
   if (!h) return fail(AFD_EINVAL, "handle is NULL");
   if (!r) return fail(AFD_EINVAL, "route is NULL");
   if (T < 0 || T > h->cfg.max_tokens) return fail(AFD_EINVAL, "T=%d not in [0, max_tokens=%d]", T, h->cfg.max_tokens);
   if (!r->topk_ids || !r->topk_gates || !r->expert_counts || !r->expert_offsets || !r->sorted_pair || !r->pair_pos)
     return fail(AFD_EINVAL, "a route buffer is NULL");
+  if (misaligned(r->topk_ids, 4) || misaligned(r->topk_gates, 4) || misaligned(r->expert_counts, 4) ||
+      misaligned(r->expert_offsets, 4) || misaligned(r->sorted_pair, 4) || misaligned(r->pair_pos, 4))
+    return fail(AFD_EINVAL, "route buffers must be 4-byte aligned");
   return AFD_OK;
 }
 
@@ -198,6 +205,8 @@ extern "C" int afd_ffn_quantize_fp8(const void* src, int32_t rows, int32_t cols,
   if (src_dtype != AFD_F32 && src_dtype != AFD_BF16) return fail(AFD_EINVAL, "source dtype must be fp32 or bf16");
   if (rows == 0) return AFD_OK;
   if (!src || !codes || !scales) return fail(AFD_EINVAL, "a buffer is NULL");
+  if (misaligned(src, 16) || misaligned(codes, 8) || misaligned(scales, 4))
+    return fail(AFD_EINVAL, "src must be 16-byte aligned, codes 8-byte and scales 4-byte aligned");
   hipError_t e = afd::launch_quant_fp8(src, rows, cols, cols, src_dtype == AFD_BF16, codes, scales,
                                        static_cast<hipStream_t>(stream));
   return e == hipSuccess ? AFD_OK : hip_fail(e, "quantisation launch");
@@ -233,6 +242,10 @@ extern "C" int afd_ffn_create(const afd_ffn_config* cfg, const void* w_gate_up, 
     return fail(AFD_EINVAL, "shared scales given without shared_inter");
   if (cfg->shared_inter > 0 && (!ws_gate_up || !ws_down)) return fail(AFD_EINVAL, "shared expert weights are NULL");
   if (cfg->shared_inter == 0 && (ws_gate_up || ws_down)) return fail(AFD_EINVAL, "shared weights given without shared_inter");
+  if (misaligned(w_gate_up, 16) || misaligned(w_down, 16) || misaligned(ws_gate_up, 16) || misaligned(ws_down, 16))
+    return fail(AFD_EINVAL, "weights must be 16-byte aligned");
+  if (misaligned(s_gate_up, 4) || misaligned(s_down, 4) || misaligned(ss_gate_up, 4) || misaligned(ss_down, 4))
+    return fail(AFD_EINVAL, "block scales must be 4-byte aligned");
   *out = nullptr;
 
   afd_ffn* h = new (std::nothrow) afd_ffn();
@@ -404,6 +417,7 @@ extern "C" int afd_ffn_route(afd_ffn_t h, const float* logits, int32_t T, const 
   int rc = check_route(h, r, T);
   if (rc) return rc;
   if (!logits) return fail(AFD_EINVAL, "logits is NULL");
+  if (misaligned(logits, 4)) return fail(AFD_EINVAL, "logits must be 4-byte aligned");
   if (T == 0) return AFD_OK;
   return route_checked(h, logits, nullptr, T, r, static_cast<hipStream_t>(stream));
 }
@@ -413,6 +427,7 @@ extern "C" int afd_ffn_route_select_bias(afd_ffn_t h, const float* scores, const
   int rc = check_route(h, r, T);
   if (rc) return rc;
   if (!scores || !bias) return fail(AFD_EINVAL, "scores or bias is NULL");
+  if (misaligned(scores, 4) || misaligned(bias, 4)) return fail(AFD_EINVAL, "scores and bias must be 4-byte aligned");
   if (T == 0) return AFD_OK;
   return route_checked(h, scores, bias, T, r, static_cast<hipStream_t>(stream));
 }
@@ -422,6 +437,8 @@ extern "C" int afd_ffn_route_hidden(afd_ffn_t h, const void* x, const void* w_ro
   int rc = check_route(h, r, T);
   if (rc) return rc;
   if (!x || !w_router || !logits) return fail(AFD_EINVAL, "x, w_router or logits is NULL");
+  if (misaligned(x, 16) || misaligned(w_router, 16)) return fail(AFD_EINVAL, "x and w_router must be 16-byte aligned");
+  if (misaligned(bias, 4) || misaligned(logits, 4)) return fail(AFD_EINVAL, "bias and logits must be 4-byte aligned");
   if (T == 0) return AFD_OK;
   {
     const afd_ffn_config& c = h->cfg;
@@ -567,6 +584,7 @@ extern "C" int afd_ffn_forward(afd_ffn_t h, const void* x, int32_t T, const afd_
   int rc = check_route(h, r, T);
   if (rc) return rc;
   if (!x || !y) return fail(AFD_EINVAL, "x or y is NULL");
+  if (misaligned(x, 16) || misaligned(y, 16)) return fail(AFD_EINVAL, "x and y must be 16-byte aligned");
   if (T == 0) return AFD_OK;
   const size_t rowb = (size_t)h->cfg.hidden * (h->cfg.dtype == AFD_F32 ? 4 : 2);
   if (overlaps(x, (size_t)T * rowb, y, (size_t)T * rowb)) return fail(AFD_EINVAL, "x and y overlap");
@@ -579,6 +597,8 @@ extern "C" int afd_ffn_forward_fp8_input(afd_ffn_t h, const uint8_t* xq, const f
   if (rc) return rc;
   if (h->cfg.dtype != AFD_FP8_E4M3) return fail(AFD_EUNSUPPORTED, "pre-quantised input needs an fp8 layer");
   if (!xq || !xs || !y) return fail(AFD_EINVAL, "xq, xs or y is NULL");
+  if (misaligned(xq, 16) || misaligned(y, 16) || misaligned(xs, 4))
+    return fail(AFD_EINVAL, "xq and y must be 16-byte aligned, xs 4-byte aligned");
   if (T == 0) return AFD_OK;
   const size_t H = h->cfg.hidden, yb = (size_t)T * H * 2, qb = (size_t)T * H, sb = (size_t)T * (H / 128) * 4;
   if (overlaps(xq, qb, y, yb) || overlaps(xs, sb, y, yb) || overlaps(xq, qb, xs, sb))

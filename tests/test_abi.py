@@ -87,12 +87,24 @@ def test_create_rejects_bad_pointers():
                               ctypes.byref(h)) == _ffi.AFD_EINVAL          # fp8 shared without scales
 
 
+def test_create_rejects_misaligned_weights():
+    lib = _ffi.load()
+    h = ctypes.c_void_p()
+    cfg = _cfg()
+    assert lib.afd_ffn_create(ctypes.byref(cfg), 0x10002, 0x20000, None, None, None, None, None, None, None,
+                              ctypes.byref(h)) == _ffi.AFD_EINVAL
+    assert "aligned" in _ffi.afd_ffn_last_error()
+    assert h.value is None
+
+
 def test_quantize_rejects_bad_arguments():
     lib = _ffi.load()
     assert lib.afd_ffn_quantize_fp8(1, 4, 100, _ffi.AFD_BF16, 1, 1, None) == _ffi.AFD_EINVAL   # cols % 128
     assert lib.afd_ffn_quantize_fp8(1, 4, 128, _ffi.AFD_FP8_E4M3, 1, 1, None) == _ffi.AFD_EINVAL
     assert lib.afd_ffn_quantize_fp8(None, 4, 128, _ffi.AFD_BF16, 1, 1, None) == _ffi.AFD_EINVAL
     assert lib.afd_ffn_quantize_fp8(None, 0, 128, _ffi.AFD_BF16, None, None, None) == _ffi.AFD_OK  # empty
+    assert lib.afd_ffn_quantize_fp8(0x10008, 4, 128, _ffi.AFD_BF16, 0x20000, 0x30000, None) == _ffi.AFD_EINVAL
+    assert "aligned" in _ffi.afd_ffn_last_error()
 
 
 def test_route_and_forward_reject_null_handle():

@@ -426,6 +426,30 @@ def test_route_bytes_matches_the_route_buffers():
     layer.close()
 
 
+def test_misaligned_buffers_are_rejected():
+    """Views off their required boundary fail with AFD_EINVAL before any work is queued."""
+    from moe_expert_ffn_softmax_amd import AfdError, afd_ffn_forward, afd_ffn_route
+    w = small("aligned", T=8, E=8, k=2)
+    weights = workloads.make_weights(w, device="cuda")
+    x, logits = workloads.make_activations(w, device="cuda")
+    layer = make_layer(w, weights)
+    rb = layer.new_route()
+    layer.route(logits, w.T, rb)
+    buf = torch.zeros(w.T * w.H + 8, dtype=torch.bfloat16, device="cuda")
+    x_off = buf[1:1 + w.T * w.H]            # 2 bytes off a 16-byte boundary
+    y = torch.empty((w.T, w.H), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(AfdError):
+        afd_ffn_forward(layer.handle, x_off, w.T, rb.c, y)
+    lg = torch.zeros(w.T * w.E + 1, dtype=torch.uint8, device="cuda")
+    with pytest.raises(AfdError):
+        afd_ffn_route(layer.handle, lg[1:], w.T, rb.c)  # logits 1 byte off
+    # the aligned call still works after the rejected ones
+    layer.forward(x, w.T, rb, y)
+    torch.cuda.synchronize()
+    assert torch.isfinite(y.float()).all()
+    layer.close()
+
+
 def test_zero_tokens_is_a_no_op():
     w = small("empty", T=8)
     weights = workloads.make_weights(w, device="cuda")
