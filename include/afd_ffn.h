@@ -38,7 +38,9 @@
  * handle), except `cfg`, `out` and the route struct itself, which are host
  * pointers.  Row-major layouts throughout.  Alignment (checked: AFD_EINVAL): the
  * weights, x, y, w_router, the fp8 codes xq and the quantiser's source 16 bytes, the
- * quantiser's codes 8 bytes, every other buffer 4 bytes.  The caller owns all buffers it passes;
+ * quantiser's codes 8 bytes, every other buffer 4 bytes.  Buffers a call writes must
+ * not overlap the ones it reads or the route buffers (checked: AFD_EINVAL), nor may the
+ * route buffers overlap each other.  The caller owns all buffers it passes;
  * the library never frees them.  afd_ffn_create copies the weights into a layout
  * of its own (tiles ordered for the matrix cores) and owns that copy and a
  * workspace sized from max_tokens until afd_ffn_destroy; the caller's weight

@@ -46,6 +46,33 @@ int check_config(const afd_ffn_config* c) {
 // in 16-byte vectors must be 16-byte aligned, the others 4-byte aligned.
 bool misaligned(const void* p, size_t a) { return p && reinterpret_cast<uintptr_t>(p) % a != 0; }
 
+
+// Do the byte ranges [a, a + na) and [b, b + nb) intersect?
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return na && nb && x < y + nb && y < x + na;
+}
+
+// Byte ranges of the route buffers for T tokens: ids, gates, sorted_pair, pair_pos
+// [T * k], counts [E], offsets [E + 1].
+struct RouteRanges {
+  const void* p[6];
+  size_t n[6];
+};
+RouteRanges route_ranges(const afd_ffn* h, const afd_route* r, int32_t T) {
+  const size_t P = (size_t)T * h->cfg.top_k * 4, E = (size_t)h->cfg.num_experts * 4;
+  return {{r->topk_ids, r->topk_gates, r->sorted_pair, r->pair_pos, r->expert_counts, r->expert_offsets},
+          {P, P, P, P, E, E + 4}};
+}
+
+// Does [p, p + n) intersect any route buffer?
+bool overlaps_route(const void* p, size_t n, const afd_ffn* h, const afd_route* r, int32_t T) {
+  const RouteRanges rr = route_ranges(h, r, T);
+  for (int i = 0; i < 6; ++i)
+    if (overlaps(p, n, rr.p[i], rr.n[i])) return true;
+  return false;
+}
+
 int check_route(const afd_ffn* h, const afd_route* r, int32_t T) {
   if (!h) return fail(AFD_EINVAL, "handle is NULL");
   if (!r) return fail(AFD_EINVAL, "route is NULL");
@@ -55,13 +82,13 @@ int check_route(const afd_ffn* h, const afd_route* r, int32_t T) {
   if (misaligned(r->topk_ids, 4) || misaligned(r->topk_gates, 4) || misaligned(r->expert_counts, 4) ||
       misaligned(r->expert_offsets, 4) || misaligned(r->sorted_pair, 4) || misaligned(r->pair_pos, 4))
     return fail(AFD_EINVAL, "route buffers must be 4-byte aligned");
+  if (T > 0) {
+    const RouteRanges rr = route_ranges(h, r, T);
+    for (int i = 0; i < 6; ++i)
+      for (int j = i + 1; j < 6; ++j)
+        if (overlaps(rr.p[i], rr.n[i], rr.p[j], rr.n[j])) return fail(AFD_EINVAL, "route buffers overlap each other");
+  }
   return AFD_OK;
-}
-
-// Do the byte ranges [a, a + na) and [b, b + nb) intersect?
-bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
-  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
-  return na && nb && x < y + nb && y < x + na;
 }
 
 void release(afd_ffn* h) {
@@ -419,6 +446,8 @@ extern "C" int afd_ffn_route(afd_ffn_t h, const float* logits, int32_t T, const 
   if (!logits) return fail(AFD_EINVAL, "logits is NULL");
   if (misaligned(logits, 4)) return fail(AFD_EINVAL, "logits must be 4-byte aligned");
   if (T == 0) return AFD_OK;
+  if (overlaps_route(logits, (size_t)T * h->cfg.num_experts * 4, h, r, T))
+    return fail(AFD_EINVAL, "logits overlap a route buffer");
   return route_checked(h, logits, nullptr, T, r, static_cast<hipStream_t>(stream));
 }
 
@@ -429,6 +458,9 @@ extern "C" int afd_ffn_route_select_bias(afd_ffn_t h, const float* scores, const
   if (!scores || !bias) return fail(AFD_EINVAL, "scores or bias is NULL");
   if (misaligned(scores, 4) || misaligned(bias, 4)) return fail(AFD_EINVAL, "scores and bias must be 4-byte aligned");
   if (T == 0) return AFD_OK;
+  if (overlaps_route(scores, (size_t)T * h->cfg.num_experts * 4, h, r, T) ||
+      overlaps_route(bias, (size_t)h->cfg.num_experts * 4, h, r, T))
+    return fail(AFD_EINVAL, "scores or bias overlap a route buffer");
   return route_checked(h, scores, bias, T, r, static_cast<hipStream_t>(stream));
 }
 
@@ -447,6 +479,7 @@ extern "C" int afd_ffn_route_hidden(afd_ffn_t h, const void* x, const void* w_ro
     if (overlaps(logits, lb, x, (size_t)T * c.hidden * a) ||
         overlaps(logits, lb, w_router, (size_t)c.num_experts * c.hidden * a))
       return fail(AFD_EINVAL, "logits overlaps x or w_router");
+    if (overlaps_route(logits, lb, h, r, T)) return fail(AFD_EINVAL, "logits overlap a route buffer");
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
   const afd_ffn_config& c = h->cfg;
@@ -588,6 +621,7 @@ extern "C" int afd_ffn_forward(afd_ffn_t h, const void* x, int32_t T, const afd_
   if (T == 0) return AFD_OK;
   const size_t rowb = (size_t)h->cfg.hidden * (h->cfg.dtype == AFD_F32 ? 4 : 2);
   if (overlaps(x, (size_t)T * rowb, y, (size_t)T * rowb)) return fail(AFD_EINVAL, "x and y overlap");
+  if (overlaps_route(y, (size_t)T * rowb, h, r, T)) return fail(AFD_EINVAL, "y overlaps a route buffer");
   return forward_checked(h, x, nullptr, nullptr, T, r, y, static_cast<hipStream_t>(stream));
 }
 
@@ -603,6 +637,7 @@ extern "C" int afd_ffn_forward_fp8_input(afd_ffn_t h, const uint8_t* xq, const f
   const size_t H = h->cfg.hidden, yb = (size_t)T * H * 2, qb = (size_t)T * H, sb = (size_t)T * (H / 128) * 4;
   if (overlaps(xq, qb, y, yb) || overlaps(xs, sb, y, yb) || overlaps(xq, qb, xs, sb))
     return fail(AFD_EINVAL, "xq, xs and y overlap");
+  if (overlaps_route(y, yb, h, r, T)) return fail(AFD_EINVAL, "y overlaps a route buffer");
   return forward_checked(h, nullptr, xq, xs, T, r, y, static_cast<hipStream_t>(stream));
 }
 

@@ -450,6 +450,41 @@ def test_misaligned_buffers_are_rejected():
     layer.close()
 
 
+def test_route_buffer_overlaps_are_rejected():
+    """Inputs or outputs aliasing the route buffers, or route buffers aliasing each
+    other, fail with AFD_EINVAL before any work is queued."""
+    from moe_expert_ffn_softmax_amd import AfdError, afd_ffn_forward, afd_ffn_route, afd_route
+    w = small("route_alias", T=8, E=8, k=2)
+    weights = workloads.make_weights(w, device="cuda")
+    x, logits = workloads.make_activations(w, device="cuda")
+    layer = make_layer(w, weights)
+    rb = layer.new_route()
+    P = w.T * w.k
+    # logits whose storage holds the route's expert ids
+    big = torch.zeros(w.T * w.E + 4 * P + 64, dtype=torch.int32, device="cuda")
+    alias = afd_route(big.data_ptr(), rb.topk_gates.data_ptr(), rb.expert_counts.data_ptr(),
+                      rb.expert_offsets.data_ptr(), rb.sorted_pair.data_ptr(), rb.pair_pos.data_ptr())
+    with pytest.raises(AfdError):
+        afd_ffn_route(layer.handle, big, w.T, alias)
+    # two route buffers at one address
+    twin = afd_route(rb.topk_ids.data_ptr(), rb.topk_ids.data_ptr(), rb.expert_counts.data_ptr(),
+                     rb.expert_offsets.data_ptr(), rb.sorted_pair.data_ptr(), rb.pair_pos.data_ptr())
+    with pytest.raises(AfdError):
+        afd_ffn_route(layer.handle, logits, w.T, twin)
+    # y on top of the permutation the combine reads
+    layer.route(logits, w.T, rb)
+    yb = torch.zeros(w.T * w.H * 2 + 4 * P, dtype=torch.uint8, device="cuda")
+    yalias = afd_route(rb.topk_ids.data_ptr(), rb.topk_gates.data_ptr(), rb.expert_counts.data_ptr(),
+                       rb.expert_offsets.data_ptr(), yb.data_ptr() + 64, rb.pair_pos.data_ptr())
+    with pytest.raises(AfdError):
+        afd_ffn_forward(layer.handle, x, w.T, yalias, yb)
+    y = torch.empty((w.T, w.H), dtype=torch.bfloat16, device="cuda")
+    layer.forward(x, w.T, rb, y)  # separate buffers still work
+    torch.cuda.synchronize()
+    assert torch.isfinite(y.float()).all()
+    layer.close()
+
+
 def test_zero_tokens_is_a_no_op():
     w = small("empty", T=8)
     weights = workloads.make_weights(w, device="cuda")
