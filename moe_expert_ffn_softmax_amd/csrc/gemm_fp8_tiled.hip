@@ -85,6 +85,10 @@ __device__ __forceinline__ i32x8 f8_load32(const uint8_t* p) {
 #endif
 constexpr int kF8MinBlocks = AFD_FP8_TILED_MIN_BLOCKS;  // workgroups per CU the registers must allow
 
+// SiLU with the hardware reciprocal (one rounding more than z / (1 + e^-z)); h is
+// quantised to e4m3 right after, whose step is 2^-3 of the value.
+__device__ __forceinline__ float silu_rcp(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
+
 template <bool SWIGLU>
 __global__ void __launch_bounds__(kF8Threads, kF8MinBlocks) gemm_fp8_tiled_kernel(GroupedGemm g) {
   __shared__ int prefix[kMaxSegments + 1];
@@ -321,7 +325,7 @@ __global__ void __launch_bounds__(kF8Threads, kF8MinBlocks) gemm_fp8_tiled_kerne
         for (int j = 0; j < kF8GroupsPerWave; ++j)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            hv[rb][j][i] = silu(acc[rb][2 * j][i]) * acc[rb][2 * j + 1][i];
+            hv[rb][j][i] = silu_rcp(acc[rb][2 * j][i]) * acc[rb][2 * j + 1][i];
             m = fmaxf(m, fabsf(hv[rb][j][i]));
           }
         m = fmaxf(m, __shfl_xor(m, 16, kWave));
@@ -339,12 +343,13 @@ __global__ void __launch_bounds__(kF8Threads, kF8MinBlocks) gemm_fp8_tiled_kerne
 #pragma unroll
         for (int v = 1; v < kF8Waves; ++v) amax = fmaxf(amax, qamax[v][t]);
         const float sc = amax > 0.f ? amax / 448.f : 1.f;
+        const float inv = 1.f / sc;  // one division per token group; codes = e4m3(v * (1 / scale))
         if (t < it.nrows) {
           const size_t row = (size_t)(it.row0 + t);
 #pragma unroll
           for (int j = 0; j < kF8GroupsPerWave; ++j)
             *reinterpret_cast<uint32_t*>(q + row * ldo + (group0 + j) * 16 + n0) =
-                e4m3_pack4(hv[rb][j][0] / sc, hv[rb][j][1] / sc, hv[rb][j][2] / sc, hv[rb][j][3] / sc);
+                e4m3_pack4(hv[rb][j][0] * inv, hv[rb][j][1] * inv, hv[rb][j][2] * inv, hv[rb][j][3] * inv);
           if (w == 0 && lane < 16) qscale[row * qgroups + it.group / 8] = sc;
         }
       }
