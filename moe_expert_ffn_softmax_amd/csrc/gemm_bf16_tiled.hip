@@ -94,6 +94,10 @@ constexpr int kTiledMinBlocks = AFD_TILED_MIN_BLOCKS;  // workgroups per CU the 
 
 __device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// SiLU with the hardware reciprocal (one rounding more than z / (1 + e^-z)); h is
+// rounded to bf16 right after.
+__device__ __forceinline__ float silu_rcp(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
+
 // Addressing of one work item for one wave: the rows it stages and the weight streams
 // of its groups.  Item-level values are wave-uniform (scalar registers); per lane
 // there are only 32-bit offsets.
@@ -329,7 +333,7 @@ __global__ void __launch_bounds__(kTiledThreads, kTiledMinBlocks) gemm_bf16_tile
               __bf16* o = out + (size_t)(cur.row0 + row) * ldo + cur.group0 * 16 + col;
 #pragma unroll
               for (int p = 0; p < kTiledGroupsPerWave / 2; ++p)
-                o[p * 32] = f32_to_bf16(silu(acc[rb][2 * p][i]) * acc[rb][2 * p + 1][i]);
+                o[p * 32] = f32_to_bf16(silu_rcp(acc[rb][2 * p][i]) * acc[rb][2 * p + 1][i]);
             }
           }
       } else {
