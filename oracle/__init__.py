@@ -16,6 +16,10 @@ Function-by-function pins (tests/test_oracle.py):
   router_scores -- a hand-computed integer example; one-hot gate vectors pick x's
                 columns; exact integer sums against brute force; bias shift invariance
                 of the routing and a dominant bias forcing an expert.
+  route_capacity -- hand-traced fixtures (tests/golden/capacity_cases.txt); unlimited
+                capacity reduces to top-1 routing; zero capacity drops every token;
+                count bounds of the preference and fallback rules; a drop only once
+                every expert holds 1.5x its limit; numpy stable argsort of assign.
   permute    -- numpy stable argsort of the flattened ids; bijection; count sums.
   layer      -- numpy float64 matmuls for one expert; a diagonal-weight closed form;
                 the k = E dense mixture; token-order equivariance; MAC count 3*H*M per
@@ -74,6 +78,9 @@ def _load():
         lib.afdo_route_select_bias.restype = None
         lib.afdo_router_scores.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, P, P]
         lib.afdo_router_scores.restype = None
+        lib.afdo_route_capacity.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, ctypes.c_int32,
+                                            ctypes.c_int, P, P, P, P, P, P]
+        lib.afdo_route_capacity.restype = None
         lib.afdo_permute.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P, P, P, P]
         lib.afdo_permute.restype = None
         lib.afdo_layer.argtypes = [ctypes.POINTER(_Problem), ctypes.c_int, P, P, P, P, P,
@@ -135,6 +142,33 @@ def router_scores(x: np.ndarray, w: np.ndarray, bias: Optional[np.ndarray] = Non
     out = np.zeros((T, E), np.float64)
     _load().afdo_router_scores(T, E, H, _p(x), _p(w), None if b is None else _p(b), _p(out))
     return out
+
+
+def route_capacity(ids: np.ndarray, gates: np.ndarray, E: int, limits: np.ndarray, base: int,
+                   adaptive: bool = True):
+    """The adaptive token dropper for one batch of preference lists ids [T,k] int32 with
+    fp32 gates [T,k].  Returns assign [T] (expert or -1), weight [T] fp32, counts [E],
+    offsets [E+1], sorted_token [n routed] and the updated limits [E] (all int32 but
+    weight); the input limits are not modified."""
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    gates = np.ascontiguousarray(gates, dtype=np.float32)
+    T, k = ids.shape
+    if gates.shape != (T, k):
+        raise ValueError("gates must match ids")
+    if ids.size and (ids.min() < 0 or ids.max() >= E):
+        raise ValueError("expert id out of range")
+    lim = np.array(limits, dtype=np.int32, copy=True)
+    if lim.shape != (E,):
+        raise ValueError("limits must have shape [E]")
+    assign = np.zeros(T, np.int32)
+    weight = np.zeros(T, np.float32)
+    counts = np.zeros(E, np.int32)
+    offsets = np.zeros(E + 1, np.int32)
+    st = np.zeros(max(T, 1), np.int32)
+    _load().afdo_route_capacity(T, E, k, _p(ids), _p(gates), int(base), int(bool(adaptive)), _p(lim), _p(assign),
+                                _p(weight), _p(counts), _p(offsets), _p(st))
+    return dict(assign=assign, weight=weight, counts=counts, offsets=offsets,
+                sorted_token=st[:int(offsets[E])].copy(), limits=lim)
 
 
 def permute(ids: np.ndarray, E: int):

@@ -12,6 +12,8 @@
  *   route   : per token, softmax over all E fp32 router logits; the k experts with
  *             the largest logits (ties -> lower expert index); gates = their softmax
  *             probabilities renormalised to sum to 1.
+ *   capacity: the adaptive token dropper (one expert per token, least-loaded
+ *             fallback at half gate, drop, adaptive per-expert limits).
  *   permute : counting sort of the T*k (token, slot) pairs by expert: per-expert
  *             counts, exclusive prefix sum, then placement of the pairs in
  *             ascending pair order.
@@ -27,8 +29,8 @@
  *   [AFD-blog]  "大模型推理的内存与计算解耦：AFD 架构解析与性能验证", §3 (the FFN
  *               service: receive activations, gate routing + expert compute, return).
  *   [MoE-eng]   "MoE 大规模分布式推理工程实战：从 All-to-All 通信到动态专家放置",
- *               §4.1 (top-k router with softmax gates), §2.2 (per-destination counts,
- *               prefix-sum offsets, pack).
+ *               §4.1 (top-k router with softmax gates), §4.2 (dynamic token dropping),
+ *               §2.2 (per-destination counts, prefix-sum offsets, pack).
  *   [AFD-news]  omica.com.cn AFD article, §2.1 (6*B*H*M FLOPs, arithmetic intensity),
  *               §3.3 (pre-sorting routed tokens, FP8/BF16 mixed precision).
  * Readings where the pages are open (softmax before/after top-k, tie order, the
@@ -241,6 +243,71 @@ void afdo_permute(int T, int E, int k, const int32_t* ids, int32_t* counts, int3
     sorted_pair[r] = p;
     pair_pos[p] = r;
   }
+  free(cursor);
+}
+
+/* ------------------------------------------------------------------ capacity-aware routing */
+
+/* The adaptive token dropper of the MoE engineering page, §4.2, for one batch.
+ * Per-expert counts start at zero (the batch's own load); limits[E] is the adaptive
+ * capacity state, read and then updated in place.  Tokens are taken in ascending
+ * order.  A token goes to the first expert of its preference list ids[t*k .. t*k+k)
+ * whose count is below its limit, with that slot's gate, and to no other expert.
+ * When every preferred expert is full, the least-loaded expert (smallest count,
+ * lowest index on ties) takes it at half the first slot's gate if its count is below
+ * 1.5 times its limit; otherwise the token is dropped (assign = -1, weight = 0).
+ * After the batch, when `adaptive` is set, each limit grows by 1.2x (truncated) if
+ * the expert's count reached it, else shrinks by 0.9x (truncated, not below `base`)
+ * if the count stayed under half of it; the products are taken in double precision
+ * as the page's code takes them, and a grown limit saturates at INT32_MAX.
+ * counts/offsets/sorted_token list each expert's tokens in token order (the page's
+ * per-expert routed lists). */
+void afdo_route_capacity(int T, int E, int k, const int32_t* ids, const float* gates, int32_t base, int adaptive,
+                         int32_t* limits, int32_t* assign, float* weight, int32_t* counts, int32_t* offsets,
+                         int32_t* sorted_token) {
+  for (int e = 0; e < E; ++e) counts[e] = 0;
+  for (int t = 0; t < T; ++t) {
+    int chosen = -1;
+    float w = 0.0f;
+    for (int j = 0; j < k; ++j) {
+      int e = ids[(size_t)t * k + j];
+      if (counts[e] < limits[e]) {
+        chosen = e;
+        w = gates[(size_t)t * k + j];
+        break;
+      }
+    }
+    if (chosen < 0) {
+      int least = 0;
+      for (int e = 1; e < E; ++e)
+        if (counts[e] < counts[least]) least = e;
+      if ((double)counts[least] < (double)limits[least] * 1.5) {
+        chosen = least;
+        w = (float)((double)gates[(size_t)t * k] * 0.5);
+      }
+    }
+    assign[t] = chosen;
+    weight[t] = chosen < 0 ? 0.0f : w;
+    if (chosen >= 0) counts[chosen] += 1;
+  }
+  if (adaptive) {
+    for (int e = 0; e < E; ++e) {
+      double L = (double)limits[e];
+      if (counts[e] >= limits[e]) {
+        double g = trunc(L * 1.2);
+        limits[e] = g > 2147483647.0 ? 2147483647 : (int32_t)g;
+      } else if ((double)counts[e] < L * 0.5) {
+        int32_t s = (int32_t)trunc(L * 0.9);
+        limits[e] = s > base ? s : base;
+      }
+    }
+  }
+  offsets[0] = 0;
+  for (int e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + counts[e];
+  int32_t* cursor = (int32_t*)malloc(sizeof(int32_t) * (size_t)(E > 0 ? E : 1));
+  for (int e = 0; e < E; ++e) cursor[e] = offsets[e];
+  for (int t = 0; t < T; ++t)
+    if (assign[t] >= 0) sorted_token[cursor[assign[t]]++] = t;
   free(cursor);
 }
 

@@ -451,3 +451,79 @@ def test_fp8_layer_equals_dequantised_reference():
     h = torch.nn.functional.silu(a[:, :M]) * a[:, M:]
     ref = quant_act(h.float()) @ deq_w(*qs[1])
     np.testing.assert_allclose(y, ref.numpy(), rtol=1e-9, atol=1e-9)
+
+
+# ----------------------------------------------------------------------------- capacity-aware routing
+def _capacity_check_lists(r, E):
+    """counts/offsets/sorted_token are a stable counting sort of the routed tokens."""
+    a = r["assign"]
+    routed = np.nonzero(a >= 0)[0]
+    assert np.array_equal(r["counts"], np.bincount(a[routed], minlength=E).astype(np.int32))
+    assert np.array_equal(r["offsets"], np.concatenate([[0], np.cumsum(r["counts"])]).astype(np.int32))
+    order = routed[np.argsort(a[routed], kind="stable")]
+    assert np.array_equal(r["sorted_token"], order.astype(np.int32))
+
+
+def test_capacity_golden_cases():
+    n = 0
+    for name, E, k, base, adaptive, limits, ids, gates, assign, weight, after in _rows("capacity_cases.txt"):
+        E, k = int(E), int(k)
+        ids = np.array([[int(v) for v in tok.split(",")] for tok in ids.split(";")], np.int32)
+        gates = np.array([[float(v) for v in tok.split(",")] for tok in gates.split(";")], np.float32)
+        assert ids.shape == gates.shape and ids.shape[1] == k, name
+        lim = np.array([int(v) for v in limits.split(",")], np.int32)
+        r = oracle.route_capacity(ids, gates, E, lim, int(base), adaptive=bool(int(adaptive)))
+        assert r["assign"].tolist() == [int(v) for v in assign.split(",")], name
+        assert r["weight"].tolist() == [float(v) for v in weight.split(",")], name
+        assert r["limits"].tolist() == [int(v) for v in after.split(",")], name
+        assert lim.tolist() == [int(v) for v in limits.split(",")], name      # input left alone
+        _capacity_check_lists(r, E)
+        n += 1
+    assert n == 7
+
+
+def _prefs(rng, T, E, k):
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    gates = rng.random((T, k)).astype(np.float32)
+    return ids, gates
+
+
+@pytest.mark.parametrize("T,E,k,seed", [(200, 16, 4, 0), (64, 8, 8, 1), (300, 1, 1, 2)])
+def test_capacity_unlimited_is_top1(T, E, k, seed):
+    """With room for every token, each takes its first preference at its first gate."""
+    ids, gates = _prefs(np.random.default_rng(seed), T, E, k)
+    r = oracle.route_capacity(ids, gates, E, np.full(E, T, np.int32), 1)
+    assert np.array_equal(r["assign"], ids[:, 0])
+    assert np.array_equal(r["weight"], gates[:, 0])
+    _capacity_check_lists(r, E)
+
+
+def test_capacity_zero_drops_every_token():
+    ids, gates = _prefs(np.random.default_rng(7), 50, 6, 3)
+    r = oracle.route_capacity(ids, gates, 6, np.zeros(6, np.int32), 0)
+    assert (r["assign"] == -1).all() and (r["weight"] == 0).all() and (r["counts"] == 0).all()
+    assert (r["limits"] == 0).all()
+
+
+@pytest.mark.parametrize("T,E,k,L,seed", [(400, 16, 4, 10, 0), (500, 8, 2, 30, 1), (100, 32, 8, 1, 2),
+                                          (257, 5, 5, 3, 3), (1000, 64, 8, 12, 4)])
+def test_capacity_bounds_and_weights(T, E, k, L, seed):
+    """Preference routing stops at the limit and the fallback at 1.5x it, so no count
+    passes ceil(1.5 L); a token is dropped only when the least-loaded expert, hence every
+    expert, already holds that many; a routed token's weight is the gate of the slot that
+    names its expert, or half its first gate (the fallback)."""
+    ids, gates = _prefs(np.random.default_rng(seed), T, E, k)
+    r = oracle.route_capacity(ids, gates, E, np.full(E, L, np.int32), 1)
+    cap = -(-3 * L // 2)
+    assert r["counts"].max() <= cap
+    dropped = r["assign"] < 0
+    if dropped.any():
+        assert (r["counts"] == cap).all()
+    for t in np.nonzero(~dropped)[0]:
+        e = r["assign"][t]
+        ok = {float(gates[t, 0]) * 0.5}
+        ok |= {float(gates[t, j]) for j in range(k) if ids[t, j] == e}
+        assert float(r["weight"][t]) in ok
+    _capacity_check_lists(r, E)
+    # a tight limit makes both rules fire on these seeds
+    assert (r["weight"] == gates[:, 0] * 0.5).any() or L >= T
