@@ -67,6 +67,9 @@ def parse():
     ap.add_argument("--router-proj", action="store_true",
                     help="one JSON line per workload shape: the router projection of afd_ffn_route_hidden "
                          "(logits = x W_r^T + bias) timed alone, with its roofline; not the benchmark line")
+    ap.add_argument("--capacity", action="store_true",
+                    help="one JSON line per workload shape: capacity-aware routing (afd_ffn_route_capacity) of the "
+                         "routed batch at capacity factors 1.25 and unlimited, timed alone; not the benchmark line")
     return ap.parse_args()
 
 
@@ -337,6 +340,54 @@ def router_proj(args, torch):
         torch.cuda.empty_cache()
 
 
+def capacity(args, torch):
+    """Time capacity-aware routing on each workload's (T, E, k): the preference lists are
+    that batch's routing of seeded logits, every expert's limit is ceil(f T / E) for
+    capacity factor f = 1.25 (the top-1 share with 25% headroom) or T (room everywhere),
+    limits held fixed so every call does the same work.  The walk is sequential by
+    definition (one workgroup); its bytes (lists read, outputs written) are reported with
+    the time, not a roofline."""
+    from moe_expert_ffn_softmax_amd import MoeExpertFFN
+    wls = list(workloads.ORDERED) + workloads.mfma_sweep("bf16") + workloads.mfma_sweep("fp8")
+    for w in wls:
+        if args.only and not any(o in w.name for o in args.only.split(",")):
+            continue
+        M = 128
+        layer = MoeExpertFFN(hidden=128, inter=M, num_experts=w.E, top_k=w.k, max_tokens=w.T, dtype="bf16",
+                             w_gate_up=torch.zeros((w.E, 128, 2 * M), dtype=torch.bfloat16, device="cuda"),
+                             w_down=torch.zeros((w.E, M, 128), dtype=torch.bfloat16, device="cuda"))
+        g = torch.Generator(device="cuda").manual_seed(2000 + w.index)
+        logits = torch.randn((w.T, w.E), generator=g, device="cuda")
+        rb = layer.new_route()
+        layer.route(logits, w.T, rb)
+        ids = rb.topk_ids[: w.T * w.k]
+        gates = rb.topk_gates[: w.T * w.k]
+        out = (torch.empty(w.T, dtype=torch.int32, device="cuda"), torch.empty(w.T, device="cuda"),
+               torch.empty(w.E + 1, dtype=torch.int32, device="cuda"),
+               torch.empty(w.T, dtype=torch.int32, device="cuda"))
+        res = {}
+        for name, f in (("cf1.25", 1.25), ("unlimited", None)):
+            L = w.T if f is None else -(-int(f * w.T * 4) // (4 * w.E))
+            limits = torch.full((w.E,), L, dtype=torch.int32, device="cuda")
+            for _ in range(3):
+                layer.route_capacity(ids, gates, w.T, limits, 1, False, out=out)
+            steps = max(5, min(args.steps, 50))
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(steps):
+                layer.route_capacity(ids, gates, w.T, limits, 1, False, out=out)
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / steps
+            kept = int(out[2][w.E].item())
+            res[name] = {"limit": L, "us": round(us, 2), "kept": kept, "dropped": w.T - kept,
+                         "tokens_per_us": round(w.T / us, 2)}
+        layer.close()
+        nbytes = w.T * w.k * 8 + w.T * 16 + (w.E + 1) * 4
+        print(json.dumps({"workload": w.name, "T": w.T, "E": w.E, "k": w.k, "bytes": nbytes, **res}), flush=True)
+
+
 def ubatches(args, torch):
     """Two micro-batches in flight on one handle (the two-micro-batch overlap of the
     AFD blog's section 4, on the FFN side): micro-batch 2's route runs on a second stream
@@ -432,6 +483,10 @@ def main():
     if args.router_proj:
         torch.cuda.set_device(0)
         router_proj(args, torch)
+        return
+    if args.capacity:
+        torch.cuda.set_device(0)
+        capacity(args, torch)
         return
     if args.batch_sweep:
         torch.cuda.set_device(0)

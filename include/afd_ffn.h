@@ -149,6 +149,33 @@ int afd_ffn_route_select_bias(afd_ffn_t h, const float* scores, const float* bia
 int afd_ffn_route_hidden(afd_ffn_t h, const void* x, const void* w_router, const float* bias, float* logits,
                          int32_t T, const afd_route* r, void* stream);
 
+/* Capacity-aware routing of T tokens: the adaptive token dropper of "MoE 大规模分布式
+ * 推理工程实战：从 All-to-All 通信到动态专家放置" (§4.2), for one batch.
+ *   ids [T, k] int32 (k = top_k; row t is token t's preference list, most preferred
+ *   first, as afd_ffn_route writes r->ids) and gates [T, k] fp32 (r->gates): inputs.
+ *   limits [E] int32, read and written: each expert's capacity; when `adaptive` is
+ *   non-zero it is updated after the batch (count >= limit: trunc(1.2 limit), at most
+ *   INT32_MAX; count < limit / 2: max(base_capacity, trunc(0.9 limit)); else kept).
+ *   Limits are expected to be >= 0; start them at base_capacity for a fresh dropper.
+ * Counts start at zero for the batch.  Tokens are decided in ascending order: token t
+ * goes to the first expert of its list whose count is below its limit, with that
+ * slot's gate, and to no other expert; if every listed expert is full, the least-loaded
+ * expert (smallest count, lowest index on ties) takes it with half of gates[t, 0] when
+ * its count is below 1.5 x its limit; otherwise the token is dropped.  Outputs:
+ *   assign [T] int32: the expert, or -1 when dropped;  weight [T] fp32: the gate it
+ *   carries (0 when dropped);  offsets [E+1] int32: exclusive prefix sum of the
+ *   per-expert counts (offsets[E] = tokens kept);  sorted_token [T] int32: the kept
+ *   tokens grouped by expert, in token order within each (entries from offsets[E]
+ *   on are not written).
+ * All buffers are caller-owned device memory, 4-byte aligned, pairwise disjoint
+ * (checked: AFD_EINVAL).  ids values outside [0, E) are never chosen.  T = 0 still
+ * writes offsets and adapts the limits.  0 <= T <= min(max_tokens, 2^21),
+ * base_capacity >= 0.
+ * The decisions are sequential by definition; one workgroup makes them. */
+int afd_ffn_route_capacity(afd_ffn_t h, const int32_t* ids, const float* gates, int32_t T, int32_t base_capacity,
+                           int32_t adaptive, int32_t* limits, int32_t* assign, float* weight, int32_t* offsets,
+                           int32_t* sorted_token, void* stream);
+
 /* Expert FFN of T routed tokens: x [T, H] (fp32 for AFD_F32, else bf16) and the
  * result of afd_ffn_route for the same T -> y [T, H] (fp32 for AFD_F32, else bf16).
  * x and y must not overlap (checked: AFD_EINVAL). */

@@ -11,7 +11,8 @@ from __future__ import annotations
 from ._ffi import (AFD_BF16, AFD_F32, AFD_FP8_E4M3, AFD_GEMM_AUTO, AFD_GEMM_STREAM,  # noqa: F401
                    AFD_GEMM_TILED, AFD_GEMM_WIDE, STAGES, AfdError, afd_ffn_config, afd_ffn_create, afd_ffn_destroy,
                    afd_ffn_device_bytes, afd_ffn_forward, afd_ffn_forward_fp8_input, afd_ffn_last_error,
-                   afd_ffn_profile_read, afd_ffn_quantize_fp8, afd_ffn_route, afd_ffn_route_hidden,
+                   afd_ffn_profile_read, afd_ffn_quantize_fp8, afd_ffn_route, afd_ffn_route_capacity,
+                   afd_ffn_route_hidden,
                    afd_ffn_route_bytes, afd_ffn_route_select_bias, afd_ffn_set_gemm_kernel, afd_ffn_set_profiling,
                    afd_ffn_strerror, afd_route, load)
 
@@ -90,6 +91,23 @@ class MoeExpertFFN:
         gates = softmax of the chosen experts' unbiased scores."""
         import torch
         afd_ffn_route_select_bias(self.handle, scores, bias, T, rb.c, _stream_handle(torch, stream))
+
+    def route_capacity(self, ids, gates, T: int, limits, base_capacity: int, adaptive: bool = True,
+                       out=None, stream=None):
+        """Capacity-aware routing (adaptive token dropper) of T preference lists ids/gates
+        [T, top_k]; limits [E] int32 is updated in place when adaptive.  Returns (assign [T],
+        weight [T], offsets [E+1], sorted_token [T]), allocated unless given in `out`."""
+        import torch
+        dev = limits.device
+        if out is None:
+            n = max(T, 1)
+            out = (torch.empty(n, dtype=torch.int32, device=dev), torch.empty(n, dtype=torch.float32, device=dev),
+                   torch.empty(self.cfg.num_experts + 1, dtype=torch.int32, device=dev),
+                   torch.empty(n, dtype=torch.int32, device=dev))
+        assign, weight, offsets, sorted_token = out
+        afd_ffn_route_capacity(self.handle, ids, gates, T, base_capacity, adaptive, limits, assign, weight, offsets,
+                               sorted_token, _stream_handle(torch, stream))
+        return assign, weight, offsets, sorted_token
 
     def route_hidden(self, x, w_router, logits, T: int, rb: RouteBuffers, bias=None, stream=None) -> None:
         """Route from hidden states: logits [T, E] (fp32, written) = x w_router^T + bias,

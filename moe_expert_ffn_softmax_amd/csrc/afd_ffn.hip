@@ -9,6 +9,7 @@
 #include <new>
 
 #include "afd_internal.h"
+#include "capacity.h"
 
 namespace {
 
@@ -462,6 +463,33 @@ extern "C" int afd_ffn_route_select_bias(afd_ffn_t h, const float* scores, const
       overlaps_route(bias, (size_t)h->cfg.num_experts * 4, h, r, T))
     return fail(AFD_EINVAL, "scores or bias overlap a route buffer");
   return route_checked(h, scores, bias, T, r, static_cast<hipStream_t>(stream));
+}
+
+extern "C" int afd_ffn_route_capacity(afd_ffn_t h, const int32_t* ids, const float* gates, int32_t T,
+                                      int32_t base_capacity, int32_t adaptive, int32_t* limits, int32_t* assign,
+                                      float* weight, int32_t* offsets, int32_t* sorted_token, void* stream) {
+  if (!h) return fail(AFD_EINVAL, "handle is NULL");
+  const afd_ffn_config& c = h->cfg;
+  if (T < 0 || T > c.max_tokens) return fail(AFD_EINVAL, "T=%d not in [0, max_tokens=%d]", T, c.max_tokens);
+  if (T > afd::kCapMaxTokens) return fail(AFD_EINVAL, "T=%d above %d for capacity routing", T, afd::kCapMaxTokens);
+  if (base_capacity < 0) return fail(AFD_EINVAL, "base_capacity=%d must be >= 0", base_capacity);
+  if (!limits || !offsets) return fail(AFD_EINVAL, "limits or offsets is NULL");
+  if (T > 0 && (!ids || !gates || !assign || !weight || !sorted_token))
+    return fail(AFD_EINVAL, "ids, gates, assign, weight or sorted_token is NULL");
+  const void* bufs[7] = {ids, gates, limits, assign, weight, offsets, sorted_token};
+  const size_t E = c.num_experts, Tk = (size_t)T * c.top_k;
+  const size_t bytes[7] = {Tk * 4, Tk * 4, E * 4, (size_t)T * 4, (size_t)T * 4, (E + 1) * 4, (size_t)T * 4};
+  for (int i = 0; i < 7; ++i)
+    if (misaligned(bufs[i], 4)) return fail(AFD_EINVAL, "capacity routing buffers must be 4-byte aligned");
+  for (int i = 0; i < 7; ++i)
+    for (int j = i + 1; j < 7; ++j)
+      if (bufs[i] && bufs[j] && bytes[i] && bytes[j] && overlaps(bufs[i], bytes[i], bufs[j], bytes[j]))
+        return fail(AFD_EINVAL, "capacity routing buffers overlap");
+  hipError_t e = afd::launch_route_capacity(ids, gates, T, c.num_experts, c.top_k, base_capacity, adaptive ? 1 : 0,
+                                            limits, assign, weight, offsets, sorted_token,
+                                            static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "capacity routing launch");
+  return AFD_OK;
 }
 
 extern "C" int afd_ffn_route_hidden(afd_ffn_t h, const void* x, const void* w_router, const float* bias,
