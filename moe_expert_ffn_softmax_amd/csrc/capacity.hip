@@ -81,8 +81,8 @@ route_capacity_kernel(const int32_t* __restrict__ ids, const float* __restrict__
                       float* __restrict__ weight, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_token) {
   __shared__ int32_t s_cnt[kCapMaxE];
   __shared__ int32_t s_lim[kCapMaxE];
-  __shared__ int32_t s_ids[kCapStageSlots];
-  __shared__ float s_g[kCapStageSlots];
+  __shared__ int32_t s_ids2[2][kCapStageSlots];  // two staging buffers: waves 1-3 fill one
+  __shared__ float s_g2[2][kCapStageSlots];       // while wave 0 decides from the other
   const int tid = threadIdx.x, lane = tid & 63;
   const bool decider = tid < 64;
 
@@ -92,16 +92,26 @@ route_capacity_kernel(const int32_t* __restrict__ ids, const float* __restrict__
   }
   const int per_pass = kCapStageSlots / k;  // k <= 32: at least 128 tokens
   const int nbits = E > 1 ? 32 - __clz(E - 1) : 0;
-  for (int tb = 0; tb < T; tb += per_pass) {
-    const int nt = min(per_pass, T - tb);
-    __syncthreads();  // the previous pass's decisions no longer read the staging buffers
+  const int npass = (T + per_pass - 1) / per_pass;
+  auto stage = [&](int p, int buf, int first, int nthr) {
+    const int tb = p * per_pass, nt = min(per_pass, T - tb);
     const long long s0 = (long long)tb * k;
-    for (int s = tid; s < nt * k; s += kCapThreads) {
-      s_ids[s] = ids[s0 + s];
-      s_g[s] = gates[s0 + s];
+    for (int s = tid - first; s < nt * k; s += nthr) {
+      s_ids2[buf][s] = ids[s0 + s];
+      s_g2[buf][s] = gates[s0 + s];
     }
-    __syncthreads();
-    if (!decider) continue;
+  };
+  if (npass > 0) stage(0, 0, 0, kCapThreads);
+  for (int p = 0; p < npass; ++p) {
+    __syncthreads();  // pass p is staged; the buffer staged next was last read in pass p - 1
+    const int buf = p & 1;
+    if (!decider) {
+      if (p + 1 < npass) stage(p + 1, buf ^ 1, 64, kCapThreads - 64);
+      continue;
+    }
+    const int tb = p * per_pass, nt = min(per_pass, T - tb);
+    const int32_t* s_ids = s_ids2[buf];
+    const float* s_g = s_g2[buf];
     int t = 0;
     while (t < nt) {
       const int i = t + lane;

@@ -527,3 +527,19 @@ def test_capacity_bounds_and_weights(T, E, k, L, seed):
     _capacity_check_lists(r, E)
     # a tight limit makes both rules fire on these seeds
     assert (r["weight"] == gates[:, 0] * 0.5).any() or L >= T
+
+
+def test_capacity_integer_limit_forms():
+    """The GPU kernel updates limits with 64-bit integer forms; they equal the page's
+    truncated float products (taken in double, as the oracle takes them).  An exhaustive
+    run over all 0 <= L < 2^31 found no difference; this re-checks the first 2^22, the
+    last 2^20 and 2^22 random values."""
+    rng = np.random.default_rng(5)
+    L = np.concatenate([np.arange(1 << 22), np.arange((1 << 31) - (1 << 20), 1 << 31),
+                        rng.integers(0, 1 << 31, 1 << 22)]).astype(np.int64)
+    f = L.astype(np.float64)
+    assert np.array_equal(np.trunc(f * 1.2).astype(np.int64), 6 * L // 5)
+    assert np.array_equal(np.trunc(f * 0.9).astype(np.int64), 9 * L // 10)
+    c = rng.integers(0, 1 << 31, L.size).astype(np.int64)
+    assert np.array_equal(c.astype(np.float64) < f * 1.5, 2 * c < 3 * L)
+    assert np.array_equal(c.astype(np.float64) < f * 0.5, 2 * c < L)
