@@ -176,6 +176,21 @@ int afd_ffn_route_capacity(afd_ffn_t h, const int32_t* ids, const float* gates, 
                            int32_t adaptive, int32_t* limits, int32_t* assign, float* weight, int32_t* offsets,
                            int32_t* sorted_token, void* stream);
 
+/* Route of a capacity result, for afd_ffn_forward: the expert FFN of the tokens the
+ * adaptive token dropper of "MoE 大规模分布式推理工程实战：从 All-to-All 通信到动态专家
+ * 放置" (§4.2) kept, each through its one expert, scaled by its weight.
+ *   assign [T], weight [T], offsets [E+1], sorted_token [T]: the outputs of
+ *   afd_ffn_route_capacity for the same T (device memory, 4-byte aligned, not
+ *   overlapping the route buffers; checked: AFD_EINVAL).
+ * Fills every field of *r: slot 0 of token t holds assign[t] and weight[t], slots 1..k-1
+ * hold id -1 and gate 0, counts/offsets are the kept tokens per expert, sorted_pair
+ * lists pair t*k of each kept token in the dropper's order.  afd_ffn_forward on this
+ * route then gives y[t] = weight[t] * FFN_assign[t](x[t]) (+ the shared expert), and
+ * y[t] = the shared expert's output alone (or 0) for a dropped token: the combine skips
+ * slots whose gate is 0.  0 <= T <= max_tokens. */
+int afd_ffn_route_from_capacity(afd_ffn_t h, const int32_t* assign, const float* weight, const int32_t* offsets,
+                                const int32_t* sorted_token, int32_t T, const afd_route* r, void* stream);
+
 /* Expert FFN of T routed tokens: x [T, H] (fp32 for AFD_F32, else bf16) and the
  * result of afd_ffn_route for the same T -> y [T, H] (fp32 for AFD_F32, else bf16).
  * x and y must not overlap (checked: AFD_EINVAL). */

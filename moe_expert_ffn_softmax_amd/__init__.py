@@ -12,6 +12,7 @@ from ._ffi import (AFD_BF16, AFD_F32, AFD_FP8_E4M3, AFD_GEMM_AUTO, AFD_GEMM_STRE
                    AFD_GEMM_TILED, AFD_GEMM_WIDE, STAGES, AfdError, afd_ffn_config, afd_ffn_create, afd_ffn_destroy,
                    afd_ffn_device_bytes, afd_ffn_forward, afd_ffn_forward_fp8_input, afd_ffn_last_error,
                    afd_ffn_profile_read, afd_ffn_quantize_fp8, afd_ffn_route, afd_ffn_route_capacity,
+                   afd_ffn_route_from_capacity,
                    afd_ffn_route_hidden,
                    afd_ffn_route_bytes, afd_ffn_route_select_bias, afd_ffn_set_gemm_kernel, afd_ffn_set_profiling,
                    afd_ffn_strerror, afd_route, load)
@@ -108,6 +109,15 @@ class MoeExpertFFN:
         afd_ffn_route_capacity(self.handle, ids, gates, T, base_capacity, adaptive, limits, assign, weight, offsets,
                                sorted_token, _stream_handle(torch, stream))
         return assign, weight, offsets, sorted_token
+
+    def route_from_capacity(self, cap, T: int, rb: RouteBuffers, stream=None) -> None:
+        """Fill rb from a capacity result cap = (assign, weight, offsets, sorted_token), as
+        returned by route_capacity, so that forward runs each kept token through its one
+        expert with its weight."""
+        import torch
+        assign, weight, offsets, sorted_token = cap
+        afd_ffn_route_from_capacity(self.handle, assign, weight, offsets, sorted_token, T, rb.c,
+                                    _stream_handle(torch, stream))
 
     def route_hidden(self, x, w_router, logits, T: int, rb: RouteBuffers, bias=None, stream=None) -> None:
         """Route from hidden states: logits [T, E] (fp32, written) = x w_router^T + bias,

@@ -56,6 +56,8 @@ def load():
     lib.afd_ffn_route_select_bias.restype = ctypes.c_int
     lib.afd_ffn_route_capacity.argtypes = [V, P, P, I32, I32, I32, P, P, P, P, P, V]
     lib.afd_ffn_route_capacity.restype = ctypes.c_int
+    lib.afd_ffn_route_from_capacity.argtypes = [V, P, P, P, P, I32, ctypes.POINTER(afd_route), V]
+    lib.afd_ffn_route_from_capacity.restype = ctypes.c_int
     lib.afd_ffn_forward.argtypes = [V, P, I32, ctypes.POINTER(afd_route), P, V]
     lib.afd_ffn_forward.restype = ctypes.c_int
     lib.afd_ffn_forward_fp8_input.argtypes = [V, P, P, I32, ctypes.POINTER(afd_route), P, V]
@@ -126,6 +128,12 @@ def afd_ffn_route_capacity(h: int, ids, gates, T: int, base_capacity: int, adapt
     _check(load().afd_ffn_route_capacity(h, _ptr(ids), _ptr(gates), int(T), int(base_capacity), int(bool(adaptive)),
                                          _ptr(limits), _ptr(assign), _ptr(weight), _ptr(offsets),
                                          _ptr(sorted_token), stream))
+
+
+def afd_ffn_route_from_capacity(h: int, assign, weight, offsets, sorted_token, T: int, route: afd_route,
+                                stream=None) -> None:
+    _check(load().afd_ffn_route_from_capacity(h, _ptr(assign), _ptr(weight), _ptr(offsets), _ptr(sorted_token),
+                                              int(T), ctypes.byref(route), stream))
 
 
 def afd_ffn_route_hidden(h: int, x, w_router, bias, logits, T: int, route: afd_route, stream=None) -> None:

@@ -492,6 +492,27 @@ extern "C" int afd_ffn_route_capacity(afd_ffn_t h, const int32_t* ids, const flo
   return AFD_OK;
 }
 
+extern "C" int afd_ffn_route_from_capacity(afd_ffn_t h, const int32_t* assign, const float* weight,
+                                           const int32_t* offsets, const int32_t* sorted_token, int32_t T,
+                                           const afd_route* r, void* stream) {
+  int rc = check_route(h, r, T);
+  if (rc) return rc;
+  if (!offsets) return fail(AFD_EINVAL, "offsets is NULL");
+  if (T > 0 && (!assign || !weight || !sorted_token)) return fail(AFD_EINVAL, "assign, weight or sorted_token is NULL");
+  if (misaligned(assign, 4) || misaligned(weight, 4) || misaligned(offsets, 4) || misaligned(sorted_token, 4))
+    return fail(AFD_EINVAL, "capacity result buffers must be 4-byte aligned");
+  const size_t tb = (size_t)T * 4, ob = ((size_t)h->cfg.num_experts + 1) * 4;
+  if ((assign && overlaps_route(assign, tb, h, r, T)) || (weight && overlaps_route(weight, tb, h, r, T)) ||
+      overlaps_route(offsets, ob, h, r, T) || (sorted_token && overlaps_route(sorted_token, tb, h, r, T)))
+    return fail(AFD_EINVAL, "a capacity result buffer overlaps a route buffer");
+  hipError_t e = afd::launch_route_from_capacity(assign, weight, offsets, sorted_token, T, h->cfg.num_experts,
+                                                 h->cfg.top_k, r->topk_ids, r->topk_gates, r->expert_counts,
+                                                 r->expert_offsets, r->sorted_pair, r->pair_pos,
+                                                 static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "route from capacity launch");
+  return AFD_OK;
+}
+
 extern "C" int afd_ffn_route_hidden(afd_ffn_t h, const void* x, const void* w_router, const float* bias,
                                     float* logits, int32_t T, const afd_route* r, void* stream) {
   int rc = check_route(h, r, T);

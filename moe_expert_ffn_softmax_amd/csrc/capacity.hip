@@ -211,7 +211,52 @@ route_capacity_kernel(const int32_t* __restrict__ ids, const float* __restrict__
   }
 }
 
+// Route of a capacity result for the expert FFN: slot 0 of each token carries its
+// expert and weight, the other slots gate 0 (the combine skips them); a dropped token
+// has gate 0 everywhere.  Unused pair positions point at row 0, which always exists.
+__global__ void route_from_capacity_slots_kernel(const int32_t* __restrict__ assign, const float* __restrict__ weight,
+                                                 const int32_t* __restrict__ cap_offsets, int T, int E, int k,
+                                                 int32_t* __restrict__ ids, float* __restrict__ gates,
+                                                 int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                 int32_t* __restrict__ pair_pos) {
+  const long long p = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (p <= E) {
+    offsets[p] = cap_offsets[p];
+    if (p < E) counts[p] = cap_offsets[p + 1] - cap_offsets[p];
+  }
+  if (p >= (long long)T * k) return;
+  const int t = (int)(p / k), j = (int)(p - (long long)t * k);
+  ids[p] = j == 0 ? assign[t] : -1;
+  gates[p] = j == 0 ? weight[t] : 0.0f;
+  pair_pos[p] = 0;
+}
+
+__global__ void route_from_capacity_rows_kernel(const int32_t* __restrict__ cap_offsets,
+                                                const int32_t* __restrict__ sorted_token, int T, int E, int k,
+                                                int32_t* __restrict__ sorted_pair, int32_t* __restrict__ pair_pos) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= T || r >= cap_offsets[E]) return;
+  const int t = sorted_token[r];
+  if ((unsigned)t >= (unsigned)T) return;
+  sorted_pair[r] = t * k;
+  pair_pos[(size_t)t * k] = r;
+}
+
 }  // namespace
+
+hipError_t launch_route_from_capacity(const int32_t* assign, const float* weight, const int32_t* cap_offsets,
+                                      const int32_t* sorted_token, int T, int E, int k, int32_t* ids, float* gates,
+                                      int32_t* counts, int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos,
+                                      hipStream_t st) {
+  if (E < 1 || k < 1 || T < 0 || (long long)T * k >= (1ll << 31)) return hipErrorInvalidValue;
+  const long long slots = (long long)T * k > E + 1 ? (long long)T * k : E + 1;
+  route_from_capacity_slots_kernel<<<(unsigned)((slots + 255) / 256), 256, 0, st>>>(
+      assign, weight, cap_offsets, T, E, k, ids, gates, counts, offsets, pair_pos);
+  if (T > 0)
+    route_from_capacity_rows_kernel<<<(unsigned)((T + 255) / 256), 256, 0, st>>>(cap_offsets, sorted_token, T, E,
+                                                                                  k, sorted_pair, pair_pos);
+  return hipGetLastError();
+}
 
 hipError_t launch_route_capacity(const int32_t* ids, const float* gates, int T, int E, int k, int32_t base,
                                  int adaptive, int32_t* limits, int32_t* assign, float* weight, int32_t* offsets,

@@ -61,14 +61,15 @@ __global__ void __launch_bounds__(kCombineThreads) combine_kernel(const void* __
   for (int c = blockIdx.y * kCombineThreads + threadIdx.x; c < H / V; c += gridDim.y * kCombineThreads) {
     i32x4 raw[KU];
 #pragma unroll
-    for (int j = 0; j < KU; ++j)
-      if (j < k) raw[j] = load16<NT>(static_cast<const char*>(O) + (size_t)pos_s[j] * row_bytes + 16 * (size_t)c);
+    for (int j = 0; j < KU; ++j)  // a slot with gate 0 adds nothing and is not read
+      if (j < k && g_s[j] != 0.f)
+        raw[j] = load16<NT>(static_cast<const char*>(O) + (size_t)pos_s[j] * row_bytes + 16 * (size_t)c);
     float acc[V];
 #pragma unroll
     for (int i = 0; i < V; ++i) acc[i] = 0.f;
 #pragma unroll
     for (int j = 0; j < KU; ++j) {
-      if (j < k) {
+      if (j < k && g_s[j] != 0.f) {
         const float gj = g_s[j];
         float v[V];
         unpack16<BF16>(raw[j], v);

@@ -268,6 +268,47 @@ def layer(x: np.ndarray, logits: np.ndarray, *, H: int, M: int, E: int, k: int, 
     return ids, gates, y, int(macs.value)
 
 
+def layer_assigned(x: np.ndarray, assign: np.ndarray, weight: np.ndarray, *, H: int, M: int, E: int, dtype: str,
+                   w_gu: Sequence, w_d: Sequence, s_gu: Optional[Sequence] = None,
+                   s_d: Optional[Sequence] = None, Ms: int = 0, ws_gu=None, ws_d=None, ss_gu=None, ss_d=None,
+                   nthreads: int = 0):
+    """Whole layer on a given one-expert-per-token assignment (the capacity-aware
+    dropper's): y[t] = weight[t] * FFN_assign[t](x[t]) (+ the shared expert), with
+    assign -1 for a dropped token.  Returns (y [n,H] f64, macs)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    n = x.shape[0]
+    ids = np.ascontiguousarray(assign, dtype=np.int32).reshape(n, 1).copy()
+    gates = np.ascontiguousarray(weight, dtype=np.float32).astype(np.float64).reshape(n, 1)
+    keep = []
+
+    def arr(seq):
+        ptrs = (ctypes.c_void_p * E)()
+        for e in range(E):
+            a = None if seq is None else seq[e]
+            if a is not None:
+                r = _raw(a)
+                keep.append(r)
+                ptrs[e] = r.ctypes.data
+        return ctypes.cast(ptrs, ctypes.POINTER(ctypes.c_void_p))
+
+    def one(a):
+        if a is None:
+            return None
+        r = _raw(a)
+        keep.append(r)
+        return r.ctypes.data
+
+    pb = _Problem(H, M, E, 1, Ms, _DT[dtype], arr(w_gu), arr(w_d), arr(s_gu), arr(s_d), one(ws_gu), one(ws_d),
+                  one(ss_gu), one(ss_d))
+    y = np.zeros((n, H), np.float64)
+    macs = ctypes.c_int64(0)
+    rc = _load().afdo_layer(ctypes.byref(pb), n, _p(x), None, _p(ids), _p(gates), _p(y), ctypes.byref(macs),
+                            int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle layer failed with code {rc}")
+    return y, int(macs.value)
+
+
 def layer_from_weights(x, logits, wl, weights, nthreads: int = 0, experts_needed=None):
     """Convenience: run `layer` with a workload description `wl` (anything with
     H, M, E, k, Ms, dtype attributes) and a dict of weight tensors as produced by the

@@ -368,16 +368,20 @@ typedef struct {
 
 /* Whole layer for n tokens given by their fp32 activations x [n, H] (bf16 inputs
  * widened exactly) and fp32 logits [n, E].  Writes ids [n, k], gates [n, k] and
- * y [n, H] (double).  *macs receives the number of multiply-adds the expert
+ * y [n, H] (double).  With logits NULL, ids and gates are inputs instead (an
+ * assignment made elsewhere, such as the capacity-aware dropper's); a slot with id -1
+ * contributes nothing.  *macs receives the number of multiply-adds the expert
  * products executed, counted in their loops (the FLOP count is twice that).  nthreads <= 0 uses the OpenMP default. */
 int afdo_layer(const afdo_problem* pb, int n, const float* x, const float* logits, int32_t* ids,
                double* gates, double* y, int64_t* macs, int nthreads) {
   const int H = pb->H, M = pb->M, E = pb->E, k = pb->k, Ms = pb->Ms;
   if (n < 0 || H <= 0 || M <= 0 || E <= 0 || k <= 0 || k > E || Ms < 0) return AFDO_EINVAL;
   if (pb->dtype == AFDO_FP8 && (H % QBLOCK || M % QBLOCK || Ms % QBLOCK)) return AFDO_EINVAL;
-  afdo_route(n, E, k, logits, ids, gates);
+  if (logits) afdo_route(n, E, k, logits, ids, gates);
   for (int p = 0; p < n * k; ++p) {
     int e = ids[p];
+    if (e < 0 && !logits) continue;
+    if (e < 0 || e >= E) return AFDO_EINVAL;
     if (!pb->w_gu[e] || !pb->w_d[e]) return AFDO_EINVAL;
     if (pb->dtype == AFDO_FP8 && (!pb->s_gu[e] || !pb->s_d[e])) return AFDO_EINVAL;
   }
@@ -409,7 +413,9 @@ int afdo_layer(const afdo_problem* pb, int n, const float* x, const float* logit
       if (!ok) continue;
       int t = u / per, j = u % per;
       mat_t gu, dn;
-      if (j < k) {
+      if (j < k && ids[(size_t)t * k + j] < 0) {
+        for (int c = 0; c < H; ++c) outs[(size_t)u * H + c] = 0.0;
+      } else if (j < k) {
         int e = ids[(size_t)t * k + j];
         gu = (mat_t){pb->dtype, pb->w_gu[e], quant ? pb->s_gu[e] : NULL, H, 2 * M};
         dn = (mat_t){pb->dtype, pb->w_d[e], quant ? pb->s_d[e] : NULL, M, H};

@@ -116,6 +116,7 @@ def test_route_and_forward_reject_null_handle():
     assert lib.afd_ffn_route_hidden(None, 1, 1, None, 1, 4, ctypes.byref(r), None) == _ffi.AFD_EINVAL
     assert lib.afd_ffn_route_select_bias(None, 1, 1, 4, ctypes.byref(r), None) == _ffi.AFD_EINVAL
     assert lib.afd_ffn_route_capacity(None, 4, 4, 4, 1, 1, 4, 4, 4, 4, 4, None) == _ffi.AFD_EINVAL
+    assert lib.afd_ffn_route_from_capacity(None, 4, 4, 4, 4, 4, ctypes.byref(r), None) == _ffi.AFD_EINVAL
     assert lib.afd_ffn_destroy(None) == _ffi.AFD_OK
     assert lib.afd_ffn_set_profiling(None, 1) == _ffi.AFD_EINVAL
     assert lib.afd_ffn_set_gemm_kernel(None, 0) == _ffi.AFD_EINVAL

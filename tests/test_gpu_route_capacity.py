@@ -127,3 +127,57 @@ def test_capacity_rejects_bad_arguments():
             afd_ffn_route_capacity(h, *args[:4], True, *args[4:])
     afd_ffn_route_capacity(h, ids, gates, T, 1, True, lim, a, w, off, st)   # the good call still works
     torch.cuda.synchronize()
+
+
+FFN_TOL = {"f32": 1e-4, "bf16": 2e-2, "fp8": 6e-2}
+
+
+@pytest.mark.parametrize("dtype,T,H,M,E,k,Ms,L,kernel", [
+    ("bf16", 200, 256, 256, 16, 4, 0, 9, "stream"),     # some fallbacks at half gate
+    ("bf16", 700, 384, 256, 8, 2, 128, 60, "tiled"),    # drops, shared expert for every token
+    ("fp8", 300, 256, 256, 12, 3, 128, 20, "auto"),
+    ("f32", 150, 128, 128, 6, 2, 0, 12, "auto"),
+    ("bf16", 64, 128, 128, 4, 2, 128, 0, "auto"),       # every token dropped: shared expert only
+])
+def test_forward_on_capacity_route(dtype, T, H, M, E, k, Ms, L, kernel):
+    """Capacity routing, then the expert FFN on its result, against the oracle layer on
+    the oracle dropper's assignment: y[t] = weight[t] FFN_assign[t](x[t]) (+ shared)."""
+    import workloads
+    w = workloads.Workload(f"cap_{dtype}_T{T}", 700 + T, T=T, H=H, M=M, E=E, k=k, Ms=Ms, dtype=dtype)
+    weights = workloads.make_weights(w, device="cuda")
+    x, logits = workloads.make_activations(w, device="cuda")
+    layer = MoeExpertFFN(hidden=H, inter=M, num_experts=E, top_k=k, max_tokens=T, dtype=dtype,
+                         w_gate_up=weights["w_gu"], w_down=weights["w_d"], s_gate_up=weights["s_gu"],
+                         s_down=weights["s_d"], shared_inter=Ms, ws_gate_up=weights["ws_gu"],
+                         ws_down=weights["ws_d"], ss_gate_up=weights["ss_gu"], ss_down=weights["ss_d"])
+    layer.set_gemm_kernel(kernel)
+    ids, gates = oracle.route(logits.cpu().numpy(), k)
+    gates = gates.astype(np.float32)
+    limits = np.full(E, L, np.int32)
+    ref = oracle.route_capacity(ids, gates, E, limits, 1, False)
+    cap = layer.route_capacity(torch.from_numpy(ids).cuda(), torch.from_numpy(gates).cuda(), T,
+                               torch.from_numpy(limits).cuda(), 1, False)
+    rb = layer.new_route()
+    layer.route_from_capacity(cap, T, rb)
+    ydt = torch.float32 if dtype == "f32" else torch.bfloat16
+    y = torch.full((T, H), float("nan"), dtype=ydt, device="cuda")
+    layer.forward(x, T, rb, y)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(cap[0].cpu().numpy()[:T], ref["assign"])
+    kept = int(ref["offsets"][E])
+    np.testing.assert_array_equal(rb.expert_offsets.cpu().numpy(), ref["offsets"])
+    np.testing.assert_array_equal(rb.sorted_pair[:kept].cpu().numpy(), ref["sorted_token"] * k)
+    yref, _ = oracle.layer_assigned(x.float().cpu().numpy(), ref["assign"], ref["weight"], H=H, M=M, E=E,
+                                    dtype=dtype, w_gu=weights["w_gu"], w_d=weights["w_d"], s_gu=weights["s_gu"],
+                                    s_d=weights["s_d"], Ms=Ms, ws_gu=weights["ws_gu"], ws_d=weights["ws_d"],
+                                    ss_gu=weights["ss_gu"], ss_d=weights["ss_d"])
+    yg = y.float().cpu().numpy().astype(np.float64)
+    assert np.isfinite(yg).all()
+    dropped = ref["assign"] < 0
+    if Ms == 0:
+        assert (yg[dropped] == 0).all()
+    scale = max(np.abs(yref).max(), 1e-30)
+    err = np.abs(yg - yref).max()
+    print(f"  kept {kept}/{T}, max|err|/max|ref| = {err / scale:.3e}", flush=True)
+    assert err <= FFN_TOL[dtype] * scale
+    layer.close()

@@ -543,3 +543,49 @@ def test_capacity_integer_limit_forms():
     c = rng.integers(0, 1 << 31, L.size).astype(np.int64)
     assert np.array_equal(c.astype(np.float64) < f * 1.5, 2 * c < 3 * L)
     assert np.array_equal(c.astype(np.float64) < f * 0.5, 2 * c < L)
+
+
+def _small_f32_layer(rng, H=32, M=16, E=4, Ms=0):
+    w_gu = [rng.standard_normal((H, 2 * M)).astype(np.float32) / 4 for _ in range(E)]
+    w_d = [rng.standard_normal((M, H)).astype(np.float32) / 4 for _ in range(E)]
+    ws = (rng.standard_normal((H, 2 * Ms)).astype(np.float32) / 4,
+          rng.standard_normal((Ms, H)).astype(np.float32) / 4) if Ms else (None, None)
+    return w_gu, w_d, ws
+
+
+def test_layer_assigned_reduces_to_top1_layer():
+    """An assignment equal to the k = 1 router's choice at weight 1 is that layer."""
+    rng = np.random.default_rng(21)
+    H, M, E, n = 32, 16, 4, 12
+    w_gu, w_d, _ = _small_f32_layer(rng, H, M, E)
+    x = rng.standard_normal((n, H)).astype(np.float32)
+    logits = rng.standard_normal((n, E)).astype(np.float32)
+    ids, gates, y1, _ = oracle.layer(x, logits, H=H, M=M, E=E, k=1, dtype="f32", w_gu=w_gu, w_d=w_d)
+    assert (gates == 1.0).all()
+    y, macs = oracle.layer_assigned(x, ids[:, 0], np.ones(n, np.float32), H=H, M=M, E=E, dtype="f32",
+                                    w_gu=w_gu, w_d=w_d)
+    assert np.array_equal(y, y1)
+    assert macs == n * 3 * H * M
+    yh, _ = oracle.layer_assigned(x, ids[:, 0], np.full(n, 0.5, np.float32), H=H, M=M, E=E, dtype="f32",
+                                  w_gu=w_gu, w_d=w_d)
+    assert np.array_equal(yh, 0.5 * y1)
+
+
+def test_layer_assigned_dropped_tokens():
+    """A dropped token gets nothing from the routed experts and still gets the shared
+    expert, which alone is a one-expert layer with the shared weights at gate 1."""
+    rng = np.random.default_rng(22)
+    H, M, E, Ms, n = 32, 16, 4, 24, 9
+    w_gu, w_d, (ws_gu, ws_d) = _small_f32_layer(rng, H, M, E, Ms)
+    x = rng.standard_normal((n, H)).astype(np.float32)
+    assign = np.array([2, -1, 0, -1, 3, 1, -1, 2, 0], np.int32)
+    w = rng.random(n).astype(np.float32)
+    y, macs = oracle.layer_assigned(x, assign, w, H=H, M=M, E=E, dtype="f32", w_gu=w_gu, w_d=w_d,
+                                    Ms=Ms, ws_gu=ws_gu, ws_d=ws_d)
+    _, _, ys, _ = oracle.layer(x, np.zeros((n, 1), np.float32), H=H, M=Ms, E=1, k=1, dtype="f32",
+                               w_gu=[ws_gu], w_d=[ws_d])
+    drop = assign < 0
+    assert np.array_equal(y[drop], ys[drop])
+    assert macs == int((~drop).sum()) * 3 * H * M + n * 3 * H * Ms
+    y0, _ = oracle.layer_assigned(x, np.full(n, -1, np.int32), w, H=H, M=M, E=E, dtype="f32", w_gu=w_gu, w_d=w_d)
+    assert (y0 == 0).all()
