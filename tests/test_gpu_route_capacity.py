@@ -181,3 +181,56 @@ def test_forward_on_capacity_route(dtype, T, H, M, E, k, Ms, L, kernel):
     print(f"  kept {kept}/{T}, max|err|/max|ref| = {err / scale:.3e}", flush=True)
     assert err <= FFN_TOL[dtype] * scale
     layer.close()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_capacity_route_and_forward_in_a_graph(dtype):
+    """route -> capacity routing -> route from capacity -> forward captured in one HIP
+    graph: every replay, with eager work and synchronisations in between, reproduces the
+    eager result bit for bit (the capacity calls allocate and clear nothing)."""
+    import workloads
+    T, H, M, E, k, Ms, L = 240, 256, 256, 16, 4, 128 if dtype == "fp8" else 0, 8
+    w = workloads.Workload(f"capgraph_{dtype}", 760, T=T, H=H, M=M, E=E, k=k, Ms=Ms, dtype=dtype)
+    weights = workloads.make_weights(w, device="cuda")
+    x, logits = workloads.make_activations(w, device="cuda")
+    layer = MoeExpertFFN(hidden=H, inter=M, num_experts=E, top_k=k, max_tokens=T, dtype=dtype,
+                         w_gate_up=weights["w_gu"], w_down=weights["w_d"], s_gate_up=weights["s_gu"],
+                         s_down=weights["s_d"], shared_inter=Ms, ws_gate_up=weights["ws_gu"],
+                         ws_down=weights["ws_d"], ss_gate_up=weights["ss_gu"], ss_down=weights["ss_d"])
+    limits = torch.full((E,), L, dtype=torch.int32, device="cuda")
+    rb_top, rb = layer.new_route(), layer.new_route()
+    cap = (torch.empty(T, dtype=torch.int32, device="cuda"), torch.empty(T, device="cuda"),
+           torch.empty(E + 1, dtype=torch.int32, device="cuda"), torch.empty(T, dtype=torch.int32, device="cuda"))
+    y = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+
+    def step(s=None):
+        layer.route(logits, T, rb_top, stream=s)
+        layer.route_capacity(rb_top.topk_ids[: T * k], rb_top.topk_gates[: T * k], T, limits, 1, False, out=cap,
+                             stream=s)
+        layer.route_from_capacity(cap, T, rb, stream=s)
+        layer.forward(x, T, rb, y, stream=s)
+
+    step()
+    torch.cuda.synchronize()
+    y_e, a_e, st_e = y.clone(), cap[0].clone(), cap[3].clone()
+    assert int(cap[2][E]) < T    # 16 experts x at most 12 tokens (1.5 x 8) < 240: some tokens are dropped
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        step(s)
+        s.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            step(s)
+    torch.cuda.current_stream().wait_stream(s)
+    for rep in range(4):
+        y.zero_()
+        cap[0].fill_(-7)
+        cap[3].fill_(-7)
+        layer.route(logits.flip(0), T, rb_top)      # unrelated eager work in between
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_e), f"replay {rep}: output differs from the eager run"
+        assert torch.equal(cap[0], a_e) and torch.equal(cap[3][: int(cap[2][E])], st_e[: int(cap[2][E])])
+    layer.close()
