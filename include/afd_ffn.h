@@ -187,7 +187,9 @@ int afd_ffn_route_capacity(afd_ffn_t h, const int32_t* ids, const float* gates, 
  * lists pair t*k of each kept token in the dropper's order.  afd_ffn_forward on this
  * route then gives y[t] = weight[t] * FFN_assign[t](x[t]) (+ the shared expert), and
  * y[t] = the shared expert's output alone (or 0) for a dropped token: the combine skips
- * slots whose gate is 0.  0 <= T <= max_tokens. */
+ * slots whose gate is 0.  0 <= T <= max_tokens.  The automatic GEMM choice of the
+ * forward that follows counts T * k rows, while at most T are kept: with few kept
+ * rows per expert, afd_ffn_set_gemm_kernel(h, AFD_GEMM_STREAM) fits them better. */
 int afd_ffn_route_from_capacity(afd_ffn_t h, const int32_t* assign, const float* weight, const int32_t* offsets,
                                 const int32_t* sorted_token, int32_t T, const afd_route* r, void* stream);
 
