@@ -314,7 +314,10 @@ __global__ void __launch_bounds__(kF8Threads, kF8MinBlocks) gemm_fp8_tiled_kerne
       // 128-channel quantisation group of each of its tokens (gate/up column tiles are
       // whole, as 2M/32 is a multiple of 8).  Per token: amax over the 4 lanes of
       // each wave holding it, then over the 4 waves through LDS; scale = amax / 448
-      // (1 for an all-zero group); codes = e4m3(v / scale) as the quantisation kernel.
+      // (1 for an all-zero group); codes = e4m3(v * (1 / scale)) with the reciprocal
+      // rounded once per token group, one rounding more than the quantisation kernel's
+      // e4m3(v / scale), and SiLU through the hardware reciprocal: h is internal to
+      // the layer, and its codes may differ from the streaming path's by one step.
       const int tok = lane & 15;
       const int n0 = (lane >> 4) * 4;
       f32x4 hv[kF8RowBlocks][kF8GroupsPerWave];

@@ -26,6 +26,10 @@ Function-by-function pins (tests/test_oracle.py):
                 token-expert pair (the 6*B*H*M FLOPs of the AFD article's §2.1).
   fp8 codec  -- every code's value from the OCP E4M3 definition; round trips;
                 torch's float8_e4m3fn cast (a library routine) on random values.
+  fp8 layer  -- x and h quantised per row and per 128 channels (fp32 decisions),
+                weights dequantised per 128x128 block: torch's e4m3 decode and float64
+                matmuls for one expert, and for three experts with scales of their own,
+                k = 2, two scale blocks in M and a block-scaled shared expert.
 """
 from __future__ import annotations
 

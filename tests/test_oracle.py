@@ -453,6 +453,106 @@ def test_fp8_layer_equals_dequantised_reference():
     np.testing.assert_allclose(y, ref.numpy(), rtol=1e-9, atol=1e-9)
 
 
+def _fp8_blocks(m):
+    """e4m3 codes and fp32 128x128 block scales (amax / 448) of a float32 matrix."""
+    R, C = m.shape
+    blk = m.view(R // 128, 128, C // 128, 128)
+    s = (blk.abs().amax(dim=(1, 3)) / 448.0).float()
+    q = (blk / s[:, None, :, None]).to(torch.float8_e4m3fn).view(R, C)
+    return q, s
+
+
+def _fp8_deq(q, s):
+    R, C = q.shape
+    return (q.to(torch.float64).view(R // 128, 128, C // 128, 128) * s.double()[:, None, :, None]).view(R, C)
+
+
+def _fp8_quant_act(a32):
+    """Activations quantised per row and per 128 channels (scale amax / 448, 1 for an
+    all-zero group; code = e4m3 of the fp32 quotient), returned dequantised in float64."""
+    n = a32.shape[1]
+    blk = a32.view(a32.shape[0], n // 128, 128)
+    amax = blk.abs().amax(dim=2)
+    s = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+    q = (blk / s[..., None]).to(torch.float8_e4m3fn)
+    return (q.to(torch.float64) * s.double()[..., None]).view(a32.shape[0], n)
+
+
+def _fp8_ffn(xf32, wgu, wd, M):
+    a = _fp8_quant_act(xf32) @ wgu
+    h = torch.nn.functional.silu(a[:, :M]) * a[:, M:]
+    return _fp8_quant_act(h.float()) @ wd
+
+
+def test_fp8_layer_several_experts_and_shared_equals_dequantised_reference():
+    """The fp8 layer as the DeepSeek-V3-like workload runs it: several experts with
+    block scales of their own, k = 2 with non-trivial gates, an intermediate size of two
+    scale blocks (gate blocks 0-1, up blocks 2-3 of [H, 2M]) and a block-scaled shared
+    expert.  Reference: per-expert dequantisation with torch's e4m3 decode, numpy
+    argsort routing, softmax gates over the chosen logits and float64 matmuls.
+
+    The experts' weight magnitudes differ by factors of 2.5-6, so their block scales do:
+    reading expert 0's scales for every expert, giving the shared expert a routed
+    expert's scales, splitting gate and up at the wrong block or dropping the shared
+    term each move the result far outside the bar (checked below on the reference
+    itself, so that an oracle making any of these mistakes would fail this pin)."""
+    H, M, E, k, Ms, T = 256, 256, 3, 2, 128, 9
+    g = torch.Generator().manual_seed(33)
+    mags = [1.0, 2.5, 0.4]
+    wgu = [_fp8_blocks(torch.randn(H, 2 * M, generator=g) * mags[e] / math.sqrt(H)) for e in range(E)]
+    wd = [_fp8_blocks(torch.randn(M, H, generator=g) * mags[e] / math.sqrt(M)) for e in range(E)]
+    sgu = _fp8_blocks(torch.randn(H, 2 * Ms, generator=g) * 1.6 / math.sqrt(H))
+    sd = _fp8_blocks(torch.randn(Ms, H, generator=g) * 1.6 / math.sqrt(Ms))
+    for e in range(E):  # the block scales of one matrix differ between its blocks too
+        assert not torch.equal(wgu[e][1][0], wgu[e][1][1])
+    x = torch.randn(T, H, generator=g).to(torch.bfloat16).float()
+    logits = torch.randn(T, E, generator=g).float().numpy()
+    ids, gates, y, _ = oracle.layer(x.numpy(), logits, H=H, M=M, E=E, k=k, dtype="fp8",
+                                    w_gu=[q for q, _ in wgu], w_d=[q for q, _ in wd],
+                                    s_gu=[s for _, s in wgu], s_d=[s for _, s in wd], Ms=Ms,
+                                    ws_gu=sgu[0], ws_d=sd[0], ss_gu=sgu[1], ss_d=sd[1])
+
+    ref_ids = np.argsort(-logits, axis=1, kind="stable")[:, :k]
+    np.testing.assert_array_equal(ids, ref_ids)
+    sel = np.take_along_axis(logits.astype(np.float64), ref_ids, axis=1)
+    ref_g = np.exp(sel - sel.max(axis=1, keepdims=True))
+    ref_g /= ref_g.sum(axis=1, keepdims=True)
+    assert len(set(ref_ids[:, 0])) == E, "every expert is some token's first choice"
+
+    def reference(scale_of, shared_scales, interleave=False, shared=True):
+        deq_gu = [_fp8_deq(wgu[e][0], scale_of(e, "gu")) for e in range(E)]
+        if interleave:  # gate = column blocks 0 and 2, up = blocks 1 and 3
+            order = torch.cat([torch.arange(0, 128), torch.arange(256, 384), torch.arange(128, 256),
+                               torch.arange(384, 512)])
+            deq_gu = [d[:, order] for d in deq_gu]
+        deq_d = [_fp8_deq(wd[e][0], scale_of(e, "d")) for e in range(E)]
+        out = np.zeros((T, H))
+        for t in range(T):
+            for j in range(k):
+                e = int(ref_ids[t, j])
+                o = _fp8_ffn(x[t:t + 1], deq_gu[e], deq_d[e], M)[0].numpy()
+                out[t] += ref_g[t, j] * o
+        if shared:
+            out += _fp8_ffn(x, _fp8_deq(sgu[0], shared_scales[0]), _fp8_deq(sd[0], shared_scales[1]),
+                            Ms).numpy()
+        return out
+
+    own = {"gu": lambda e: wgu[e][1], "d": lambda e: wd[e][1]}
+    ref = reference(lambda e, m: own[m](e), (sgu[1], sd[1]))
+    np.testing.assert_allclose(y, ref, rtol=1e-9, atol=1e-9 * np.abs(ref).max())
+
+    bar = 6e-2 * np.abs(ref).max()   # the fp8 layer's parity bar
+    wrong = {
+        "expert 0's scales for every expert": reference(lambda e, m: own[m](0), (sgu[1], sd[1])),
+        "routed scales for the shared expert": reference(lambda e, m: own[m](e), (wgu[0][1][:, :2], wd[0][1][:1])),
+        "gate and up split per 128-column block": reference(lambda e, m: own[m](e), (sgu[1], sd[1]),
+                                                            interleave=True),
+        "no shared expert": reference(lambda e, m: own[m](e), (sgu[1], sd[1]), shared=False),
+    }
+    for what, bad in wrong.items():
+        assert np.abs(bad - ref).max() > 3 * bar, (what, np.abs(bad - ref).max() / bar)
+
+
 # ----------------------------------------------------------------------------- capacity-aware routing
 def _capacity_check_lists(r, E):
     """counts/offsets/sorted_token are a stable counting sort of the routed tokens."""
