@@ -48,7 +48,7 @@ def parse():
                     help="override the workload's batch size T (same layer, same input distributions)")
     ap.add_argument("--batches", type=int, default=16, help="distinct resident batches cycled over the steps")
     ap.add_argument("--graph", action="store_true", help="replay route+forward from a captured HIP graph")
-    ap.add_argument("--gemm", default="auto", choices=["auto", "stream", "tiled", "wide"],
+    ap.add_argument("--gemm", default="auto", choices=["auto", "stream", "tiled"],
                     help="grouped-GEMM kernel: automatic choice, 16-row streaming tiles or 128-row tiles")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)

@@ -187,9 +187,10 @@ int afd_ffn_route_capacity(afd_ffn_t h, const int32_t* ids, const float* gates, 
  * lists pair t*k of each kept token in the dropper's order.  afd_ffn_forward on this
  * route then gives y[t] = weight[t] * FFN_assign[t](x[t]) (+ the shared expert), and
  * y[t] = the shared expert's output alone (or 0) for a dropped token: the combine skips
- * slots whose gate is 0.  0 <= T <= max_tokens.  The automatic GEMM choice of the
- * forward that follows counts T * k rows, while at most T are kept: with few kept
- * rows per expert, afd_ffn_set_gemm_kernel(h, AFD_GEMM_STREAM) fits them better. */
+ * slots whose gate is 0.  0 <= T <= max_tokens.  The handle remembers (by the route's
+ * sorted_pair buffer, for up to 16 routes) that this route holds at most T rows, and
+ * the automatic GEMM choice of a forward on it counts T rows rather than T * k; a
+ * later afd_ffn_route* call on the same buffers clears that. */
 int afd_ffn_route_from_capacity(afd_ffn_t h, const int32_t* assign, const float* weight, const int32_t* offsets,
                                 const int32_t* sorted_token, int32_t T, const afd_route* r, void* stream);
 
@@ -243,17 +244,9 @@ int afd_ffn_quantize_fp8(const void* src, int32_t rows, int32_t cols, int32_t sr
  * uses 16-row weight-streaming tiles while experts average at most 8 (bf16) or 12
  * (fp8) routed rows per batch (T * top_k <= 8 * E, resp. 12 * E) and 128-row tiles
  * above that (the measured crossovers); the other values force one kernel (results
- * agree to rounding; a tuning and testing knob).
- * AFD_GEMM_WIDE (256x256 tiles, both operands staged in LDS) is never chosen
- * automatically and applies to bf16 layers only (fp8 layers take the 128-row kernel
- * instead).  fp32 layers always use their own kernel.  Takes effect for later
- * forward calls. */
-typedef enum afd_gemm_kernel {
-  AFD_GEMM_AUTO = 0,
-  AFD_GEMM_STREAM = 1,
-  AFD_GEMM_TILED = 2,
-  AFD_GEMM_WIDE = 3
-} afd_gemm_kernel;
+ * agree to rounding; a tuning and testing knob).  fp32 layers always use their own
+ * kernel.  Takes effect for later forward calls.  Other values: AFD_EINVAL. */
+typedef enum afd_gemm_kernel { AFD_GEMM_AUTO = 0, AFD_GEMM_STREAM = 1, AFD_GEMM_TILED = 2 } afd_gemm_kernel;
 int afd_ffn_set_gemm_kernel(afd_ffn_t h, int kernel);
 
 /* Per-kernel timing.  With profiling on, route and forward bracket each kernel

@@ -143,17 +143,28 @@ struct StageScope {
 //     streaming 2% faster at 12 rows, tiled 18% faster at 16).
 bool use_tiled(const afd_ffn* h, int P) {
   if (h->gemm_mode == AFD_GEMM_STREAM) return false;
-  if (h->gemm_mode == AFD_GEMM_TILED || h->gemm_mode == AFD_GEMM_WIDE) return true;
+  if (h->gemm_mode == AFD_GEMM_TILED) return true;
   const long long rows_per_expert = h->cfg.dtype == AFD_FP8_E4M3 ? 12 : 8;
   return (long long)P > rows_per_expert * h->cfg.num_experts;
 }
 
-// bf16 layers: the 256x256-tile GEMM only when forced.  It moves a third less operand
-// traffic per FLOP through L1/L2, but twice the LDS traffic, and measured no faster
-// than the 128-row kernel at 512 and 1024 rows per expert.
-bool use_wide(const afd_ffn* h, int P) {
-  (void)P;
-  return h->gemm_mode == AFD_GEMM_WIDE;
+// Bookkeeping of routes whose rows are fewer than T * top_k (capacity routes).
+void forget_route(afd_ffn* h, const afd_route* r) {
+  for (int i = 0; i < afd_ffn::kCapRoutes; ++i)
+    if (h->cap_route[i] == r->sorted_pair) h->cap_route[i] = nullptr;
+}
+void note_capacity_route(afd_ffn* h, const afd_route* r, int T) {
+  forget_route(h, r);
+  h->cap_route[h->cap_next] = r->sorted_pair;
+  h->cap_rows[h->cap_next] = T;
+  h->cap_next = (h->cap_next + 1) % afd_ffn::kCapRoutes;
+}
+// Upper bound of the rows a forward on route r computes: T * top_k, or T for a route
+// built from a capacity result (one expert per kept token).
+int route_rows(const afd_ffn* h, const afd_route* r, int T) {
+  for (int i = 0; i < afd_ffn::kCapRoutes; ++i)
+    if (h->cap_route[i] == r->sorted_pair) return T < h->cap_rows[i] ? T : h->cap_rows[i];
+  return T * h->cfg.top_k;
 }
 
 // fp8 layer: quantise x -> gate/up GEMM -> quantise h (in the tiled GEMM's epilogue, else a
@@ -164,13 +175,14 @@ int forward_fp8(afd_ffn* h, const void* x, int T, const afd_route* r, void* y, h
   const afd_ffn_config& c = h->cfg;
   const int H = c.hidden, M = c.inter, Ms = c.shared_inter, E = c.num_experts, k = c.top_k;
   const int P = T * k;
+  const int rows = route_rows(h, r, T);
   if (x) {
     StageScope s(h, st, AFD_STAGE_QUANT);
     hipError_t e = afd::launch_quant_fp8(x, T, H, H, true, h->xq, h->xs, st);
     if (e != hipSuccess) return hip_fail(e, "x quantisation launch");
     s.done();
   }
-  const bool tiled = use_tiled(h, P);
+  const bool tiled = use_tiled(h, rows);
   long long items1, items2;
   if (tiled) {
     const int tr = afd::fp8_tiled_rows(), tg = afd::fp8_tiled_groups();
@@ -293,7 +305,6 @@ extern "C" int afd_ffn_create(const afd_ffn_config* cfg, const void* w_gate_up, 
   }
   h->num_cus = prop.multiProcessorCount;
   e = afd::configure_gemm_bf16_tiled();
-  if (e == hipSuccess) e = afd::configure_gemm_bf16_wide();
   if (e == hipSuccess) e = afd::configure_gemm_fp8_tiled();
   if (e != hipSuccess) {
     release(h);
@@ -416,6 +427,7 @@ extern "C" size_t afd_ffn_route_bytes(afd_ffn_t h) {
 static int route_checked(afd_ffn_t h, const float* logits, const float* sel_bias, int32_t T, const afd_route* r,
                          hipStream_t st) {
   const int E = h->cfg.num_experts, k = h->cfg.top_k;
+  forget_route(h, r);
   if (T <= afd::route_small_tokens()) {
     // decode batches: router and permute in one launch (timed as the router stage)
     StageScope s(h, st, AFD_STAGE_ROUTER);
@@ -510,6 +522,7 @@ extern "C" int afd_ffn_route_from_capacity(afd_ffn_t h, const int32_t* assign, c
                                                  r->expert_offsets, r->sorted_pair, r->pair_pos,
                                                  static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "route from capacity launch");
+  note_capacity_route(h, r, T);
   return AFD_OK;
 }
 
@@ -613,18 +626,10 @@ static int forward_checked(afd_ffn_t h, const void* x, const uint8_t* xq, const 
   }
 
   // Few rows per expert (decode batches): 16-row weight-streaming tiles.  Many rows:
-  // 128-row tiles, so each expert's weights are read once per 128 of its rows; several
-  // hundred rows: 256x256 tiles.
-  const bool tiled = !f32 && use_tiled(h, P);
-  const bool wide = tiled && use_wide(h, P);
+  // 128-row tiles, so each expert's weights are read once per 128 of its rows.
+  const bool tiled = !f32 && use_tiled(h, route_rows(h, r, T));
   long long items1, items2;
-  if (wide) {
-    const int tr = afd::wide_rows(), tg = afd::wide_groups();
-    items1 = afd::grouped_items_bound(P, E, (g1.groups_routed + tg - 1) / tg, g1.shared_rows,
-                                      (g1.groups_shared + tg - 1) / tg, tr);
-    items2 = afd::grouped_items_bound(P, E, (g2.groups_routed + tg - 1) / tg, g2.shared_rows,
-                                      (g2.groups_shared + tg - 1) / tg, tr);
-  } else if (tiled) {
+  if (tiled) {
     const int tr = afd::tiled_rows(), tg = afd::tiled_groups();
     items1 = afd::grouped_items_bound(P, E, (g1.groups_routed + tg - 1) / tg, g1.shared_rows,
                                       (g1.groups_shared + tg - 1) / tg, tr);
@@ -637,7 +642,6 @@ static int forward_checked(afd_ffn_t h, const void* x, const uint8_t* xq, const 
   {
     StageScope s(h, st, AFD_STAGE_GATE_UP);
     hipError_t e = f32     ? afd::launch_gemm_f32(g1, true, items1, h->gemm_blocks[2], st)
-                   : wide  ? afd::launch_gemm_bf16_wide(g1, true, items1, h->num_cus, st)
                    : tiled ? afd::launch_gemm_bf16_tiled(g1, true, items1, h->num_cus, st)
                            : afd::launch_gemm_bf16(g1, true, items1, h->gemm_blocks[0], st);
     if (e != hipSuccess) return hip_fail(e, "gate/up GEMM launch");
@@ -646,7 +650,6 @@ static int forward_checked(afd_ffn_t h, const void* x, const uint8_t* xq, const 
   {
     StageScope s(h, st, AFD_STAGE_DOWN);
     hipError_t e = f32     ? afd::launch_gemm_f32(g2, false, items2, h->gemm_blocks[3], st)
-                   : wide  ? afd::launch_gemm_bf16_wide(g2, false, items2, h->num_cus, st)
                    : tiled ? afd::launch_gemm_bf16_tiled(g2, false, items2, h->num_cus, st)
                            : afd::launch_gemm_bf16(g2, false, items2, h->gemm_blocks[1], st);
     if (e != hipSuccess) return hip_fail(e, "down GEMM launch");
@@ -692,7 +695,7 @@ extern "C" int afd_ffn_forward_fp8_input(afd_ffn_t h, const uint8_t* xq, const f
 
 extern "C" int afd_ffn_set_gemm_kernel(afd_ffn_t h, int kernel) {
   if (!h) return fail(AFD_EINVAL, "handle is NULL");
-  if (kernel < AFD_GEMM_AUTO || kernel > AFD_GEMM_WIDE) return fail(AFD_EINVAL, "unknown GEMM kernel %d", kernel);
+  if (kernel < AFD_GEMM_AUTO || kernel > AFD_GEMM_TILED) return fail(AFD_EINVAL, "unknown GEMM kernel %d", kernel);
   h->gemm_mode = kernel;
   return AFD_OK;
 }

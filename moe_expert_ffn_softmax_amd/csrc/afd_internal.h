@@ -88,20 +88,14 @@ hipError_t launch_gemm_bf16(const GroupedGemm& g, bool swiglu, long long max_ite
 hipError_t launch_gemm_f32(const GroupedGemm& g, bool swiglu, long long max_items, int max_blocks, hipStream_t st);
 // Large-tile variant (128-row tiles, 8 column groups per item) for experts with many
 // rows; `max_blocks` as above.
-// The 128-row and 256x256 GEMM kernels use more than the default dynamic LDS; these
-// raise the limit for the current device (called once per handle at creation).
+// The 128-row GEMM kernels use more than the default dynamic LDS; these raise the
+// limit for the current device (called once per handle at creation).
 hipError_t configure_gemm_bf16_tiled();
-hipError_t configure_gemm_bf16_wide();
 hipError_t configure_gemm_fp8_tiled();
 hipError_t launch_gemm_bf16_tiled(const GroupedGemm& g, bool swiglu, long long max_items, int max_blocks,
                                   hipStream_t st);
 int tiled_rows();
 int tiled_groups();
-// 256x256-tile variant (both operands through LDS) for experts with hundreds of rows.
-hipError_t launch_gemm_bf16_wide(const GroupedGemm& g, bool swiglu, long long max_items, int max_blocks,
-                                 hipStream_t st);
-int wide_rows();
-int wide_groups();
 
 // fp8 (e4m3, fp32 block scales) streaming variant; weights packed by launch_pack_fp8,
 // A = fp8 codes with per-row per-128 scales `as_*`, weight scales `s_*`; writes fp32.
@@ -166,7 +160,15 @@ struct afd_ffn {
   float* hs_shared;   // [T_max, Ms/128]
   int gemm_blocks[6];  // resident workgroups of each GEMM kernel on the whole device
                        // (bf16 gate/up, down; fp32 gate/up, down; fp8 gate/up, down)
-  int gemm_mode;       // afd_gemm_kernel: automatic, or always 16-row, 128-row or 256x256 tiles
+  int gemm_mode;       // afd_gemm_kernel: automatic, or always 16-row or 128-row tiles
+  // Routes last filled by afd_ffn_route_from_capacity (keyed by their sorted_pair
+  // buffer), with the batch size T: such a route keeps at most T of its T * top_k
+  // pairs, so the automatic GEMM choice counts T rows for it.  Any other route call on
+  // the same buffers removes the entry.
+  static constexpr int kCapRoutes = 16;
+  const void* cap_route[kCapRoutes];
+  int cap_rows[kCapRoutes];
+  int cap_next;
   size_t device_bytes;
   // profiling
   bool profiling;

@@ -15,7 +15,7 @@ import torch
 
 import oracle
 import workloads
-from moe_expert_ffn_softmax_amd import AfdError, MoeExpertFFN, quantize_fp8
+from moe_expert_ffn_softmax_amd import AfdError, MoeExpertFFN, afd_ffn_forward_fp8_input, quantize_fp8
 
 pytestmark = pytest.mark.gpu
 
@@ -109,8 +109,10 @@ def test_fp8_input_rejects_other_layers_and_overlap():
     xq = torch.zeros((8, 128), dtype=torch.uint8, device="cuda")
     xs = torch.ones((8, 1), dtype=torch.float32, device="cuda")
     y = torch.empty((8, 128), dtype=torch.bfloat16, device="cuda")
-    with pytest.raises(AfdError):
+    with pytest.raises(ValueError):  # the binding refuses first
         layer.forward_fp8_input(xq, xs, 8, rb, y)
+    with pytest.raises(AfdError):    # and so does the C ABI
+        afd_ffn_forward_fp8_input(layer.handle, xq, xs, 8, rb.c, y)
     layer.close()
     w8 = CASES[0]
     weights = workloads.make_weights(w8, device="cuda")
@@ -118,9 +120,9 @@ def test_fp8_input_rejects_other_layers_and_overlap():
     rb = layer.new_route()
     buf = torch.zeros(w8.T * w8.H * 2, dtype=torch.uint8, device="cuda")
     xs = torch.ones((w8.T, w8.H // 128), dtype=torch.float32, device="cuda")
-    with pytest.raises(AfdError):  # y on top of xq
-        layer.forward_fp8_input(buf, xs, w8.T, rb, buf)
-    layer.forward_fp8_input(buf, xs, 0, rb, buf)  # T = 0: no-op, nothing checked past the route
+    with pytest.raises(AfdError):  # y on top of xq (the C ABI's own overlap check)
+        afd_ffn_forward_fp8_input(layer.handle, buf, xs, w8.T, rb.c, buf)
+    afd_ffn_forward_fp8_input(layer.handle, buf, xs, 0, rb.c, buf)  # T = 0: no-op, nothing checked past the route
     torch.cuda.synchronize()
     layer.close()
 

@@ -129,12 +129,14 @@ def test_zero_bias_equals_plain_route(T, E, k):
 
 
 def test_select_bias_rejects_null_bias_and_handles_empty():
-    from moe_expert_ffn_softmax_amd import AfdError
+    from moe_expert_ffn_softmax_amd import AfdError, afd_ffn_route_select_bias
     layer = _layer(8, 2, 4)
     rb = layer.new_route()
     s = torch.zeros((4, 8), dtype=torch.float32, device="cuda")
-    with pytest.raises(AfdError):
+    with pytest.raises(TypeError):  # the binding
         layer.route_select_bias(s, None, 4, rb)
+    with pytest.raises(AfdError):   # the C ABI
+        afd_ffn_route_select_bias(layer.handle, s, None, 4, rb.c)
     layer.route_select_bias(s, torch.zeros(8, device="cuda"), 0, rb)  # T = 0: no-op
     torch.cuda.synchronize()
     layer.close()
