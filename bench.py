@@ -1,20 +1,27 @@
 """Benchmark of one MoE layer's expert FFN (route + forward) on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--graph] [--no-cpu]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--launch graph|eager]
+                    [--no-cpu] [--no-context]
 
-A step is one pass of the whole layer -- router, permute, gate/up GEMM + SwiGLU,
-down GEMM (+ shared expert), combine -- over one batch already resident in HBM.
-The default workload is the long-context starved-decode layer (T=6 tokens, H=4096,
-M=1536, 128 experts, top-8, bf16): the weight-streaming regime.  Each step uses its
-own batch (a ring of independently drawn batches), so successive steps touch
-different experts, as successive decode steps do.
+A step is one pass of the whole layer -- router, permute, fp8 quantisation of x,
+gate/up GEMM + SwiGLU, down GEMM (+ shared expert), combine -- over one batch already
+resident in HBM.  The default workload is the DeepSeek-V3-like layer, the largest
+configuration that fits one GPU: T=4096 tokens, H=7168, M=2048, 256 experts, top-8,
+a shared expert of 2048, e4m3 weights with 128x128 fp32 block scales, activations
+quantised per token per 128 channels.  Steps cycle over a ring of independently
+drawn batches, replayed from captured HIP graphs (the production launch form).
 
 Prints one JSON line: tokens/s of the whole job, TFLOPS, the roofline of the
 dominant kernel (the gate/up GEMM; HIP events around each launch on the launch
-stream) and the CPU oracle timed on a bounded sample of the same workload.
+stream; HBM traffic from committed rocprofv3 counters when they were taken on the
+current kernel sources), the CPU oracle timed on a bounded token sample of the same
+workload, and under "context" the starved-decode layer (T=6, the HBM-bound regime)
+and the 1024-tokens-per-expert bf16 and fp8 batches (the matrix-core regime).
 
 --copy-calibration runs only a 1 GiB device-to-device copy (a kernel of known
 traffic, used to scale rocprofv3's FETCH_SIZE / WRITE_SIZE counters).
+--pmc-summary turns the rocprofv3 counter CSVs of a workload's runs into its entry of
+profiles/traffic_counters.json.
 """
 from __future__ import annotations
 
@@ -43,16 +50,24 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default=workloads.STARVED_DECODE.name)
+    ap.add_argument("--workload", default=workloads.FP8_DSV3.name)
     ap.add_argument("--tokens", type=int, default=0,
                     help="override the workload's batch size T (same layer, same input distributions)")
-    ap.add_argument("--batches", type=int, default=16, help="distinct resident batches cycled over the steps")
-    ap.add_argument("--graph", action="store_true", help="replay route+forward from a captured HIP graph")
+    ap.add_argument("--batches", type=int, default=0,
+                    help="distinct resident batches cycled over the steps (default 16 up to 64 tokens, else 4)")
+    ap.add_argument("--launch", default="graph", choices=["graph", "eager"],
+                    help="timed steps replayed from captured HIP graphs (default) or launched eagerly")
+    ap.add_argument("--graph", action="store_true", help="same as --launch graph (kept for old command lines)")
+    ap.add_argument("--no-context", action="store_true",
+                    help="only the headline workload: skip the decode and matrix-core records")
     ap.add_argument("--gemm", default="auto", choices=["auto", "stream", "tiled"],
                     help="grouped-GEMM kernel: automatic choice, 16-row streaming tiles or 128-row tiles")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="write the gate/up launch's HBM bytes of --workload into profiles/traffic_counters.json "
+                         "from rocprofv3 counter_collection CSVs")
     ap.add_argument("--sweep", action="store_true",
                     help="one JSON line per workload: every layer shape plus the 256/512/1024 tokens-per-expert "
                          "bf16 and fp8 sweeps (HBM and MFMA fractions); not the benchmark line")
@@ -90,11 +105,18 @@ def algorithmic_bytes(w, counts):
 
 def gate_up_bytes(w, counts):
     """Algorithmic bytes of one gate/up launch: 2*H*M weights per touched expert (+ the
-    shared expert's 2*H*Ms), x in, h out."""
-    wb = weight_bytes(w)
+    shared expert's 2*H*Ms), x in and h out, in the forms the launch reads and writes:
+    bf16 (fp32 in the fp32 layer), or for the fp8 layer e4m3 codes plus one fp32 scale
+    per 128 (weights: per 128x128 block; x and h: per row and 128 channels)."""
     touched = int((counts > 0).sum())
+    T, H, M, Ms, P = w.T, w.H, w.M, w.Ms, w.T * w.k
+    if w.dtype == "fp8":
+        wts = touched * (2 * H * M + (H // 128) * (2 * M // 128) * 4) + \
+            (2 * H * Ms + (H // 128) * (2 * Ms // 128) * 4 if Ms else 0)
+        return wts + T * H * (1 + 4 / 128) + (P * M + T * Ms) * (1 + 4 / 128)
+    wb = weight_bytes(w)
     act = 4 if w.dtype == "f32" else 2
-    return touched * 2 * w.H * w.M * wb + 2 * w.H * w.Ms * wb + w.T * w.H * act + w.T * w.k * w.M * act
+    return touched * 2 * H * M * wb + 2 * H * Ms * wb + T * H * act + (P * M + T * Ms) * act
 
 
 def copy_calibration():
@@ -110,12 +132,27 @@ def copy_calibration():
     print(json.dumps({"copy_bytes": n, "launches": 3}))
 
 
-# Sources the bf16 weight-streaming gate/up kernel (the dominant launch of the default
-# workload) is built from: its counters stay valid while these files are unchanged.
-STREAM_KERNEL_SOURCES = ("gemm_bf16.hip", "grouped.h", "afd_device.h", "afd_internal.h")
+# Device sources each gate/up kernel is built from: committed counters of a kernel
+# stay valid while these files are unchanged.
+KERNEL_SOURCES = {
+    "gemm_bf16_stream_kernel<true>": ("gemm_bf16.hip", "grouped.h", "afd_device.h", "afd_internal.h"),
+    "gemm_bf16_tiled_kernel<true>": ("gemm_bf16_tiled.hip", "grouped.h", "afd_device.h", "afd_internal.h"),
+    "gemm_fp8_stream_kernel<true>": ("gemm_fp8.hip", "grouped.h", "afd_device.h", "afd_internal.h"),
+    "gemm_fp8_tiled_kernel<true>": ("gemm_fp8_tiled.hip", "grouped.h", "afd_device.h", "afd_internal.h"),
+    "gemm_f32_kernel<true>": ("gemm_f32.hip", "grouped.h", "afd_device.h", "afd_internal.h"),
+}
 
 
-def source_digest(files=STREAM_KERNEL_SOURCES):
+def gate_up_kernel(w, gemm="auto"):
+    """Name of the gate/up kernel the layer launches for workload w (the automatic
+    choice: 16-row streaming tiles up to 8 rows per expert in bf16, 12 in fp8)."""
+    if w.dtype == "f32":
+        return "gemm_f32_kernel<true>"
+    tiled = gemm == "tiled" or (gemm == "auto" and w.T * w.k > (12 if w.dtype == "fp8" else 8) * w.E)
+    return f"gemm_{w.dtype}_{'tiled' if tiled else 'stream'}_kernel<true>"
+
+
+def source_digest(files):
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "moe_expert_ffn_softmax_amd", "csrc")
@@ -125,68 +162,159 @@ def source_digest(files=STREAM_KERNEL_SOURCES):
     return h.hexdigest()[:16]
 
 
-def traffic_from_counters(w, kernel):
-    """HBM bytes per launch of `kernel` from committed rocprofv3 counter runs, if they
-    were taken on the current kernel sources and this workload; else None."""
+def traffic_from_counters(w, gemm="auto"):
+    """HBM bytes per gate/up launch from committed rocprofv3 counter runs, if they were
+    taken on this workload with the kernel that runs now, built from the current
+    sources; else None."""
     try:
         with open(PMC_FILE) as f:
             d = json.load(f)
     except (OSError, ValueError):
         return None
-    e = d.get(w.name, {}).get(kernel)
-    if not e or e.get("source_digest") != source_digest():
+    e = d.get(w.name, {}).get("gate_up")
+    kern = gate_up_kernel(w, gemm)
+    if not e or e.get("kernel") != kern or e.get("source_digest") != source_digest(KERNEL_SOURCES[kern]):
         return None
     return e.get("bytes_per_launch")
 
 
-def cpu_baseline(w, weights, batches, seconds, single_seconds=3.0):
-    """The oracle (as it stands) on whole batches of the timed workload, cycling over
-    the timed ring of batches until about `seconds` of oracle time have passed, on
-    every host core; then the same on one thread for about `single_seconds`.
-    Copying experts to host memory (once per expert) is not timed."""
-    import torch
+def _counter_means(path, name_filter=None):
+    """{kernel name: (dispatches, mean Counter_Value)} of a rocprofv3 counter_collection CSV."""
+    import collections
+    import csv
+    acc = collections.defaultdict(list)
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            n = r["Kernel_Name"]
+            if name_filter and name_filter not in n:
+                continue
+            acc[n].append(float(r["Counter_Value"]))
+    return {k: (len(v), sum(v) / len(v)) for k, v in acc.items()}
 
+
+def pmc_summary(args):
+    """Scale FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the workload's gate/up launch
+    by what the same counters read for a 1 GiB copy, and record the bytes per launch
+    with the digest of the kernel's sources."""
+    w = workloads.get(args.workload)
+    fetch_csv, write_csv, cfetch_csv, cwrite_csv = args.pmc_summary
+    kern = gate_up_kernel(w, args.gemm)
+    n = 1 << 30
+    cf, cw = _counter_means(cfetch_csv), _counter_means(cwrite_csv)
+    copy = max(cf, key=lambda k: cf[k][1])   # the copy is the largest fetch of that run
+    fetch_scale = round(n / 1024 / cf[copy][1], 4)
+    write_scale = round(n / 1024 / cw[copy][1], 4)
+    f, wr = _counter_means(fetch_csv, "afd::"), _counter_means(write_csv, "afd::")
+    key = next(k for k in f if kern in k)
+    nbytes = int(f[key][1] * 1024 * fetch_scale + wr[key][1] * 1024 * write_scale)
+    try:
+        with open(PMC_FILE) as fh:
+            d = json.load(fh)
+    except (OSError, ValueError):
+        d = {}
+    d.setdefault(w.name, {})["gate_up"] = {
+        "kernel": kern, "sources": sorted(KERNEL_SOURCES[kern]), "source_digest": source_digest(KERNEL_SOURCES[kern]),
+        "bytes_per_launch": nbytes, "fetch_kib": round(f[key][1], 1), "write_kib": round(wr[key][1], 1),
+        "dispatches": f[key][0], "fetch_scale": fetch_scale, "write_scale": write_scale}
+    with open(PMC_FILE, "w") as fh:
+        json.dump(d, fh, indent=1)
+        fh.write("\n")
+    rows = [f"| {k} | {f[k][0]} | {f[k][1]:.1f} | {wr.get(k, (0, 0.0))[1]:.1f} | "
+            f"{(f[k][1] * 1024 * fetch_scale + wr.get(k, (0, 0.0))[1] * 1024 * write_scale) / 1e6:.2f} |"
+            for k in sorted(f, key=lambda k: -f[k][1])]
+    print(json.dumps(d[w.name]["gate_up"]))
+    print("| kernel | dispatches | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | scaled HBM bytes per dispatch (MB) |")
+    print("|---|---|---|---|---|")
+    print("\n".join(rows))
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+class HostExperts:
+    """Host copies of a workload's per-expert weights, made on first use (not timed)."""
+
+    def __init__(self, weights):
+        self.weights = weights
+        self.host = {k: (v.cpu() if v is not None else None) for k, v in weights.items()
+                     if k not in ("w_gu", "w_d", "s_gu", "s_d")}
+        for k in ("w_gu", "w_d", "s_gu", "s_d"):
+            self.host[k] = {} if weights[k] is not None else None
+
+    def need(self, experts):
+        for k in ("w_gu", "w_d", "s_gu", "s_d"):
+            if self.host[k] is not None:
+                for e in experts:
+                    if int(e) not in self.host[k]:
+                        self.host[k][int(e)] = self.weights[k][int(e)].cpu()
+        return self.host
+
+
+def oracle_rate(w, hx, tokens, seconds, nthreads, chunk):
+    """Oracle tokens/s on the rows of `tokens` = (x, logits) [bf16-exact fp32, fp32],
+    `chunk` tokens per call, cycling until about `seconds` of oracle time; the host
+    copies of the experts each chunk needs are made before its timer starts."""
     import oracle
-    host = {k: (v.cpu() if v is not None else None) for k, v in weights.items()
-            if k not in ("w_gu", "w_d", "s_gu", "s_d")}
-    for k in ("w_gu", "w_d", "s_gu", "s_d"):
-        host[k] = {} if weights[k] is not None else None
-    inputs = {}
+    x, logits = tokens
+    n = x.shape[0]
+    spent, done, calls = 0.0, 0, 0
+    while spent < seconds:
+        r0 = (calls * chunk) % n
+        xs, ls = x[r0:r0 + chunk], logits[r0:r0 + chunk]
+        need = np.unique(oracle.route(ls, w.k)[0])
+        host = hx.need(need)
+        t0 = time.perf_counter()
+        oracle.layer_from_weights(xs, ls, w, host, experts_needed=need, nthreads=nthreads)
+        spent += time.perf_counter() - t0
+        done += xs.shape[0]
+        calls += 1
+    return done, spent, calls
 
-    def batch(b):
-        if b not in inputs:
-            x = workloads.tokens_f32(w, batch=b)
-            if w.dtype != "f32":
-                x = torch.from_numpy(x).to(torch.bfloat16).float().numpy()
-            logits = workloads.router_logits(w, batch=b)
-            need = np.unique(oracle.route(logits, w.k)[0])
-            for k in ("w_gu", "w_d", "s_gu", "s_d"):
-                if host[k] is not None:
-                    for e in need:
-                        if int(e) not in host[k]:
-                            host[k][int(e)] = weights[k][int(e)].cpu()
-            inputs[b] = (x, logits, need)
-        return inputs[b]
 
-    def timed(limit, nthreads):
-        spent, done = 0.0, 0
-        while spent < limit:
-            x, logits, need = batch(done % batches)
-            t0 = time.perf_counter()
-            oracle.layer_from_weights(x, logits, w, host, experts_needed=need, nthreads=nthreads)
-            spent += time.perf_counter() - t0
-            done += 1
-        return spent, done
+def host_tokens(w, batch=0):
+    import torch
+    x = workloads.tokens_f32(w, batch=batch)
+    if w.dtype != "f32":
+        x = torch.from_numpy(x).to(torch.bfloat16).float().numpy()
+    return x, workloads.router_logits(w, batch=batch)
 
-    spent, done = timed(seconds, 0)
-    spent1, done1 = timed(single_seconds, 1) if single_seconds > 0 else (0.0, 0)
-    out = {"value": round(done * w.T / spent, 3), "unit": "tokens/s", "cores": oracle.max_threads(),
-           "kind": "oracle",
-           "sample": f"{done} whole batches of {w.T} tokens (the timed ring of {min(done, batches)} batches, "
-                     f"cycled), {spent:.1f} s of oracle time on the host, double precision"}
-    if done1:
-        out["single_thread"] = {"value": round(done1 * w.T / spent1, 3), "unit": "tokens/s", "cores": 1,
-                                "sample": f"{done1} whole batches, {spent1:.1f} s on one thread"}
+
+def cpu_baseline(w, weights, seconds, single_seconds=3.0, single_workloads=()):
+    """The oracle (as it stands) on a bounded token sample of the timed workload: its
+    first batch's tokens in calls of up to 64 tokens (whole batches when smaller),
+    cycling until about `seconds` of oracle time, on every host core; then about
+    `single_seconds` on one thread.  `single_workloads`: (workload, weights) pairs also
+    timed on one thread."""
+    import oracle
+    chunk = min(w.T, 64)
+    toks = host_tokens(w)
+    hx = HostExperts(weights)
+    done, spent, calls = oracle_rate(w, hx, toks, seconds, 0, chunk)
+    out = {"value": round(done / spent, 3), "unit": "tokens/s", "cores": oracle.max_threads(), "kind": "oracle",
+           "cpu_model": cpu_model(),
+           "sample": f"{done} tokens of the workload's first batch ({calls} oracle calls of {chunk} tokens, the "
+                     f"first {min(done, w.T)} tokens cycled), {spent:.1f} s of oracle time on the host, "
+                     f"double precision"}
+    if single_seconds > 0:
+        d1, s1, c1 = oracle_rate(w, hx, toks, single_seconds, 1, min(chunk, 8))
+        out["single_thread"] = {"value": round(d1 / s1, 3), "unit": "tokens/s", "cores": 1,
+                                "sample": f"{d1} tokens in {c1} calls, {s1:.1f} s on one thread"}
+    by = {}
+    for sw, sweights in single_workloads:
+        sc = min(sw.T, 16)
+        d1, s1, c1 = oracle_rate(sw, HostExperts(sweights), host_tokens(sw), single_seconds, 1, sc)
+        by[sw.name] = {"value": round(d1 / s1, 3), "unit": "tokens/s", "cores": 1,
+                       "sample": f"{d1} tokens in {c1} calls of {sc}, {s1:.1f} s on one thread"}
+    if by:
+        out["single_thread_by_workload"] = by
     return out
 
 
@@ -476,6 +604,9 @@ def main():
     if args.copy_calibration:
         copy_calibration()
         return
+    if args.pmc_summary:
+        pmc_summary(args)
+        return
     if args.sweep:
         torch.cuda.set_device(0)
         sweep(args, torch)
@@ -496,20 +627,66 @@ def main():
         torch.cuda.set_device(0)
         ubatches(args, torch)
         return
-    from moe_expert_ffn_softmax_amd import MoeExpertFFN, afd_ffn_profile_read, afd_ffn_set_profiling
-
     w = workloads.get(args.workload)
     if args.tokens > 0 and args.tokens != w.T:
         w = dataclasses.replace(w, T=args.tokens, name=f"{w.name}_at_T{args.tokens}")
     torch.cuda.set_device(0)
+    launch = "graph" if args.graph else args.launch
+    nb = args.batches or (16 if w.T <= 64 else 4)
+    rec, weights = measure(w, torch, args.steps, args.warmup, nb, launch, args.gemm, min(args.steps, 100),
+                           keep_weights=not args.no_cpu)
+    out = {
+        "metric": METRIC,
+        "value": rec["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": rec["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": rec["config"],
+    }
+    out.update({k: v for k, v in rec.items() if k not in ("tokens_per_s", "ms_per_step", "config", "workload")})
+    if not args.no_context:
+        ctx = {}
+        for cw in (workloads.STARVED_DECODE, workloads.mfma_sweep("bf16")[-1], workloads.mfma_sweep("fp8")[-1]):
+            if cw.name == w.name:
+                continue
+            small = cw.T <= 64
+            r, _ = measure(cw, torch, 200 if small else 10, 20 if small else 3, 16 if small else 2, launch, "auto",
+                           0, keep_weights=False)
+            ctx[r["config"]["workload"]] = {k: r[k] for k in ("ms_per_step", "tokens_per_s", "tflops", "mfma_frac",
+                                                               "step_hbm", "roofline", "kernels_us")}
+            torch.cuda.empty_cache()
+        out["context"] = ctx
+    if not args.no_cpu:
+        singles = []
+        for sw in (workloads.TINY, workloads.STARVED_DECODE, workloads.AGGREGATED):
+            if sw.name != w.name:
+                singles.append((sw, workloads.make_weights(sw, device="cuda")))
+        out["cpu_baseline"] = cpu_baseline(w, weights, args.cpu_seconds, single_workloads=singles)
+        del singles
+    print(json.dumps(out), flush=True)
+
+
+def measure(w, torch, steps, warmup, nb, launch, gemm, cold_n, keep_weights):
+    """Time `steps` route+forward steps of workload w over a ring of nb resident batches
+    (wall clock between synchronisations), then cold_n steps after a cache flush each,
+    then per-kernel HIP-event times; returns (record, weights or None)."""
+    from moe_expert_ffn_softmax_amd import MoeExpertFFN, afd_ffn_profile_read, afd_ffn_set_profiling
     dev = "cuda"
     weights = workloads.make_weights(w, device=dev)
     layer = MoeExpertFFN(hidden=w.H, inter=w.M, num_experts=w.E, top_k=w.k, max_tokens=w.T, dtype=w.dtype,
                          w_gate_up=weights["w_gu"], w_down=weights["w_d"], s_gate_up=weights["s_gu"],
                          s_down=weights["s_d"], shared_inter=w.Ms, ws_gate_up=weights["ws_gu"],
                          ws_down=weights["ws_d"], ss_gate_up=weights["ss_gu"], ss_down=weights["ss_d"])
-    layer.set_gemm_kernel(args.gemm)
-    nb = max(1, args.batches)
+    layer.set_gemm_kernel(gemm)
+    if not keep_weights:
+        weights = None
     xs, lgs = [], []
     for b in range(nb):
         x, lg = workloads.make_activations(w, device=dev, batch=b)
@@ -525,7 +702,9 @@ def main():
         layer.forward(xs[b], w.T, rbs[b], ys[b])
 
     graphs = None
-    if args.graph:
+    if launch == "graph":
+        # capture one graph per batch; every replay is checked bit for bit against the
+        # eager result, three times, with eager work in between
         for b in range(nb):
             step(b)
         torch.cuda.synchronize()
@@ -548,6 +727,8 @@ def main():
             for b in range(nb):
                 if not torch.equal(ys[b], ref[b]):
                     raise RuntimeError(f"graph replay {rep} of batch {b} differs from the eager result")
+            step(rep)
+            torch.cuda.synchronize()
 
     def run(i):
         if graphs is not None:
@@ -555,85 +736,76 @@ def main():
         else:
             step(i)
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         run(i)
     torch.cuda.synchronize()
-
     # timed region: exactly `steps` steps
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         run(i)
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    ms_per_step = elapsed * 1e3 / args.steps
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / steps
 
     # the same steps with caches flushed before each one (reported beside the value)
-    cold = cold_steps(run, min(args.steps, 100), torch)
+    cold = cold_steps(run, cold_n, torch) if cold_n else None
 
-    # per-kernel durations: the same steps again with HIP events around every launch
-    # (eager launches on the same stream; the events add small gaps between kernels,
-    # so this pass only feeds the per-kernel figures)
+    # per-kernel durations: the same steps again, eager, with HIP events around every
+    # launch on the launch stream (the events add small gaps between kernels, so this
+    # pass only feeds the per-kernel figures)
     afd_ffn_set_profiling(layer.handle, True)
-    for i in range(args.steps):
+    for i in range(steps):
         step(i)
     torch.cuda.synchronize()
     prof = afd_ffn_profile_read(layer.handle)
     afd_ffn_set_profiling(layer.handle, False)
 
     counts = [rbs[b].expert_counts.cpu().numpy() for b in range(nb)]
+    layer.close()
+    del graphs, xs, lgs, ys, rbs
     step_bytes = np.mean([algorithmic_bytes(w, c)[0] for c in counts])
     touched = np.mean([algorithmic_bytes(w, c)[1] for c in counts])
     gu_bytes = np.mean([gate_up_bytes(w, c) for c in counts])
     gu_ms, gu_n = prof["gate_up"]
     gu_avg_s = gu_ms / max(gu_n, 1) / 1e3
-    achieved = gu_bytes / gu_avg_s / 1e9
-    traffic = traffic_from_counters(w, "gate_up")
+    traffic = traffic_from_counters(w, gemm)
+    kern = gate_up_kernel(w, gemm)
 
     # the gate/up launch is bound by HBM below the ridge point (peak FLOP/s / peak B/s)
     # and by the matrix cores above it
     gu_flops = 4.0 * w.T * w.k * w.H * w.M + 4.0 * w.T * w.H * w.Ms
     ridge = MFMA_PEAK_TFLOPS[w.dtype] * 1e12 / (HBM_PEAK_GBS * 1e9)
+    gu_tf = gu_flops / gu_avg_s / 1e12
     if gu_flops / gu_bytes <= ridge:
-        roofline = {"kernel": "gate_up", "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                    "algorithmic_bytes": int(gu_bytes), "avg_launch_us": round(gu_avg_s * 1e6, 2)}
+        achieved = gu_bytes / gu_avg_s / 1e9
+        roofline = {"kernel": "gate_up", "name": kern, "bound": "hbm", "achieved": round(achieved, 1),
+                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                    "traffic": traffic, "algorithmic_bytes": int(gu_bytes), "avg_launch_us": round(gu_avg_s * 1e6, 2),
+                    "mfma_frac": round(gu_tf / MFMA_PEAK_TFLOPS[w.dtype], 4)}
     else:
-        tf = gu_flops / gu_avg_s / 1e12
-        roofline = {"kernel": "gate_up", "bound": "mfma", "achieved": round(tf, 1),
+        roofline = {"kernel": "gate_up", "name": kern, "bound": "mfma", "achieved": round(gu_tf, 1),
                     "peak": MFMA_PEAK_TFLOPS[w.dtype], "unit": "TFLOP/s",
-                    "frac": round(tf / MFMA_PEAK_TFLOPS[w.dtype], 4), "traffic": traffic,
+                    "frac": round(gu_tf / MFMA_PEAK_TFLOPS[w.dtype], 4), "traffic": traffic,
                     "algorithmic_flops": gu_flops, "algorithmic_bytes": int(gu_bytes),
-                    "avg_launch_us": round(gu_avg_s * 1e6, 2)}
-
-    tokens_per_s = w.T / (ms_per_step / 1e3)
+                    "avg_launch_us": round(gu_avg_s * 1e6, 2),
+                    "hbm_frac": round(gu_bytes / gu_avg_s / 1e9 / HBM_PEAK_GBS, 4)}
     tflops = w.flops() / (ms_per_step / 1e3) / 1e12
-    out = {
-        "metric": METRIC,
-        "value": round(tokens_per_s, 2),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+    rec = {
+        "workload": w.name,
         "ms_per_step": round(ms_per_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": w.dtype,
-        "data": "synthetic",
+        "tokens_per_s": round(w.T / (ms_per_step / 1e3), 2),
         "config": {"workload": w.name, "T": w.T, "H": w.H, "M": w.M, "E": w.E, "top_k": w.k, "shared_inter": w.Ms,
-                   "batches": nb, "launch": "hip_graph" if graphs is not None else "eager", "gemm": args.gemm},
+                   "tokens_per_expert": round(w.tokens_per_expert, 2), "batches": nb, "launch": launch, "gemm": gemm},
         "tflops": round(tflops, 3),
+        "mfma_frac": round(tflops / MFMA_PEAK_TFLOPS[w.dtype], 4),
         "step_hbm": {"algorithmic_bytes": int(step_bytes), "touched_experts": round(float(touched), 2),
                      "achieved_GBps": round(step_bytes / (ms_per_step / 1e3) / 1e9, 1),
                      "frac": round(step_bytes / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4)},
         "roofline": roofline,
-        "cold": cold,
         "kernels_us": {k: round(v[0] / max(v[1], 1) * 1e3, 2) for k, v in prof.items() if v[1]},
     }
-    if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(w, weights, nb, args.cpu_seconds)
-    print(json.dumps(out), flush=True)
-    layer.close()
+    if cold is not None:
+        rec["cold"] = cold
+    return rec, weights
 
 
 if __name__ == "__main__":

@@ -52,3 +52,15 @@ def test_decode_layer_bytes_count_only_touched_experts():
 def test_flops_are_six_hm_per_pair_plus_shared():
     for w in workloads.ORDERED + workloads.CONTEXT:
         assert w.flops() == 6 * w.T * w.k * w.H * w.M + 6 * w.T * w.H * w.Ms
+
+
+def test_fp8_gate_up_launch_bytes_count_codes_and_scales():
+    """The fp8 gate/up launch reads e4m3 x codes with one fp32 scale per 128 channels and
+    writes h the same way; weights are codes plus one fp32 scale per 128x128 block."""
+    w = workloads.FP8_DSV3
+    counts = np.ones(w.E, np.int64)
+    T, H, M, Ms, P = 4096, 7168, 2048, 2048, 4096 * 8
+    want = (256 * (2 * H * M + 56 * 32 * 4) + 2 * H * Ms + 56 * 32 * 4 + T * H + T * 56 * 4
+            + (P * M + T * Ms) + (P * 16 + T * 16) * 4)
+    assert bench.gate_up_bytes(w, counts) == want
+    assert abs(want / 7.70e9 - 1) < 0.01

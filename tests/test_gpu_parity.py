@@ -82,11 +82,59 @@ def oracle_rows(w, weights, x, logits_np, rows):
     xs = x[torch.as_tensor(rows, device=x.device)].float().cpu().numpy()
     ls = logits_np[rows]
     ids, _ = oracle.route(ls, w.k)
-    _, _, yref, _ = oracle.layer_from_weights(xs, ls, w, weights, experts_needed=np.unique(ids))
+    need = np.unique(ids)
+    # host copies of the experts the rows use, once; then the oracle in chunks, with a
+    # progress line per chunk
+    host = {k: v for k, v in weights.items() if k not in ("w_gu", "w_d", "s_gu", "s_d")}
+    for k in ("w_gu", "w_d", "s_gu", "s_d"):
+        host[k] = None if weights.get(k) is None else {int(e): weights[k][int(e)].cpu() for e in need}
+    host = {k: (v.cpu() if hasattr(v, "cpu") else v) for k, v in host.items()}
+    yref = np.zeros((len(rows), w.H))
+    chunk = 256
+    for c0 in range(0, len(rows), chunk):
+        sl = slice(c0, c0 + chunk)
+        _, _, yref[sl], _ = oracle.layer_from_weights(xs[sl], ls[sl], w, host, experts_needed=np.unique(ids[sl]))
+        if len(rows) > chunk:
+            say(f"  oracle: {min(c0 + chunk, len(rows))} of {len(rows)} tokens")
     return rows, yref
 
 
-def full_case(w, sample=None, kernel="auto"):
+def tile_boundary_rows(counts, offsets, sorted_pair, k, T, Ms, tile_rows, even):
+    """Tokens holding the first and the last row of every row tile of every expert (and
+    of the shared expert's T rows), with the tiling of the kernel that runs: 128-row
+    tiles with an expert's rows split evenly over them (the tiled kernels), or 16-row
+    tiles cut in order (the streaming kernels).  Returns (tokens, experts, tiles)."""
+    def bounds(n):
+        if n == 0:
+            return []
+        nt = -(-n // tile_rows)
+        if not even:
+            return [(t * tile_rows, min(n, (t + 1) * tile_rows) - 1) for t in range(nt)]
+        base, extra = divmod(n, nt)
+        out, r0 = [], 0
+        for t in range(nt):
+            r1 = r0 + base + (1 if t < extra else 0)
+            out.append((r0, r1 - 1))
+            r0 = r1
+        return out
+
+    tokens, tiles, experts = set(), 0, 0
+    for e in range(len(counts)):
+        b = bounds(int(counts[e]))
+        experts += bool(b)
+        tiles += len(b)
+        for r0, r1 in b:
+            tokens.add(int(sorted_pair[offsets[e] + r0]) // k)
+            tokens.add(int(sorted_pair[offsets[e] + r1]) // k)
+    if Ms:
+        b = bounds(T)
+        tiles += len(b)
+        for r0, r1 in b:
+            tokens.update((r0, r1))
+    return sorted(tokens), experts, tiles
+
+
+def full_case(w, sample=None, kernel="auto", tiles=False):
     say(f"case {w.name}: T={w.T} H={w.H} M={w.M} E={w.E} k={w.k} Ms={w.Ms} {w.dtype} gemm={kernel}")
     weights = workloads.make_weights(w, device="cuda")
     x, logits = workloads.make_activations(w, device="cuda")
@@ -106,6 +154,16 @@ def full_case(w, sample=None, kernel="auto"):
         sp = rb.sorted_pair.cpu().numpy()
         tail = sp[max(off[hot], off[hot + 1] - 3):off[hot + 1]] // w.k
         rows = np.concatenate([[0, 1, w.T - 1], rng.integers(0, w.T, sample), tail])
+        if tiles:
+            # every row tile of every expert: first and last row, in the tiling of the
+            # kernel the automatic choice (or `kernel`) runs
+            P = w.T * w.k
+            tiled = kernel == "tiled" or (kernel == "auto" and P > (12 if w.dtype == "fp8" else 8) * w.E)
+            bt, ne, nt = tile_boundary_rows(counts, off, sp, w.k, w.T, w.Ms, 128 if tiled else 16, tiled)
+            rows = np.concatenate([rows, bt])
+            say(f"{w.name}: {len(set(rows.tolist()))} tokens cover the first and last row of all {nt} row tiles "
+                f"({'128-row even split' if tiled else '16-row'}) of {ne} experts" + (" and the shared expert"
+                                                                                        if w.Ms else ""))
     rows, yref = oracle_rows(w, weights, x, logits_np, rows)
     check_y(y[torch.as_tensor(rows, device="cuda")], yref, TOL[w.dtype], w.name)
     return layer, x, logits, y
@@ -127,12 +185,12 @@ def test_starved_decode_full():
 
 
 @pytest.mark.parametrize("kernel", ["auto", "stream"])
-def test_afd_aggregated_sampled(kernel):
-    full_case(workloads.AGGREGATED, sample=6, kernel=kernel)
+def test_afd_aggregated_every_tile(kernel):
+    full_case(workloads.AGGREGATED, sample=6, kernel=kernel, tiles=True)
 
 
-def test_coarse_experts_with_shared_sampled():
-    full_case(workloads.COARSE, sample=3)
+def test_coarse_experts_with_shared_every_tile():
+    full_case(workloads.COARSE, sample=3, tiles=True)
 
 
 def test_fp8_decode_full():
@@ -145,17 +203,18 @@ def test_starved_decode_tiled_kernel():
     full_case(workloads.STARVED_DECODE, kernel="tiled")
 
 
-def test_fp8_blockscaled_sampled():
-    full_case(workloads.FP8_DSV3, sample=3)
+def test_fp8_blockscaled_every_tile():
+    full_case(workloads.FP8_DSV3, sample=3, tiles=True)
 
 
 @pytest.mark.parametrize("w", [workloads.mfma_sweep("bf16")[0], workloads.mfma_sweep("bf16")[-1],
                                workloads.mfma_sweep("fp8")[-1]], ids=lambda w: w.name)
-def test_mfma_sweep_sampled(w):
+def test_mfma_sweep_every_tile(w):
     """The 256 / 1024 tokens-per-expert batches on which the matrix-core rate is
     measured, at full size and in the launch configuration timed there (automatic
-    kernel choice: the 128-row tiled GEMMs), on sampled tokens."""
-    full_case(w, sample=3)
+    kernel choice: the 128-row tiled GEMMs), on the tokens at both ends of every row
+    tile of every expert."""
+    full_case(w, sample=3, tiles=True)
 
 
 @pytest.mark.parametrize("src", ["bf16", "f32"])
