@@ -49,28 +49,53 @@
 
 namespace afd {
 
-constexpr int kF8Waves = 4;
+#ifndef AFD_FP8_TILED_WAVES
+#define AFD_FP8_TILED_WAVES 8
+#endif
+constexpr int kF8Waves = AFD_FP8_TILED_WAVES;   // 4: one wave per SIMD; 8: two
 constexpr int kF8Threads = kF8Waves * kWave;
 constexpr int kF8RowBlocks = 8;                 // 16-token blocks per tile
 constexpr int kF8Rows = 16 * kF8RowBlocks;      // 128
-#ifndef AFD_FP8_TILED_GPW
-#define AFD_FP8_TILED_GPW 2
-#endif
-constexpr int kF8GroupsPerWave = AFD_FP8_TILED_GPW;  // 32-column groups per wave
-constexpr int kF8Groups = kF8Waves * kF8GroupsPerWave;
+constexpr int kF8Groups = 8;                    // 32-column groups per tile (one h quantisation group)
+constexpr int kF8GroupsPerWave = kF8Groups / kF8Waves;  // 32-column groups per wave
 constexpr int kF8CB = 2 * kF8GroupsPerWave;     // 16-column blocks per wave
-static_assert(kF8CB == 4, "the step anchors below name four 16-column blocks");
+static_assert(kF8Waves == 4 || kF8Waves == 8, "4 or 8 waves per workgroup");
 constexpr int kF8Slot = 272;                    // bytes per staging slot (16 rows x 16 B + padding)
 constexpr int kF8A = kF8RowBlocks * 16 * kF8Slot;  // activation bytes per buffer
-constexpr int kF8WScales = 2 * kF8Waves * 2 * AFD_FP8_TILED_GPW;  // weight scales per chunk (2 blocks)
+constexpr int kF8WScales = 2 * kF8Waves * kF8CB;  // weight scales per chunk (2 blocks)
 constexpr int kF8Buf = kF8A + 2 * kF8Rows * 4 + kF8WScales * 4;  // + the chunk's token and weight scales
-constexpr int kF8Loads = 8;                     // staging loads per thread per chunk (4 rows each)
-constexpr int kF8BAhead = 2;                    // scale blocks of weights in flight per wave
+constexpr int kF8StageRows = kF8Rows / kF8Waves;  // rows each wave stages per chunk
+constexpr int kF8Loads = kF8StageRows / 4;      // staging loads per thread per chunk (4 rows each)
+#ifndef AFD_FP8_TILED_RING
+#define AFD_FP8_TILED_RING 2
+#endif
+#ifndef AFD_FP8_TILED_STAGE_SETS
+#define AFD_FP8_TILED_STAGE_SETS 1
+#endif
+constexpr int kF8BAhead = AFD_FP8_TILED_RING;   // scale blocks of weights in flight per wave (2 or 4)
+constexpr int kF8StageSets = AFD_FP8_TILED_STAGE_SETS;  // chunks of activations loading ahead (1 or 2)
+static_assert(kF8BAhead == 2 || kF8BAhead == 4, "weight ring of 2 or 4 blocks");
+static_assert(kF8StageSets == 1 || kF8StageSets == 2, "1 or 2 staging register sets");
+#ifndef AFD_FP8_TILED_LDS_AHEAD
+#define AFD_FP8_TILED_LDS_AHEAD 1
+#endif
+constexpr int kF8LdsAhead = AFD_FP8_TILED_LDS_AHEAD;  // token blocks of operands read from LDS ahead
+// The chunk loop is unrolled by two when a ring slot (block % kF8BAhead) or a staging
+// set (chunk % kF8StageSets) would otherwise depend on the chunk's parity.
+constexpr int kF8Unroll = (kF8BAhead == 4 || kF8StageSets == 2) ? 2 : 1;
 constexpr int kF8Xcds = 8;
 
+#ifndef AFD_FP8_PLAIN_MFMA
+#define AFD_FP8_PLAIN_MFMA 1
+#endif
 __device__ __forceinline__ f32x4 f8_mfma(const i32x8& a, const i32x8& b) {
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+#if AFD_FP8_PLAIN_MFMA
+  // scale operands 0: the compiler emits the unscaled v_mfma_f32_16x16x128_f8f6f4
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 0, 0, 0, 0, 0, 0);
+#else
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 0, 0, 0, 0x7f7f7f7f, 0, 0x7f7f7f7f);
+#endif
 }
 
 // A lane's 32 weight bytes of a packed fragment: 16 at p, 16 at p + 1 KiB.
@@ -88,6 +113,319 @@ constexpr int kF8MinBlocks = AFD_FP8_TILED_MIN_BLOCKS;  // workgroups per CU the
 // SiLU with the hardware reciprocal (one rounding more than z / (1 + e^-z)); h is
 // quantised to e4m3 right after, whose step is 2^-3 of the value.
 __device__ __forceinline__ float silu_rcp(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
+
+// One item: a tile of it.nrows <= 16 * NRB rows (NRB 16-row blocks hold all of them)
+// times the workgroup's 8 column groups.  Blocks past NRB are not computed.
+template <bool SWIGLU, int NRB>
+__device__ __forceinline__ void fp8_tile(const GroupedGemm& g, const Item& it, const int w, unsigned char* lds,
+                                         float (*qamax)[kF8Rows]) {
+  // lane-derived indices are recomputed per item (hoisted out of the item loop they
+  // do not fit the register budget)
+  int lane = lane_id();
+  asm volatile("" : "+v"(lane));
+    const int K = it.shared ? g.K_shared : g.K_routed;
+  const int KB = K / 128;
+  const int NC = (KB + 1) / 2;  // 256-deep chunks; an odd KB leaves the last chunk half live
+  const int groups = it.shared ? g.groups_shared : g.groups_routed;
+  const int N = groups * 32;
+  const int NB = N / 128;
+  // A wave past the last group of a partial column tile recomputes the tile's last
+  // two groups and stores nothing (group counts are multiples of 4).
+  const bool active = it.group + w * kF8GroupsPerWave < groups;  // wave-uniform
+  const int group0 = active ? it.group + w * kF8GroupsPerWave : groups - kF8GroupsPerWave;
+
+  // staged rows: w*kF8StageRows + i*4 + lane/16 (i < kF8Loads); the lane loads piece
+  // lane % 16 of each row's chunk
+  const int lda = it.shared ? g.lda_shared : g.lda_routed;
+  const uint8_t* abase = static_cast<const uint8_t*>(it.shared ? g.a_shared : g.a_routed);
+  const int piece = lane & 15;
+  const uint8_t* arow[kF8Loads];
+#pragma unroll
+  for (int i = 0; i < kF8Loads; ++i) {
+    int r = w * kF8StageRows + i * 4 + (lane >> 4);
+    r = r < it.nrows ? r : 0;
+    int ar;
+    if (it.shared)
+      ar = it.row0 + r;
+    else
+      ar = g.gather_routed ? g.sorted_pair[it.row0 + r] / g.k : it.row0 + r;
+    arow[i] = abase + (size_t)ar * lda;
+  }
+  // token scales of the chunk: thread t < 128 stages row t's two scale-block values
+  const float* asbase = it.shared ? g.as_shared : g.as_routed;
+  const float* srow;
+  {
+    const int t = threadIdx.x < kF8Rows ? threadIdx.x : 0;
+    const int r = t < it.nrows ? t : 0;
+    int ar;
+    if (it.shared)
+      ar = it.row0 + r;
+    else
+      ar = g.gather_routed ? g.sorted_pair[it.row0 + r] / g.k : it.row0 + r;
+    srow = asbase + (size_t)ar * KB;
+  }
+  // byte offset in the row of chunk c's piece for this lane (clamped past the end of
+  // K: that scale block is multiplied with weight scale 0)
+  auto a_off = [&](int c) {
+    const int o = c * 256 + piece * 16;
+    return o < K ? o : o - 128;
+  };
+  // LDS: write slot of load i (token block (w*kF8StageRows + i*4 + lane/16) / 16 =
+  // w*kF8StageRows/16 + i/4, slot = piece, row in block (i % 4) * 4 + lane / 16)
+  const int wr_off = ((w * (kF8StageRows / 16)) * 16 + piece) * kF8Slot + (lane >> 4) * 16;
+  // token block of staging load i (wave-uniform): rows of blocks past NRB are neither
+  // loaded nor written
+  auto stage_tb = [&](const int i) { return w * (kF8StageRows / 16) + i / 4; };
+  // read: slot (lane / 16) * 2 (+1 for the upper 16 bytes) of the scale block's 8
+  const int rd_off = ((lane >> 4) * 2) * kF8Slot + (lane & 15) * 16;
+
+  const uint8_t* wbase = it.shared ? static_cast<const uint8_t*>(g.w_shared)
+                                   : static_cast<const uint8_t*>(g.w_routed) + (size_t)it.seg * g.w_expert_elems;
+  const size_t group_stride = (size_t)KB * 4096;  // bytes per 32-column group
+  // 16-column block cb = (group group0 + cb / 2, half cb % 2): 2 KiB per scale block
+  const uint8_t* B = wbase + (size_t)group0 * group_stride + lane * 16;
+  const float* ws = it.shared ? g.s_shared : g.s_routed + (size_t)it.seg * g.s_expert_elems;
+  // Weight scales are staged through LDS with the activations: thread t <
+  // kF8WScales loads, for block t / (kF8WScales / 2) of a chunk, the scale of wave
+  // (t / kF8CB) % kF8Waves's 16-column block t % kF8CB.
+  int wnb;
+  {
+    const int t = threadIdx.x % (kF8WScales / 2);
+    const int w2 = t / kF8CB, cb = t % kF8CB;
+    const int g0 = it.group + w2 * kF8GroupsPerWave < groups ? it.group + w2 * kF8GroupsPerWave
+                                                             : groups - kF8GroupsPerWave;
+    const int j = g0 + (cb >> 1), half = cb & 1;
+    wnb = (SWIGLU ? half * (N / 2) + j * 16 : j * 32 + half * 16) / 128;
+  }
+
+  f32x4 acc[NRB][kF8CB];
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < kF8CB; ++cb) acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  i32x8 bring[kF8BAhead][kF8CB];
+#pragma unroll
+  for (int u = 0; u < kF8BAhead; ++u) {
+    const int s = u < KB ? u : KB - 1;
+#pragma unroll
+    for (int cb = 0; cb < kF8CB; ++cb) bring[u][cb] = f8_load32(B + (cb >> 1) * group_stride + (s * 2 + (cb & 1)) * 2048);
+  }
+
+  // Staging register sets: set (c % kF8StageSets) holds chunk c between its loads and
+  // its LDS write.  Chunk 0 -> LDS buffer 0; chunks 1 .. kF8StageSets (clamped to the
+  // last chunk) -> the sets.
+  bf16x8 stage[kF8StageSets][kF8Loads];
+  float sstage0[kF8StageSets], sstage1[kF8StageSets], wstage[kF8StageSets];
+  auto load_stage = [&](const int set, int c) {
+    c = c < NC ? c : NC - 1;
+#pragma unroll
+    for (int i = 0; i < kF8Loads; ++i)
+      if (NRB == kF8RowBlocks || stage_tb(i) < NRB)
+        stage[set][i] = *reinterpret_cast<const bf16x8*>(arow[i] + a_off(c));
+    if (threadIdx.x < kF8Rows) {
+      const int k1 = 2 * c + 1 < KB ? 2 * c + 1 : KB - 1;
+      sstage0[set] = srow[2 * c];
+      sstage1[set] = srow[k1];
+    }
+    if (threadIdx.x < kF8WScales) {
+      // a scale block past the end of K (odd K / 128) gets weight scale 0
+      const int kb = 2 * c + threadIdx.x / (kF8WScales / 2);
+      const int kbc = kb < KB ? kb : KB - 1;
+      wstage[set] = ws[(size_t)kbc * NB + wnb] * (kb < KB ? 1.f : 0.f);
+    }
+  };
+  auto write_stage = [&](const int set, int buf) {
+#pragma unroll
+    for (int i = 0; i < kF8Loads; ++i)
+      if (NRB == kF8RowBlocks || stage_tb(i) < NRB)
+        *reinterpret_cast<bf16x8*>(lds + buf + wr_off + (i >> 2) * 16 * kF8Slot + (i & 3) * 64) = stage[set][i];
+    if (threadIdx.x < kF8Rows) {
+      float* s = reinterpret_cast<float*>(lds + buf + kF8A);
+      s[threadIdx.x] = sstage0[set];
+      s[kF8Rows + threadIdx.x] = sstage1[set];
+    }
+    if (threadIdx.x < kF8WScales)
+      reinterpret_cast<float*>(lds + buf + kF8A)[2 * kF8Rows + threadIdx.x] = wstage[set];
+  };
+  load_stage(0, 0);
+  write_stage(0, 0);
+#pragma unroll
+  for (int u = 1; u <= kF8StageSets; ++u) load_stage(u % kF8StageSets, u);
+  __syncthreads();
+
+  // One 128-deep scale block: h is the block within the chunk, r its weight-ring slot
+  // (block % kF8BAhead).
+  auto block = [&](const int c, const int h, const int r, const int buf) {
+    const int kb = 2 * c + h;
+    const float* swl = reinterpret_cast<const float*>(lds + buf + kF8A) + 2 * kF8Rows +
+                       h * (kF8WScales / 2) + w * kF8CB;
+    float wsc[kF8CB];
+#pragma unroll
+    for (int cb = 0; cb < kF8CB; ++cb) wsc[cb] = swl[cb];
+    const float* sbuf = reinterpret_cast<const float*>(lds + buf + kF8A) + h * kF8Rows + (lane & 15);
+    // Software pipeline over token blocks: block rb + D's operand is read from LDS
+    // (D = kF8LdsAhead) and block rb - 1's products are rescaled while block rb's MFMAs
+    // run.  The products alternate between two register sets; operands rotate over
+    // D + 1 slots and token scales over D + 2, as step rb reads block rb + D's while
+    // block rb - 1's is in use.
+    constexpr int D = kF8LdsAhead;
+    f32x4 p[2][kF8CB];
+    i32x8 av[D + 1];
+    float sa[D + 2];
+    auto rd = [&](const int rb) {
+      const unsigned char* ap = lds + buf + (rb * 16 + h * 8) * kF8Slot + rd_off;
+      const i32x4 l4 = *reinterpret_cast<const i32x4*>(ap);
+      const i32x4 h4 = *reinterpret_cast<const i32x4*>(ap + kF8Slot);
+      av[rb % (D + 1)] = i32x8{l4[0], l4[1], l4[2], l4[3], h4[0], h4[1], h4[2], h4[3]};
+      sa[rb % (D + 2)] = sbuf[rb * 16];
+    };
+    auto fm = [&](const int rb) {
+#pragma unroll
+      for (int cb = 0; cb < kF8CB; ++cb) {
+        const float sc = sa[rb % (D + 2)] * wsc[cb];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[rb][cb][i] = fmaf(p[rb & 1][cb][i], sc, acc[rb][cb][i]);
+      }
+    };
+#pragma unroll
+    for (int rb = 0; rb < D; ++rb) rd(rb);
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (rb + D < NRB) rd(rb + D);
+      f32x4* pc = p[rb & 1];
+#pragma unroll
+      for (int cb = 0; cb < kF8CB; ++cb) pc[cb] = f8_mfma(bring[r][cb], av[rb % (D + 1)]);
+      if (rb > 0) fm(rb - 1);
+      if (rb + D < NRB) __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+#pragma unroll
+      for (int cb = 0; cb < kF8CB; ++cb) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (rb > 0) __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+      }
+      // keep this step's MFMAs and the previous step's rescaling inside the step
+#pragma unroll
+      for (int cb = 0; cb < kF8CB; ++cb) asm volatile("" ::"v"(pc[cb]));
+      if (rb > 0) {
+        f32x4* ac = acc[rb - 1];
+#pragma unroll
+        for (int cb = 0; cb < kF8CB; ++cb) asm volatile("" : "+v"(ac[cb]));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    fm(NRB - 1);
+    // refill this ring slot with the block kF8BAhead ahead (clamped to the last)
+    int sn = kb + kF8BAhead;
+    sn = sn < KB ? sn : KB - 1;
+#pragma unroll
+    for (int cb = 0; cb < kF8CB; ++cb)
+      bring[r][cb] = f8_load32(B + (cb >> 1) * group_stride + (sn * 2 + (cb & 1)) * 2048);
+  };
+
+  // Chunk c (parity u = c % 2 when unrolled) computes from LDS buffer c % 2; at its
+  // end chunk c + 1 leaves its staging set for the other buffer, and that set starts
+  // loading chunk c + 1 + kF8StageSets (clamped past the end; never consumed there).
+  auto chunk = [&](const int c, const int u) {
+    const int buf = u * kF8Buf;
+    block(c, 0, (2 * u) % kF8BAhead, buf);
+    block(c, 1, (2 * u + 1) % kF8BAhead, buf);
+    const int set = (u + 1) % kF8StageSets;
+    write_stage(set, kF8Buf - buf);
+    __syncthreads();
+    load_stage(set, c + 1 + kF8StageSets);
+  };
+  for (int c = 0; c < NC; c += kF8Unroll) {
+    if (kF8Unroll == 1) {
+      chunk(c, c & 1);
+    } else {
+      chunk(c, 0);
+      if (c + 1 < NC) chunk(c + 1, 1);
+    }
+  }
+
+  float* qscale = it.shared ? g.outs_shared : g.outs_routed;
+  if (SWIGLU && qscale) {
+    // h quantised in place of the separate pass: the tile's 8 groups are exactly one
+    // 128-channel quantisation group of each of its tokens (gate/up column tiles are
+    // whole, as 2M/32 is a multiple of 8).  Per token: amax over the 4 lanes of
+    // each wave holding it, then over the 4 waves through LDS; scale = amax / 448
+    // (1 for an all-zero group); codes = e4m3(v * (1 / scale)) with the reciprocal
+    // rounded once per token group, one rounding more than the quantisation kernel's
+    // e4m3(v / scale), and SiLU through the hardware reciprocal: h is internal to
+    // the layer, and its codes may differ from the streaming path's by one step.
+    const int tok = lane & 15;
+    const int n0 = (lane >> 4) * 4;
+    f32x4 hv[NRB][kF8GroupsPerWave];
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      float m = 0.f;
+#pragma unroll
+      for (int j = 0; j < kF8GroupsPerWave; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          hv[rb][j][i] = silu_rcp(acc[rb][2 * j][i]) * acc[rb][2 * j + 1][i];
+          m = fmaxf(m, fabsf(hv[rb][j][i]));
+        }
+      m = fmaxf(m, __shfl_xor(m, 16, kWave));
+      m = fmaxf(m, __shfl_xor(m, 32, kWave));
+      if (lane < 16) qamax[w][rb * 16 + tok] = m;
+    }
+    __syncthreads();
+    uint8_t* q = static_cast<uint8_t*>(it.shared ? g.out_shared : g.out_routed);
+    const int ldo = it.shared ? g.ldo_shared : g.ldo_routed;
+    const int qgroups = ldo / 128;
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      const int t = rb * 16 + tok;
+      float amax = qamax[0][t];
+#pragma unroll
+      for (int v = 1; v < kF8Waves; ++v) amax = fmaxf(amax, qamax[v][t]);
+      const float sc = amax > 0.f ? amax / 448.f : 1.f;
+      const float inv = 1.f / sc;  // one division per token group; codes = e4m3(v * (1 / scale))
+      if (t < it.nrows) {
+        const size_t row = (size_t)(it.row0 + t);
+#pragma unroll
+        for (int j = 0; j < kF8GroupsPerWave; ++j)
+          *reinterpret_cast<uint32_t*>(q + row * ldo + (group0 + j) * 16 + n0) =
+              e4m3_pack4(hv[rb][j][0] * inv, hv[rb][j][1] * inv, hv[rb][j][2] * inv, hv[rb][j][3] * inv);
+        if (w == 0 && lane < 16) qscale[row * qgroups + it.group / 8] = sc;
+      }
+    }
+  } else if (active) {
+    const int tok = lane & 15;
+    const int n0 = (lane >> 4) * 4;
+    float* out = static_cast<float*>(it.shared ? g.out_shared : g.out_routed);
+    const int ldo = it.shared ? g.ldo_shared : g.ldo_routed;
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      const int t = rb * 16 + tok;
+      if (t >= it.nrows) continue;
+      float* o = out + (size_t)(it.row0 + t) * ldo;
+#pragma unroll
+      for (int j = 0; j < kF8GroupsPerWave; ++j) {
+        if (SWIGLU) {
+          f32x4 v;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] = silu(acc[rb][2 * j][i]) * acc[rb][2 * j + 1][i];
+          *reinterpret_cast<f32x4*>(o + (group0 + j) * 16 + n0) = v;
+        } else {
+          // bf16 output rows for the combine: 4 consecutive channels, one 8-byte store
+          __bf16* orow = static_cast<__bf16*>(it.shared ? g.out_shared : g.out_routed) +
+                         (size_t)(it.row0 + t) * ldo;
+#pragma unroll
+          for (int hlf = 0; hlf < 2; ++hlf) {
+            const f32x4 v = acc[rb][2 * j + hlf];
+            uint2 pk;
+            pk.x = (uint32_t)bf16_bits(f32_to_bf16(v[0])) | ((uint32_t)bf16_bits(f32_to_bf16(v[1])) << 16);
+            pk.y = (uint32_t)bf16_bits(f32_to_bf16(v[2])) | ((uint32_t)bf16_bits(f32_to_bf16(v[3])) << 16);
+            *reinterpret_cast<uint2*>(orow + (group0 + j) * 32 + hlf * 16 + n0) = pk;
+          }
+        }
+      }
+    }
+  }
+}
 
 template <bool SWIGLU>
 __global__ void __launch_bounds__(kF8Threads, kF8MinBlocks) gemm_fp8_tiled_kernel(GroupedGemm g) {
@@ -108,287 +446,22 @@ __global__ void __launch_bounds__(kF8Threads, kF8MinBlocks) gemm_fp8_tiled_kerne
   const int end = (int)((long long)total * (xcd + 1) / kF8Xcds);
 
   for (int item = begin + slot; item < end; item += slots) {
-    // lane-derived indices are recomputed per item (hoisted out of the item loop they
-    // do not fit the register budget)
-    int lane = lane_id();
-    asm volatile("" : "+v"(lane));
     const Item it = decode_item_tiled(g, kF8Rows, kF8Groups, prefix, item);
-    const int K = it.shared ? g.K_shared : g.K_routed;
-    const int KB = K / 128;
-    const int NC = (KB + 1) / 2;  // 256-deep chunks; an odd KB leaves the last chunk half live
-    const int groups = it.shared ? g.groups_shared : g.groups_routed;
-    const int N = groups * 32;
-    const int NB = N / 128;
-    // A wave past the last group of a partial column tile recomputes the tile's last
-    // two groups and stores nothing (group counts are multiples of 4).
-    const bool active = it.group + w * kF8GroupsPerWave < groups;  // wave-uniform
-    const int group0 = active ? it.group + w * kF8GroupsPerWave : groups - kF8GroupsPerWave;
-
-    // staged rows: w*32 + i*4 + lane/16 (i = 0..7); the lane loads piece lane % 16 of
-    // each row's chunk
-    const int lda = it.shared ? g.lda_shared : g.lda_routed;
-    const uint8_t* abase = static_cast<const uint8_t*>(it.shared ? g.a_shared : g.a_routed);
-    const int piece = lane & 15;
-    const uint8_t* arow[kF8Loads];
-#pragma unroll
-    for (int i = 0; i < kF8Loads; ++i) {
-      int r = w * 32 + i * 4 + (lane >> 4);
-      r = r < it.nrows ? r : 0;
-      int ar;
-      if (it.shared)
-        ar = it.row0 + r;
-      else
-        ar = g.gather_routed ? g.sorted_pair[it.row0 + r] / g.k : it.row0 + r;
-      arow[i] = abase + (size_t)ar * lda;
-    }
-    // token scales of the chunk: thread t < 128 stages row t's two scale-block values
-    const float* asbase = it.shared ? g.as_shared : g.as_routed;
-    const float* srow;
-    {
-      const int t = threadIdx.x < kF8Rows ? threadIdx.x : 0;
-      const int r = t < it.nrows ? t : 0;
-      int ar;
-      if (it.shared)
-        ar = it.row0 + r;
-      else
-        ar = g.gather_routed ? g.sorted_pair[it.row0 + r] / g.k : it.row0 + r;
-      srow = asbase + (size_t)ar * KB;
-    }
-    // byte offset in the row of chunk c's piece for this lane (clamped past the end of
-    // K: that scale block is multiplied with weight scale 0)
-    auto a_off = [&](int c) {
-      const int o = c * 256 + piece * 16;
-      return o < K ? o : o - 128;
-    };
-    // LDS: write slot of load i (token block (w*32 + i*4 + lane/16) / 16 = w*2 + i/4,
-    // slot = piece, row in block (i % 4) * 4 + lane / 16)
-    const int wr_off = ((w * 2) * 16 + piece) * kF8Slot + (lane >> 4) * 16;
-    // read: slot (lane / 16) * 2 (+1 for the upper 16 bytes) of the scale block's 8
-    const int rd_off = ((lane >> 4) * 2) * kF8Slot + (lane & 15) * 16;
-
-    const uint8_t* wbase = it.shared ? static_cast<const uint8_t*>(g.w_shared)
-                                     : static_cast<const uint8_t*>(g.w_routed) + (size_t)it.seg * g.w_expert_elems;
-    const size_t group_stride = (size_t)KB * 4096;  // bytes per 32-column group
-    // 16-column block cb = (group group0 + cb / 2, half cb % 2): 2 KiB per scale block
-    const uint8_t* B = wbase + (size_t)group0 * group_stride + lane * 16;
-    const float* ws = it.shared ? g.s_shared : g.s_routed + (size_t)it.seg * g.s_expert_elems;
-    // Weight scales are staged through LDS with the activations: thread t <
-    // kF8WScales loads, for block t / (kF8WScales / 2) of a chunk, the scale of wave
-    // (t / kF8CB) % kF8Waves's 16-column block t % kF8CB.
-    int wnb;
-    {
-      const int t = threadIdx.x % (kF8WScales / 2);
-      const int w2 = t / kF8CB, cb = t % kF8CB;
-      const int g0 = it.group + w2 * kF8GroupsPerWave < groups ? it.group + w2 * kF8GroupsPerWave
-                                                               : groups - kF8GroupsPerWave;
-      const int j = g0 + (cb >> 1), half = cb & 1;
-      wnb = (SWIGLU ? half * (N / 2) + j * 16 : j * 32 + half * 16) / 128;
-    }
-
-    f32x4 acc[kF8RowBlocks][kF8CB];
-#pragma unroll
-    for (int rb = 0; rb < kF8RowBlocks; ++rb)
-#pragma unroll
-      for (int cb = 0; cb < kF8CB; ++cb) acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    i32x8 bring[kF8BAhead][kF8CB];
-#pragma unroll
-    for (int u = 0; u < kF8BAhead; ++u) {
-      const int s = u < KB ? u : KB - 1;
-#pragma unroll
-      for (int cb = 0; cb < kF8CB; ++cb) bring[u][cb] = f8_load32(B + (cb >> 1) * group_stride + (s * 2 + (cb & 1)) * 2048);
-    }
-
-    // chunk 0 -> LDS buffer 0, chunk 1 (or 0 again) -> staging registers
-    bf16x8 stage[kF8Loads];
-    float sstage0 = 0.f, sstage1 = 0.f, wstage = 0.f;
-    auto load_stage = [&](int c) {
-#pragma unroll
-      for (int i = 0; i < kF8Loads; ++i) stage[i] = *reinterpret_cast<const bf16x8*>(arow[i] + a_off(c));
-      if (threadIdx.x < kF8Rows) {
-        const int k1 = 2 * c + 1 < KB ? 2 * c + 1 : KB - 1;
-        sstage0 = srow[2 * c];
-        sstage1 = srow[k1];
-      }
-      if (threadIdx.x < kF8WScales) {
-        // a scale block past the end of K (odd K / 128) gets weight scale 0
-        const int kb = 2 * c + threadIdx.x / (kF8WScales / 2);
-        const int kbc = kb < KB ? kb : KB - 1;
-        wstage = ws[(size_t)kbc * NB + wnb] * (kb < KB ? 1.f : 0.f);
-      }
-    };
-    auto write_stage = [&](int buf) {
-#pragma unroll
-      for (int i = 0; i < kF8Loads; ++i)
-        *reinterpret_cast<bf16x8*>(lds + buf + wr_off + (i >> 2) * 16 * kF8Slot + (i & 3) * 64) = stage[i];
-      if (threadIdx.x < kF8Rows) {
-        float* s = reinterpret_cast<float*>(lds + buf + kF8A);
-        s[threadIdx.x] = sstage0;
-        s[kF8Rows + threadIdx.x] = sstage1;
-      }
-      if (threadIdx.x < kF8WScales) reinterpret_cast<float*>(lds + buf + kF8A)[2 * kF8Rows + threadIdx.x] = wstage;
-    };
-    load_stage(0);
-    write_stage(0);
-    load_stage(NC > 1 ? 1 : 0);
-    __syncthreads();
-
-    // One 128-deep scale block: h is the block within the chunk and also the weight-ring
-    // slot (scale blocks alternate slots; a chunk holds one of each).
-    auto block = [&](const int c, const int h, const int buf) {
-      const int kb = 2 * c + h;
-      const float* swl = reinterpret_cast<const float*>(lds + buf + kF8A) + 2 * kF8Rows +
-                         h * (kF8WScales / 2) + w * kF8CB;
-      float wsc[kF8CB];
-#pragma unroll
-      for (int cb = 0; cb < kF8CB; ++cb) wsc[cb] = swl[cb];
-      const float* sbuf = reinterpret_cast<const float*>(lds + buf + kF8A) + h * kF8Rows + (lane & 15);
-      // Software pipeline over token blocks: block rb + 1's operand is read from LDS
-      // and block rb - 1's products are rescaled while block rb's MFMAs run.  The
-      // products alternate between two register sets; the token scales rotate over
-      // three slots, as step rb reads block rb + 1's while block rb - 1's is in use.
-      f32x4 p[2][kF8CB];
-      i32x8 av[2];
-      float sa[3];
-      auto rd = [&](const int rb) {
-        const unsigned char* ap = lds + buf + (rb * 16 + h * 8) * kF8Slot + rd_off;
-        const i32x4 l4 = *reinterpret_cast<const i32x4*>(ap);
-        const i32x4 h4 = *reinterpret_cast<const i32x4*>(ap + kF8Slot);
-        av[rb & 1] = i32x8{l4[0], l4[1], l4[2], l4[3], h4[0], h4[1], h4[2], h4[3]};
-        sa[rb % 3] = sbuf[rb * 16];
-      };
-      auto fm = [&](const int rb) {
-#pragma unroll
-        for (int cb = 0; cb < kF8CB; ++cb) {
-          const float sc = sa[rb % 3] * wsc[cb];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[rb][cb][i] = fmaf(p[rb & 1][cb][i], sc, acc[rb][cb][i]);
-        }
-      };
-      rd(0);
-#pragma unroll
-      for (int rb = 0; rb < kF8RowBlocks; ++rb) {
-        __builtin_amdgcn_sched_barrier(0);
-        if (rb + 1 < kF8RowBlocks) rd(rb + 1);
-        f32x4* pc = p[rb & 1];
-#pragma unroll
-        for (int cb = 0; cb < kF8CB; ++cb) pc[cb] = f8_mfma(bring[h][cb], av[rb & 1]);
-        if (rb > 0) fm(rb - 1);
-        if (rb + 1 < kF8RowBlocks) __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
-#pragma unroll
-        for (int cb = 0; cb < kF8CB; ++cb) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          if (rb > 0) __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
-        }
-        // keep this step's MFMAs and the previous step's rescaling inside the step
-        asm volatile("" ::"v"(pc[0]), "v"(pc[1]), "v"(pc[2]), "v"(pc[3]));
-        if (rb > 0) {
-          f32x4* ac = acc[rb - 1];
-          asm volatile("" : "+v"(ac[0]), "+v"(ac[1]), "+v"(ac[2]), "+v"(ac[3]));
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      fm(kF8RowBlocks - 1);
-      // refill this ring slot with the block kF8BAhead ahead (clamped to the last)
-      int sn = kb + kF8BAhead;
-      sn = sn < KB ? sn : KB - 1;
-#pragma unroll
-      for (int cb = 0; cb < kF8CB; ++cb)
-        bring[h][cb] = f8_load32(B + (cb >> 1) * group_stride + (sn * 2 + (cb & 1)) * 2048);
-    };
-
-    for (int c = 0; c < NC; ++c) {
-      const int buf = (c & 1) * kF8Buf;
-      block(c, 0, buf);
-      block(c, 1, buf);
-      // chunk boundary: the next chunk (in registers) goes to the other buffer, then
-      // the one after it is loaded (clamped past the end; never consumed there)
-      write_stage(kF8Buf - buf);
-      __syncthreads();
-      load_stage(c + 2 < NC ? c + 2 : NC - 1);
-    }
-
-    float* qscale = it.shared ? g.outs_shared : g.outs_routed;
-    if (SWIGLU && qscale) {
-      // h quantised in place of the separate pass: the tile's 8 groups are exactly one
-      // 128-channel quantisation group of each of its tokens (gate/up column tiles are
-      // whole, as 2M/32 is a multiple of 8).  Per token: amax over the 4 lanes of
-      // each wave holding it, then over the 4 waves through LDS; scale = amax / 448
-      // (1 for an all-zero group); codes = e4m3(v * (1 / scale)) with the reciprocal
-      // rounded once per token group, one rounding more than the quantisation kernel's
-      // e4m3(v / scale), and SiLU through the hardware reciprocal: h is internal to
-      // the layer, and its codes may differ from the streaming path's by one step.
-      const int tok = lane & 15;
-      const int n0 = (lane >> 4) * 4;
-      f32x4 hv[kF8RowBlocks][kF8GroupsPerWave];
-#pragma unroll
-      for (int rb = 0; rb < kF8RowBlocks; ++rb) {
-        float m = 0.f;
-#pragma unroll
-        for (int j = 0; j < kF8GroupsPerWave; ++j)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            hv[rb][j][i] = silu_rcp(acc[rb][2 * j][i]) * acc[rb][2 * j + 1][i];
-            m = fmaxf(m, fabsf(hv[rb][j][i]));
-          }
-        m = fmaxf(m, __shfl_xor(m, 16, kWave));
-        m = fmaxf(m, __shfl_xor(m, 32, kWave));
-        if (lane < 16) qamax[w][rb * 16 + tok] = m;
-      }
-      __syncthreads();
-      uint8_t* q = static_cast<uint8_t*>(it.shared ? g.out_shared : g.out_routed);
-      const int ldo = it.shared ? g.ldo_shared : g.ldo_routed;
-      const int qgroups = ldo / 128;
-#pragma unroll
-      for (int rb = 0; rb < kF8RowBlocks; ++rb) {
-        const int t = rb * 16 + tok;
-        float amax = qamax[0][t];
-#pragma unroll
-        for (int v = 1; v < kF8Waves; ++v) amax = fmaxf(amax, qamax[v][t]);
-        const float sc = amax > 0.f ? amax / 448.f : 1.f;
-        const float inv = 1.f / sc;  // one division per token group; codes = e4m3(v * (1 / scale))
-        if (t < it.nrows) {
-          const size_t row = (size_t)(it.row0 + t);
-#pragma unroll
-          for (int j = 0; j < kF8GroupsPerWave; ++j)
-            *reinterpret_cast<uint32_t*>(q + row * ldo + (group0 + j) * 16 + n0) =
-                e4m3_pack4(hv[rb][j][0] * inv, hv[rb][j][1] * inv, hv[rb][j][2] * inv, hv[rb][j][3] * inv);
-          if (w == 0 && lane < 16) qscale[row * qgroups + it.group / 8] = sc;
-        }
-      }
-    } else if (active) {
-      const int tok = lane & 15;
-      const int n0 = (lane >> 4) * 4;
-      float* out = static_cast<float*>(it.shared ? g.out_shared : g.out_routed);
-      const int ldo = it.shared ? g.ldo_shared : g.ldo_routed;
-#pragma unroll
-      for (int rb = 0; rb < kF8RowBlocks; ++rb) {
-        const int t = rb * 16 + tok;
-        if (t >= it.nrows) continue;
-        float* o = out + (size_t)(it.row0 + t) * ldo;
-#pragma unroll
-        for (int j = 0; j < kF8GroupsPerWave; ++j) {
-          if (SWIGLU) {
-            f32x4 v;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) v[i] = silu(acc[rb][2 * j][i]) * acc[rb][2 * j + 1][i];
-            *reinterpret_cast<f32x4*>(o + (group0 + j) * 16 + n0) = v;
-          } else {
-            // bf16 output rows for the combine: 4 consecutive channels, one 8-byte store
-            __bf16* orow = static_cast<__bf16*>(it.shared ? g.out_shared : g.out_routed) +
-                           (size_t)(it.row0 + t) * ldo;
-#pragma unroll
-            for (int hlf = 0; hlf < 2; ++hlf) {
-              const f32x4 v = acc[rb][2 * j + hlf];
-              uint2 pk;
-              pk.x = (uint32_t)bf16_bits(f32_to_bf16(v[0])) | ((uint32_t)bf16_bits(f32_to_bf16(v[1])) << 16);
-              pk.y = (uint32_t)bf16_bits(f32_to_bf16(v[2])) | ((uint32_t)bf16_bits(f32_to_bf16(v[3])) << 16);
-              *reinterpret_cast<uint2*>(orow + (group0 + j) * 32 + hlf * 16 + n0) = pk;
-            }
-          }
-        }
-      }
-    }
+    // the item's computation is specialised on its count of 16-row blocks, so the
+    // padding of a partly filled tile costs neither matrix-core nor rescaling work
+    const int nb = (it.nrows + 15) / 16;  // wave-uniform
+    if (nb == 8)
+      fp8_tile<SWIGLU, 8>(g, it, w, lds, qamax);
+    else if (nb == 7)
+      fp8_tile<SWIGLU, 7>(g, it, w, lds, qamax);
+    else if (nb == 6)
+      fp8_tile<SWIGLU, 6>(g, it, w, lds, qamax);
+    else if (nb == 5)
+      fp8_tile<SWIGLU, 5>(g, it, w, lds, qamax);
+    else if (nb >= 3)
+      fp8_tile<SWIGLU, 4>(g, it, w, lds, qamax);
+    else
+      fp8_tile<SWIGLU, 2>(g, it, w, lds, qamax);
     // every LDS read of this item happened before its last chunk's barrier
   }
 }
