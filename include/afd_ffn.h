@@ -211,6 +211,21 @@ int afd_ffn_forward(afd_ffn_t h, const void* x, int32_t T, const afd_route* r, v
 int afd_ffn_forward_fp8_input(afd_ffn_t h, const uint8_t* xq, const float* xs, int32_t T, const afd_route* r,
                               void* y, void* stream);
 
+/* afd_ffn_forward for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same kernels
+ * and the same result, bit for bit, but the intermediate buffers (h, the expert
+ * outputs, the fp8 codes and scales of x and h) come from a static device array of
+ * 64 MiB that the library holds on each GPU it runs on (the handle's workspace is not
+ * used).  It allocates nothing and needs no zeroed memory.  Calls on one GPU share
+ * that array: two calls in flight at once on one GPU, on any handles or streams, race.
+ * The buffers are laid out for the handle's max_tokens (so that every route the handle
+ * accepts fits them): a handle whose layout exceeds 64 MiB (roughly
+ * (max_tokens * top_k) * (M + H) * 2 bytes for a bf16 layer, plus the shared expert's
+ * max_tokens * (Ms + H) * 2; about 25 KB per pair at H = 7168, M = 2048 in fp8) is
+ * refused with AFD_EINVAL and nothing is enqueued.  Arguments and errors otherwise as
+ * afd_ffn_forward. */
+int afd_ffn_forward_noalloc(afd_ffn_t h, const void* x, int32_t T, const afd_route* r, void* y, void* stream);
+
 /* Release the handle's weights and workspace.  The caller must have synchronised
  * every stream with work of this handle.  NULL is a no-op. */
 int afd_ffn_destroy(afd_ffn_t h);

@@ -61,6 +61,8 @@ def load():
     lib.afd_ffn_forward.argtypes = [V, P, I32, ctypes.POINTER(afd_route), P, V]
     lib.afd_ffn_forward.restype = ctypes.c_int
     lib.afd_ffn_forward_fp8_input.argtypes = [V, P, P, I32, ctypes.POINTER(afd_route), P, V]
+    lib.afd_ffn_forward_noalloc.argtypes = [V, P, I32, ctypes.POINTER(afd_route), P, V]
+    lib.afd_ffn_forward_noalloc.restype = ctypes.c_int
     lib.afd_ffn_forward_fp8_input.restype = ctypes.c_int
     lib.afd_ffn_destroy.argtypes = [V]
     lib.afd_ffn_destroy.restype = ctypes.c_int
@@ -143,6 +145,10 @@ def afd_ffn_route_hidden(h: int, x, w_router, bias, logits, T: int, route: afd_r
 
 def afd_ffn_forward(h: int, x, T: int, route: afd_route, y, stream=None) -> None:
     _check(load().afd_ffn_forward(h, _ptr(x), int(T), ctypes.byref(route), _ptr(y), stream))
+
+
+def afd_ffn_forward_noalloc(h: int, x, T: int, route: afd_route, y, stream=None) -> None:
+    _check(load().afd_ffn_forward_noalloc(h, _ptr(x), int(T), ctypes.byref(route), _ptr(y), stream))
 
 
 def afd_ffn_forward_fp8_input(h: int, xq, xs, T: int, route: afd_route, y, stream=None) -> None:

@@ -6,12 +6,24 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <new>
 
 #include "afd_internal.h"
 #include "capacity.h"
 
 namespace {
+
+// Device scratch of afd_ffn_forward_noalloc: the intermediate buffers of one forward
+// call, for callers that cannot allocate device memory.  Each GPU the library runs on
+// holds its own copy until the process ends.  In host code `scratch` only names the
+// symbol; kernels get its device address, looked up once per device at handle
+// creation (with that device current) and kept in g_scratch.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
 
 thread_local char g_last_error[512] = "";
 
@@ -24,6 +36,18 @@ int fail(int code, const char* fmt, ...) {
 }
 
 int hip_fail(hipError_t e, const char* what) { return fail(AFD_EHIP, "%s: %s", what, hipGetErrorString(e)); }
+
+// Device address of `scratch` on device `dev`, which must be current.
+int scratch_address(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return fail(AFD_EUNSUPPORTED, "device %d above the %d devices supported", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev]) return AFD_OK;
+  void* p = nullptr;
+  hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+  g_scratch[dev] = p;
+  return AFD_OK;
+}
 
 size_t elem_size(int dtype) { return dtype == AFD_F32 ? 4 : dtype == AFD_BF16 ? 2 : 1; }
 
@@ -170,15 +194,15 @@ int route_rows(const afd_ffn* h, const afd_route* r, int T) {
 // fp8 layer: quantise x -> gate/up GEMM -> quantise h (in the tiled GEMM's epilogue, else a
 // separate pass over fp32 h) -> down GEMM -> combine.
 // x == NULL: g1 already points at caller-quantised activations (no quantisation launch).
-int forward_fp8(afd_ffn* h, const void* x, int T, const afd_route* r, void* y, hipStream_t st,
-                const afd::GroupedGemm& g1, const afd::GroupedGemm& g2) {
+int forward_fp8(afd_ffn* h, const afd_workspace& ws, const void* x, int T, const afd_route* r, void* y,
+                hipStream_t st, const afd::GroupedGemm& g1, const afd::GroupedGemm& g2) {
   const afd_ffn_config& c = h->cfg;
   const int H = c.hidden, M = c.inter, Ms = c.shared_inter, E = c.num_experts, k = c.top_k;
   const int P = T * k;
   const int rows = route_rows(h, r, T);
   if (x) {
     StageScope s(h, st, AFD_STAGE_QUANT);
-    hipError_t e = afd::launch_quant_fp8(x, T, H, H, true, h->xq, h->xs, st);
+    hipError_t e = afd::launch_quant_fp8(x, T, H, H, true, ws.xq, ws.xs, st);
     if (e != hipSuccess) return hip_fail(e, "x quantisation launch");
     s.done();
   }
@@ -197,10 +221,10 @@ int forward_fp8(afd_ffn* h, const void* x, int T, const afd_route* r, void* y, h
   if (tiled) {
     // the tiled gate/up GEMM quantises h in its epilogue (no fp32 h round trip)
     afd::GroupedGemm gq = g1;
-    gq.out_routed = h->hq_routed;
-    gq.outs_routed = h->hs_routed;
-    gq.out_shared = h->hq_shared;
-    gq.outs_shared = h->hs_shared;
+    gq.out_routed = ws.hq_routed;
+    gq.outs_routed = ws.hs_routed;
+    gq.out_shared = ws.hq_shared;
+    gq.outs_shared = ws.hs_shared;
     StageScope s(h, st, AFD_STAGE_GATE_UP);
     hipError_t e = afd::launch_gemm_fp8_tiled(gq, true, items1, h->num_cus, st);
     if (e != hipSuccess) return hip_fail(e, "fp8 gate/up GEMM launch");
@@ -214,8 +238,8 @@ int forward_fp8(afd_ffn* h, const void* x, int T, const afd_route* r, void* y, h
     }
     StageScope s(h, st, AFD_STAGE_QUANT);
     // routed and shared h in one launch
-    const afd::QuantSeg routed = {h->h_routed, P, M, M, h->hq_routed, h->hs_routed};
-    const afd::QuantSeg shared = {h->h_shared, Ms ? T : 0, Ms ? Ms : 128, Ms ? Ms : 128, h->hq_shared, h->hs_shared};
+    const afd::QuantSeg routed = {ws.h_routed, P, M, M, ws.hq_routed, ws.hs_routed};
+    const afd::QuantSeg shared = {ws.h_shared, Ms ? T : 0, Ms ? Ms : 128, Ms ? Ms : 128, ws.hq_shared, ws.hs_shared};
     hipError_t e = afd::launch_quant_fp8_segments(routed, shared, false, st);
     if (e != hipSuccess) return hip_fail(e, "h quantisation launch");
     s.done();
@@ -229,7 +253,7 @@ int forward_fp8(afd_ffn* h, const void* x, int T, const afd_route* r, void* y, h
   }
   {
     StageScope s(h, st, AFD_STAGE_COMBINE);
-    hipError_t e = afd::launch_combine(h->o_routed, Ms ? h->o_shared : nullptr, r->topk_gates, r->pair_pos, T, k, H, y,
+    hipError_t e = afd::launch_combine(ws.o_routed, Ms ? ws.o_shared : nullptr, r->topk_gates, r->pair_pos, T, k, H, y,
                                        true, st);
     if (e != hipSuccess) return hip_fail(e, "combine launch");
     s.done();
@@ -304,6 +328,13 @@ extern "C" int afd_ffn_create(const afd_ffn_config* cfg, const void* w_gate_up, 
     return hip_fail(e, "hipGetDeviceProperties");
   }
   h->num_cus = prop.multiProcessorCount;
+  {
+    const int rc2 = scratch_address(h->device);
+    if (rc2 != AFD_OK) {
+      release(h);
+      return rc2;
+    }
+  }
   e = afd::configure_gemm_bf16_tiled();
   if (e == hipSuccess) e = afd::configure_gemm_fp8_tiled();
   if (e != hipSuccess) {
@@ -555,10 +586,15 @@ extern "C" int afd_ffn_route_hidden(afd_ffn_t h, const void* x, const void* w_ro
   return afd_ffn_route(h, logits, T, r, stream);
 }
 
+static afd_workspace handle_workspace(const afd_ffn* h) {
+  return {h->h_routed, h->h_shared, h->o_routed, h->o_shared, h->xq, h->xs,
+          h->hq_routed, h->hs_routed, h->hq_shared, h->hs_shared};
+}
+
 // Steps a0 and a5-a8 on checked arguments.  fp8 layers: x (bf16) is quantised here,
 // or, when x is NULL, xq / xs are the caller's e4m3 codes and scales of it.
-static int forward_checked(afd_ffn_t h, const void* x, const uint8_t* xq, const float* xs, int32_t T,
-                           const afd_route* r, void* y, hipStream_t st) {
+static int forward_checked(afd_ffn_t h, const afd_workspace& ws, const void* x, const uint8_t* xq, const float* xs,
+                           int32_t T, const afd_route* r, void* y, hipStream_t st) {
   const afd_ffn_config& c = h->cfg;
   const int H = c.hidden, M = c.inter, Ms = c.shared_inter, E = c.num_experts, k = c.top_k;
   const int P = T * k;
@@ -584,8 +620,8 @@ static int forward_checked(afd_ffn_t h, const void* x, const uint8_t* xq, const 
   g1.a_shared = x;
   g1.lda_routed = H;
   g1.lda_shared = H;
-  g1.out_routed = h->h_routed;
-  g1.out_shared = h->h_shared;
+  g1.out_routed = ws.h_routed;
+  g1.out_shared = ws.h_shared;
   g1.ldo_routed = M;
   g1.ldo_shared = Ms;
 
@@ -598,31 +634,31 @@ static int forward_checked(afd_ffn_t h, const void* x, const uint8_t* xq, const 
   g2.w_routed = h->w_d;
   g2.w_expert_elems = h->w_d_expert_elems;
   g2.w_shared = h->ws_d;
-  g2.a_routed = h->h_routed;
-  g2.a_shared = h->h_shared;
+  g2.a_routed = ws.h_routed;
+  g2.a_shared = ws.h_shared;
   g2.lda_routed = M;
   g2.lda_shared = Ms;
-  g2.out_routed = h->o_routed;
-  g2.out_shared = h->o_shared;
+  g2.out_routed = ws.o_routed;
+  g2.out_shared = ws.o_shared;
   g2.ldo_routed = H;
   g2.ldo_shared = H;
 
   if (fp8) {
-    g1.a_routed = x ? h->xq : xq;
+    g1.a_routed = x ? ws.xq : xq;
     g1.a_shared = g1.a_routed;
-    g1.as_routed = x ? h->xs : xs;
+    g1.as_routed = x ? ws.xs : xs;
     g1.as_shared = g1.as_routed;
     g1.s_routed = h->s_gu;
     g1.s_expert_elems = (size_t)(H / 128) * (2 * M / 128);
     g1.s_shared = h->ss_gu;
-    g2.a_routed = h->hq_routed;
-    g2.a_shared = h->hq_shared;
-    g2.as_routed = h->hs_routed;
-    g2.as_shared = h->hs_shared;
+    g2.a_routed = ws.hq_routed;
+    g2.a_shared = ws.hq_shared;
+    g2.as_routed = ws.hs_routed;
+    g2.as_shared = ws.hs_shared;
     g2.s_routed = h->s_d;
     g2.s_expert_elems = (size_t)(M / 128) * (H / 128);
     g2.s_shared = h->ss_d;
-    return forward_fp8(h, x, T, r, y, st, g1, g2);
+    return forward_fp8(h, ws, x, T, r, y, st, g1, g2);
   }
 
   // Few rows per expert (decode batches): 16-row weight-streaming tiles.  Many rows:
@@ -657,7 +693,7 @@ static int forward_checked(afd_ffn_t h, const void* x, const uint8_t* xq, const 
   }
   {
     StageScope s(h, st, AFD_STAGE_COMBINE);
-    hipError_t e = afd::launch_combine(h->o_routed, Ms ? h->o_shared : nullptr, r->topk_gates, r->pair_pos, T, k, H, y,
+    hipError_t e = afd::launch_combine(ws.o_routed, Ms ? ws.o_shared : nullptr, r->topk_gates, r->pair_pos, T, k, H, y,
                                        !f32, st);
     if (e != hipSuccess) return hip_fail(e, "combine launch");
     s.done();
@@ -674,7 +710,50 @@ extern "C" int afd_ffn_forward(afd_ffn_t h, const void* x, int32_t T, const afd_
   const size_t rowb = (size_t)h->cfg.hidden * (h->cfg.dtype == AFD_F32 ? 4 : 2);
   if (overlaps(x, (size_t)T * rowb, y, (size_t)T * rowb)) return fail(AFD_EINVAL, "x and y overlap");
   if (overlaps_route(y, (size_t)T * rowb, h, r, T)) return fail(AFD_EINVAL, "y overlaps a route buffer");
-  return forward_checked(h, x, nullptr, nullptr, T, r, y, static_cast<hipStream_t>(stream));
+  return forward_checked(h, handle_workspace(h), x, nullptr, nullptr, T, r, y, static_cast<hipStream_t>(stream));
+}
+
+// The intermediate buffers of a forward over T tokens carved from `base` (256-byte
+// aligned pieces, in the sizes the handle's workspace has for max_tokens); returns the
+// bytes needed.  base == NULL: only the size.
+static size_t carve_workspace(const afd_ffn_config& c, size_t T, unsigned char* base, afd_workspace* ws) {
+  const size_t H = c.hidden, M = c.inter, Ms = c.shared_inter, P = T * c.top_k;
+  const bool fp8 = c.dtype == AFD_FP8_E4M3;
+  const size_t hes = c.dtype == AFD_BF16 ? 2 : 4, oes = c.dtype == AFD_F32 ? 4 : 2;
+  const size_t bytes[10] = {P * M * hes,   T * Ms * hes,  P * H * oes,   Ms ? T * H * oes : 0,
+                            fp8 ? T * H : 0, fp8 ? T * (H / 128) * 4 : 0, fp8 ? P * M : 0,
+                            fp8 ? P * (M / 128) * 4 : 0, fp8 ? T * Ms : 0, fp8 ? T * (Ms / 128) * 4 : 0};
+  void** dst[10] = {&ws->h_routed, &ws->h_shared, &ws->o_routed, &ws->o_shared, (void**)&ws->xq, (void**)&ws->xs,
+                    (void**)&ws->hq_routed, (void**)&ws->hs_routed, (void**)&ws->hq_shared, (void**)&ws->hs_shared};
+  size_t off = 0;
+  for (int i = 0; i < 10; ++i) {
+    if (base) *dst[i] = bytes[i] ? base + off : nullptr;
+    off += (bytes[i] + 255) / 256 * 256;
+  }
+  return off;
+}
+
+extern "C" int afd_ffn_forward_noalloc(afd_ffn_t h, const void* x, int32_t T, const afd_route* r, void* y,
+                                       void* stream) {
+  int rc = check_route(h, r, T);
+  if (rc) return rc;
+  if (!x || !y) return fail(AFD_EINVAL, "x or y is NULL");
+  if (misaligned(x, 16) || misaligned(y, 16)) return fail(AFD_EINVAL, "x and y must be 16-byte aligned");
+  if (T == 0) return AFD_OK;
+  const size_t rowb = (size_t)h->cfg.hidden * (h->cfg.dtype == AFD_F32 ? 4 : 2);
+  if (overlaps(x, (size_t)T * rowb, y, (size_t)T * rowb)) return fail(AFD_EINVAL, "x and y overlap");
+  if (overlaps_route(y, (size_t)T * rowb, h, r, T)) return fail(AFD_EINVAL, "y overlaps a route buffer");
+  // The buffers are laid out for the handle's max_tokens, as its own workspace is: any
+  // route the handle accepts (at most max_tokens * top_k rows) then stays inside them.
+  afd_workspace ws = {};
+  const size_t need = carve_workspace(h->cfg, (size_t)h->cfg.max_tokens, nullptr, &ws);
+  if (need > kScratchBytes)
+    return fail(AFD_EINVAL, "max_tokens=%d needs %zu bytes of intermediate buffers, above the %zu-byte static scratch",
+                h->cfg.max_tokens, need, kScratchBytes);
+  void* base = h->device >= 0 && h->device < kMaxDevices ? g_scratch[h->device] : nullptr;
+  if (!base) return fail(AFD_EHIP, "no scratch address for device %d", h->device);
+  carve_workspace(h->cfg, (size_t)h->cfg.max_tokens, static_cast<unsigned char*>(base), &ws);
+  return forward_checked(h, ws, x, nullptr, nullptr, T, r, y, static_cast<hipStream_t>(stream));
 }
 
 extern "C" int afd_ffn_forward_fp8_input(afd_ffn_t h, const uint8_t* xq, const float* xs, int32_t T,
@@ -690,7 +769,7 @@ extern "C" int afd_ffn_forward_fp8_input(afd_ffn_t h, const uint8_t* xq, const f
   if (overlaps(xq, qb, y, yb) || overlaps(xs, sb, y, yb) || overlaps(xq, qb, xs, sb))
     return fail(AFD_EINVAL, "xq, xs and y overlap");
   if (overlaps_route(y, yb, h, r, T)) return fail(AFD_EINVAL, "y overlaps a route buffer");
-  return forward_checked(h, nullptr, xq, xs, T, r, y, static_cast<hipStream_t>(stream));
+  return forward_checked(h, handle_workspace(h), nullptr, xq, xs, T, r, y, static_cast<hipStream_t>(stream));
 }
 
 extern "C" int afd_ffn_set_gemm_kernel(afd_ffn_t h, int kernel) {

@@ -132,6 +132,22 @@ hipError_t launch_combine(const void* O, const void* Os, const float* gates, con
 
 }  // namespace afd
 
+// Intermediate buffers of one forward call (h, the expert outputs O, and for fp8
+// layers the e4m3 codes and scales of x and h): the handle's own workspace, or for
+// afd_ffn_forward_noalloc a carve-up of the library's static device scratch array.
+struct afd_workspace {
+  void* h_routed;
+  void* h_shared;
+  void* o_routed;
+  void* o_shared;
+  uint8_t* xq;
+  float* xs;
+  uint8_t* hq_routed;
+  float* hs_routed;
+  uint8_t* hq_shared;
+  float* hs_shared;
+};
+
 struct afd_ffn {
   afd_ffn_config cfg;
   int device;

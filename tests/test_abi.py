@@ -113,6 +113,7 @@ def test_route_and_forward_reject_null_handle():
     assert lib.afd_ffn_route(None, 1, 4, ctypes.byref(r), None) == _ffi.AFD_EINVAL
     assert lib.afd_ffn_forward(None, 1, 4, ctypes.byref(r), 1, None) == _ffi.AFD_EINVAL
     assert lib.afd_ffn_forward_fp8_input(None, 1, 1, 4, ctypes.byref(r), 1, None) == _ffi.AFD_EINVAL
+    assert lib.afd_ffn_forward_noalloc(None, 1, 4, ctypes.byref(r), 1, None) == _ffi.AFD_EINVAL
     assert lib.afd_ffn_route_hidden(None, 1, 1, None, 1, 4, ctypes.byref(r), None) == _ffi.AFD_EINVAL
     assert lib.afd_ffn_route_select_bias(None, 1, 1, 4, ctypes.byref(r), None) == _ffi.AFD_EINVAL
     assert lib.afd_ffn_route_capacity(None, 4, 4, 4, 1, 1, 4, 4, 4, 4, 4, None) == _ffi.AFD_EINVAL
