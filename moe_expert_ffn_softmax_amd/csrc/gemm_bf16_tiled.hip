@@ -71,6 +71,8 @@ constexpr int kTiledLoads = 8;                          // staging loads per wav
 #define AFD_TILED_B_AHEAD (8 / AFD_TILED_GPW)
 #endif
 constexpr int kTiledBAhead = AFD_TILED_B_AHEAD;         // 32-deep weight steps in flight per wave
+// a ring slot is the step's index within its chunk modulo the ring depth
+static_assert(kTiledKC % kTiledBAhead == 0, "the weight ring depth divides the steps of a chunk");
 constexpr int kXcds = 8;
 
 static_assert(kTiledRowBlocks == kTiledWaves, "each wave stages one 32-row block");
@@ -220,7 +222,8 @@ __global__ void __launch_bounds__(kTiledThreads, kTiledMinBlocks) gemm_bf16_tile
 #pragma unroll
         for (int cb = 0; cb < kTiledGroupsPerWave; ++cb)
 #pragma unroll
-          for (int kh = 0; kh < 2; ++kh) bring[u][cb][kh] = tiled_load_b(cur.wbase + cur.boff[cb] + u * 128 + kh * 32);
+          for (int kh = 0; kh < 2; ++kh)
+            bring[u][cb][kh] = tiled_load_b(cur.wbase + cur.boff[cb] + (u < cur.KB ? u : cur.KB - 1) * 128 + kh * 32);
       // chunk 0 -> LDS buffer `base`, chunk 1 (or chunk 0 again) -> staging registers;
       // a chunk is 16 pieces of 16 bytes per row
 #pragma unroll
