@@ -65,6 +65,9 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--attainable", action="store_true",
+                    help="measured HBM read rates (the streaming GEMM's pattern, a device copy) and matrix-core rates "
+                         "on random operands, from the in-tree probes; not the benchmark line")
     ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                     help="write the gate/up launch's HBM bytes of --workload into profiles/traffic_counters.json "
                          "from rocprofv3 counter_collection CSVs")
@@ -594,6 +597,91 @@ def ubatches(args, torch):
         torch.cuda.empty_cache()
 
 
+def attainable(args, torch):
+    """What the part attains, measured with the in-tree probes (libafd_probe.so): HBM
+    reads in the weight-streaming GEMM's pattern (private runs per wave, 16-byte
+    nontemporal loads, a ring of steps in flight), a plain 1 GiB device copy, and
+    matrix-core loops on random bf16 and e4m3 operands.  One JSON line per probe; the
+    read probes' sums are checked against the buffer's."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "moe_expert_ffn_softmax_amd", "libafd_probe.so"))
+    V = ctypes.c_void_p
+    lib.afd_probe_stream.argtypes = [V, ctypes.c_longlong, ctypes.c_int, ctypes.c_int, V, V]
+    lib.afd_probe_mfma.argtypes = [ctypes.c_int, V, ctypes.c_int, ctypes.c_int, V, V]
+    st = torch.cuda.current_stream()
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(reps):
+            fn()
+        e1.record(st)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps / 1e3
+
+    KiB = 1024
+    cases = [("decode gate/up pattern", 3360, 256 * KiB, 8), ("same runs, 16 steps in flight", 3360, 256 * KiB, 16),
+             ("twice the runs, half as long, 16 in flight", 6720, 128 * KiB, 16),
+             ("one 4 MiB run per resident wave", 2048, 4096 * KiB, 8)]
+    nbytes = max(r * b for _, r, b, _ in cases)
+    g = torch.Generator(device="cuda").manual_seed(7)
+    buf = torch.randint(-2 ** 31, 2 ** 31 - 1, (nbytes // 4,), dtype=torch.int32, device="cuda", generator=g)
+    for name, runs, rb, depth in cases:
+        out = torch.empty(runs * 256, dtype=torch.int32, device="cuda")
+
+        def run():
+            rc = lib.afd_probe_stream(buf.data_ptr(), rb, runs, depth, out.data_ptr(), st.cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"afd_probe_stream returned {rc}")
+        t = timed(run, args.steps if args.steps <= 50 else 20)
+        want = int(buf[: runs * rb // 4].to(torch.int64).sum().item()) % (1 << 32)
+        got = int(out.to(torch.int64).sum().item()) % (1 << 32)
+        if got != want:
+            raise RuntimeError(f"stream probe read the wrong bytes ({got} vs {want})")
+        print(json.dumps({"probe": "hbm_read", "pattern": name, "runs": runs, "run_bytes": rb,
+                          "steps_in_flight": depth, "bytes": runs * rb, "us": round(t * 1e6, 1),
+                          "GBps": round(runs * rb / t / 1e9, 1),
+                          "frac_of_8TBps": round(runs * rb / t / 1e9 / HBM_PEAK_GBS, 4)}), flush=True)
+    del buf
+    a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    t = timed(lambda: b.copy_(a), 10)
+    print(json.dumps({"probe": "device_copy", "bytes_read": 1 << 30, "bytes_written": 1 << 30,
+                      "us": round(t * 1e6, 1), "GBps_read_plus_write": round(2 * (1 << 30) / t / 1e9, 1)}),
+          flush=True)
+    del a, b
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    waves = cus * 8  # two waves per SIMD
+    chains = 8       # independent accumulators per wave (the probe's kChains)
+    for kind, dt, per, peak, opbytes in ((0, "bf16", 32768, MFMA_PEAK_TFLOPS["bf16"], 16),
+                                         (1, "fp8", 65536, MFMA_PEAK_TFLOPS["fp8"], 32)):
+        n = waves * 2 * chains * 64 * opbytes
+        for operands in ("random", "constant"):
+            if kind == 0:
+                ops = (torch.randn(n // 2, generator=g, device="cuda") if operands == "random"
+                       else torch.full((n // 2,), 0.5, device="cuda")).to(torch.bfloat16)
+            else:
+                ops = (torch.randn(n, generator=g, device="cuda") if operands == "random"
+                       else torch.full((n,), 0.5, device="cuda")).to(torch.float8_e4m3fn).view(torch.uint8)
+            out = torch.empty(waves * 64, dtype=torch.float32, device="cuda")
+            iters = 2048
+
+            def run():
+                rc = lib.afd_probe_mfma(kind, ops.data_ptr(), waves, iters, out.data_ptr(), st.cuda_stream)
+                if rc != 0:
+                    raise RuntimeError(f"afd_probe_mfma returned {rc}")
+            t = timed(run, 10)
+            flops = waves * iters * chains * per
+            print(json.dumps({"probe": "mfma", "instruction": "v_mfma_f32_32x32x16_bf16" if kind == 0 else
+                              "v_mfma_f32_16x16x128_f8f6f4", "operands": f"{operands} {dt}", "waves": waves,
+                              "chains_per_wave": chains, "flops": flops, "us": round(t * 1e6, 1),
+                              "TFLOPs": round(flops / t / 1e12, 1),
+                              "frac_of_peak": round(flops / t / 1e12 / peak, 4)}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -606,6 +694,10 @@ def main():
         return
     if args.pmc_summary:
         pmc_summary(args)
+        return
+    if args.attainable:
+        torch.cuda.set_device(0)
+        attainable(args, torch)
         return
     if args.sweep:
         torch.cuda.set_device(0)

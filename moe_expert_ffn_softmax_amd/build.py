@@ -15,6 +15,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(ROOT, "_build", "afd_ffn")
 LIB = os.path.join(PKG, "libafd_ffn.so")
+PROBE_LIB = os.path.join(PKG, "libafd_probe.so")  # measurement probes of bench.py --attainable
+PROBE_SRC = os.path.join(CSRC, "probe", "attainable.hip")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
@@ -51,20 +53,26 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(jobs: int = 0) -> str:
-    """Compile every .hip source of the library and link libafd_ffn.so.  Always
-    recompiles (the caller asked for a build)."""
-    os.makedirs(OBJDIR, exist_ok=True)
-    srcs = sources()
-    jobs = jobs or min(len(srcs), max(1, min(16, os.cpu_count() or 1)))
-    with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+def _link(objs, lib):
+    tmp = lib + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(jobs: int = 0) -> str:
+    """Compile every .hip source of the library and link libafd_ffn.so, and the
+    measurement probes into libafd_probe.so.  Always recompiles (the caller asked for
+    a build)."""
+    os.makedirs(OBJDIR, exist_ok=True)
+    srcs = sources()
+    jobs = jobs or min(len(srcs) + 1, max(1, min(16, os.cpu_count() or 1)))
+    with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
+        objs = list(ex.map(_compile, srcs + [PROBE_SRC]))
+    _link(objs[:-1], LIB)
+    _link(objs[-1:], PROBE_LIB)
     return LIB
 
 

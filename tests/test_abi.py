@@ -142,3 +142,22 @@ def test_product_path_does_not_touch_the_oracle():
             if f.endswith((".py", ".hip", ".h", ".cpp")):
                 text = open(os.path.join(dirpath, f), encoding="utf-8").read()
                 assert "import oracle" not in text and "from oracle" not in text and "afdo_" not in text, f
+
+
+def test_probe_library_exports_its_entry_points():
+    """The measurement probes of bench.py --attainable live in their own library."""
+    import os
+    path = os.path.join(os.path.dirname(_ffi.LIB_PATH), "libafd_probe.so")
+    lib = ctypes.CDLL(path)
+    for n in ("afd_probe_stream", "afd_probe_mfma"):
+        assert hasattr(lib, n), n
+    lib.afd_probe_stream.argtypes = [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_void_p, ctypes.c_void_p]
+    lib.afd_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                   ctypes.c_void_p]
+    # argument checks run on the host before any launch
+    assert lib.afd_probe_stream(None, 8192, 4, 8, 64, None) == -1
+    assert lib.afd_probe_stream(64, 1000, 4, 8, 64, None) == -1      # not a multiple of depth KiB
+    assert lib.afd_probe_stream(64, 8192, 4, 5, 64, None) == -1      # unsupported depth
+    assert lib.afd_probe_mfma(2, 64, 8, 1, 64, None) == -1           # unknown kind
+    assert lib.afd_probe_mfma(0, 64, 6, 1, 64, None) == -1           # waves not a multiple of 4
