@@ -60,7 +60,7 @@ def parse():
     ap.add_argument("--graph", action="store_true", help="same as --launch graph (kept for old command lines)")
     ap.add_argument("--no-context", action="store_true",
                     help="only the headline workload: skip the decode and matrix-core records")
-    ap.add_argument("--gemm", default="auto", choices=["auto", "stream", "tiled"],
+    ap.add_argument("--gemm", default="auto", choices=["auto", "stream", "tiled", "fused"],
                     help="grouped-GEMM kernel: automatic choice, 16-row streaming tiles or 128-row tiles")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -120,6 +120,16 @@ def gate_up_bytes(w, counts):
     wb = weight_bytes(w)
     act = 4 if w.dtype == "f32" else 2
     return touched * 2 * H * M * wb + 2 * H * Ms * wb + T * H * act + (P * M + T * Ms) * act
+
+
+def down_bytes(w, counts):
+    """Algorithmic bytes of one down launch (bf16/fp32 layers): H*M weights per touched
+    expert (+ the shared expert's H*Ms), h in, the expert output rows out."""
+    touched = int((counts > 0).sum())
+    T, H, M, Ms, P = w.T, w.H, w.M, w.Ms, w.T * w.k
+    wb = weight_bytes(w)
+    act = 4 if w.dtype == "f32" else 2
+    return touched * H * M * wb + H * Ms * wb + (P * M + T * Ms) * act + (P * H + (T * H if Ms else 0)) * act
 
 
 def copy_calibration():
@@ -398,7 +408,7 @@ def sweep(args, torch):
         if args.only and not any(o in w.name for o in args.only.split(",")):
             continue
         steps = args.steps if w.T <= 64 else max(3, min(args.steps, 20))
-        r = run_workload(w, steps, min(args.warmup, 3), min(args.batches, 4 if w.T <= 64 else 2), args.gemm, torch)
+        r = run_workload(w, steps, min(args.warmup, 3), args.batches or (4 if w.T <= 64 else 2), args.gemm, torch)
         print(json.dumps(r), flush=True)
         torch.cuda.empty_cache()
 
@@ -415,7 +425,7 @@ def batch_sweep(args, torch):
         for T in BATCH_SWEEP_T:
             w = dataclasses.replace(base, T=T, dtype=dt, name=f"decode_layer_{dt}_T{T}_H4096_M1536_E128_k8")
             steps = args.steps if T <= 64 else max(3, min(args.steps, 50))
-            r = run_workload(w, steps, min(args.warmup, 5), min(args.batches, 8), args.gemm, torch)
+            r = run_workload(w, steps, min(args.warmup, 5), args.batches or 8, args.gemm, torch)
             print(json.dumps(r), flush=True)
             torch.cuda.empty_cache()
 
@@ -858,23 +868,30 @@ def measure(w, torch, steps, warmup, nb, launch, gemm, cold_n, keep_weights):
     touched = np.mean([algorithmic_bytes(w, c)[1] for c in counts])
     gu_bytes = np.mean([gate_up_bytes(w, c) for c in counts])
     gu_ms, gu_n = prof["gate_up"]
-    gu_avg_s = gu_ms / max(gu_n, 1) / 1e3
-    traffic = traffic_from_counters(w, gemm)
     kern = gate_up_kernel(w, gemm)
+    traffic = traffic_from_counters(w, gemm)
+    kname = "gate_up"
+    gu_flops = 4.0 * w.T * w.k * w.H * w.M + 4.0 * w.T * w.H * w.Ms
+    if gu_n == 0 and prof.get("fused", (0, 0))[1]:
+        # both GEMMs in one launch: its roofline covers both
+        gu_ms, gu_n = prof["fused"]
+        kern, kname, traffic = "gemm_bf16_fused_kernel", "fused_gate_up_down", None
+        gu_bytes = np.mean([gate_up_bytes(w, c) + down_bytes(w, c) for c in counts])
+        gu_flops = 6.0 * w.T * w.k * w.H * w.M + 6.0 * w.T * w.H * w.Ms
+    gu_avg_s = gu_ms / max(gu_n, 1) / 1e3
 
     # the gate/up launch is bound by HBM below the ridge point (peak FLOP/s / peak B/s)
     # and by the matrix cores above it
-    gu_flops = 4.0 * w.T * w.k * w.H * w.M + 4.0 * w.T * w.H * w.Ms
     ridge = MFMA_PEAK_TFLOPS[w.dtype] * 1e12 / (HBM_PEAK_GBS * 1e9)
     gu_tf = gu_flops / gu_avg_s / 1e12
     if gu_flops / gu_bytes <= ridge:
         achieved = gu_bytes / gu_avg_s / 1e9
-        roofline = {"kernel": "gate_up", "name": kern, "bound": "hbm", "achieved": round(achieved, 1),
+        roofline = {"kernel": kname, "name": kern, "bound": "hbm", "achieved": round(achieved, 1),
                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                     "traffic": traffic, "algorithmic_bytes": int(gu_bytes), "avg_launch_us": round(gu_avg_s * 1e6, 2),
                     "mfma_frac": round(gu_tf / MFMA_PEAK_TFLOPS[w.dtype], 4)}
     else:
-        roofline = {"kernel": "gate_up", "name": kern, "bound": "mfma", "achieved": round(gu_tf, 1),
+        roofline = {"kernel": kname, "name": kern, "bound": "mfma", "achieved": round(gu_tf, 1),
                     "peak": MFMA_PEAK_TFLOPS[w.dtype], "unit": "TFLOP/s",
                     "frac": round(gu_tf / MFMA_PEAK_TFLOPS[w.dtype], 4), "traffic": traffic,
                     "algorithmic_flops": gu_flops, "algorithmic_bytes": int(gu_bytes),

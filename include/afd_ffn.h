@@ -258,10 +258,25 @@ int afd_ffn_quantize_fp8(const void* src, int32_t rows, int32_t cols, int32_t sr
 /* Choice of grouped-GEMM kernel for bf16 and fp8 layers.  AFD_GEMM_AUTO (the default)
  * uses 16-row weight-streaming tiles while experts average at most 8 (bf16) or 12
  * (fp8) routed rows per batch (T * top_k <= 8 * E, resp. 12 * E) and 128-row tiles
- * above that (the measured crossovers); the other values force one kernel (results
- * agree to rounding; a tuning and testing knob).  fp32 layers always use their own
- * kernel.  Takes effect for later forward calls.  Other values: AFD_EINVAL. */
-typedef enum afd_gemm_kernel { AFD_GEMM_AUTO = 0, AFD_GEMM_STREAM = 1, AFD_GEMM_TILED = 2 } afd_gemm_kernel;
+ * above that (the measured crossovers); AFD_GEMM_STREAM and AFD_GEMM_TILED force one
+ * kernel (results agree to rounding; a tuning and testing knob).
+ * AFD_GEMM_FUSED (bf16 layers whose hidden, inter and shared_inter are multiples of
+ * 256; others behave as AFD_GEMM_STREAM) runs both grouped GEMMs of the streaming form
+ * in one persistent launch: the single-launch expert kernel of "大模型推理的内存与计算
+ * 解耦：AFD 架构解析与性能验证" (§5, MegaMoE) -- gate/up items, the first down weights
+ * loaded ahead, a grid-wide barrier, then the down items with each routed row's gate
+ * applied in their epilogue (the combine then sums unweighted).  Its workgroups must
+ * all be resident at once: the launch uses the device's resident count, and a
+ * workgroup that waits at the barrier for longer than ~0.1-1 s gives up (wrong
+ * output, no hang); nothing else may occupy the device meanwhile.  fp32 layers always
+ * use their own kernel.  Takes effect for later forward calls.  Other values:
+ * AFD_EINVAL. */
+typedef enum afd_gemm_kernel {
+  AFD_GEMM_AUTO = 0,
+  AFD_GEMM_STREAM = 1,
+  AFD_GEMM_TILED = 2,
+  AFD_GEMM_FUSED = 3
+} afd_gemm_kernel;
 int afd_ffn_set_gemm_kernel(afd_ffn_t h, int kernel);
 
 /* Per-kernel timing.  With profiling on, route and forward bracket each kernel
@@ -277,7 +292,8 @@ typedef enum afd_stage {
   AFD_STAGE_DOWN = 4,    /* grouped down-projection GEMM */
   AFD_STAGE_COMBINE = 5, /* gate-weighted combine back to token order */
   AFD_STAGE_ROUTER_PROJ = 6, /* router projection of afd_ffn_route_hidden */
-  AFD_NUM_STAGES = 7
+  AFD_STAGE_FUSED = 7,   /* gate/up + down in one launch (AFD_GEMM_FUSED) */
+  AFD_NUM_STAGES = 8
 } afd_stage;
 int afd_ffn_set_profiling(afd_ffn_t h, int on);
 int afd_ffn_profile_read(afd_ffn_t h, double* ms, int64_t* launches, int n_stages);

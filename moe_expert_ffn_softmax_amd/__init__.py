@@ -9,7 +9,7 @@ PyTorch fallback: if libafd_ffn.so is missing, constructing a layer raises.
 from __future__ import annotations
 
 from ._ffi import (AFD_BF16, AFD_F32, AFD_FP8_E4M3, AFD_GEMM_AUTO, AFD_GEMM_STREAM,  # noqa: F401
-                   AFD_GEMM_TILED, STAGES, AfdError, afd_ffn_config, afd_ffn_create, afd_ffn_destroy,
+                   AFD_GEMM_TILED, AFD_GEMM_FUSED, STAGES, AfdError, afd_ffn_config, afd_ffn_create, afd_ffn_destroy,
                    afd_ffn_device_bytes, afd_ffn_forward, afd_ffn_forward_fp8_input, afd_ffn_forward_noalloc,
                    afd_ffn_last_error,
                    afd_ffn_profile_read, afd_ffn_quantize_fp8, afd_ffn_route, afd_ffn_route_capacity,
@@ -18,7 +18,7 @@ from ._ffi import (AFD_BF16, AFD_F32, AFD_FP8_E4M3, AFD_GEMM_AUTO, AFD_GEMM_STRE
                    afd_ffn_route_bytes, afd_ffn_route_select_bias, afd_ffn_set_gemm_kernel, afd_ffn_set_profiling,
                    afd_ffn_strerror, afd_route, load)
 
-GEMM_KERNELS = {"auto": AFD_GEMM_AUTO, "stream": AFD_GEMM_STREAM, "tiled": AFD_GEMM_TILED}
+GEMM_KERNELS = {"auto": AFD_GEMM_AUTO, "stream": AFD_GEMM_STREAM, "tiled": AFD_GEMM_TILED, "fused": AFD_GEMM_FUSED}
 
 DTYPES = {"f32": AFD_F32, "bf16": AFD_BF16, "fp8": AFD_FP8_E4M3}
 
@@ -148,7 +148,8 @@ class MoeExpertFFN:
             raise ValueError("route buffers must come from this layer's new_route()")
 
     def set_gemm_kernel(self, name: str) -> None:
-        """'auto', 'stream' (16-row weight-streaming tiles) or 'tiled' (128-row tiles)."""
+        """'auto', 'stream' (16-row weight-streaming tiles), 'tiled' (128-row tiles) or 'fused'
+        (bf16 decode layers: both streaming GEMMs in one persistent launch)."""
         afd_ffn_set_gemm_kernel(self.handle, GEMM_KERNELS[name])
 
     def new_route(self) -> RouteBuffers:

@@ -12,8 +12,8 @@ LIB_PATH = os.path.join(_PKG, "libafd_ffn.so")
 
 AFD_OK, AFD_EINVAL, AFD_EUNSUPPORTED, AFD_ENOMEM, AFD_EHIP = 0, -1, -2, -3, -4
 AFD_F32, AFD_BF16, AFD_FP8_E4M3 = 0, 1, 2
-AFD_GEMM_AUTO, AFD_GEMM_STREAM, AFD_GEMM_TILED = 0, 1, 2
-STAGES = ("router", "permute", "quant", "gate_up", "down", "combine", "router_proj")
+AFD_GEMM_AUTO, AFD_GEMM_STREAM, AFD_GEMM_TILED, AFD_GEMM_FUSED = 0, 1, 2, 3
+STAGES = ("router", "permute", "quant", "gate_up", "down", "combine", "router_proj", "fused")
 AFD_NUM_STAGES = len(STAGES)
 
 

@@ -45,6 +45,9 @@ int scratch_address(int dev) {
   void* p = nullptr;
   hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
   if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+  // the fused decode launch's barrier counters live in the first 256 bytes: zero
+  e = hipMemset(p, 0, 256);
+  if (e != hipSuccess) return hip_fail(e, "hipMemset(scratch counters)");
   g_scratch[dev] = p;
   return AFD_OK;
 }
@@ -119,7 +122,8 @@ int check_route(const afd_ffn* h, const afd_route* r, int32_t T) {
 void release(afd_ffn* h) {
   void* bufs[] = {h->w_gu,      h->w_d,     h->ws_gu,    h->ws_d,      h->h_routed,  h->h_shared,
                   h->o_routed,  h->o_shared, h->s_gu,    h->s_d,       h->ss_gu,     h->ss_d,
-                  h->xq,        h->xs,      h->hq_routed, h->hs_routed, h->hq_shared, h->hs_shared};
+                  h->xq,        h->xs,      h->hq_routed, h->hs_routed, h->hq_shared, h->hs_shared,
+                  h->fused_sync};
   for (void* b : bufs)
     if (b) (void)hipFree(b);
   for (hipEvent_t e : h->ev_pool) (void)hipEventDestroy(e);
@@ -166,7 +170,7 @@ struct StageScope {
 //     tokens, 10% at 12 rows; tiled 15% faster at 16; with a 2048-wide shared expert
 //     streaming 2% faster at 12 rows, tiled 18% faster at 16).
 bool use_tiled(const afd_ffn* h, int P) {
-  if (h->gemm_mode == AFD_GEMM_STREAM) return false;
+  if (h->gemm_mode == AFD_GEMM_STREAM || h->gemm_mode == AFD_GEMM_FUSED) return false;
   if (h->gemm_mode == AFD_GEMM_TILED) return true;
   const long long rows_per_expert = h->cfg.dtype == AFD_FP8_E4M3 ? 12 : 8;
   return (long long)P > rows_per_expert * h->cfg.num_experts;
@@ -351,6 +355,13 @@ extern "C" int afd_ffn_create(const afd_ffn_config* cfg, const void* w_gate_up, 
       return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
     }
     for (int i = 0; i < 6; ++i) h->gemm_blocks[i] = (occ[i] > 0 ? occ[i] : 1) * h->num_cus;
+    int fo = 0;
+    e = afd::gemm_occupancy_bf16_fused(&fo);
+    if (e != hipSuccess) {
+      release(h);
+      return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
+    }
+    h->fused_blocks = fo * h->num_cus;
   }
 
   const size_t H = cfg->hidden, M = cfg->inter, Ms = cfg->shared_inter, E = cfg->num_experts;
@@ -385,6 +396,7 @@ extern "C" int afd_ffn_create(const afd_ffn_config* cfg, const void* w_gate_up, 
       {(void**)&h->hs_routed, fp8 ? P * (M / 128) * 4 : 0},
       {(void**)&h->hq_shared, fp8 ? T * Ms : 0},
       {(void**)&h->hs_shared, fp8 ? T * (Ms / 128) * 4 : 0},
+      {(void**)&h->fused_sync, 256},
   };
   for (auto& a : allocs) {
     if (a.bytes == 0) continue;
@@ -431,6 +443,7 @@ extern "C" int afd_ffn_create(const afd_ffn_config* cfg, const void* w_gate_up, 
     if (e == hipSuccess && Ms) e = hipMemcpyAsync(h->ws_gu, ws_gate_up, H * 2 * Ms * es, hipMemcpyDeviceToDevice, st);
     if (e == hipSuccess && Ms) e = hipMemcpyAsync(h->ws_d, ws_down, Ms * H * es, hipMemcpyDeviceToDevice, st);
   }
+  if (e == hipSuccess) e = hipMemsetAsync(h->fused_sync, 0, 256, st);
   if (e == hipSuccess) e = hipStreamSynchronize(st);
   if (e != hipSuccess) {
     release(h);
@@ -587,8 +600,8 @@ extern "C" int afd_ffn_route_hidden(afd_ffn_t h, const void* x, const void* w_ro
 }
 
 static afd_workspace handle_workspace(const afd_ffn* h) {
-  return {h->h_routed, h->h_shared, h->o_routed, h->o_shared, h->xq, h->xs,
-          h->hq_routed, h->hs_routed, h->hq_shared, h->hs_shared};
+  return {h->h_routed, h->h_shared, h->o_routed, h->o_shared, h->xq,        h->xs,
+          h->hq_routed, h->hs_routed, h->hq_shared, h->hs_shared, h->fused_sync};
 }
 
 // Steps a0 and a5-a8 on checked arguments.  fp8 layers: x (bf16) is quantised here,
@@ -664,6 +677,23 @@ static int forward_checked(afd_ffn_t h, const afd_workspace& ws, const void* x, 
   // Few rows per expert (decode batches): 16-row weight-streaming tiles.  Many rows:
   // 128-row tiles, so each expert's weights are read once per 128 of its rows.
   const bool tiled = !f32 && use_tiled(h, route_rows(h, r, T));
+  if (!f32 && !tiled && h->gemm_mode == AFD_GEMM_FUSED && H % 256 == 0 && M % 256 == 0 && Ms % 256 == 0 &&
+      h->fused_blocks > 0 && ws.fused_sync) {
+    // both GEMMs in one persistent launch; the down epilogue applies the gates
+    {
+      StageScope s(h, st, AFD_STAGE_FUSED);
+      hipError_t e = afd::launch_gemm_bf16_fused(g1, g2, r->topk_gates, ws.fused_sync,
+                                                 reinterpret_cast<int*>(ws.fused_sync + 2), h->fused_blocks, st);
+      if (e != hipSuccess) return hip_fail(e, "fused gate/up + down launch");
+      s.done();
+    }
+    StageScope s(h, st, AFD_STAGE_COMBINE);
+    hipError_t e = afd::launch_combine(ws.o_routed, Ms ? ws.o_shared : nullptr, r->topk_gates, r->pair_pos, T, k, H, y,
+                                       true, st, true);
+    if (e != hipSuccess) return hip_fail(e, "combine launch");
+    s.done();
+    return AFD_OK;
+  }
   long long items1, items2;
   if (tiled) {
     const int tr = afd::tiled_rows(), tg = afd::tiled_groups();
@@ -720,13 +750,16 @@ static size_t carve_workspace(const afd_ffn_config& c, size_t T, unsigned char* 
   const size_t H = c.hidden, M = c.inter, Ms = c.shared_inter, P = T * c.top_k;
   const bool fp8 = c.dtype == AFD_FP8_E4M3;
   const size_t hes = c.dtype == AFD_BF16 ? 2 : 4, oes = c.dtype == AFD_F32 ? 4 : 2;
-  const size_t bytes[10] = {P * M * hes,   T * Ms * hes,  P * H * oes,   Ms ? T * H * oes : 0,
+  // the fused decode launch's barrier counters come first: the array is zero at load
+  // and every launch leaves them at zero
+  const size_t bytes[11] = {256, P * M * hes,   T * Ms * hes,  P * H * oes,   Ms ? T * H * oes : 0,
                             fp8 ? T * H : 0, fp8 ? T * (H / 128) * 4 : 0, fp8 ? P * M : 0,
                             fp8 ? P * (M / 128) * 4 : 0, fp8 ? T * Ms : 0, fp8 ? T * (Ms / 128) * 4 : 0};
-  void** dst[10] = {&ws->h_routed, &ws->h_shared, &ws->o_routed, &ws->o_shared, (void**)&ws->xq, (void**)&ws->xs,
-                    (void**)&ws->hq_routed, (void**)&ws->hs_routed, (void**)&ws->hq_shared, (void**)&ws->hs_shared};
+  void** dst[11] = {(void**)&ws->fused_sync, &ws->h_routed, &ws->h_shared, &ws->o_routed, &ws->o_shared,
+                    (void**)&ws->xq, (void**)&ws->xs, (void**)&ws->hq_routed, (void**)&ws->hs_routed,
+                    (void**)&ws->hq_shared, (void**)&ws->hs_shared};
   size_t off = 0;
-  for (int i = 0; i < 10; ++i) {
+  for (int i = 0; i < 11; ++i) {
     if (base) *dst[i] = bytes[i] ? base + off : nullptr;
     off += (bytes[i] + 255) / 256 * 256;
   }
@@ -774,7 +807,7 @@ extern "C" int afd_ffn_forward_fp8_input(afd_ffn_t h, const uint8_t* xq, const f
 
 extern "C" int afd_ffn_set_gemm_kernel(afd_ffn_t h, int kernel) {
   if (!h) return fail(AFD_EINVAL, "handle is NULL");
-  if (kernel < AFD_GEMM_AUTO || kernel > AFD_GEMM_TILED) return fail(AFD_EINVAL, "unknown GEMM kernel %d", kernel);
+  if (kernel < AFD_GEMM_AUTO || kernel > AFD_GEMM_FUSED) return fail(AFD_EINVAL, "unknown GEMM kernel %d", kernel);
   h->gemm_mode = kernel;
   return AFD_OK;
 }

@@ -85,6 +85,13 @@ inline long long grouped_items_bound(int P, int E, int groups_routed, int shared
 // Persistent grids: `max_items` bounds the work items, `max_blocks` is the number of
 // workgroups the device keeps resident at once (from the occupancy query at create).
 hipError_t launch_gemm_bf16(const GroupedGemm& g, bool swiglu, long long max_items, int max_blocks, hipStream_t st);
+// Decode layers: g1 (gate/up) and g2 (down) in one persistent launch of
+// `resident_blocks` workgroups with a grid-wide barrier between them; routed down rows
+// are multiplied by gates[pair].  sync: 2 counters that start (and are left) at zero;
+// status[0] is set to 1 if a workgroup gave up waiting at the barrier.
+hipError_t launch_gemm_bf16_fused(const GroupedGemm& g1, const GroupedGemm& g2, const float* gates, unsigned* sync,
+                                  int* status, int resident_blocks, hipStream_t st);
+hipError_t gemm_occupancy_bf16_fused(int* blocks);
 hipError_t launch_gemm_f32(const GroupedGemm& g, bool swiglu, long long max_items, int max_blocks, hipStream_t st);
 // Large-tile variant (128-row tiles, 8 column groups per item) for experts with many
 // rows; `max_blocks` as above.
@@ -127,8 +134,10 @@ hipError_t gemm_occupancy_fp8(int* gate_up, int* down);
 
 // y[t] = sum_j gate[t,j] * O[pair_pos[t*k+j]] (+ Os[t]); O, Os and y all bf16
 // (bf16 = true) or all fp32.
+// gates_applied: the rows already carry their gates (a slot whose gate is 0 is still
+// skipped, but the others are summed unweighted).
 hipError_t launch_combine(const void* O, const void* Os, const float* gates, const int32_t* pair_pos,
-                          int T, int k, int H, void* y, bool bf16, hipStream_t st);
+                          int T, int k, int H, void* y, bool bf16, hipStream_t st, bool gates_applied = false);
 
 }  // namespace afd
 
@@ -146,6 +155,7 @@ struct afd_workspace {
   float* hs_routed;
   uint8_t* hq_shared;
   float* hs_shared;
+  unsigned* fused_sync;  // barrier counters and status of the fused decode launch
 };
 
 struct afd_ffn {
@@ -176,7 +186,9 @@ struct afd_ffn {
   float* hs_shared;   // [T_max, Ms/128]
   int gemm_blocks[6];  // resident workgroups of each GEMM kernel on the whole device
                        // (bf16 gate/up, down; fp32 gate/up, down; fp8 gate/up, down)
-  int gemm_mode;       // afd_gemm_kernel: automatic, or always 16-row or 128-row tiles
+  int gemm_mode;       // afd_gemm_kernel: automatic, 16-row or 128-row tiles, or the fused decode launch
+  int fused_blocks;    // resident workgroups of the fused decode kernel on the whole device
+  unsigned* fused_sync;  // its barrier counters [2] and status [1] (owned, zeroed at create)
   // Routes last filled by afd_ffn_route_from_capacity (keyed by their sorted_pair
   // buffer), with the batch size T: such a route keeps at most T of its T * top_k
   // pairs, so the automatic GEMM choice counts T rows for it.  Any other route call on

@@ -41,7 +41,7 @@ __device__ __forceinline__ void unpack16(const i32x4 r, float* v) {
   }
 }
 
-template <bool BF16, int KU, bool NT>
+template <bool BF16, int KU, bool NT, bool APPLY = true>
 __global__ void __launch_bounds__(kCombineThreads) combine_kernel(const void* __restrict__ O,
                                                                   const void* __restrict__ Os,
                                                                   const float* __restrict__ gates,
@@ -74,7 +74,7 @@ __global__ void __launch_bounds__(kCombineThreads) combine_kernel(const void* __
         float v[V];
         unpack16<BF16>(raw[j], v);
 #pragma unroll
-        for (int i = 0; i < V; ++i) acc[i] = fmaf(gj, v[i], acc[i]);
+        for (int i = 0; i < V; ++i) acc[i] = APPLY ? fmaf(gj, v[i], acc[i]) : acc[i] + v[i];
       }
     }
     if (Os) {
@@ -99,15 +99,21 @@ __global__ void __launch_bounds__(kCombineThreads) combine_kernel(const void* __
 
 template <bool BF16, bool NT>
 static void launch_combine_t(dim3 grid, const void* O, const void* Os, const float* gates, const int32_t* pair_pos,
-                             int k, int H, void* y, hipStream_t st) {
-  if (k <= 8)
+                             int k, int H, void* y, hipStream_t st, bool applied) {
+  if (applied) {  // the fused decode launch's rows (bf16, decode batches: k <= 32, plain loads)
+    if (k <= 8)
+      combine_kernel<BF16, 8, NT, false><<<grid, kCombineThreads, 0, st>>>(O, Os, gates, pair_pos, k, H, y);
+    else
+      combine_kernel<BF16, kCombineMaxK, NT, false><<<grid, kCombineThreads, 0, st>>>(O, Os, gates, pair_pos, k, H, y);
+  } else if (k <= 8) {
     combine_kernel<BF16, 8, NT><<<grid, kCombineThreads, 0, st>>>(O, Os, gates, pair_pos, k, H, y);
-  else
+  } else {
     combine_kernel<BF16, kCombineMaxK, NT><<<grid, kCombineThreads, 0, st>>>(O, Os, gates, pair_pos, k, H, y);
+  }
 }
 
 hipError_t launch_combine(const void* O, const void* Os, const float* gates, const int32_t* pair_pos, int T, int k,
-                          int H, void* y, bool bf16, hipStream_t st) {
+                          int H, void* y, bool bf16, hipStream_t st, bool gates_applied) {
   if (T <= 0) return hipSuccess;
   const int v = bf16 ? 8 : 4;
   if (k > kCombineMaxK || H % v) return hipErrorInvalidValue;
@@ -119,14 +125,14 @@ hipError_t launch_combine(const void* O, const void* Os, const float* gates, con
   const bool nt = (long long)T * k * H * (bf16 ? 2 : 4) > (256ll << 20);
   if (bf16) {
     if (nt)
-      launch_combine_t<true, true>(grid, O, Os, gates, pair_pos, k, H, y, st);
+      launch_combine_t<true, true>(grid, O, Os, gates, pair_pos, k, H, y, st, gates_applied);
     else
-      launch_combine_t<true, false>(grid, O, Os, gates, pair_pos, k, H, y, st);
+      launch_combine_t<true, false>(grid, O, Os, gates, pair_pos, k, H, y, st, gates_applied);
   } else {
     if (nt)
-      launch_combine_t<false, true>(grid, O, Os, gates, pair_pos, k, H, y, st);
+      launch_combine_t<false, true>(grid, O, Os, gates, pair_pos, k, H, y, st, gates_applied);
     else
-      launch_combine_t<false, false>(grid, O, Os, gates, pair_pos, k, H, y, st);
+      launch_combine_t<false, false>(grid, O, Os, gates, pair_pos, k, H, y, st, gates_applied);
   }
   return hipGetLastError();
 }

@@ -65,6 +65,96 @@ __device__ __forceinline__ void stream_mfma(const bf16x8* __restrict__ A, const 
   }
 }
 
+// Weights of the first D steps of an item's column group, loaded ahead of its
+// activations (the fused decode launch issues them before its grid barrier).
+template <int D>
+__device__ __forceinline__ void prime_weights(const i32x4* __restrict__ B, bf16x8* b0, bf16x8* b1) {
+#pragma unroll
+  for (int u = 0; u < D; ++u) {
+    b0[u] = load_weight_frag(B + (u * 2) * 64);
+    b1[u] = load_weight_frag(B + (u * 2 + 1) * 64);
+  }
+}
+
+// stream_mfma with the weights of the first D steps already in b0 / b1.
+template <int D>
+__device__ __forceinline__ void stream_mfma_primed(const bf16x8* __restrict__ A, const i32x4* __restrict__ B,
+                                                   int KB, f32x4& acc0, f32x4& acc1, bf16x8* b0, bf16x8* b1) {
+  bf16x8 a[D];
+#pragma unroll
+  for (int u = 0; u < D; ++u) a[u] = A[u * 4];
+  for (int s0 = D; s0 < KB; s0 += D) {
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], b0[u], acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], b1[u], acc1, 0, 0, 0);
+      const int s = s0 + u;
+      a[u] = A[s * 4];
+      b0[u] = load_weight_frag(B + (s * 2) * 64);
+      b1[u] = load_weight_frag(B + (s * 2 + 1) * 64);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < D; ++u) {
+    acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], b0[u], acc0, 0, 0, 0);
+    acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u], b1[u], acc1, 0, 0, 0);
+  }
+}
+
+// Operand addresses of one work item for this lane: A row of the tile (rows past the
+// tile end repeat its first row; their results are not stored) and the column group's
+// weight stream.
+struct StreamOps {
+  const bf16x8* A;
+  const i32x4* B;
+  int KB;
+};
+__device__ __forceinline__ StreamOps stream_ops(const GroupedGemm& g, const Item& it, int lane) {
+  const int K = it.shared ? g.K_shared : g.K_routed;
+  const int r = lane & 15;
+  const int rr = r < it.nrows ? r : 0;
+  int arow;
+  if (it.shared)
+    arow = it.row0 + rr;
+  else
+    arow = g.gather_routed ? g.sorted_pair[it.row0 + rr] / g.k : it.row0 + rr;
+  const int lda = it.shared ? g.lda_shared : g.lda_routed;
+  StreamOps o;
+  o.A = reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(it.shared ? g.a_shared : g.a_routed) +
+                                        (size_t)arow * lda) +
+        (lane >> 4);
+  const __bf16* wbase = it.shared ? static_cast<const __bf16*>(g.w_shared)
+                                  : static_cast<const __bf16*>(g.w_routed) + (size_t)it.seg * g.w_expert_elems;
+  o.KB = K / 32;
+  o.B = reinterpret_cast<const i32x4*>(wbase) + (size_t)it.group * o.KB * 128 + lane;
+  return o;
+}
+
+// Epilogue of one item: SwiGLU h rows (gate/up) or expert output rows O (down), bf16.
+// gates != NULL (down only): routed rows are stored already multiplied by their pair's
+// gate, so the combine sums them unweighted.
+template <bool SWIGLU>
+__device__ __forceinline__ void stream_store(const GroupedGemm& g, const Item& it, int lane, const f32x4& acc0,
+                                             const f32x4& acc1, const float* gates) {
+  const int col = lane & 15;
+  const int rbase = (lane >> 4) * 4;
+  __bf16* out = static_cast<__bf16*>(it.shared ? g.out_shared : g.out_routed);
+  const int ldo = it.shared ? g.ldo_shared : g.ldo_routed;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = rbase + i;
+    if (row >= it.nrows) continue;
+    if (SWIGLU) {
+      out[(size_t)(it.row0 + row) * ldo + it.group * 16 + col] = f32_to_bf16(silu(acc0[i]) * acc1[i]);
+    } else {
+      const float gs = gates && !it.shared ? gates[g.sorted_pair[it.row0 + row]] : 1.f;
+      __bf16* o = out + (size_t)(it.row0 + row) * ldo + it.group * 32 + col;
+      o[0] = f32_to_bf16(gs * acc0[i]);
+      o[16] = f32_to_bf16(gs * acc1[i]);
+    }
+  }
+}
+
 template <bool SWIGLU>
 __global__ void __launch_bounds__(kGemmThreads) gemm_bf16_stream_kernel(GroupedGemm g) {
   __shared__ int prefix[kMaxSegments + 1];
@@ -76,56 +166,125 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_bf16_stream_kernel(GroupedG
 
   for (int item = wave; item < total; item += waves_in_launch) {
     const Item it = decode_item(g, kTileRows, prefix, item);
-    const int K = it.shared ? g.K_shared : g.K_routed;
-    const int KB = K / 32;
-    // A row of this lane (rows past the tile end repeat its first row; their
-    // results are not stored)
-    const int r = lane & 15;
-    const int rr = r < it.nrows ? r : 0;
-    int arow;
-    if (it.shared)
-      arow = it.row0 + rr;
-    else
-      arow = g.gather_routed ? g.sorted_pair[it.row0 + rr] / g.k : it.row0 + rr;
-    const int lda = it.shared ? g.lda_shared : g.lda_routed;
-    const bf16x8* A = reinterpret_cast<const bf16x8*>(
-                          static_cast<const __bf16*>(it.shared ? g.a_shared : g.a_routed) + (size_t)arow * lda) +
-                      (lane >> 4);
-    const __bf16* wbase = it.shared ? static_cast<const __bf16*>(g.w_shared)
-                                    : static_cast<const __bf16*>(g.w_routed) + (size_t)it.seg * g.w_expert_elems;
-    const i32x4* B = reinterpret_cast<const i32x4*>(wbase) + (size_t)it.group * KB * 128 + lane;
-
+    const StreamOps o = stream_ops(g, it, lane);
     f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-    if (KB % 8 == 0)
-      stream_mfma<8>(A, B, KB, acc0, acc1);
+    if (o.KB % 8 == 0)
+      stream_mfma<8>(o.A, o.B, o.KB, acc0, acc1);
     else
-      stream_mfma<4>(A, B, KB, acc0, acc1);
+      stream_mfma<4>(o.A, o.B, o.KB, acc0, acc1);
+    stream_store<SWIGLU>(g, it, lane, acc0, acc1, nullptr);
+  }
+}
 
-    const int col = lane & 15;
-    const int rbase = (lane >> 4) * 4;
-    if (SWIGLU) {
-      __bf16* out = static_cast<__bf16*>(it.shared ? g.out_shared : g.out_routed);
-      const int ldo = it.shared ? g.ldo_shared : g.ldo_routed;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = rbase + i;
-        if (row < it.nrows)
-          out[(size_t)(it.row0 + row) * ldo + it.group * 16 + col] = f32_to_bf16(silu(acc0[i]) * acc1[i]);
-      }
-    } else {
-      __bf16* out = static_cast<__bf16*>(it.shared ? g.out_shared : g.out_routed);
-      const int ldo = it.shared ? g.ldo_shared : g.ldo_routed;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = rbase + i;
-        if (row < it.nrows) {
-          __bf16* o = out + (size_t)(it.row0 + row) * ldo + it.group * 32 + col;
-          o[0] = f32_to_bf16(acc0[i]);
-          o[16] = f32_to_bf16(acc1[i]);
-        }
+// The decode layer's two grouped GEMMs in one persistent launch (the single-launch
+// expert kernel of "大模型推理的内存与计算解耦：AFD 架构解析与性能验证", §5, MegaMoE, and
+// the persistent, tile-scheduled expert kernel of the ExpertPlex summary in
+// "AF分离论文串讲"): every wave runs its gate/up items, loads the weights of its first
+// down item's first steps (they do not depend on h), and passes a grid-wide barrier
+// once every workgroup has stored its h rows; then the down items run, with each
+// routed row's gate applied in the epilogue.
+//
+// The barrier: after a workgroup barrier, one thread makes the workgroup's h stores
+// visible device-wide (agent-scope release fence), counts the workgroup in `sync[0]`
+// and polls (sleeping between polls) until all gridDim.x workgroups have arrived, then
+// takes an agent-scope acquire fence.  Measured on MI355X at the starved-decode layer
+// (T=6): the launch takes 296 us against 212 us for the two separate GEMM launches
+// (with two fences per workgroup 321 us; with h written through and no fences 268 us;
+// polling 32x less often ~8 us less), so the separate launches stay the default.
+// The spin is bounded: after ~kFusedSpinLimit polls it gives up, sets
+// status[0] = 1 and the workgroup skips its down items (results are then wrong, but
+// every wave exits).  The grid is the device's resident workgroup count (occupancy
+// query at handle creation), so the workgroups are co-resident when nothing else runs
+// on the device.  The counters are returned to zero by the last workgroup to leave
+// (sync[1] counts departures), so consecutive launches, and replays of a captured
+// launch, start from zero without a memset.  Two launches that overlap on one set of
+// counters (one handle's workspace) race.  Needs K % 256 == 0 for every segment (both
+// phases use 8-step rings; checked by the host).
+constexpr unsigned kFusedSpinLimit = 1u << 18;
+
+__global__ void __launch_bounds__(kGemmThreads) gemm_bf16_fused_kernel(GroupedGemm g1, GroupedGemm g2,
+                                                                       const float* gates, unsigned* sync,
+                                                                       int* status) {
+  __shared__ int prefix1[kMaxSegments + 1];
+  __shared__ int prefix2[kMaxSegments + 1];
+  __shared__ int scan_tmp[kGemmWaves + 1];
+  __shared__ int passed;
+  const int total1 = build_item_prefix(g1, kTileRows, prefix1, scan_tmp);
+  const int total2 = build_item_prefix(g2, kTileRows, prefix2, scan_tmp);
+  const int lane = lane_id();
+  const int waves_in_launch = gridDim.x * kGemmWaves;
+  const int wave = blockIdx.x * kGemmWaves + threadIdx.x / kWave;
+
+  for (int item = wave; item < total1; item += waves_in_launch) {
+    const Item it = decode_item(g1, kTileRows, prefix1, item);
+    const StreamOps o = stream_ops(g1, it, lane);
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    stream_mfma<8>(o.A, o.B, o.KB, acc0, acc1);
+    stream_store<true>(g1, it, lane, acc0, acc1, nullptr);
+  }
+
+  // the first down item's weights, ahead of the barrier
+  bf16x8 b0[8], b1[8];
+  Item first = {};
+  const bool has_first = wave < total2;
+  if (has_first) {
+    first = decode_item(g2, kTileRows, prefix2, wave);
+    prime_weights<8>(stream_ops(g2, first, lane).B, b0, b1);
+  }
+
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    atomicAdd(&sync[0], 1u);
+    unsigned polls = 0;
+    int ok = 1;
+    while (__hip_atomic_load(&sync[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < gridDim.x) {
+      __builtin_amdgcn_s_sleep(64);
+      if (++polls > kFusedSpinLimit) {
+        ok = 0;
+        atomicExch(status, 1);
+        break;
       }
     }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    passed = ok;
   }
+  __syncthreads();
+
+  if (passed) {
+    if (has_first) {
+      const StreamOps o = stream_ops(g2, first, lane);
+      f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+      stream_mfma_primed<8>(o.A, o.B, o.KB, acc0, acc1, b0, b1);
+      stream_store<false>(g2, first, lane, acc0, acc1, gates);
+    }
+    for (int item = wave + waves_in_launch; item < total2; item += waves_in_launch) {
+      const Item it = decode_item(g2, kTileRows, prefix2, item);
+      const StreamOps o = stream_ops(g2, it, lane);
+      f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+      stream_mfma<8>(o.A, o.B, o.KB, acc0, acc1);
+      stream_store<false>(g2, it, lane, acc0, acc1, gates);
+    }
+  }
+
+  // the last workgroup to leave returns both counters to zero
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned d = atomicAdd(&sync[1], 1u);
+    if (d == gridDim.x - 1) {
+      atomicExch(&sync[0], 0u);
+      atomicExch(&sync[1], 0u);
+    }
+  }
+}
+
+hipError_t launch_gemm_bf16_fused(const GroupedGemm& g1, const GroupedGemm& g2, const float* gates, unsigned* sync,
+                                  int* status, int resident_blocks, hipStream_t st) {
+  if (g1.K_routed % 256 || g2.K_routed % 256 || (g1.shared_rows > 0 && (g1.K_shared % 256 || g2.K_shared % 256)))
+    return hipErrorInvalidValue;
+  if (resident_blocks <= 0) return hipErrorInvalidValue;
+  gemm_bf16_fused_kernel<<<(unsigned)resident_blocks, kGemmThreads, 0, st>>>(g1, g2, gates, sync, status);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm_bf16(const GroupedGemm& g, bool swiglu, long long max_items, int max_blocks, hipStream_t st) {
@@ -149,5 +308,8 @@ hipError_t gemm_occupancy_bf16(int* gate_up, int* down) {
   if (e == hipSuccess)
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(down, gemm_bf16_stream_kernel<false>, kGemmThreads, 0);
   return e;
+}
+hipError_t gemm_occupancy_bf16_fused(int* blocks) {
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, gemm_bf16_fused_kernel, kGemmThreads, 0);
 }
 }  // namespace afd

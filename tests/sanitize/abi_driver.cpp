@@ -112,7 +112,8 @@ int main() {
   }
   // knobs, profiling, sizes, errors
   EXPECT(afd_ffn_set_gemm_kernel(h, AFD_GEMM_TILED) == AFD_OK, "gemm knob");
-  EXPECT(afd_ffn_set_gemm_kernel(h, 3) == AFD_EINVAL, "unknown gemm kernel");
+  EXPECT(afd_ffn_set_gemm_kernel(h, AFD_GEMM_FUSED) == AFD_OK, "fused knob");
+  EXPECT(afd_ffn_set_gemm_kernel(h, 4) == AFD_EINVAL, "unknown gemm kernel");
   EXPECT(afd_ffn_set_profiling(h, 1) == AFD_OK && afd_ffn_set_profiling(h, 0) == AFD_OK, "profiling");
   double ms[AFD_NUM_STAGES];
   int64_t n[AFD_NUM_STAGES];

@@ -358,6 +358,7 @@ def test_integer_logits_ties():
     (small("graph_decode", T=6, E=16, k=4, Ms=128), "auto"),        # one-launch route, streaming GEMMs
     (small("graph_tiled", T=200, E=4, k=2, H=256, M=256), "tiled"),  # two-kernel route, 128-row tiles
     (small("graph_fp8", dtype="fp8", T=50, H=384, M=256, E=6, k=2, Ms=256), "tiled"),
+    (small("graph_fused", T=6, H=512, M=512, E=16, k=4, Ms=256), "fused"),  # one persistent GEMM launch
 ], ids=lambda v: v if isinstance(v, str) else v.name)
 def test_hip_graph_replays_match_eager(w, kernel):
     """route + forward captured in a HIP graph: every replay, with eager work and
@@ -587,3 +588,58 @@ def test_profiling_counts_launches(T):
         else:
             assert prof[st][1] == 3 and prof[st][0] > 0
     assert afd_ffn_profile_read(layer.handle)["gate_up"][1] == 0
+
+
+# ----------------------------------------------------------------------------- fused decode launch
+def test_fused_decode_layer_every_token():
+    """AFD_GEMM_FUSED on the starved-decode layer: both GEMMs in one persistent launch
+    with a grid barrier, the gates applied in the down epilogue; every token against
+    the oracle, and two calls in a row bitwise equal (the barrier counters return to
+    zero)."""
+    layer, x, logits, y = full_case(workloads.STARVED_DECODE, kernel="fused")
+    _, y2 = run_layer(layer, x, logits)
+    assert torch.equal(y, y2)
+    layer.set_gemm_kernel("stream")
+    _, y3 = run_layer(layer, x, logits)
+    d = (y3.float() - y.float()).abs().max().item()
+    say(f"fused vs separate launches: max |diff| = {d:.3e}")  # the gate is applied before O's rounding
+    assert d <= 2e-2 * y3.float().abs().max().item()
+    layer.close()
+
+
+@pytest.mark.parametrize("w", [
+    small("fused_shared", T=37, H=512, M=256, E=16, k=4, Ms=256),
+    small("fused_k1", T=40, H=256, M=512, E=8, k=1),
+    small("fused_k_equals_E", T=9, H=256, M=256, E=4, k=4, Ms=512),
+    small("fused_one_token", T=1, H=768, M=512, E=8, k=2),
+    small("fused_many_items", T=60, H=1024, M=768, E=32, k=8, Ms=256),
+], ids=lambda w: w.name)
+def test_fused_decode_shapes(w):
+    full_case(w, kernel="fused")
+
+
+def test_fused_decode_on_a_capacity_route():
+    """Empty slots of a capacity route carry gate 0: the fused launch computes no row for
+    them and the combine skips them."""
+    w = small("fused_capacity", T=48, H=512, M=256, E=8, k=4, Ms=256)
+    weights = workloads.make_weights(w, device="cuda")
+    x, logits = workloads.make_activations(w, device="cuda")
+    layer = make_layer(w, weights)
+    layer.set_gemm_kernel("fused")
+    rb = layer.new_route()
+    layer.route(logits, w.T, rb)
+    limits = torch.full((w.E,), 2, dtype=torch.int32, device="cuda")  # at most 3 per expert: drops
+    cap = layer.route_capacity(rb.topk_ids[:w.T * w.k].contiguous(), rb.topk_gates[:w.T * w.k].contiguous(), w.T,
+                               limits, 2, False)
+    rc = layer.new_route()
+    layer.route_from_capacity(cap, w.T, rc)
+    y = torch.full((w.T, w.H), float("nan"), dtype=torch.bfloat16, device="cuda")
+    layer.forward(x, w.T, rc, y)
+    torch.cuda.synchronize()
+    assign, weight = cap[0].cpu().numpy(), cap[1].cpu().numpy()
+    assert (assign < 0).any(), "the case drops some tokens"
+    yref, _ = oracle.layer_assigned(x.float().cpu().numpy(), assign, weight, H=w.H, M=w.M, E=w.E, dtype=w.dtype,
+                                    w_gu=weights["w_gu"], w_d=weights["w_d"], Ms=w.Ms, ws_gu=weights["ws_gu"],
+                                    ws_d=weights["ws_d"])
+    check_y(y, yref, TOL[w.dtype], w.name)
+    layer.close()

@@ -36,10 +36,13 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("w", CASES, ids=lambda w: w.name)
-def test_noalloc_forward_equals_forward_twice(w):
-    print(f"no-alloc case {w.name}", flush=True)
+@pytest.mark.parametrize("w,kernel", [(w, "auto") for w in CASES] +
+                         [(workloads.Workload("noalloc_fused", 506, T=6, H=512, M=512, E=16, k=4, Ms=256,
+                                              dtype="bf16"), "fused")], ids=lambda v: v if isinstance(v, str) else v.name)
+def test_noalloc_forward_equals_forward_twice(w, kernel):
+    print(f"no-alloc case {w.name} gemm={kernel}", flush=True)
     layer = layer_of(w, w.T)
+    layer.set_gemm_kernel(kernel)
     x, logits = workloads.make_activations(w, device="cuda")
     ydt = torch.float32 if w.dtype == "f32" else torch.bfloat16
     for T in (w.T, max(1, w.T // 3)):     # the second call with a smaller batch
