@@ -137,17 +137,23 @@ __device__ __forceinline__ void tiled_ctx(const GroupedGemm& g, const int* prefi
   // tile; the lane carries the 16-byte piece lane % 16 of each row's 256-byte chunk.
   const int lda = x.shared ? g.lda_shared : g.lda_routed;
   x.abase = static_cast<const bf16x8*>(x.shared ? g.a_shared : g.a_routed);
+  // The sorted_pair lookups are all issued before the first is used: in a branch per
+  // row, each would wait for its load (and every load in flight) before the next one
+  // issues.
+  int ar[kTiledLoads];
 #pragma unroll
   for (int i = 0; i < kTiledLoads; ++i) {
-    int r = w * 32 + i * 4 + (lane >> 4);
-    r = r < x.nrows ? r : 0;
-    int ar;
-    if (x.shared)
-      ar = x.row0 + r;
-    else
-      ar = g.gather_routed ? g.sorted_pair[x.row0 + r] / g.k : x.row0 + r;
-    x.aoff[i] = (uint32_t)ar * (uint32_t)(lda / 8) + (uint32_t)(lane & 15);
+    const int r = w * 32 + i * 4 + (lane >> 4);
+    ar[i] = x.row0 + (r < x.nrows ? r : 0);
   }
+  if (!x.shared && g.gather_routed) {
+#pragma unroll
+    for (int i = 0; i < kTiledLoads; ++i) ar[i] = g.sorted_pair[ar[i]];
+#pragma unroll
+    for (int i = 0; i < kTiledLoads; ++i) ar[i] /= g.k;
+  }
+#pragma unroll
+  for (int i = 0; i < kTiledLoads; ++i) x.aoff[i] = (uint32_t)ar[i] * (uint32_t)(lda / 8) + (uint32_t)(lane & 15);
   // weights: 16-byte chunk of (step s, half kh) of block cb at boff[cb] + s*128 + kh*32
   x.wbase = x.shared ? static_cast<const bf16x8*>(g.w_shared)
                      : static_cast<const bf16x8*>(g.w_routed) + (size_t)x.seg * (g.w_expert_elems / 8);

@@ -3,11 +3,12 @@
 // receive many rows (the DeepSeek-V3-like layer of an FFN instance aggregating
 // attention batches; FP8/BF16 mixed precision: the omica.com.cn AFD article, §3.3).
 //
-// A workgroup of 4 waves computes a 128-token tile of one expert times 8 32-column
-// groups; wave w owns groups 2w and 2w+1 for all 128 tokens.  The matrix-core
-// instruction is v_mfma_scale_f32_16x16x128_f8f6f4 (unit E8M0 scales): one
-// instruction covers one 128-deep scale block of a 16 x 16 output block, and its fp32
-// partial product is added to the accumulator times s_act[token][kb] * s_w[kb][nb].
+// A workgroup of 8 waves (two per SIMD) computes a 128-token tile of one expert times
+// 8 32-column groups; wave w owns group w for all 128 tokens.  The matrix-core
+// instruction is v_mfma_f32_16x16x128_f8f6f4 (the scaled builtin with zero scale
+// operands, which the compiler emits as the unscaled instruction): one instruction
+// covers one 128-deep scale block of a 16 x 16 output block, and its fp32 partial
+// product is added to the accumulator times s_act[token][kb] * s_w[kb][nb].
 //
 // Operand roles.  The weights are the instruction's first operand and the tokens its
 // second, so the 16 x 16 result is (weight column) x (token): lane l holds columns
@@ -25,16 +26,20 @@
 // has 16 slots of 272 bytes, slot q holding piece q of its 16 rows at (row % 16) * 16.
 // Piece q of a chunk is (scale block q / 8, reduction group (q % 8) / 2, 16-byte half
 // q % 2) of the operand.  The 16 lanes writing one row hit 16 different bank groups;
-// a 16-lane quarter of an operand read is one slot, contiguous.  The tokens' scales of
-// the chunk are staged beside them.  Double-buffered; the next chunk is loaded into
-// registers while the current one is multiplied.
+// a 16-lane quarter of an operand read is one slot, contiguous.  Double-buffered; the
+// next chunk is loaded into registers while the current one is multiplied.  Each wave
+// stages one 16-row block.
 //
-// The weight scales of a chunk's two blocks are staged through LDS beside the token
-// scales, so inside a block the only memory waits are for the weight ring.
+// The chunk's token scales and the weight scales of its two blocks are staged through
+// LDS beside the activations (one scale per lane per chunk), so inside a block the only
+// memory waits are for the weight ring.  Every staging load is issued unconditionally
+// and its value is first used at the LDS write a chunk later: a load under a divergent
+// branch, or one whose value is used at once, makes the compiler wait for every load
+// in flight, the weight ring's included.
 //
 // Schedule of a block.  Rescaling costs one multiply and four FMAs per MFMA, about
-// half the MFMA time, and with one wave per SIMD it only overlaps the matrix core when
-// the instruction order interleaves them.  Each step rb of a block reads token block
+// half the MFMA time; with two waves per SIMD one wave's rescaling overlaps the other
+// wave's MFMAs, and within a wave the instruction order interleaves them.  Each step rb of a block reads token block
 // rb + 1's operand from LDS, then alternates block rb's MFMAs with the rescaling of
 // block rb - 1's products (kept in a second register set).  The compiler would
 // otherwise gather the pure arithmetic of the whole unrolled block in one place, so
@@ -49,23 +54,25 @@
 
 namespace afd {
 
-#ifndef AFD_FP8_TILED_WAVES
-#define AFD_FP8_TILED_WAVES 8
-#endif
-constexpr int kF8Waves = AFD_FP8_TILED_WAVES;   // 4: one wave per SIMD; 8: two
+constexpr int kF8Waves = 8;                     // two per SIMD
 constexpr int kF8Threads = kF8Waves * kWave;
 constexpr int kF8RowBlocks = 8;                 // 16-token blocks per tile
 constexpr int kF8Rows = 16 * kF8RowBlocks;      // 128
 constexpr int kF8Groups = 8;                    // 32-column groups per tile (one h quantisation group)
 constexpr int kF8GroupsPerWave = kF8Groups / kF8Waves;  // 32-column groups per wave
 constexpr int kF8CB = 2 * kF8GroupsPerWave;     // 16-column blocks per wave
-static_assert(kF8Waves == 4 || kF8Waves == 8, "4 or 8 waves per workgroup");
 constexpr int kF8Slot = 272;                    // bytes per staging slot (16 rows x 16 B + padding)
 constexpr int kF8A = kF8RowBlocks * 16 * kF8Slot;  // activation bytes per buffer
 constexpr int kF8WScales = 2 * kF8Waves * kF8CB;  // weight scales per chunk (2 blocks)
-constexpr int kF8Buf = kF8A + 2 * kF8Rows * 4 + kF8WScales * 4;  // + the chunk's token and weight scales
+// + the chunk's token and weight scales, and one 16-byte word that the threads with no
+// scale to stage write to
+constexpr int kF8Buf = kF8A + 2 * kF8Rows * 4 + kF8WScales * 4 + 16;
+constexpr int kF8Dummy = kF8A + 2 * kF8Rows * 4 + kF8WScales * 4;  // byte offset of that word
 constexpr int kF8StageRows = kF8Rows / kF8Waves;  // rows each wave stages per chunk
 constexpr int kF8Loads = kF8StageRows / 4;      // staging loads per thread per chunk (4 rows each)
+// Each wave stages its rows' token scales of a chunk (2 blocks) in lanes 0-31 and the
+// chunk's weight scales in lanes 32-63 (written by wave 0 only): one load per lane.
+static_assert(2 * kF8StageRows + kF8WScales == kWave, "one scale per lane per chunk");
 #ifndef AFD_FP8_TILED_RING
 #define AFD_FP8_TILED_RING 2
 #endif
@@ -123,7 +130,7 @@ __device__ __forceinline__ void fp8_tile(const GroupedGemm& g, const Item& it, c
   // do not fit the register budget)
   int lane = lane_id();
   asm volatile("" : "+v"(lane));
-    const int K = it.shared ? g.K_shared : g.K_routed;
+  const int K = it.shared ? g.K_shared : g.K_routed;
   const int KB = K / 128;
   const int NC = (KB + 1) / 2;  // 256-deep chunks; an odd KB leaves the last chunk half live
   const int groups = it.shared ? g.groups_shared : g.groups_routed;
@@ -139,31 +146,31 @@ __device__ __forceinline__ void fp8_tile(const GroupedGemm& g, const Item& it, c
   const int lda = it.shared ? g.lda_shared : g.lda_routed;
   const uint8_t* abase = static_cast<const uint8_t*>(it.shared ? g.a_shared : g.a_routed);
   const int piece = lane & 15;
-  const uint8_t* arow[kF8Loads];
+  // Source rows of the staged rows and of this thread's token-scale row (t % 128).
+  // The sorted_pair lookups are
+  // all issued before the first is used: in a branch per row, each would wait for
+  // its load before the next one issues.
+  int ar[kF8Loads + 1];
 #pragma unroll
   for (int i = 0; i < kF8Loads; ++i) {
-    int r = w * kF8StageRows + i * 4 + (lane >> 4);
-    r = r < it.nrows ? r : 0;
-    int ar;
-    if (it.shared)
-      ar = it.row0 + r;
-    else
-      ar = g.gather_routed ? g.sorted_pair[it.row0 + r] / g.k : it.row0 + r;
-    arow[i] = abase + (size_t)ar * lda;
+    const int r = w * kF8StageRows + i * 4 + (lane >> 4);
+    ar[i] = it.row0 + (r < it.nrows ? r : 0);
   }
-  // token scales of the chunk: thread t < 128 stages row t's two scale-block values
-  const float* asbase = it.shared ? g.as_shared : g.as_routed;
-  const float* srow;
   {
-    const int t = threadIdx.x < kF8Rows ? threadIdx.x : 0;
-    const int r = t < it.nrows ? t : 0;
-    int ar;
-    if (it.shared)
-      ar = it.row0 + r;
-    else
-      ar = g.gather_routed ? g.sorted_pair[it.row0 + r] / g.k : it.row0 + r;
-    srow = asbase + (size_t)ar * KB;
+    const int t = w * kF8StageRows + (lane & (kF8StageRows - 1));
+    ar[kF8Loads] = it.row0 + (t < it.nrows ? t : 0);
   }
+  if (!it.shared && g.gather_routed) {
+#pragma unroll
+    for (int i = 0; i <= kF8Loads; ++i) ar[i] = g.sorted_pair[ar[i]];
+#pragma unroll
+    for (int i = 0; i <= kF8Loads; ++i) ar[i] /= g.k;
+  }
+  const uint8_t* arow[kF8Loads];
+#pragma unroll
+  for (int i = 0; i < kF8Loads; ++i) arow[i] = abase + (size_t)ar[i] * lda;
+  const float* asbase = it.shared ? g.as_shared : g.as_routed;
+  const float* srow = asbase + (size_t)ar[kF8Loads] * KB;
   // byte offset in the row of chunk c's piece for this lane (clamped past the end of
   // K: that scale block is multiplied with weight scale 0)
   auto a_off = [&](int c) {
@@ -173,9 +180,6 @@ __device__ __forceinline__ void fp8_tile(const GroupedGemm& g, const Item& it, c
   // LDS: write slot of load i (token block (w*kF8StageRows + i*4 + lane/16) / 16 =
   // w*kF8StageRows/16 + i/4, slot = piece, row in block (i % 4) * 4 + lane / 16)
   const int wr_off = ((w * (kF8StageRows / 16)) * 16 + piece) * kF8Slot + (lane >> 4) * 16;
-  // token block of staging load i (wave-uniform): rows of blocks past NRB are neither
-  // loaded nor written
-  auto stage_tb = [&](const int i) { return w * (kF8StageRows / 16) + i / 4; };
   // read: slot (lane / 16) * 2 (+1 for the upper 16 bytes) of the scale block's 8
   const int rd_off = ((lane >> 4) * 2) * kF8Slot + (lane & 15) * 16;
 
@@ -185,12 +189,20 @@ __device__ __forceinline__ void fp8_tile(const GroupedGemm& g, const Item& it, c
   // 16-column block cb = (group group0 + cb / 2, half cb % 2): 2 KiB per scale block
   const uint8_t* B = wbase + (size_t)group0 * group_stride + lane * 16;
   const float* ws = it.shared ? g.s_shared : g.s_routed + (size_t)it.seg * g.s_expert_elems;
-  // Weight scales are staged through LDS with the activations: thread t <
-  // kF8WScales loads, for block t / (kF8WScales / 2) of a chunk, the scale of wave
-  // (t / kF8CB) % kF8Waves's 16-column block t % kF8CB.
+  // Scales staged with the activations (one per lane per chunk): lane l < 32 stages
+  // the value of block l / 16 of the chunk for the wave's row l % 16; lane 32 + u
+  // stages, for block u / 16 of the chunk, the scale of wave (u % 16) / kF8CB's
+  // 16-column block u % kF8CB (wave 0 writes them, the other waves' copies go to the
+  // dummy word).  Loads and LDS writes of the staging are branch-free: a load under a
+  // divergent branch whose value is used a chunk later makes the compiler wait, at
+  // the use, for every load in flight, the weight ring's included.
+  const bool sc_tok = lane < 2 * kF8StageRows;
+  const int sc_blk = sc_tok ? lane / kF8StageRows : (lane - 2 * kF8StageRows) / (kF8WScales / 2);
+  const int sc_off = sc_tok ? kF8A + (sc_blk * kF8Rows + w * kF8StageRows + (lane % kF8StageRows)) * 4
+                            : (w == 0 ? kF8A + (2 * kF8Rows + lane - 2 * kF8StageRows) * 4 : kF8Dummy);
   int wnb;
   {
-    const int t = threadIdx.x % (kF8WScales / 2);
+    const int t = lane % (kF8WScales / 2);  // used by lanes >= 32
     const int w2 = t / kF8CB, cb = t % kF8CB;
     const int g0 = it.group + w2 * kF8GroupsPerWave < groups ? it.group + w2 * kF8GroupsPerWave
                                                              : groups - kF8GroupsPerWave;
@@ -204,6 +216,35 @@ __device__ __forceinline__ void fp8_tile(const GroupedGemm& g, const Item& it, c
 #pragma unroll
     for (int cb = 0; cb < kF8CB; ++cb) acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // Staging register sets: set (c % kF8StageSets) holds chunk c between its loads and
+  // its LDS write.  Chunk 0 -> LDS buffer 0; chunks 1 .. kF8StageSets (clamped to the
+  // last chunk) -> the sets.  Rows of token blocks past NRB are loaded (their rows
+  // read the item's row 0) and written like the others, and never read.
+  bf16x8 stage[kF8StageSets][kF8Loads];
+  // sstage holds the lane's loaded scale and slive whether its block is inside K (a
+  // block past the end of K, odd K / 128, gets weight scale 0): the zeroing is applied
+  // when the value is written to LDS, so that no instruction needs the loaded value
+  // before the write.
+  float sstage[kF8StageSets];
+  bool slive[kF8StageSets];
+  auto load_stage = [&](const int set, int c) {
+    c = c < NC ? c : NC - 1;
+#pragma unroll
+    for (int i = 0; i < kF8Loads; ++i) stage[set][i] = *reinterpret_cast<const bf16x8*>(arow[i] + a_off(c));
+    const int kb = 2 * c + sc_blk;
+    const int kbc = kb < KB ? kb : KB - 1;
+    sstage[set] = *(sc_tok ? srow + kbc : ws + (size_t)kbc * NB + wnb);
+    slive[set] = sc_tok || kb < KB;
+  };
+  auto write_stage = [&](const int set, int buf) {
+#pragma unroll
+    for (int i = 0; i < kF8Loads; ++i)
+      *reinterpret_cast<bf16x8*>(lds + buf + wr_off + (i >> 2) * 16 * kF8Slot + (i & 3) * 64) = stage[set][i];
+    *reinterpret_cast<float*>(lds + buf + sc_off) = slive[set] ? sstage[set] : 0.f;
+  };
+  // chunk 0's activations are loaded before the weight ring, so that the wait for
+  // them before their LDS write does not include the ring's loads
+  load_stage(0, 0);
   i32x8 bring[kF8BAhead][kF8CB];
 #pragma unroll
   for (int u = 0; u < kF8BAhead; ++u) {
@@ -212,43 +253,6 @@ __device__ __forceinline__ void fp8_tile(const GroupedGemm& g, const Item& it, c
     for (int cb = 0; cb < kF8CB; ++cb) bring[u][cb] = f8_load32(B + (cb >> 1) * group_stride + (s * 2 + (cb & 1)) * 2048);
   }
 
-  // Staging register sets: set (c % kF8StageSets) holds chunk c between its loads and
-  // its LDS write.  Chunk 0 -> LDS buffer 0; chunks 1 .. kF8StageSets (clamped to the
-  // last chunk) -> the sets.
-  bf16x8 stage[kF8StageSets][kF8Loads];
-  float sstage0[kF8StageSets], sstage1[kF8StageSets], wstage[kF8StageSets];
-  auto load_stage = [&](const int set, int c) {
-    c = c < NC ? c : NC - 1;
-#pragma unroll
-    for (int i = 0; i < kF8Loads; ++i)
-      if (NRB == kF8RowBlocks || stage_tb(i) < NRB)
-        stage[set][i] = *reinterpret_cast<const bf16x8*>(arow[i] + a_off(c));
-    if (threadIdx.x < kF8Rows) {
-      const int k1 = 2 * c + 1 < KB ? 2 * c + 1 : KB - 1;
-      sstage0[set] = srow[2 * c];
-      sstage1[set] = srow[k1];
-    }
-    if (threadIdx.x < kF8WScales) {
-      // a scale block past the end of K (odd K / 128) gets weight scale 0
-      const int kb = 2 * c + threadIdx.x / (kF8WScales / 2);
-      const int kbc = kb < KB ? kb : KB - 1;
-      wstage[set] = ws[(size_t)kbc * NB + wnb] * (kb < KB ? 1.f : 0.f);
-    }
-  };
-  auto write_stage = [&](const int set, int buf) {
-#pragma unroll
-    for (int i = 0; i < kF8Loads; ++i)
-      if (NRB == kF8RowBlocks || stage_tb(i) < NRB)
-        *reinterpret_cast<bf16x8*>(lds + buf + wr_off + (i >> 2) * 16 * kF8Slot + (i & 3) * 64) = stage[set][i];
-    if (threadIdx.x < kF8Rows) {
-      float* s = reinterpret_cast<float*>(lds + buf + kF8A);
-      s[threadIdx.x] = sstage0[set];
-      s[kF8Rows + threadIdx.x] = sstage1[set];
-    }
-    if (threadIdx.x < kF8WScales)
-      reinterpret_cast<float*>(lds + buf + kF8A)[2 * kF8Rows + threadIdx.x] = wstage[set];
-  };
-  load_stage(0, 0);
   write_stage(0, 0);
 #pragma unroll
   for (int u = 1; u <= kF8StageSets; ++u) load_stage(u % kF8StageSets, u);
@@ -321,6 +325,9 @@ __device__ __forceinline__ void fp8_tile(const GroupedGemm& g, const Item& it, c
 #pragma unroll
     for (int cb = 0; cb < kF8CB; ++cb)
       bring[r][cb] = f8_load32(B + (cb >> 1) * group_stride + (sn * 2 + (cb & 1)) * 2048);
+    // issue the refill here, not after the chunk's staging writes (which wait for the
+    // staging loads)
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   // Chunk c (parity u = c % 2 when unrolled) computes from LDS buffer c % 2; at its
