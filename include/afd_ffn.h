@@ -267,8 +267,12 @@ int afd_ffn_quantize_fp8(const void* src, int32_t rows, int32_t cols, int32_t sr
  * loaded ahead, a grid-wide barrier, then the down items with each routed row's gate
  * applied in their epilogue (the combine then sums unweighted).  Its workgroups must
  * all be resident at once: the launch uses the device's resident count, and a
- * workgroup that waits at the barrier for longer than ~0.1-1 s gives up (wrong
- * output, no hang); nothing else may occupy the device meanwhile.  fp32 layers always
+ * workgroup that waits at the barrier for longer than ~0.1-1 s gives up and writes NaN
+ * into the down-projection rows it owns, so the tokens those rows feed get NaN
+ * outputs (a loud failure, no hang); nothing else may occupy the device meanwhile.
+ * The environment variable AFD_FUSED_SPIN_LIMIT, read when a handle is created,
+ * lowers the number of polls before giving up (0 up to 262144; for failure-injection
+ * tests).  fp32 layers always
  * use their own kernel.  Takes effect for later forward calls.  Other values:
  * AFD_EINVAL. */
 typedef enum afd_gemm_kernel {

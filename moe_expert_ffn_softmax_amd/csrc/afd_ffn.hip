@@ -4,6 +4,7 @@
 #include <stdarg.h>
 #include <stdint.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <mutex>
@@ -363,6 +364,14 @@ extern "C" int afd_ffn_create(const afd_ffn_config* cfg, const void* w_gate_up, 
     }
     h->fused_blocks = fo * h->num_cus;
   }
+  // polls at the fused decode launch's barrier before a workgroup gives up; the
+  // environment can lower it to provoke the give-up path (failure-injection tests)
+  h->fused_spin_limit = afd::kFusedSpinLimit;
+  if (const char* v = getenv("AFD_FUSED_SPIN_LIMIT")) {
+    char* end = nullptr;
+    const unsigned long n = strtoul(v, &end, 10);
+    if (end != v && *end == '\0' && n <= afd::kFusedSpinLimit) h->fused_spin_limit = (unsigned)n;
+  }
 
   const size_t H = cfg->hidden, M = cfg->inter, Ms = cfg->shared_inter, E = cfg->num_experts;
   const size_t P = (size_t)cfg->max_tokens * cfg->top_k, T = cfg->max_tokens;
@@ -683,7 +692,8 @@ static int forward_checked(afd_ffn_t h, const afd_workspace& ws, const void* x, 
     {
       StageScope s(h, st, AFD_STAGE_FUSED);
       hipError_t e = afd::launch_gemm_bf16_fused(g1, g2, r->topk_gates, ws.fused_sync,
-                                                 reinterpret_cast<int*>(ws.fused_sync + 2), h->fused_blocks, st);
+                                                 reinterpret_cast<int*>(ws.fused_sync + 2), h->fused_blocks,
+                                                 h->fused_spin_limit, st);
       if (e != hipSuccess) return hip_fail(e, "fused gate/up + down launch");
       s.done();
     }

@@ -88,9 +88,11 @@ hipError_t launch_gemm_bf16(const GroupedGemm& g, bool swiglu, long long max_ite
 // Decode layers: g1 (gate/up) and g2 (down) in one persistent launch of
 // `resident_blocks` workgroups with a grid-wide barrier between them; routed down rows
 // are multiplied by gates[pair].  sync: 2 counters that start (and are left) at zero;
-// status[0] is set to 1 if a workgroup gave up waiting at the barrier.
+// status[0] is set to 1 if a workgroup gave up waiting at the barrier (after
+// spin_limit polls), and such a workgroup writes NaN into its down rows.
 hipError_t launch_gemm_bf16_fused(const GroupedGemm& g1, const GroupedGemm& g2, const float* gates, unsigned* sync,
-                                  int* status, int resident_blocks, hipStream_t st);
+                                  int* status, int resident_blocks, unsigned spin_limit, hipStream_t st);
+constexpr unsigned kFusedSpinLimit = 1u << 18;  // default polls before giving up
 hipError_t gemm_occupancy_bf16_fused(int* blocks);
 hipError_t launch_gemm_f32(const GroupedGemm& g, bool swiglu, long long max_items, int max_blocks, hipStream_t st);
 // Large-tile variant (128-row tiles, 8 column groups per item) for experts with many
@@ -188,6 +190,7 @@ struct afd_ffn {
                        // (bf16 gate/up, down; fp32 gate/up, down; fp8 gate/up, down)
   int gemm_mode;       // afd_gemm_kernel: automatic, 16-row or 128-row tiles, or the fused decode launch
   int fused_blocks;    // resident workgroups of the fused decode kernel on the whole device
+  unsigned fused_spin_limit;  // polls at its barrier before a workgroup gives up
   unsigned* fused_sync;  // its barrier counters [2] and status [1] (owned, zeroed at create)
   // Routes last filled by afd_ffn_route_from_capacity (keyed by their sorted_pair
   // buffer), with the batch size T: such a route keeps at most T of its T * top_k

@@ -191,20 +191,19 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_bf16_stream_kernel(GroupedG
 // (T=6): the launch takes 296 us against 212 us for the two separate GEMM launches
 // (with two fences per workgroup 321 us; with h written through and no fences 268 us;
 // polling 32x less often ~8 us less), so the separate launches stay the default.
-// The spin is bounded: after ~kFusedSpinLimit polls it gives up, sets
-// status[0] = 1 and the workgroup skips its down items (results are then wrong, but
-// every wave exits).  The grid is the device's resident workgroup count (occupancy
+// The spin is bounded: after `spin_limit` polls (~0.1-1 s at the default) it gives up,
+// sets status[0] = 1 and the workgroup writes NaN into the rows of its down items
+// instead of computing them, so every token those rows feed gets a NaN output (a loud
+// failure, not a silently wrong one), and every wave exits.  The grid is the device's resident workgroup count (occupancy
 // query at handle creation), so the workgroups are co-resident when nothing else runs
 // on the device.  The counters are returned to zero by the last workgroup to leave
 // (sync[1] counts departures), so consecutive launches, and replays of a captured
 // launch, start from zero without a memset.  Two launches that overlap on one set of
 // counters (one handle's workspace) race.  Needs K % 256 == 0 for every segment (both
 // phases use 8-step rings; checked by the host).
-constexpr unsigned kFusedSpinLimit = 1u << 18;
-
 __global__ void __launch_bounds__(kGemmThreads) gemm_bf16_fused_kernel(GroupedGemm g1, GroupedGemm g2,
                                                                        const float* gates, unsigned* sync,
-                                                                       int* status) {
+                                                                       int* status, unsigned spin_limit) {
   __shared__ int prefix1[kMaxSegments + 1];
   __shared__ int prefix2[kMaxSegments + 1];
   __shared__ int scan_tmp[kGemmWaves + 1];
@@ -240,7 +239,7 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_bf16_fused_kernel(GroupedGe
     int ok = 1;
     while (__hip_atomic_load(&sync[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < gridDim.x) {
       __builtin_amdgcn_s_sleep(64);
-      if (++polls > kFusedSpinLimit) {
+      if (++polls > spin_limit) {
         ok = 0;
         atomicExch(status, 1);
         break;
@@ -265,6 +264,11 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_bf16_fused_kernel(GroupedGe
       stream_mfma<8>(o.A, o.B, o.KB, acc0, acc1);
       stream_store<false>(g2, it, lane, acc0, acc1, gates);
     }
+  } else {
+    const float nan = __builtin_nanf("");
+    const f32x4 q = {nan, nan, nan, nan};
+    for (int item = wave; item < total2; item += waves_in_launch)
+      stream_store<false>(g2, decode_item(g2, kTileRows, prefix2, item), lane, q, q, gates);
   }
 
   // the last workgroup to leave returns both counters to zero
@@ -279,11 +283,12 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_bf16_fused_kernel(GroupedGe
 }
 
 hipError_t launch_gemm_bf16_fused(const GroupedGemm& g1, const GroupedGemm& g2, const float* gates, unsigned* sync,
-                                  int* status, int resident_blocks, hipStream_t st) {
+                                  int* status, int resident_blocks, unsigned spin_limit, hipStream_t st) {
   if (g1.K_routed % 256 || g2.K_routed % 256 || (g1.shared_rows > 0 && (g1.K_shared % 256 || g2.K_shared % 256)))
     return hipErrorInvalidValue;
   if (resident_blocks <= 0) return hipErrorInvalidValue;
-  gemm_bf16_fused_kernel<<<(unsigned)resident_blocks, kGemmThreads, 0, st>>>(g1, g2, gates, sync, status);
+  gemm_bf16_fused_kernel<<<(unsigned)resident_blocks, kGemmThreads, 0, st>>>(g1, g2, gates, sync, status,
+                                                                             spin_limit);
   return hipGetLastError();
 }
 

@@ -618,6 +618,34 @@ def test_fused_decode_shapes(w):
     full_case(w, kernel="fused")
 
 
+def test_fused_decode_barrier_give_up_writes_nan(monkeypatch):
+    """A workgroup that gives up waiting at the fused launch's barrier writes NaN into the
+    down rows it owns instead of leaving them stale.  The poll limit is forced to 0 from
+    the host (AFD_FUSED_SPIN_LIMIT, read at handle creation): every workgroup but the
+    last to arrive gives up at once, and every wave still exits.  Some outputs are then
+    NaN, every other output equals a normal fused call's bitwise, and a later call on the
+    same handle does not hang (the barrier counters were returned to zero)."""
+    w = workloads.STARVED_DECODE
+    weights = workloads.make_weights(w, device="cuda")
+    x, logits = workloads.make_activations(w, device="cuda")
+    ref = make_layer(w, weights)
+    ref.set_gemm_kernel("fused")
+    _, y_ref = run_layer(ref, x, logits)
+    assert not torch.isnan(y_ref.float()).any()
+    monkeypatch.setenv("AFD_FUSED_SPIN_LIMIT", "0")
+    bad = make_layer(w, weights)
+    monkeypatch.delenv("AFD_FUSED_SPIN_LIMIT")
+    bad.set_gemm_kernel("fused")
+    for call in range(2):
+        _, y = run_layer(bad, x, logits)
+        nan = torch.isnan(y.float())
+        say(f"call {call}: {int(nan.sum())} of {nan.numel()} outputs NaN")
+        assert nan.any()
+        assert torch.equal(y[~nan], y_ref[~nan])
+    bad.close()
+    ref.close()
+
+
 def test_fused_decode_on_a_capacity_route():
     """Empty slots of a capacity route carry gate 0: the fused launch computes no row for
     them and the combine skips them."""
