@@ -109,24 +109,31 @@ struct StreamOps {
   const i32x4* B;
   int KB;
 };
-__device__ __forceinline__ StreamOps stream_ops(const GroupedGemm& g, const Item& it, int lane) {
-  const int K = it.shared ? g.K_shared : g.K_routed;
-  const int r = lane & 15;
-  const int rr = r < it.nrows ? r : 0;
-  int arow;
-  if (it.shared)
-    arow = it.row0 + rr;
-  else
-    arow = g.gather_routed ? g.sorted_pair[it.row0 + rr] / g.k : it.row0 + rr;
+// The lane's A operand stream when its tile row is activation row `arow`.
+__device__ __forceinline__ const bf16x8* stream_a(const GroupedGemm& g, const Item& it, int lane, int arow) {
   const int lda = it.shared ? g.lda_shared : g.lda_routed;
+  return reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(it.shared ? g.a_shared : g.a_routed) +
+                                         (size_t)arow * lda) +
+         (lane >> 4);
+}
+// Operands with A read from row `row` of the segment's rows (tiles that are not
+// gathered), and the weights.
+__device__ __forceinline__ StreamOps stream_ops_rows(const GroupedGemm& g, const Item& it, int lane, int row) {
+  const int K = it.shared ? g.K_shared : g.K_routed;
   StreamOps o;
-  o.A = reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(it.shared ? g.a_shared : g.a_routed) +
-                                        (size_t)arow * lda) +
-        (lane >> 4);
+  o.A = stream_a(g, it, lane, row);
   const __bf16* wbase = it.shared ? static_cast<const __bf16*>(g.w_shared)
                                   : static_cast<const __bf16*>(g.w_routed) + (size_t)it.seg * g.w_expert_elems;
   o.KB = K / 32;
   o.B = reinterpret_cast<const i32x4*>(wbase) + (size_t)it.group * o.KB * 128 + lane;
+  return o;
+}
+
+__device__ __forceinline__ StreamOps stream_ops(const GroupedGemm& g, const Item& it, int lane) {
+  const int r = lane & 15;
+  const int row = it.row0 + (r < it.nrows ? r : 0);
+  StreamOps o = stream_ops_rows(g, it, lane, row);
+  if (!it.shared && g.gather_routed) o.A = stream_a(g, it, lane, g.sorted_pair[row] / g.k);
   return o;
 }
 
@@ -157,21 +164,35 @@ __device__ __forceinline__ void stream_store(const GroupedGemm& g, const Item& i
 
 template <bool SWIGLU>
 __global__ void __launch_bounds__(kGemmThreads) gemm_bf16_stream_kernel(GroupedGemm g) {
-  __shared__ int prefix[kMaxSegments + 1];
+  __shared__ SegTable tab;
   __shared__ int scan_tmp[kGemmWaves + 1];
-  const int total = build_item_prefix(g, kTileRows, prefix, scan_tmp);
+  const int total = build_item_prefix(g, kTileRows, tab, scan_tmp);
   const int lane = lane_id();
   const int waves_in_launch = gridDim.x * kGemmWaves;
   const int wave = blockIdx.x * kGemmWaves + threadIdx.x / kWave;
 
   for (int item = wave; item < total; item += waves_in_launch) {
-    const Item it = decode_item(g, kTileRows, prefix, item);
-    const StreamOps o = stream_ops(g, it, lane);
+    const Item it = decode_item(g, kTileRows, tab, item);
+    // The weight stream starts before the lane's activation row is known: its
+    // sorted_pair entry is loaded first (an in-bounds entry is read for every tile, used
+    // only when the tile's rows are gathered), then the first weight steps, so that the
+    // wait for the entry does not include the weights.
+    const int r = lane & 15;
+    const int row = it.row0 + (r < it.nrows ? r : 0);
+    const int pair = g.sorted_pair[row];
+    const StreamOps o = stream_ops_rows(g, it, lane, row);
     f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-    if (o.KB % 8 == 0)
-      stream_mfma<8>(o.A, o.B, o.KB, acc0, acc1);
-    else
-      stream_mfma<4>(o.A, o.B, o.KB, acc0, acc1);
+    bf16x8 b0[8], b1[8];
+    const bool gather = !it.shared && g.gather_routed;
+    if (o.KB % 8 == 0) {
+      prime_weights<8>(o.B, b0, b1);
+      __builtin_amdgcn_sched_barrier(0);  // the weight loads issue before the use of `pair`
+      stream_mfma_primed<8>(gather ? stream_a(g, it, lane, pair / g.k) : o.A, o.B, o.KB, acc0, acc1, b0, b1);
+    } else {
+      prime_weights<4>(o.B, b0, b1);
+      __builtin_amdgcn_sched_barrier(0);  // the weight loads issue before the use of `pair`
+      stream_mfma_primed<4>(gather ? stream_a(g, it, lane, pair / g.k) : o.A, o.B, o.KB, acc0, acc1, b0, b1);
+    }
     stream_store<SWIGLU>(g, it, lane, acc0, acc1, nullptr);
   }
 }
@@ -204,8 +225,8 @@ __global__ void __launch_bounds__(kGemmThreads) gemm_bf16_stream_kernel(GroupedG
 __global__ void __launch_bounds__(kGemmThreads) gemm_bf16_fused_kernel(GroupedGemm g1, GroupedGemm g2,
                                                                        const float* gates, unsigned* sync,
                                                                        int* status, unsigned spin_limit) {
-  __shared__ int prefix1[kMaxSegments + 1];
-  __shared__ int prefix2[kMaxSegments + 1];
+  __shared__ SegTable prefix1;
+  __shared__ SegTable prefix2;
   __shared__ int scan_tmp[kGemmWaves + 1];
   __shared__ int passed;
   const int total1 = build_item_prefix(g1, kTileRows, prefix1, scan_tmp);

@@ -115,7 +115,7 @@ struct TiledCtx {
 };
 
 template <bool SWIGLU>
-__device__ __forceinline__ void tiled_ctx(const GroupedGemm& g, const int* prefix, int item, int w, int lane,
+__device__ __forceinline__ void tiled_ctx(const GroupedGemm& g, const SegTable& prefix, int item, int w, int lane,
                                           TiledCtx& x) {
   const Item it = decode_item_tiled(g, kTiledRows, kTiledGroups, prefix, item);
   x.seg = uni(it.seg);
@@ -172,7 +172,7 @@ __device__ __forceinline__ void tiled_ctx(const GroupedGemm& g, const int* prefi
 // sorted_pair entries) are computed at the start of the current one.
 template <bool SWIGLU>
 __global__ void __launch_bounds__(kTiledThreads, kTiledMinBlocks) gemm_bf16_tiled_kernel(GroupedGemm g) {
-  __shared__ int prefix[kMaxSegments + 1];
+  __shared__ SegTable prefix;
   __shared__ int scan_tmp[kTiledWaves + 1];
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
 

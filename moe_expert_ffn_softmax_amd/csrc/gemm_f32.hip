@@ -19,7 +19,7 @@ constexpr int kF32Ahead = 2;  // 4-step groups of the reduction in flight per la
 
 template <bool SWIGLU>
 __global__ void __launch_bounds__(kF32Threads) gemm_f32_kernel(GroupedGemm g) {
-  __shared__ int prefix[kMaxSegments + 1];
+  __shared__ SegTable prefix;
   __shared__ int scan_tmp[kF32Waves + 1];
   const int total = build_item_prefix(g, kTileRows, prefix, scan_tmp);
   const int lane = lane_id();

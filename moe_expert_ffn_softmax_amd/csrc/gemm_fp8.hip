@@ -58,47 +58,93 @@ __device__ __forceinline__ int block_col(bool gate_up, int N, int j, int half) {
 // D blocks in flight holds the operands and the block's scales (two weight scales,
 // the activation scales of the lane's four rows), so a block waits on no load issued
 // in its own iteration; no branch inside (KB % D == 0, KB >= D), so the compiler
-// waits only for the oldest loads.
+// waits only for the oldest loads.  The weight half of the first D blocks is loaded
+// first (fp8_prime_weights), before the activation rows are known.
 template <int D>
-__device__ __forceinline__ void stream_fp8(const uint8_t* __restrict__ A, const uint8_t* __restrict__ B,
-                                           const float* __restrict__ ws, int NB, int nb0, int nb1,
-                                           const float* const (&as_row)[4], int KB, f32x4& acc0, f32x4& acc1) {
+struct Fp8Ring {
   i32x8 a[D], b0[D], b1[D];
   float w0r[D], w1r[D], sar[D][4];
-  auto fetch = [&](const int u, const int kb) {
-    a[u] = load32(A + kb * 128);
-    b0[u] = load_frag_nt(B + (kb * 2) * 2048);
-    b1[u] = load_frag_nt(B + (kb * 2 + 1) * 2048);
-    w0r[u] = ws[(size_t)kb * NB + nb0];
-    w1r[u] = ws[(size_t)kb * NB + nb1];
+};
+
+template <int D>
+__device__ __forceinline__ void fp8_fetch_w(Fp8Ring<D>& r, const uint8_t* __restrict__ B,
+                                            const float* __restrict__ ws, int NB, int nb0, int nb1, int u, int kb) {
+  r.b0[u] = load_frag_nt(B + (kb * 2) * 2048);
+  r.b1[u] = load_frag_nt(B + (kb * 2 + 1) * 2048);
+  r.w0r[u] = ws[(size_t)kb * NB + nb0];
+  r.w1r[u] = ws[(size_t)kb * NB + nb1];
+}
+
+template <int D>
+__device__ __forceinline__ void fp8_fetch_a(Fp8Ring<D>& r, const uint8_t* __restrict__ A,
+                                            const float* const (&as_row)[4], int u, int kb) {
+  r.a[u] = load32(A + kb * 128);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sar[u][i] = as_row[i][kb];
-  };
+  for (int i = 0; i < 4; ++i) r.sar[u][i] = as_row[i][kb];
+}
+
+template <int D>
+__device__ __forceinline__ void fp8_prime_weights(Fp8Ring<D>& r, const uint8_t* __restrict__ B,
+                                                  const float* __restrict__ ws, int NB, int nb0, int nb1) {
+#pragma unroll
+  for (int u = 0; u < D; ++u) fp8_fetch_w(r, B, ws, NB, nb0, nb1, u, u);
+}
+
+template <int D>
+__device__ __forceinline__ void stream_fp8_primed(Fp8Ring<D>& r, const uint8_t* __restrict__ A,
+                                                  const uint8_t* __restrict__ B, const float* __restrict__ ws,
+                                                  int NB, int nb0, int nb1, const float* const (&as_row)[4], int KB,
+                                                  f32x4& acc0, f32x4& acc1) {
   auto compute = [&](const int u) {
-    const f32x4 p0 = mfma_fp8_block(a[u], b0[u]);
-    const f32x4 p1 = mfma_fp8_block(a[u], b1[u]);
+    const f32x4 p0 = mfma_fp8_block(r.a[u], r.b0[u]);
+    const f32x4 p1 = mfma_fp8_block(r.a[u], r.b1[u]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      acc0[i] = fmaf(p0[i], sar[u][i] * w0r[u], acc0[i]);
-      acc1[i] = fmaf(p1[i], sar[u][i] * w1r[u], acc1[i]);
+      acc0[i] = fmaf(p0[i], r.sar[u][i] * r.w0r[u], acc0[i]);
+      acc1[i] = fmaf(p1[i], r.sar[u][i] * r.w1r[u], acc1[i]);
     }
   };
 #pragma unroll
-  for (int u = 0; u < D; ++u) fetch(u, u);
+  for (int u = 0; u < D; ++u) fp8_fetch_a(r, A, as_row, u, u);
   for (int kb0 = D; kb0 < KB; kb0 += D) {
 #pragma unroll
     for (int u = 0; u < D; ++u) {
       compute(u);
-      fetch(u, kb0 + u);
+      fp8_fetch_a(r, A, as_row, u, kb0 + u);
+      fp8_fetch_w(r, B, ws, NB, nb0, nb1, u, kb0 + u);
     }
   }
 #pragma unroll
   for (int u = 0; u < D; ++u) compute(u);
 }
 
+// One item's reduction: the weight half of the ring's first blocks, then the activation
+// rows (rows[], or the rows behind pairs[] when the tile is gathered), then the stream.
+template <int D>
+__device__ __forceinline__ void fp8_stream_item(const GroupedGemm& g, const Item& it, int lane, int (&rows)[5],
+                                                const int (&pairs)[5], const uint8_t* __restrict__ B,
+                                                const float* __restrict__ ws, int NB, int nb0, int nb1, int KB,
+                                                f32x4& acc0, f32x4& acc1) {
+  Fp8Ring<D> ring;
+  fp8_prime_weights<D>(ring, B, ws, NB, nb0, nb1);
+  __builtin_amdgcn_sched_barrier(0);  // the weight loads issue before the entries are used
+  if (!it.shared && g.gather_routed) {
+#pragma unroll
+    for (int i = 0; i < 5; ++i) rows[i] = pairs[i] / g.k;
+  }
+  const int lda = it.shared ? g.lda_shared : g.lda_routed;
+  const uint8_t* A = static_cast<const uint8_t*>(it.shared ? g.a_shared : g.a_routed) + (size_t)rows[0] * lda +
+                     (lane >> 4) * 32;
+  const float* as_base = it.shared ? g.as_shared : g.as_routed;
+  const float* as_row[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) as_row[i] = as_base + (size_t)rows[1 + i] * KB;
+  stream_fp8_primed<D>(ring, A, B, ws, NB, nb0, nb1, as_row, KB, acc0, acc1);
+}
+
 template <bool SWIGLU>
 __global__ void __launch_bounds__(kFp8Threads) gemm_fp8_stream_kernel(GroupedGemm g) {
-  __shared__ int prefix[kMaxSegments + 1];
+  __shared__ SegTable prefix;
   __shared__ int scan_tmp[kFp8Waves + 1];
   const int total = build_item_prefix(g, kTileRows, prefix, scan_tmp);
   const int lane = lane_id();
@@ -112,44 +158,34 @@ __global__ void __launch_bounds__(kFp8Threads) gemm_fp8_stream_kernel(GroupedGem
     const int groups = it.shared ? g.groups_shared : g.groups_routed;
     const int N = groups * 32;
     const int NB = N / 128;  // weight scale blocks per reduction block
-    // A row of this lane (rows past the tile end repeat its first row)
+    // Rows of this lane: its A row (tile row lane % 16) and the 4 output rows whose
+    // activation scales it applies (rows past the tile end repeat its first row).
+    // Their sorted_pair entries are loaded first (in-bounds entries are read for every
+    // tile, used only when the tile's rows are gathered), then the weight half of the
+    // first ring blocks, so that the wait for the entries does not include the weights.
     const int r = lane & 15;
-    const int rr = r < it.nrows ? r : 0;
-    int arow;
-    if (it.shared)
-      arow = it.row0 + rr;
-    else
-      arow = g.gather_routed ? g.sorted_pair[it.row0 + rr] / g.k : it.row0 + rr;
-    const int lda = it.shared ? g.lda_shared : g.lda_routed;
-    const uint8_t* A = static_cast<const uint8_t*>(it.shared ? g.a_shared : g.a_routed) + (size_t)arow * lda +
-                       (lane >> 4) * 32;
-    // activation scales of the 4 output rows this lane accumulates
-    const float* as_base = it.shared ? g.as_shared : g.as_routed;
-    const float* as_row[4];
+    int rows[5];
+    rows[0] = it.row0 + (r < it.nrows ? r : 0);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int orow = (lane >> 4) * 4 + i;
-      const int orr = orow < it.nrows ? orow : 0;
-      int srow;
-      if (it.shared)
-        srow = it.row0 + orr;
-      else
-        srow = g.gather_routed ? g.sorted_pair[it.row0 + orr] / g.k : it.row0 + orr;
-      as_row[i] = as_base + (size_t)srow * KB;
+      rows[1 + i] = it.row0 + (orow < it.nrows ? orow : 0);
     }
+    int pairs[5];
+#pragma unroll
+    for (int i = 0; i < 5; ++i) pairs[i] = g.sorted_pair[rows[i]];
     const uint8_t* wbase = it.shared ? static_cast<const uint8_t*>(g.w_shared)
                                      : static_cast<const uint8_t*>(g.w_routed) + (size_t)it.seg * g.w_expert_elems;
     const uint8_t* B = wbase + (size_t)it.group * KB * 4096 + lane * 16;  // [kb][half][2][lane][16 B]
     const float* ws = it.shared ? g.s_shared : g.s_routed + (size_t)it.seg * g.s_expert_elems;
     const int nb0 = block_col(SWIGLU, N, it.group, 0) / 128, nb1 = block_col(SWIGLU, N, it.group, 1) / 128;
-
     f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
     if (KB % 4 == 0)
-      stream_fp8<4>(A, B, ws, NB, nb0, nb1, as_row, KB, acc0, acc1);
+      fp8_stream_item<4>(g, it, lane, rows, pairs, B, ws, NB, nb0, nb1, KB, acc0, acc1);
     else if (KB % 2 == 0)
-      stream_fp8<2>(A, B, ws, NB, nb0, nb1, as_row, KB, acc0, acc1);
+      fp8_stream_item<2>(g, it, lane, rows, pairs, B, ws, NB, nb0, nb1, KB, acc0, acc1);
     else
-      stream_fp8<1>(A, B, ws, NB, nb0, nb1, as_row, KB, acc0, acc1);
+      fp8_stream_item<1>(g, it, lane, rows, pairs, B, ws, NB, nb0, nb1, KB, acc0, acc1);
 
     const int col = lane & 15;
     const int rbase = (lane >> 4) * 4;

@@ -436,7 +436,7 @@ __device__ __forceinline__ void fp8_tile(const GroupedGemm& g, const Item& it, c
 
 template <bool SWIGLU>
 __global__ void __launch_bounds__(kF8Threads, kF8MinBlocks) gemm_fp8_tiled_kernel(GroupedGemm g) {
-  __shared__ int prefix[kMaxSegments + 1];
+  __shared__ SegTable prefix;
   __shared__ int scan_tmp[kF8Waves + 1];
   __shared__ float qamax[kF8Waves][kF8Rows];  // per-wave token amax of the quantising epilogue
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
