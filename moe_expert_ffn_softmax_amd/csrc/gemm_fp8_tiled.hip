@@ -49,7 +49,7 @@
 // For the gate/up projection the epilogue can write h already quantised (e4m3 codes
 // and per-token per-128 scales; see below) instead of fp32 h.
 //
-// Items and XCD ranges as in the bf16 tiled kernel.
+// Items as in the bf16 tiled kernel; the XCD ranges carry equal costs (f8_xcd_range).
 #include "grouped.h"
 
 namespace afd {
@@ -434,6 +434,70 @@ __device__ __forceinline__ void fp8_tile(const GroupedGemm& g, const Item& it, c
   }
 }
 
+// 16-row blocks an item of `nrows` rows is computed with (its block count, rounded up
+// to 4 for 3 blocks and to 2 below that: fewer specialisations of the item body).
+__device__ __forceinline__ int f8_item_blocks(int nrows) {
+  const int nb = (nrows + 15) / 16;
+  return nb >= 5 ? nb : (nb >= 3 ? 4 : 2);
+}
+
+// Cost of an item in units of one 16-row block's matrix-core and rescale work: that
+// work is proportional to the item's block count, while its weight stream is the same
+// for every item.  Measured at the DeepSeek-V3-like layer (ablations of the kernel:
+// with and without its loads) the stream weighs about as much as 3 blocks.
+constexpr int kF8ItemFixedCost = 3;
+
+// This XCD's range [begin, end) of the launch's items, the 8 ranges carrying equal
+// costs rather than equal item counts.  Items differ in cost by their block count, and
+// segments are ordered (the shared expert, whose tiles are all full, comes last), so
+// equal counts left the last XCD ~10% more work than the mean at that layer.  Within
+// a segment all items cost about the same (row counts differ by at most one), so a
+// boundary inside a segment is placed by the segment's mean item cost.  costp needs
+// kMaxSegments + 1 ints of LDS.  Contains __syncthreads().
+__device__ __forceinline__ void f8_xcd_range(const GroupedGemm& g, const SegTable& t, int* costp, int* scan_tmp,
+                                             int xcd, int& begin, int& end) {
+  const int S = g.E + (g.shared_rows > 0 ? 1 : 0);
+  int carry = 0;
+  for (int s0 = 0; s0 < S; s0 += blockDim.x) {
+    const int s = s0 + threadIdx.x;
+    int c = 0;
+    if (s < S && t.rows[s] > 0) {
+      const int rows = t.rows[s];
+      const int rt = (rows + kF8Rows - 1) / kF8Rows;
+      const int base = rows / rt, extra = rows - base * rt;  // the row split of decode_item_tiled
+      const int groups = s >= g.E ? g.groups_shared : g.groups_routed;
+      const int nct = (groups + kF8Groups - 1) / kF8Groups;
+      c = nct * (extra * (f8_item_blocks(base + 1) + kF8ItemFixedCost) +
+                 (rt - extra) * (f8_item_blocks(base) + kF8ItemFixedCost));
+    }
+    int tot = 0;
+    const int ex = block_exclusive_scan(c, scan_tmp, &tot);
+    if (s < S) costp[s] = carry + ex;
+    carry += tot;
+  }
+  if (threadIdx.x == 0) costp[S] = carry;
+  __syncthreads();
+  const long long total_cost = carry;
+  // first item whose cost prefix reaches C (by the segment's mean item cost)
+  auto item_at = [&](long long C) {
+    int lo = 0, hi = S;  // largest lo < S with costp[lo] <= C
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (costp[mid] <= C)
+        lo = mid;
+      else
+        hi = mid;
+    }
+    const int items = t.prefix[lo + 1] - t.prefix[lo];
+    const long long cs = costp[lo + 1] - costp[lo];
+    long long local = cs > 0 ? (C - costp[lo]) * items / cs : 0;
+    local = local < items ? local : items;
+    return t.prefix[lo] + (int)local;
+  };
+  begin = xcd == 0 ? 0 : item_at(total_cost * xcd / kF8Xcds);
+  end = xcd == kF8Xcds - 1 ? t.prefix[S] : item_at(total_cost * (xcd + 1) / kF8Xcds);
+}
+
 template <bool SWIGLU>
 __global__ void __launch_bounds__(kF8Threads, kF8MinBlocks) gemm_fp8_tiled_kernel(GroupedGemm g) {
   __shared__ SegTable prefix;
@@ -441,7 +505,8 @@ __global__ void __launch_bounds__(kF8Threads, kF8MinBlocks) gemm_fp8_tiled_kerne
   __shared__ float qamax[kF8Waves][kF8Rows];  // per-wave token amax of the quantising epilogue
   extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
 
-  const int total = build_item_prefix(g, kF8Rows, kF8Groups, prefix, scan_tmp);
+  __shared__ int costp[kMaxSegments + 1];
+  build_item_prefix(g, kF8Rows, kF8Groups, prefix, scan_tmp);
   // wave index, made visibly uniform so that per-wave values (group, scale indices,
   // weight bases) live in scalar registers and use scalar loads
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -449,14 +514,14 @@ __global__ void __launch_bounds__(kF8Threads, kF8MinBlocks) gemm_fp8_tiled_kerne
   const int xcd = blockIdx.x % kF8Xcds;
   const int slot = blockIdx.x / kF8Xcds;
   const int slots = gridDim.x / kF8Xcds;
-  const int begin = (int)((long long)total * xcd / kF8Xcds);
-  const int end = (int)((long long)total * (xcd + 1) / kF8Xcds);
+  int begin, end;
+  f8_xcd_range(g, prefix, costp, scan_tmp, xcd, begin, end);
 
   for (int item = begin + slot; item < end; item += slots) {
     const Item it = decode_item_tiled(g, kF8Rows, kF8Groups, prefix, item);
     // the item's computation is specialised on its count of 16-row blocks, so the
     // padding of a partly filled tile costs neither matrix-core nor rescaling work
-    const int nb = (it.nrows + 15) / 16;  // wave-uniform
+    const int nb = f8_item_blocks(it.nrows);  // wave-uniform
     if (nb == 8)
       fp8_tile<SWIGLU, 8>(g, it, w, lds, qamax);
     else if (nb == 7)
@@ -465,7 +530,7 @@ __global__ void __launch_bounds__(kF8Threads, kF8MinBlocks) gemm_fp8_tiled_kerne
       fp8_tile<SWIGLU, 6>(g, it, w, lds, qamax);
     else if (nb == 5)
       fp8_tile<SWIGLU, 5>(g, it, w, lds, qamax);
-    else if (nb >= 3)
+    else if (nb == 4)
       fp8_tile<SWIGLU, 4>(g, it, w, lds, qamax);
     else
       fp8_tile<SWIGLU, 2>(g, it, w, lds, qamax);
