@@ -55,10 +55,7 @@ constexpr int kTiledWaves = 4;
 constexpr int kTiledThreads = kTiledWaves * kWave;
 constexpr int kTiledRowBlocks = 4;                      // 32-row blocks per tile (one per staging wave)
 constexpr int kTiledRows = 32 * kTiledRowBlocks;        // 128
-#ifndef AFD_TILED_GPW
-#define AFD_TILED_GPW 2
-#endif
-constexpr int kTiledGroupsPerWave = AFD_TILED_GPW;      // 32-column groups per wave (2 or 4)
+constexpr int kTiledGroupsPerWave = 2;                 // 32-column groups per wave (2 or 4)
 constexpr int kTiledGroups = kTiledWaves * kTiledGroupsPerWave;  // per item
 static_assert(kTiledGroupsPerWave == 2 || kTiledGroupsPerWave == 4, "2 or 4 groups per wave");
 constexpr int kTiledKC = 4;                             // 32-deep steps per staged chunk (128 deep)
@@ -67,10 +64,7 @@ constexpr int kTiledSlot = 1056;                        // bytes per fragment sl
 constexpr int kTiledHalfOff = 528;                      // byte offset of reduction half 1 in a slot
 constexpr int kTiledBuf = kTiledRowBlocks * kTiledFrags * kTiledSlot;  // bytes per LDS buffer
 constexpr int kTiledLoads = 8;                          // staging loads per wave and chunk (4 rows each)
-#ifndef AFD_TILED_B_AHEAD
-#define AFD_TILED_B_AHEAD (8 / AFD_TILED_GPW)
-#endif
-constexpr int kTiledBAhead = AFD_TILED_B_AHEAD;         // 32-deep weight steps in flight per wave
+constexpr int kTiledBAhead = 8 / kTiledGroupsPerWave;   // 32-deep weight steps in flight per wave
 // a ring slot is the step's index within its chunk modulo the ring depth
 static_assert(kTiledKC % kTiledBAhead == 0, "the weight ring depth divides the steps of a chunk");
 constexpr int kXcds = 8;
@@ -85,14 +79,7 @@ struct IntC {
   static constexpr int value = N;
 };
 
-#ifndef AFD_TILED_SCHED
-#define AFD_TILED_SCHED 1
-#endif
-
-#ifndef AFD_TILED_MIN_BLOCKS
-#define AFD_TILED_MIN_BLOCKS 1
-#endif
-constexpr int kTiledMinBlocks = AFD_TILED_MIN_BLOCKS;  // workgroups per CU the registers must allow
+constexpr int kTiledMinBlocks = 1;  // workgroups per CU the registers must allow
 
 __device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
@@ -313,7 +300,6 @@ __global__ void __launch_bounds__(kTiledThreads, kTiledMinBlocks) gemm_bf16_tile
               for (int k2 = 0; k2 < 2; ++k2) bring[slotb][cb][k2] = tiled_load_b(bp + k2 * 32);
             }
           }
-#if AFD_TILED_SCHED
           // keep the next half-step's LDS reads spread between this half-step's MFMAs
           // (left alone, the scheduler sinks each read to just before its first use)
 #pragma unroll
@@ -321,7 +307,6 @@ __global__ void __launch_bounds__(kTiledThreads, kTiledMinBlocks) gemm_bf16_tile
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                    // one LDS read
             __builtin_amdgcn_sched_group_barrier(0x008, kTiledGroupsPerWave, 0);  // one row block's MFMAs
           }
-#endif
         }
       }
     };

@@ -73,36 +73,18 @@ constexpr int kF8Loads = kF8StageRows / 4;      // staging loads per thread per 
 // Each wave stages its rows' token scales of a chunk (2 blocks) in lanes 0-31 and the
 // chunk's weight scales in lanes 32-63 (written by wave 0 only): one load per lane.
 static_assert(2 * kF8StageRows + kF8WScales == kWave, "one scale per lane per chunk");
-#ifndef AFD_FP8_TILED_RING
-#define AFD_FP8_TILED_RING 2
-#endif
-#ifndef AFD_FP8_TILED_STAGE_SETS
-#define AFD_FP8_TILED_STAGE_SETS 1
-#endif
-constexpr int kF8BAhead = AFD_FP8_TILED_RING;   // scale blocks of weights in flight per wave (2 or 4)
-constexpr int kF8StageSets = AFD_FP8_TILED_STAGE_SETS;  // chunks of activations loading ahead (1 or 2)
-static_assert(kF8BAhead == 2 || kF8BAhead == 4, "weight ring of 2 or 4 blocks");
-static_assert(kF8StageSets == 1 || kF8StageSets == 2, "1 or 2 staging register sets");
-#ifndef AFD_FP8_TILED_LDS_AHEAD
-#define AFD_FP8_TILED_LDS_AHEAD 1
-#endif
-constexpr int kF8LdsAhead = AFD_FP8_TILED_LDS_AHEAD;  // token blocks of operands read from LDS ahead
+constexpr int kF8BAhead = 2;                    // scale blocks of weights in flight per wave
+constexpr int kF8StageSets = 1;                 // chunks of activations loading ahead
+constexpr int kF8LdsAhead = 1;                  // token blocks of operands read from LDS ahead
 // The chunk loop is unrolled by two when a ring slot (block % kF8BAhead) or a staging
 // set (chunk % kF8StageSets) would otherwise depend on the chunk's parity.
 constexpr int kF8Unroll = (kF8BAhead == 4 || kF8StageSets == 2) ? 2 : 1;
 constexpr int kF8Xcds = 8;
 
-#ifndef AFD_FP8_PLAIN_MFMA
-#define AFD_FP8_PLAIN_MFMA 1
-#endif
 __device__ __forceinline__ f32x4 f8_mfma(const i32x8& a, const i32x8& b) {
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-#if AFD_FP8_PLAIN_MFMA
   // scale operands 0: the compiler emits the unscaled v_mfma_f32_16x16x128_f8f6f4
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 0, 0, 0, 0, 0, 0);
-#else
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 0, 0, 0, 0x7f7f7f7f, 0, 0x7f7f7f7f);
-#endif
 }
 
 // A lane's 32 weight bytes of a packed fragment: 16 at p, 16 at p + 1 KiB.
@@ -112,10 +94,7 @@ __device__ __forceinline__ i32x8 f8_load32(const uint8_t* p) {
   return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-#ifndef AFD_FP8_TILED_MIN_BLOCKS
-#define AFD_FP8_TILED_MIN_BLOCKS 1
-#endif
-constexpr int kF8MinBlocks = AFD_FP8_TILED_MIN_BLOCKS;  // workgroups per CU the registers must allow
+constexpr int kF8MinBlocks = 1;  // workgroups per CU the registers must allow
 
 // SiLU with the hardware reciprocal (one rounding more than z / (1 + e^-z)); h is
 // quantised to e4m3 right after, whose step is 2^-3 of the value.
