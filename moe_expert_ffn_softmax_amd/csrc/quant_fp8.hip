@@ -18,61 +18,86 @@ constexpr int kQuantThreads = 256;
 // spans 128 / VPL lanes and a wave covers 64 * VPL channels of one row; the group
 // amax is a max over those lanes.  One launch covers up to two row segments (the
 // routed and the shared expert's h of the fp8 layer); a wave's rows all belong to one.
+// A wave's work item wj: the row segment, row and first channel of its lane.
+struct QuantWork {
+  const QuantSeg* sg;
+  int r, c0;
+  bool ok;  // the lane's channels are inside the row (cols is a multiple of 128, so a
+            // group is all in or all out)
+};
+
 template <bool BF16>
 __global__ void __launch_bounds__(kQuantThreads) quant_fp8_kernel(QuantSeg s0, QuantSeg s1) {
   constexpr int VPL = BF16 ? 8 : 4;       // values per lane
   constexpr int LPG = 128 / VPL;          // lanes per 128-channel group
   constexpr int CPW = kWave * VPL;        // channels per wave
+  constexpr int U = 2;                    // work items per wave per pass: their loads are in flight together
   const int lane = lane_id();
   const long long work0 = (long long)s0.rows * ((s0.cols + CPW - 1) / CPW);
   const long long work = work0 + (long long)s1.rows * ((s1.cols + CPW - 1) / CPW);
   const long long wave = (long long)blockIdx.x * (kQuantThreads / kWave) + threadIdx.x / kWave;
   const long long waves = (long long)gridDim.x * (kQuantThreads / kWave);
-  for (long long wj = wave; wj < work; wj += waves) {
+  auto locate = [&](long long wj) {
+    QuantWork q;
     const bool first = wj < work0;  // uniform over the wave
-    const QuantSeg& sg = first ? s0 : s1;
+    q.sg = first ? &s0 : &s1;
     const long long wi = first ? wj : wj - work0;
-    const int cols = sg.cols, ld = sg.ld;
-    const int groups = cols / 128;
-    const int chunks = (cols + CPW - 1) / CPW;
-    const int r = (int)(wi / chunks);
-    const int c0 = (int)(wi % chunks) * CPW + lane * VPL;
-    const bool ok = c0 < cols;  // cols is a multiple of 128, so a group is all in or all out
-    float v[VPL];
+    const int chunks = q.sg->cols > 0 ? (q.sg->cols + CPW - 1) / CPW : 1;  // past the work: any row
+    q.r = (int)(wi / chunks);
+    q.c0 = (int)(wi % chunks) * CPW + lane * VPL;
+    q.ok = wj < work && q.c0 < q.sg->cols;
+    return q;
+  };
+  for (long long wj = wave; wj < work; wj += U * waves) {
+    QuantWork q[U];
+    float v[U][VPL];
 #pragma unroll
-    for (int i = 0; i < VPL; ++i) v[i] = 0.f;
-    if (ok) {
-      if (BF16) {
-        const uint4 raw = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(sg.src) + (size_t)r * ld + c0);
-        const uint32_t wds[4] = {raw.x, raw.y, raw.z, raw.w};
+    for (int u = 0; u < U; ++u) {
+      q[u] = locate(wj + u * waves);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          v[2 * i] = bf16_bits_to_f32((uint16_t)(wds[i] & 0xffffu));
-          v[2 * i + 1] = bf16_bits_to_f32((uint16_t)(wds[i] >> 16));
+      for (int i = 0; i < VPL; ++i) v[u][i] = 0.f;
+      if (q[u].ok) {
+        const QuantSeg& sg = *q[u].sg;
+        if (BF16) {
+          const uint4 raw =
+              *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(sg.src) + (size_t)q[u].r * sg.ld + q[u].c0);
+          const uint32_t wds[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            v[u][2 * i] = bf16_bits_to_f32((uint16_t)(wds[i] & 0xffffu));
+            v[u][2 * i + 1] = bf16_bits_to_f32((uint16_t)(wds[i] >> 16));
+          }
+        } else {
+          const float4 f =
+              *reinterpret_cast<const float4*>(static_cast<const float*>(sg.src) + (size_t)q[u].r * sg.ld + q[u].c0);
+          v[u][0] = f.x;
+          v[u][1] = f.y;
+          v[u][2] = f.z;
+          v[u][3] = f.w;
         }
-      } else {
-        const float4 f = *reinterpret_cast<const float4*>(static_cast<const float*>(sg.src) + (size_t)r * ld + c0);
-        v[0] = f.x;
-        v[1] = f.y;
-        v[2] = f.z;
-        v[3] = f.w;
       }
     }
-    float amax = 0.f;
 #pragma unroll
-    for (int i = 0; i < VPL; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    for (int u = 0; u < U; ++u) {
+      const QuantSeg& sg = *q[u].sg;
+      float amax = 0.f;
 #pragma unroll
-    for (int off = LPG / 2; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, kWave));
-    const float s = amax > 0.f ? amax / 448.f : 1.f;
-    if (ok) {
-      uint32_t pk[VPL / 4];
+      for (int i = 0; i < VPL; ++i) amax = fmaxf(amax, fabsf(v[u][i]));
 #pragma unroll
-      for (int i = 0; i < VPL / 4; ++i) pk[i] = e4m3_pack4(v[4 * i] / s, v[4 * i + 1] / s, v[4 * i + 2] / s, v[4 * i + 3] / s);
-      if (BF16)
-        *reinterpret_cast<uint2*>(sg.q + (size_t)r * cols + c0) = make_uint2(pk[0], pk[VPL / 4 - 1]);
-      else
-        *reinterpret_cast<uint32_t*>(sg.q + (size_t)r * cols + c0) = pk[0];
-      if (lane % LPG == 0) sg.scales[(size_t)r * groups + c0 / 128] = s;
+      for (int off = LPG / 2; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, kWave));
+      const float s = amax > 0.f ? amax / 448.f : 1.f;
+      if (q[u].ok) {
+        const int cols = sg.cols;
+        uint32_t pk[VPL / 4];
+#pragma unroll
+        for (int i = 0; i < VPL / 4; ++i)
+          pk[i] = e4m3_pack4(v[u][4 * i] / s, v[u][4 * i + 1] / s, v[u][4 * i + 2] / s, v[u][4 * i + 3] / s);
+        if (BF16)
+          *reinterpret_cast<uint2*>(sg.q + (size_t)q[u].r * cols + q[u].c0) = make_uint2(pk[0], pk[VPL / 4 - 1]);
+        else
+          *reinterpret_cast<uint32_t*>(sg.q + (size_t)q[u].r * cols + q[u].c0) = pk[0];
+        if (lane % LPG == 0) sg.scales[(size_t)q[u].r * (cols / 128) + q[u].c0 / 128] = s;
+      }
     }
   }
 }
