@@ -403,7 +403,7 @@ def run_workload(w, steps, warmup, batches, gemm, torch):
 
 def sweep(args, torch):
     wls = (list(workloads.ORDERED) + list(workloads.CONTEXT) + workloads.mfma_sweep("bf16") +
-           workloads.mfma_sweep("fp8"))
+           workloads.mfma_sweep("fp8") + list(workloads.SHARES))
     for w in wls:
         if args.only and not any(o in w.name for o in args.only.split(",")):
             continue

@@ -50,7 +50,7 @@ def test_decode_layer_bytes_count_only_touched_experts():
 
 
 def test_flops_are_six_hm_per_pair_plus_shared():
-    for w in workloads.ORDERED + workloads.CONTEXT:
+    for w in workloads.ORDERED + workloads.CONTEXT + workloads.SHARES:
         assert w.flops() == 6 * w.T * w.k * w.H * w.M + 6 * w.T * w.H * w.Ms
 
 

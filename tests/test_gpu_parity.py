@@ -207,6 +207,19 @@ def test_fp8_blockscaled_every_tile():
     full_case(workloads.FP8_DSV3, sample=3, tiles=True)
 
 
+def test_tp4_share_of_the_decode_layer_full():
+    """One GPU's share of the starved-decode layer under 4-way tensor parallelism in the
+    experts (M = 384 of 1536), every token."""
+    full_case(workloads.TP4_SHARE)
+
+
+def test_ep8_share_of_the_fp8_layer_every_tile():
+    """One GPU's share of the DeepSeek-V3-like fp8 layer under 8-way expert parallelism
+    (32 local experts, 4096 received rows, each to one local expert), on the tokens at
+    both ends of every row tile."""
+    full_case(workloads.EP8_SHARE, sample=3, tiles=True)
+
+
 @pytest.mark.parametrize("w", [workloads.mfma_sweep("bf16")[0], workloads.mfma_sweep("bf16")[-1],
                                workloads.mfma_sweep("fp8")[-1]], ids=lambda w: w.name)
 def test_mfma_sweep_every_tile(w):

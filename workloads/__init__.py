@@ -123,6 +123,27 @@ FP8_DECODE = _add(Workload(
     note="DeepSeek-V3-like fp8 layer at a decode batch of 6: weight streaming"))
 CONTEXT = [FP8_DECODE]
 
+# One GPU's share of a layer sharded over 8 GPUs of a node (measured here on one GPU,
+# at its real shape):
+#  * expert parallelism over 8 GPUs for the DeepSeek-V3-like fp8 layer: a GPU owns 32
+#    of the 256 experts and, after the dispatch exchange, runs the grouped GEMMs on
+#    the ~T*k/8 = 4096 token rows routed to them, each row to one local expert
+#    (top-1 over the local experts; the weighted sum over a token's k rows happens on
+#    the token's owner after the return exchange).  The local routing is uniform.
+#  * tensor parallelism over 4 GPUs inside the experts of the starved-decode layer: a
+#    GPU holds M/4 = 384 of the 1536 intermediate columns of every expert and runs the
+#    whole routing (the same logits as the full layer: same seed stream) on the same 6
+#    tokens; a reduce-scatter of y ends the layer.  (Over 8 GPUs the share would be
+#    M = 192, which the kernels' 128-column blocking does not divide.)
+EP8_SHARE = _add(Workload(
+    "fp8_ep8_share_T4096_H7168_M2048_E32_k1", 6, T=4096, H=7168, M=2048, E=32, k=1, Ms=0, dtype="fp8",
+    note="one GPU's share of the DeepSeek-V3-like fp8 layer under 8-way expert parallelism"))
+TP4_SHARE = _add(Workload(
+    "starved_decode_tp4_share_bf16_T6_H4096_M384_E128_k8", 1, T=6, H=4096, M=384, E=128, k=8, Ms=0,
+    dtype="bf16", bias="normal", bias_param=0.5,
+    note="one GPU's share of the starved-decode layer under 4-way tensor parallelism in the experts"))
+SHARES = [EP8_SHARE, TP4_SHARE]
+
 
 def mfma_sweep(dtype: str = "bf16"):
     """Token-count sweep at 256/512/1024 routed tokens per expert (the regime where the
