@@ -272,9 +272,8 @@ int afd_ffn_quantize_fp8(const void* src, int32_t rows, int32_t cols, int32_t sr
  * outputs (a loud failure, no hang); nothing else may occupy the device meanwhile.
  * The environment variable AFD_FUSED_SPIN_LIMIT, read when a handle is created,
  * lowers the number of polls before giving up (0 up to 262144; for failure-injection
- * tests).  fp32 layers always
- * use their own kernel.  Takes effect for later forward calls.  Other values:
- * AFD_EINVAL. */
+ * tests).  fp32 layers always use their own kernel.  Takes effect for later forward
+ * calls.  Other values: AFD_EINVAL. */
 typedef enum afd_gemm_kernel {
   AFD_GEMM_AUTO = 0,
   AFD_GEMM_STREAM = 1,
