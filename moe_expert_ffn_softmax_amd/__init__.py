@@ -8,14 +8,12 @@ PyTorch fallback: if libafd_ffn.so is missing, constructing a layer raises.
 """
 from __future__ import annotations
 
-from ._ffi import (AFD_BF16, AFD_F32, AFD_FP8_E4M3, AFD_GEMM_AUTO, AFD_GEMM_STREAM,  # noqa: F401
-                   AFD_GEMM_TILED, AFD_GEMM_FUSED, STAGES, AfdError, afd_ffn_config, afd_ffn_create, afd_ffn_destroy,
-                   afd_ffn_device_bytes, afd_ffn_forward, afd_ffn_forward_fp8_input, afd_ffn_forward_noalloc,
-                   afd_ffn_last_error,
-                   afd_ffn_profile_read, afd_ffn_quantize_fp8, afd_ffn_route, afd_ffn_route_capacity,
-                   afd_ffn_route_from_capacity,
-                   afd_ffn_route_hidden,
-                   afd_ffn_route_bytes, afd_ffn_route_select_bias, afd_ffn_set_gemm_kernel, afd_ffn_set_profiling,
+from ._ffi import (AFD_BF16, AFD_F32, AFD_FP8_E4M3, AFD_GEMM_AUTO, AFD_GEMM_FUSED,  # noqa: F401
+                   AFD_GEMM_STREAM, AFD_GEMM_TILED, STAGES, AfdError, afd_ffn_config, afd_ffn_create,
+                   afd_ffn_destroy, afd_ffn_device_bytes, afd_ffn_forward, afd_ffn_forward_fp8_input,
+                   afd_ffn_forward_noalloc, afd_ffn_last_error, afd_ffn_profile_read, afd_ffn_quantize_fp8,
+                   afd_ffn_route, afd_ffn_route_bytes, afd_ffn_route_capacity, afd_ffn_route_from_capacity,
+                   afd_ffn_route_hidden, afd_ffn_route_select_bias, afd_ffn_set_gemm_kernel, afd_ffn_set_profiling,
                    afd_ffn_strerror, afd_route, load)
 
 GEMM_KERNELS = {"auto": AFD_GEMM_AUTO, "stream": AFD_GEMM_STREAM, "tiled": AFD_GEMM_TILED, "fused": AFD_GEMM_FUSED}
