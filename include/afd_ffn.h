@@ -103,7 +103,10 @@ typedef struct afd_route {
 
 typedef struct afd_ffn* afd_ffn_t;
 
-/* Create a layer.  w_gate_up [E, H, 2M] (columns [0, M) gate, [M, 2M) up) and
+/* Create a layer: the routed experts (and the optional shared expert) of one MoE
+ * layer as an FFN instance holds them ("大模型推理的内存与计算解耦：AFD 架构解析与性能
+ * 验证", §3; expert shapes of the omica.com.cn AFD article, §2.1).
+ * w_gate_up [E, H, 2M] (columns [0, M) gate, [M, 2M) up) and
  * w_down [E, M, H] in the config's dtype.  For AFD_FP8_E4M3, s_gate_up
  * [E, H/128, 2M/128] and s_down [E, M/128, H/128] are the fp32 block scales
  * (weight = code * scale); they must be NULL otherwise.  With shared_inter > 0,
@@ -116,8 +119,10 @@ int afd_ffn_create(const afd_ffn_config* cfg, const void* w_gate_up, const void*
                    const void* ws_down, const float* ss_gate_up, const float* ss_down, void* stream,
                    afd_ffn_t* out);
 
-/* Route T tokens: fp32 logits [T, E] -> every field of *r (see afd_route).
- * 0 <= T <= max_tokens. */
+/* Route T tokens: fp32 logits [T, E] -> every field of *r (see afd_route): the
+ * top-k softmax router of "MoE 大规模分布式推理工程实战：从 All-to-All 通信到动态专家
+ * 放置" (§4.1) and the count / prefix-offset / pack steps of its §2.2 (the "route"
+ * of the operation above).  0 <= T <= max_tokens. */
 int afd_ffn_route(afd_ffn_t h, const float* logits, int32_t T, const afd_route* r, void* stream);
 
 /* Route T tokens with a bias that steers only the choice of experts: the dynamic
@@ -194,9 +199,12 @@ int afd_ffn_route_capacity(afd_ffn_t h, const int32_t* ids, const float* gates, 
 int afd_ffn_route_from_capacity(afd_ffn_t h, const int32_t* assign, const float* weight, const int32_t* offsets,
                                 const int32_t* sorted_token, int32_t T, const afd_route* r, void* stream);
 
-/* Expert FFN of T routed tokens: x [T, H] (fp32 for AFD_F32, else bf16) and the
- * result of afd_ffn_route for the same T -> y [T, H] (fp32 for AFD_F32, else bf16).
- * x and y must not overlap (checked: AFD_EINVAL). */
+/* Expert FFN of T routed tokens (the "forward" of the operation above: the FFN
+ * service's expert computation of "大模型推理的内存与计算解耦：AFD 架构解析与性能验证",
+ * §3, SwiGLU experts and gate-weighted combine; fp8 layers quantise x and h as the
+ * omica.com.cn AFD article's §3.3 describes): x [T, H] (fp32 for AFD_F32, else bf16)
+ * and the result of afd_ffn_route for the same T -> y [T, H] (fp32 for AFD_F32,
+ * else bf16).  x and y must not overlap (checked: AFD_EINVAL). */
 int afd_ffn_forward(afd_ffn_t h, const void* x, int32_t T, const afd_route* r, void* y, void* stream);
 
 /* Expert FFN of an AFD_FP8_E4M3 layer on activations that arrive already quantised
@@ -226,8 +234,9 @@ int afd_ffn_forward_fp8_input(afd_ffn_t h, const uint8_t* xq, const float* xs, i
  * afd_ffn_forward. */
 int afd_ffn_forward_noalloc(afd_ffn_t h, const void* x, int32_t T, const afd_route* r, void* y, void* stream);
 
-/* Release the handle's weights and workspace.  The caller must have synchronised
- * every stream with work of this handle.  NULL is a no-op. */
+/* Release the handle's weights and workspace (the handle's life cycle; no page
+ * defines it).  The caller must have synchronised every stream with work of this
+ * handle.  NULL is a no-op. */
 int afd_ffn_destroy(afd_ffn_t h);
 
 /* Static description of an error code. */
@@ -282,7 +291,9 @@ typedef enum afd_gemm_kernel {
 } afd_gemm_kernel;
 int afd_ffn_set_gemm_kernel(afd_ffn_t h, int kernel);
 
-/* Per-kernel timing.  With profiling on, route and forward bracket each kernel
+/* Per-kernel timing, for the per-stage measurement the omica.com.cn AFD article's
+ * §4.1 asks for (achieved against expected work per kernel).  With profiling on,
+ * route and forward bracket each kernel
  * with HIP events on the launch stream.  afd_ffn_profile_read synchronises on the
  * recorded events, writes the summed milliseconds and launch counts of each stage
  * (index = afd_stage) into ms[n_stages] and launches[n_stages], and clears them.
