@@ -545,6 +545,8 @@ hipError_t configure_gemm_fp8_tiled() {
 hipError_t launch_gemm_fp8_tiled(const GroupedGemm& g, bool swiglu, long long max_items, int max_blocks,
                                  hipStream_t st) {
   if (max_items <= 0) return hipSuccess;
+  // item costs (at most 8 + kF8ItemFixedCost each) are summed in 32-bit ints
+  if (max_items > 0x7fffffff / (kF8RowBlocks + kF8ItemFixedCost)) return hipErrorInvalidValue;
   if (g.K_routed % 128 || g.groups_routed % 4 || g.ldo_routed % 4 ||
       (g.shared_rows > 0 && (g.K_shared % 128 || g.groups_shared % 4 || g.ldo_shared % 4)))
     return hipErrorInvalidValue;
