@@ -618,6 +618,8 @@ def attainable(args, torch):
     V = ctypes.c_void_p
     lib.afd_probe_stream.argtypes = [V, ctypes.c_longlong, ctypes.c_int, ctypes.c_int, V, V]
     lib.afd_probe_mfma.argtypes = [ctypes.c_int, V, ctypes.c_int, ctypes.c_int, V, V]
+    lib.afd_probe_lds.argtypes = [ctypes.c_int, ctypes.c_int, V, V]
+    lib.afd_probe_fp8_block.argtypes = [ctypes.c_int, V, ctypes.c_int, ctypes.c_int, V, V, V]
     st = torch.cuda.current_stream()
 
     def timed(fn, reps):
@@ -690,6 +692,53 @@ def attainable(args, torch):
                               "chains_per_wave": chains, "flops": flops, "us": round(t * 1e6, 1),
                               "TFLOPs": round(flops / t / 1e12, 1),
                               "frac_of_peak": round(flops / t / 1e12 / peak, 4)}), flush=True)
+    # LDS reads in the tiled GEMMs' operand pattern, one 8-wave workgroup per compute unit
+    iters = 20000
+    cyc = torch.zeros(cus * 8, dtype=torch.int64, device="cuda")
+
+    def run_lds():
+        rc = lib.afd_probe_lds(cus, iters, cyc.data_ptr(), st.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"afd_probe_lds returned {rc}")
+    t = timed(run_lds, 5)
+    per_wg = 8 * 16 * 1024 * iters
+    cmax = int(cyc.max().item())
+    print(json.dumps({"probe": "lds_read", "pattern": "16-byte reads, one 256-byte slot per 16-lane quarter",
+                      "workgroups": cus, "waves_per_cu": 8, "bytes": per_wg * cus, "us": round(t * 1e6, 1),
+                      "bytes_per_clk_per_cu": round(per_wg / cmax, 1), "clock_GHz": round(cmax / t / 1e9, 3),
+                      "TBps": round(per_wg * cus / t / 1e12, 1)}), flush=True)
+    # the fp8 tiled GEMM's inner loop without global memory, piece by piece
+    ops = (torch.randn(cus * 8 * 12 * 64 * 32, generator=g, device="cuda")
+           .to(torch.float8_e4m3fn).view(torch.uint8))
+    out = torch.empty(cus * 8 * 64, dtype=torch.float32, device="cuda")
+    cyc = torch.zeros(cus * 8, dtype=torch.int64, device="cuda")
+    iters = 512
+    names = ("MFMAs accumulating directly, operands in registers", "+ block rescale of the products",
+             "+ token operands read from LDS", "+ a chunk's staging writes and barrier every two blocks",
+             "the same writes spread over the second block's steps, the barrier at its end",
+             "the barrier alone every two blocks, no writes",
+             "4 waves of 64 columns: rescale, token operands from LDS",
+             "4 waves of 64 columns: + a chunk's staging writes and barrier every two blocks")
+    for mode in range(8):
+        waves = cus * (4 if mode >= 6 else 8)  # one workgroup per compute unit
+        per_wave = 32 if mode >= 6 else 16    # instructions per wave per iteration
+
+        def run_blk():
+            rc = lib.afd_probe_fp8_block(mode, ops.data_ptr(), waves, iters, out.data_ptr(), cyc.data_ptr(),
+                                         st.cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"afd_probe_fp8_block returned {rc}")
+        t = timed(run_blk, 10)
+        flops = waves * iters * per_wave * 65536
+        cmax = int(cyc[:waves].max().item())
+        # a SIMD's matrix core gets 32 instructions of 32 cycles per iteration (two waves
+        # of 16, or one of 32)
+        print(json.dumps({"probe": "fp8_block", "mode": mode, "what": names[mode], "waves": waves,
+                          "flops": flops, "us": round(t * 1e6, 1), "TFLOPs": round(flops / t / 1e12, 1),
+                          "frac_of_peak": round(flops / t / 1e12 / MFMA_PEAK_TFLOPS["fp8"], 4),
+                          "cycles_per_iteration": round(cmax / iters, 1),
+                          "matrix_core_busy": round(1024 * iters / cmax, 4),
+                          "clock_GHz": round(cmax / t / 1e9, 3)}), flush=True)
 
 
 def main():

@@ -11,6 +11,19 @@
 //   afd_probe_mfma: back-to-back matrix-core instructions on operands drawn at random
 //     (eight independent accumulators per wave, each with its own operands): kind 0 is
 //     v_mfma_f32_32x32x16_bf16, kind 1 v_mfma_f32_16x16x128_f8f6f4 (e4m3 x e4m3).
+//   afd_probe_lds: LDS reads in the tiled GEMMs' operand pattern (16-byte reads, each
+//     16-lane quarter of a wave reading one contiguous 256-byte slot), 8 waves per
+//     compute unit; reports each wave's cycle count.
+//   afd_probe_fp8_block: the fp8 tiled GEMM's inner loop without global memory, on
+//     random operands, 8 waves per workgroup (two per SIMD), each with 8 token blocks x
+//     2 weight column blocks, two v_mfma_f32_16x16x128_f8f6f4 per token block.  mode 0:
+//     the instructions accumulate directly; mode 1: their products are added to the
+//     accumulators times a per-token, per-column-block scale (one multiply and four
+//     FMAs per instruction, the previous token block's while the current one's
+//     instructions run), token operands in registers; mode 2: as 1, token operands read
+//     from LDS one token block ahead, in the GEMM's slot layout; mode 3: as 2, plus,
+//     every two scale blocks, the staging writes of a chunk (four 16-byte and one
+//     4-byte LDS write per thread) and a workgroup barrier.  Reports each wave's cycles.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -95,6 +108,159 @@ __global__ void __launch_bounds__(kThreads) probe_mfma_fp8_kernel(const i32x8* o
   out[wid * kWave + lane] = s;
 }
 
+constexpr int kLdsThreads = 512;  // 8 waves per workgroup, two per SIMD
+
+__global__ void __launch_bounds__(kLdsThreads) probe_lds_kernel(int iters, unsigned long long* cycles) {
+  extern __shared__ i32x4 lds_buf[];  // 64 KiB used: 256 slots of 256 bytes
+  for (int i = threadIdx.x; i < 4096; i += kLdsThreads) lds_buf[i] = i32x4{i, i + 1, i + 2, i + 3};
+  __syncthreads();
+  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+  const unsigned long long t0 = clock64();
+  for (int it = 0; it < iters; ++it) {
+    i32x4 v[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) v[j] = lds_buf[((j * 4 + lane / 16 + w * 8 + it * 3) & 255) * 16 + lane % 16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) asm volatile("" ::"v"(v[j]));
+  }
+  const unsigned long long t1 = clock64();
+  if (lane == 0) cycles[blockIdx.x * (kLdsThreads / kWave) + w] = t1 - t0;
+}
+
+constexpr int kF8Slot = 272;  // the fp8 tiled GEMM's LDS slot: 16 rows x 16 bytes + padding
+
+// NCB weight column blocks of 16 per wave: 2 with 8 waves per workgroup (two per SIMD,
+// the GEMM's split), 4 with 4 waves (one per SIMD, half the LDS operand reads per
+// instruction).  ops: 12 operands of 2 KiB per wave (NCB weight fragments, 8 token blocks).
+template <int MODE, int NCB>
+__global__ void __launch_bounds__(NCB == 2 ? 512 : 256) probe_fp8_block_kernel(const i32x8* ops, int iters, float* out,
+                                                                                unsigned long long* cycles) {
+  constexpr int kWaves = NCB == 2 ? 8 : 4;
+  constexpr int kTbPerWave = 8 / kWaves;  // token blocks each wave initialises and stages
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];  // 8 x 16 slots, + staging area
+  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+  const long long wid = (long long)blockIdx.x * kWaves + w;
+  const i32x8* o = ops + wid * 12 * kWave + lane;
+  i32x8 wf[NCB], tb[8];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) wf[cb] = o[cb * kWave];
+#pragma unroll
+  for (int rb = 0; rb < 8; ++rb) tb[rb] = o[(4 + rb) * kWave];
+  if (MODE >= 2) {
+    // every slot of this wave's token blocks gets random bytes (the wave's own operands)
+    for (int q = 0; q < 16 * kTbPerWave; ++q) {
+      const i32x8 v = tb[q & 7];
+      *reinterpret_cast<i32x4*>(lds + (w * 16 * kTbPerWave + q) * kF8Slot + (lane % 16) * 16) =
+          (lane & 16) ? i32x4{v[4], v[5], v[6], v[7]} : i32x4{v[0], v[1], v[2], v[3]};
+    }
+    __syncthreads();
+  }
+  float sa[8], wsc[NCB];
+#pragma unroll
+  for (int rb = 0; rb < 8; ++rb) sa[rb] = 1.0f + (float)((lane * 8 + rb) & 63) * (1.0f / 64.0f);
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) wsc[cb] = 0.5f + (float)((w + cb) & 3) * 0.125f;
+  f32x4 acc[8][NCB] = {};
+  f32x4 p[2][NCB];
+  const int rd_off = ((lane >> 4) * 2) * kF8Slot + (lane & 15) * 16;
+  const unsigned long long t0 = clock64();
+  for (int it = 0; it < iters; ++it) {
+    // the scales change from block to block in the GEMM
+#pragma unroll
+    for (int rb = 0; rb < 8; ++rb) asm volatile("" : "+v"(sa[rb]));
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) asm volatile("" : "+v"(wsc[cb]));
+    const int h = it & 1;
+    i32x8 av[2];
+    auto rd = [&](int rb) {
+      if (MODE >= 2) {
+        const unsigned char* ap = lds + (rb * 16 + h * 8) * kF8Slot + rd_off;
+        const i32x4 l4 = *reinterpret_cast<const i32x4*>(ap);
+        const i32x4 h4 = *reinterpret_cast<const i32x4*>(ap + kF8Slot);
+        av[rb & 1] = i32x8{l4[0], l4[1], l4[2], l4[3], h4[0], h4[1], h4[2], h4[3]};
+      } else {
+        av[rb & 1] = tb[rb];
+      }
+    };
+    auto fm = [&](int rb) {
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        const float sc = sa[rb] * wsc[cb];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[rb][cb][i] = fmaf(p[rb & 1][cb][i], sc, acc[rb][cb][i]);
+      }
+    };
+    rd(0);
+#pragma unroll
+    for (int rb = 0; rb < 8; ++rb) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (rb + 1 < 8) rd(rb + 1);
+      const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+      if (MODE == 0) {
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+          acc[rb][cb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[cb], av[rb & 1], acc[rb][cb], 0, 0, 0, 0, 0, 0);
+          p[rb & 1][cb] = acc[rb][cb];
+        }
+      } else {
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+          p[rb & 1][cb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[cb], av[rb & 1], zero, 0, 0, 0, 0, 0, 0);
+        if (rb > 0) fm(rb - 1);
+      }
+      if (MODE == 4 && h == 1 && rb < 5) {
+        // the chunk's staging writes spread over the second block's first steps
+        unsigned char* st = lds + 8 * 16 * kF8Slot + w * 1024 * 5 + lane * 16;
+        static_assert(MODE != 4 || NCB == 2, "spread writes with the 8-wave split only");
+        if (rb < 4)
+          *reinterpret_cast<i32x4*>(st + rb * 1024) = i32x4{it, rb, lane, w};
+        else
+          *reinterpret_cast<float*>(st + 4 * 1024) = sa[0];
+      }
+      if (MODE >= 2 && rb + 1 < 8) {
+        if (MODE == 4 && rb < 5)
+          __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+        else
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (MODE >= 1 && rb > 0) __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+      }
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) asm volatile("" ::"v"(p[rb & 1][cb]));
+      if (rb > 0) {
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) asm volatile("" : "+v"(acc[rb - 1][cb]));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (MODE >= 1) fm(7);
+    if ((MODE == 4 || MODE == 5) && h == 1) __syncthreads();
+    if (MODE == 3 && h == 1) {
+      // a chunk's staging writes (into an area no operand read touches) and its barrier:
+      // the workgroup writes 8 x 5 KiB per chunk whatever its wave count
+      unsigned char* st = lds + 8 * 16 * kF8Slot + w * 1024 * 5 * kTbPerWave + lane * 16;
+#pragma unroll
+      for (int i = 0; i < 4 * kTbPerWave; ++i) *reinterpret_cast<i32x4*>(st + i * 1024) = i32x4{it, i, lane, w};
+#pragma unroll
+      for (int i = 0; i < kTbPerWave; ++i) *reinterpret_cast<float*>(st + (4 * kTbPerWave + i) * 1024) = sa[i];
+      __syncthreads();
+    }
+  }
+  const unsigned long long t1 = clock64();
+  float s = 0.f;
+#pragma unroll
+  for (int rb = 0; rb < 8; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s += acc[rb][cb][i];
+  out[wid * kWave + lane] = s;
+  if (lane == 0) cycles[wid] = t1 - t0;
+}
+
 }  // namespace
 
 // buf: runs * run_bytes readable bytes (16-byte aligned); out: runs * 1 KiB.
@@ -130,5 +296,57 @@ extern "C" int afd_probe_mfma(int kind, const void* ops, int waves, int iters, f
     probe_mfma_bf16_kernel<<<blocks, kThreads, 0, st>>>(static_cast<const bf16x8*>(ops), iters, out);
   else
     probe_mfma_fp8_kernel<<<blocks, kThreads, 0, st>>>(static_cast<const i32x8*>(ops), iters, out);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+// LDS reads: `workgroups` workgroups of 8 waves, one per compute unit (96 KiB of LDS
+// each), each wave reading 16 KiB per iteration; cycles: workgroups * 8 entries, each
+// wave's clock64() cycles over its loop.  Returns 0, -1 on bad arguments, -4 on a launch
+// error.
+extern "C" int afd_probe_lds(int workgroups, int iters, unsigned long long* cycles, void* stream) {
+  if (workgroups <= 0 || iters <= 0 || !cycles) return -1;
+  const size_t smem = 96 * 1024;
+  if (hipFuncSetAttribute(reinterpret_cast<const void*>(probe_lds_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                          (int)smem) != hipSuccess)
+    return -4;
+  probe_lds_kernel<<<workgroups, kLdsThreads, smem, static_cast<hipStream_t>(stream)>>>(iters, cycles);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+// The fp8 tiled GEMM's inner loop without global memory (mode 0 to 5, see above, with 8
+// waves of 2 column blocks; modes 6 and 7: modes 2 and 3 with 4 waves of 4 column
+// blocks): ops: waves * 12 * 2 KiB of random e4m3 bytes; waves a multiple of 8; out:
+// waves * 64 floats; cycles: waves entries, each wave's clock64() cycles over its loop.
+// FLOPs per launch: waves * iters * 16 * 65536 (modes 0-5), * 32 * 65536 (modes 6, 7).
+extern "C" int afd_probe_fp8_block(int mode, const void* ops, int waves, int iters, float* out,
+                                   unsigned long long* cycles, void* stream) {
+  if (!ops || !out || !cycles || waves <= 0 || waves % (kLdsThreads / kWave) || iters <= 0 || mode < 0 || mode > 7)
+    return -1;
+  const unsigned blocks = (unsigned)(waves / (mode >= 6 ? 4 : 8));
+  // 96 KiB (the loop uses 8 * 16 slots + 40 KiB of staging area): one workgroup per
+  // compute unit, as the GEMM runs
+  const size_t smem = 96 * 1024;
+  static_assert(8 * 16 * kF8Slot + 8 * 5 * 1024 <= 96 * 1024, "the probe's LDS fits");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const i32x8* o = static_cast<const i32x8*>(ops);
+  const void* fns[8] = {reinterpret_cast<const void*>(probe_fp8_block_kernel<0, 2>),
+                        reinterpret_cast<const void*>(probe_fp8_block_kernel<1, 2>),
+                        reinterpret_cast<const void*>(probe_fp8_block_kernel<2, 2>),
+                        reinterpret_cast<const void*>(probe_fp8_block_kernel<3, 2>),
+                        reinterpret_cast<const void*>(probe_fp8_block_kernel<4, 2>),
+                        reinterpret_cast<const void*>(probe_fp8_block_kernel<5, 2>),
+                        reinterpret_cast<const void*>(probe_fp8_block_kernel<2, 4>),
+                        reinterpret_cast<const void*>(probe_fp8_block_kernel<3, 4>)};
+  if (hipFuncSetAttribute(fns[mode], hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem) != hipSuccess) return -4;
+  switch (mode) {
+    case 0: probe_fp8_block_kernel<0, 2><<<blocks, 512, smem, st>>>(o, iters, out, cycles); break;
+    case 1: probe_fp8_block_kernel<1, 2><<<blocks, 512, smem, st>>>(o, iters, out, cycles); break;
+    case 2: probe_fp8_block_kernel<2, 2><<<blocks, 512, smem, st>>>(o, iters, out, cycles); break;
+    case 3: probe_fp8_block_kernel<3, 2><<<blocks, 512, smem, st>>>(o, iters, out, cycles); break;
+    case 4: probe_fp8_block_kernel<4, 2><<<blocks, 512, smem, st>>>(o, iters, out, cycles); break;
+    case 5: probe_fp8_block_kernel<5, 2><<<blocks, 512, smem, st>>>(o, iters, out, cycles); break;
+    case 6: probe_fp8_block_kernel<2, 4><<<blocks, 256, smem, st>>>(o, iters, out, cycles); break;
+    default: probe_fp8_block_kernel<3, 4><<<blocks, 256, smem, st>>>(o, iters, out, cycles); break;
+  }
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
