@@ -256,6 +256,28 @@ def test_fp8_quantisation_bit_exact(src):
         np.testing.assert_array_equal(codes[r], c_ref, err_msg=f"row {r}")
 
 
+def test_fp8_quantisation_more_rows_than_waves():
+    """Step a0 on more rows than the launch has waves (32768): the rows past the grid are
+    taken in a second pass.  Sampled rows at both ends and across that boundary are
+    bit-exact against the oracle, for a row length that is not a multiple of a wave's
+    step (640 bf16 channels: 512 + 128)."""
+    from moe_expert_ffn_softmax_amd import quantize_fp8
+    rng = np.random.default_rng(23)
+    rows, cols = 32768 + 300, 640
+    v = rng.standard_normal((rows, cols)).astype(np.float32)
+    v *= rng.choice([1e-3, 1.0, 50.0], size=(rows, 1)).astype(np.float32)
+    t = torch.from_numpy(v).to(torch.bfloat16)
+    v = t.float().numpy()
+    codes, scales = quantize_fp8(t.cuda())
+    torch.cuda.synchronize()
+    codes, scales = codes.cpu().numpy(), scales.cpu().numpy()
+    sample = list(range(40)) + list(range(32768 - 40, 32768 + 40)) + list(range(rows - 40, rows))
+    for r in sample:
+        c_ref, s_ref, _ = oracle.quant_row_fp8(v[r])
+        np.testing.assert_array_equal(scales[r], s_ref, err_msg=f"row {r}")
+        np.testing.assert_array_equal(codes[r], c_ref, err_msg=f"row {r}")
+
+
 @pytest.mark.parametrize("w", workloads.ORDERED, ids=lambda w: w.name)
 def test_route_full_size_every_workload(w):
     """Routing alone at every workload's full T, E, k (small H, M: routing does not
