@@ -620,6 +620,7 @@ def attainable(args, torch):
     lib.afd_probe_mfma.argtypes = [ctypes.c_int, V, ctypes.c_int, ctypes.c_int, V, V]
     lib.afd_probe_lds.argtypes = [ctypes.c_int, ctypes.c_int, V, V]
     lib.afd_probe_fp8_block.argtypes = [ctypes.c_int, V, ctypes.c_int, ctypes.c_int, V, V, V]
+    lib.afd_probe_bf16_block.argtypes = [ctypes.c_int, V, ctypes.c_int, ctypes.c_int, V, V, V]
     st = torch.cuda.current_stream()
 
     def timed(fn, reps):
@@ -738,6 +739,30 @@ def attainable(args, torch):
                           "frac_of_peak": round(flops / t / 1e12 / MFMA_PEAK_TFLOPS["fp8"], 4),
                           "cycles_per_iteration": round(cmax / iters, 1),
                           "matrix_core_busy": round(1024 * iters / cmax, 4),
+                          "clock_GHz": round(cmax / t / 1e9, 3)}), flush=True)
+    # the bf16 tiled GEMM's inner loop without global memory: one 4-wave workgroup per
+    # compute unit (one wave per SIMD), 64 MFMAs of 32 cycles per wave per chunk
+    waves = cus * 4
+    ops = (torch.randn(waves * 6 * 64 * 8, generator=g, device="cuda").to(torch.bfloat16))
+    out = torch.empty(waves * 64, dtype=torch.float32, device="cuda")
+    cyc = torch.zeros(waves, dtype=torch.int64, device="cuda")
+    iters = 256
+    names = ("MFMAs, operands in registers", "+ row blocks' operands read from LDS",
+             "+ a chunk's staging writes and barrier")
+    for mode in range(3):
+        def run_bf():
+            rc = lib.afd_probe_bf16_block(mode, ops.data_ptr(), waves, iters, out.data_ptr(), cyc.data_ptr(),
+                                          st.cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"afd_probe_bf16_block returned {rc}")
+        t = timed(run_bf, 10)
+        flops = waves * iters * 64 * 32768
+        cmax = int(cyc.max().item())
+        print(json.dumps({"probe": "bf16_block", "mode": mode, "what": names[mode], "waves": waves,
+                          "flops": flops, "us": round(t * 1e6, 1), "TFLOPs": round(flops / t / 1e12, 1),
+                          "frac_of_peak": round(flops / t / 1e12 / MFMA_PEAK_TFLOPS["bf16"], 4),
+                          "cycles_per_chunk": round(cmax / iters, 1),
+                          "matrix_core_busy": round(2048 * iters / cmax, 4),
                           "clock_GHz": round(cmax / t / 1e9, 3)}), flush=True)
 
 

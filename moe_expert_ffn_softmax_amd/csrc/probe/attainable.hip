@@ -24,6 +24,12 @@
 //     from LDS one token block ahead, in the GEMM's slot layout; mode 3: as 2, plus,
 //     every two scale blocks, the staging writes of a chunk (four 16-byte and one
 //     4-byte LDS write per thread) and a workgroup barrier.  Reports each wave's cycles.
+//   afd_probe_bf16_block: the bf16 tiled GEMM's inner loop without global memory: 4
+//     waves per workgroup (one per SIMD), each with 4 row blocks of 32 x 2 column blocks
+//     of 32, v_mfma_f32_32x32x16_bf16 accumulating directly, 64 per wave per 128-deep
+//     chunk.  mode 0: operands in registers; mode 1: the row blocks' operands read from
+//     LDS in the GEMM's fragment layout; mode 2: as 1, plus a chunk's staging writes
+//     (eight 16-byte LDS writes per thread) and a workgroup barrier per chunk.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -261,6 +267,64 @@ __global__ void __launch_bounds__(NCB == 2 ? 512 : 256) probe_fp8_block_kernel(c
   if (lane == 0) cycles[wid] = t1 - t0;
 }
 
+constexpr int kBfSlot = 1056;  // the bf16 tiled GEMM's fragment slot: 1 KiB + bank padding
+
+template <int MODE>
+__global__ void __launch_bounds__(256) probe_bf16_block_kernel(const bf16x8* ops, int iters, float* out,
+                                                               unsigned long long* cycles) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char lds[];  // 4 x 8 fragment slots + staging
+  const int lane = threadIdx.x % kWave, w = threadIdx.x / kWave;
+  const long long wid = (long long)blockIdx.x * 4 + w;
+  const bf16x8* o = ops + wid * 6 * kWave + lane;
+  bf16x8 b[2], a[4];
+  b[0] = o[0];
+  b[1] = o[kWave];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) a[rb] = o[(2 + rb) * kWave];
+  // lane l's fragment piece: row l % 32, reduction half l / 32
+  const int frag_off = (lane % 32) * 16 + (lane / 32) * 528;
+  if (MODE >= 1) {
+    // wave w fills row block w's 8 fragment slots with its own random operand
+    for (int f = 0; f < 8; ++f) *reinterpret_cast<bf16x8*>(lds + (w * 8 + f) * kBfSlot + frag_off) = a[f & 3];
+    __syncthreads();
+  }
+  f32x16 acc[4][2] = {};
+  const unsigned long long t0 = clock64();
+  for (int it = 0; it < iters; ++it) {
+    // one 128-deep chunk: 8 fragments of 16, each feeding 4 row blocks x 2 column blocks
+#pragma unroll
+    for (int f = 0; f < 8; ++f) {
+      bf16x8 av[4];
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+        // the fragment order alternates between iterations, so the reads are not hoisted
+        av[rb] = MODE >= 1 ? *reinterpret_cast<const bf16x8*>(lds + (rb * 8 + ((f + 4 * (it & 1)) & 7)) * kBfSlot + frag_off)
+                           : a[rb];
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[rb], b[cb], acc[rb][cb], 0, 0, 0);
+    }
+    if (MODE == 2) {
+      // a chunk's staging writes (into an area no operand read touches) and its barrier
+      unsigned char* st = lds + 4 * 8 * kBfSlot + w * 8 * 1024 + lane * 16;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) *reinterpret_cast<i32x4*>(st + i * 1024) = i32x4{it, i, lane, w};
+      __syncthreads();
+    }
+  }
+  const unsigned long long t1 = clock64();
+  float sum = 0.f;
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sum += acc[rb][cb][i];
+  out[wid * kWave + lane] = sum;
+  if (lane == 0) cycles[wid] = t1 - t0;
+}
+
 }  // namespace
 
 // buf: runs * run_bytes readable bytes (16-byte aligned); out: runs * 1 KiB.
@@ -347,6 +411,31 @@ extern "C" int afd_probe_fp8_block(int mode, const void* ops, int waves, int ite
     case 5: probe_fp8_block_kernel<5, 2><<<blocks, 512, smem, st>>>(o, iters, out, cycles); break;
     case 6: probe_fp8_block_kernel<2, 4><<<blocks, 256, smem, st>>>(o, iters, out, cycles); break;
     default: probe_fp8_block_kernel<3, 4><<<blocks, 256, smem, st>>>(o, iters, out, cycles); break;
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+// The bf16 tiled GEMM's inner loop without global memory (mode 0, 1 or 2, see above):
+// ops: waves * 6 KiB of random bf16 bytes; waves a multiple of 4; out: waves * 64 floats;
+// cycles: waves entries, each wave's clock64() cycles over its loop.  FLOPs per launch:
+// waves * iters * 64 * 32768.
+extern "C" int afd_probe_bf16_block(int mode, const void* ops, int waves, int iters, float* out,
+                                    unsigned long long* cycles, void* stream) {
+  if (!ops || !out || !cycles || waves <= 0 || waves % 4 || iters <= 0 || mode < 0 || mode > 2) return -1;
+  const unsigned blocks = (unsigned)(waves / 4);
+  // 96 KiB: one workgroup per compute unit, as the GEMM runs
+  const size_t smem = 96 * 1024;
+  static_assert(4 * 8 * kBfSlot + 4 * 8 * 1024 <= 96 * 1024, "the probe's LDS fits");
+  const void* fns[3] = {reinterpret_cast<const void*>(probe_bf16_block_kernel<0>),
+                        reinterpret_cast<const void*>(probe_bf16_block_kernel<1>),
+                        reinterpret_cast<const void*>(probe_bf16_block_kernel<2>)};
+  if (hipFuncSetAttribute(fns[mode], hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem) != hipSuccess) return -4;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bf16x8* o = static_cast<const bf16x8*>(ops);
+  switch (mode) {
+    case 0: probe_bf16_block_kernel<0><<<blocks, 256, smem, st>>>(o, iters, out, cycles); break;
+    case 1: probe_bf16_block_kernel<1><<<blocks, 256, smem, st>>>(o, iters, out, cycles); break;
+    default: probe_bf16_block_kernel<2><<<blocks, 256, smem, st>>>(o, iters, out, cycles); break;
   }
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
