@@ -78,7 +78,9 @@ typedef enum afd_dtype { AFD_F32 = 0, AFD_BF16 = 1, AFD_FP8_E4M3 = 2 } afd_dtype
 
 /* Layer shape.  hidden, inter and shared_inter must be multiples of 128;
  * 1 <= top_k <= min(num_experts, 32); 1 <= num_experts <= 1024;
- * 1 <= max_tokens and max_tokens * top_k < 2^31. */
+ * 1 <= max_tokens and max_tokens * top_k < 2^31; for the fp8 dtype also
+ * max_tokens * hidden, max_tokens * top_k * inter and max_tokens * shared_inter
+ * below 2^32 (activation matrices under 4 GiB). */
 typedef struct afd_ffn_config {
   int32_t hidden;       /* H */
   int32_t inter;        /* M, intermediate size of each routed expert */

@@ -7,6 +7,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 #include <new>
 
@@ -68,6 +69,13 @@ int check_config(const afd_ffn_config* c) {
   if ((long long)c->max_tokens * c->top_k >= (1ll << 31)) return fail(AFD_EINVAL, "max_tokens * top_k >= 2^31");
   if (c->dtype != AFD_F32 && c->dtype != AFD_BF16 && c->dtype != AFD_FP8_E4M3)
     return fail(AFD_EINVAL, "unknown dtype %d", c->dtype);
+  // the fp8 128-row GEMMs address activation rows (x: max_tokens x hidden codes; h:
+  // max_tokens * top_k x inter and max_tokens x shared_inter) by 32-bit byte offsets
+  if (c->dtype == AFD_FP8_E4M3) {
+    const long long T = c->max_tokens;
+    const long long most = std::max({T * c->hidden, T * c->top_k * c->inter, T * c->shared_inter});
+    if (most >= (1ll << 32)) return fail(AFD_EINVAL, "fp8 layer: an activation matrix of max_tokens rows exceeds 4 GiB");
+  }
   return AFD_OK;
 }
 
@@ -231,7 +239,7 @@ int forward_fp8(afd_ffn* h, const afd_workspace& ws, const void* x, int T, const
     gq.out_shared = ws.hq_shared;
     gq.outs_shared = ws.hs_shared;
     StageScope s(h, st, AFD_STAGE_GATE_UP);
-    hipError_t e = afd::launch_gemm_fp8_tiled(gq, true, items1, h->num_cus, st);
+    hipError_t e = afd::launch_gemm_fp8_tiled(gq, true, T, items1, h->num_cus, st);
     if (e != hipSuccess) return hip_fail(e, "fp8 gate/up GEMM launch");
     s.done();
   } else {
@@ -251,7 +259,7 @@ int forward_fp8(afd_ffn* h, const afd_workspace& ws, const void* x, int T, const
   }
   {
     StageScope s(h, st, AFD_STAGE_DOWN);
-    hipError_t e = tiled ? afd::launch_gemm_fp8_tiled(g2, false, items2, h->num_cus, st)
+    hipError_t e = tiled ? afd::launch_gemm_fp8_tiled(g2, false, rows, items2, h->num_cus, st)
                          : afd::launch_gemm_fp8(g2, false, items2, h->gemm_blocks[5], st);
     if (e != hipSuccess) return hip_fail(e, "fp8 down GEMM launch");
     s.done();

@@ -109,8 +109,10 @@ int tiled_groups();
 // fp8 (e4m3, fp32 block scales) streaming variant; weights packed by launch_pack_fp8,
 // A = fp8 codes with per-row per-128 scales `as_*`, weight scales `s_*`; writes fp32.
 hipError_t launch_gemm_fp8(const GroupedGemm& g, bool swiglu, long long max_items, int max_blocks, hipStream_t st);
-hipError_t launch_gemm_fp8_tiled(const GroupedGemm& g, bool swiglu, long long max_items, int max_blocks,
-                                 hipStream_t st);
+// a_rows: rows of the routed A matrix (tokens when gathered, else expert-sorted rows);
+// refused when a row offset of either A matrix does not fit in 32 bits.
+hipError_t launch_gemm_fp8_tiled(const GroupedGemm& g, bool swiglu, long long a_rows, long long max_items,
+                                 int max_blocks, hipStream_t st);
 int fp8_tiled_rows();
 int fp8_tiled_groups();
 hipError_t launch_pack_fp8(const uint8_t* src, uint8_t* dst, int nmat, int R, int C, int gate_up, hipStream_t st);

@@ -39,9 +39,10 @@
 //
 // Schedule of a block.  Rescaling costs one multiply and four FMAs per MFMA, about
 // half the MFMA time; with two waves per SIMD one wave's rescaling overlaps the other
-// wave's MFMAs, and within a wave the instruction order interleaves them.  Each step rb of a block reads token block
-// rb + 1's operand from LDS, then alternates block rb's MFMAs with the rescaling of
-// block rb - 1's products (kept in a second register set).  The compiler would
+// wave's MFMAs, and within a wave the instruction order interleaves them.  Each step
+// rb of a block issues block rb's first MFMA, then the LDS reads of token block rb + 1's
+// operand, then the rescaling of block rb - 1's products (kept in a second register
+// set) around block rb's second MFMA.  The compiler would
 // otherwise gather the pure arithmetic of the whole unrolled block in one place, so
 // empty asm statements that consume a step's products and accumulators keep each step
 // between scheduling barriers.
@@ -50,6 +51,13 @@
 // and per-token per-128 scales; see below) instead of fp32 h.
 //
 // Items as in the bf16 tiled kernel; the XCD ranges carry equal costs (f8_xcd_range).
+// A workgroup takes its items as runs: consecutive items (of its strided sequence)
+// with the same count of 16-row blocks share one body specialised on that count.  In
+// the down projection the items of a run are chained: an item's last chunk loads the
+// next item's first chunks and weight blocks where it would otherwise reload its own,
+// so the next item starts without waiting for memory (see the kernel).  The gate/up
+// projection, whose items are 3.5x longer, measured no faster chained and runs each
+// item on its own.
 #include "grouped.h"
 
 namespace afd {
@@ -73,12 +81,10 @@ constexpr int kF8Loads = kF8StageRows / 4;      // staging loads per thread per 
 // Each wave stages its rows' token scales of a chunk (2 blocks) in lanes 0-31 and the
 // chunk's weight scales in lanes 32-63 (written by wave 0 only): one load per lane.
 static_assert(2 * kF8StageRows + kF8WScales == kWave, "one scale per lane per chunk");
-constexpr int kF8BAhead = 2;                    // scale blocks of weights in flight per wave
-constexpr int kF8StageSets = 1;                 // chunks of activations loading ahead
+// Weight blocks in flight per wave: one chunk's two scale blocks (ring slot = the
+// block's index in its chunk).  The staging registers hold one chunk.
+constexpr int kF8BAhead = 2;
 constexpr int kF8LdsAhead = 1;                  // token blocks of operands read from LDS ahead
-// The chunk loop is unrolled by two when a ring slot (block % kF8BAhead) or a staging
-// set (chunk % kF8StageSets) would otherwise depend on the chunk's parity.
-constexpr int kF8Unroll = (kF8BAhead == 4 || kF8StageSets == 2) ? 2 : 1;
 constexpr int kF8Xcds = 8;
 
 __device__ __forceinline__ f32x4 f8_mfma(const i32x8& a, const i32x8& b) {
@@ -87,9 +93,15 @@ __device__ __forceinline__ f32x4 f8_mfma(const i32x8& a, const i32x8& b) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 0, 0, 0, 0, 0, 0);
 }
 
+// Global-memory views of pointers rebuilt from scalar registers (without them the
+// compiler emits flat loads, which also count against the LDS wait counter).
+typedef const __attribute__((address_space(1))) uint8_t gu8;
+typedef const __attribute__((address_space(1))) float gf32;
+typedef const __attribute__((address_space(1))) bf16x8 gbf16x8;
+typedef const __attribute__((address_space(1))) i32x4 gi32x4;
 // A lane's 32 weight bytes of a packed fragment: 16 at p, 16 at p + 1 KiB.
-__device__ __forceinline__ i32x8 f8_load32(const uint8_t* p) {
-  const i32x4* q = reinterpret_cast<const i32x4*>(p);
+__device__ __forceinline__ i32x8 f8_load32g(gu8* p) {
+  gi32x4* q = reinterpret_cast<gi32x4*>(p);
   const i32x4 lo = q[0], hi = q[64];
   return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
@@ -100,248 +112,116 @@ constexpr int kF8MinBlocks = 1;  // workgroups per CU the registers must allow
 // quantised to e4m3 right after, whose step is 2^-3 of the value.
 __device__ __forceinline__ float silu_rcp(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
-// One item: a tile of it.nrows <= 16 * NRB rows (NRB 16-row blocks hold all of them)
-// times the workgroup's 8 column groups.  Blocks past NRB are not computed.
-template <bool SWIGLU, int NRB>
-__device__ __forceinline__ void fp8_tile(const GroupedGemm& g, const Item& it, const int w, unsigned char* lds,
-                                         float (*qamax)[kF8Rows]) {
-  // lane-derived indices are recomputed per item (hoisted out of the item loop they
-  // do not fit the register budget)
-  int lane = lane_id();
-  asm volatile("" : "+v"(lane));
-  const int K = it.shared ? g.K_shared : g.K_routed;
-  const int KB = K / 128;
-  const int NC = (KB + 1) / 2;  // 256-deep chunks; an odd KB leaves the last chunk half live
-  const int groups = it.shared ? g.groups_shared : g.groups_routed;
-  const int N = groups * 32;
-  const int NB = N / 128;
-  // A wave past the last group of a partial column tile recomputes the tile's last
-  // two groups and stores nothing (group counts are multiples of 4).
-  const bool active = it.group + w * kF8GroupsPerWave < groups;  // wave-uniform
-  const int group0 = active ? it.group + w * kF8GroupsPerWave : groups - kF8GroupsPerWave;
+// A pointer held in scalar registers (the value must be the same in every lane).
+template <typename T>
+__device__ __forceinline__ T* f8_uniform(T* p) {
+  const unsigned long long v = reinterpret_cast<unsigned long long>(p);
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)v);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(v >> 32));
+  return reinterpret_cast<T*>(((unsigned long long)hi << 32) | lo);
+}
 
-  // staged rows: w*kF8StageRows + i*4 + lane/16 (i < kF8Loads); the lane loads piece
-  // lane % 16 of each row's chunk
-  const int lda = it.shared ? g.lda_shared : g.lda_routed;
-  const uint8_t* abase = static_cast<const uint8_t*>(it.shared ? g.a_shared : g.a_routed);
-  const int piece = lane & 15;
-  // Source rows of the staged rows and of this thread's token-scale row (t % 128).
-  // The sorted_pair lookups are
-  // all issued before the first is used: in a branch per row, each would wait for
-  // its load before the next one issues.
-  int ar[kF8Loads + 1];
+// What an item's loads read: the rows it stages (gathered through sorted_pair for
+// routed gate/up rows), its token and weight block scales, and the wave's weight
+// fragments.  Bases are wave-uniform (scalar registers) and the per-lane parts 32-bit
+// byte offsets, so that a load is one instruction on a scalar base and a vector offset
+// (no 64-bit address arithmetic per load).
+struct F8Src {
+  const uint8_t* abase;         // activation rows of the item's segment (uniform)
+  unsigned aoff[kF8Loads];      // staged row w*kF8StageRows + i*4 + lane/16: byte offset from abase
+  const float* sp;              // the scale this lane stages, at block 0 (token scales for lanes
+                                //   < 32, weight scales for lanes >= 32)
+  int sstep;                    // floats between consecutive blocks' scales of this lane
+  const uint8_t* Bu;            // the wave's weight fragments (uniform; lane l reads at l * 16)
+  unsigned gs;                  // bytes per 32-column group of weights (uniform)
+  int K, KB;                    // reduction length, 128-deep blocks (uniform)
+};
+
+// Issue the sorted_pair lookups of an item's staged rows and of this thread's token-scale
+// row.  Branch-free: rows that are not gathered read counts[0], which f8_source ignores
+// (a load under a wave-uniform branch makes the compiler's later waits conservative).
+__device__ __forceinline__ void f8_lookup(const GroupedGemm& g, const Item& it, int w, int lane,
+                                          int (&lk)[kF8Loads + 1]) {
+  const bool gather = !it.shared && g.gather_routed;
+  const int32_t* src = gather ? g.sorted_pair : g.counts;
 #pragma unroll
   for (int i = 0; i < kF8Loads; ++i) {
     const int r = w * kF8StageRows + i * 4 + (lane >> 4);
-    ar[i] = it.row0 + (r < it.nrows ? r : 0);
+    lk[i] = src[gather ? it.row0 + (r < it.nrows ? r : 0) : 0];
   }
-  {
-    const int t = w * kF8StageRows + (lane & (kF8StageRows - 1));
-    ar[kF8Loads] = it.row0 + (t < it.nrows ? t : 0);
-  }
-  if (!it.shared && g.gather_routed) {
-#pragma unroll
-    for (int i = 0; i <= kF8Loads; ++i) ar[i] = g.sorted_pair[ar[i]];
-#pragma unroll
-    for (int i = 0; i <= kF8Loads; ++i) ar[i] /= g.k;
-  }
-  const uint8_t* arow[kF8Loads];
-#pragma unroll
-  for (int i = 0; i < kF8Loads; ++i) arow[i] = abase + (size_t)ar[i] * lda;
-  const float* asbase = it.shared ? g.as_shared : g.as_routed;
-  const float* srow = asbase + (size_t)ar[kF8Loads] * KB;
-  // byte offset in the row of chunk c's piece for this lane (clamped past the end of
-  // K: that scale block is multiplied with weight scale 0)
-  auto a_off = [&](int c) {
-    const int o = c * 256 + piece * 16;
-    return o < K ? o : o - 128;
-  };
-  // LDS: write slot of load i (token block (w*kF8StageRows + i*4 + lane/16) / 16 =
-  // w*kF8StageRows/16 + i/4, slot = piece, row in block (i % 4) * 4 + lane / 16)
-  const int wr_off = ((w * (kF8StageRows / 16)) * 16 + piece) * kF8Slot + (lane >> 4) * 16;
-  // read: slot (lane / 16) * 2 (+1 for the upper 16 bytes) of the scale block's 8
-  const int rd_off = ((lane >> 4) * 2) * kF8Slot + (lane & 15) * 16;
+  const int t = w * kF8StageRows + (lane & (kF8StageRows - 1));
+  lk[kF8Loads] = src[gather ? it.row0 + (t < it.nrows ? t : 0) : 0];
+}
 
+// An item's sources, from its lookups (the first use of their values).
+template <bool SWIGLU>
+__device__ __forceinline__ void f8_source(const GroupedGemm& g, const Item& it, int w, int lane,
+                                          const int (&lk)[kF8Loads + 1], F8Src& s) {
+  const bool gather = !it.shared && g.gather_routed;
+  s.K = it.shared ? g.K_shared : g.K_routed;
+  s.KB = s.K / 128;
+  const int groups = it.shared ? g.groups_shared : g.groups_routed;
+  const int N = groups * 32;
+  const int NB = N / 128;
+  const unsigned lda = (unsigned)(it.shared ? g.lda_shared : g.lda_routed);
+  s.abase = f8_uniform(static_cast<const uint8_t*>(it.shared ? g.a_shared : g.a_routed));
+#pragma unroll
+  for (int i = 0; i < kF8Loads; ++i) {
+    const int r = w * kF8StageRows + i * 4 + (lane >> 4);
+    const int row = it.row0 + (r < it.nrows ? r : 0);
+    s.aoff[i] = (unsigned)(gather ? lk[i] / g.k : row) * lda;
+  }
+  // a wave past the last group of a partial column tile recomputes the tile's last two
+  // groups and stores nothing (group counts are multiples of 4)
+  const int group0 = it.group + w * kF8GroupsPerWave < groups ? it.group + w * kF8GroupsPerWave
+                                                               : groups - kF8GroupsPerWave;
   const uint8_t* wbase = it.shared ? static_cast<const uint8_t*>(g.w_shared)
                                    : static_cast<const uint8_t*>(g.w_routed) + (size_t)it.seg * g.w_expert_elems;
-  const size_t group_stride = (size_t)KB * 4096;  // bytes per 32-column group
+  s.gs = (unsigned)s.KB * 4096;
   // 16-column block cb = (group group0 + cb / 2, half cb % 2): 2 KiB per scale block
-  const uint8_t* B = wbase + (size_t)group0 * group_stride + lane * 16;
+  s.Bu = f8_uniform(wbase + (size_t)group0 * s.gs);
   const float* ws = it.shared ? g.s_shared : g.s_routed + (size_t)it.seg * g.s_expert_elems;
-  // Scales staged with the activations (one per lane per chunk): lane l < 32 stages
-  // the value of block l / 16 of the chunk for the wave's row l % 16; lane 32 + u
-  // stages, for block u / 16 of the chunk, the scale of wave (u % 16) / kF8CB's
-  // 16-column block u % kF8CB (wave 0 writes them, the other waves' copies go to the
-  // dummy word).  Loads and LDS writes of the staging are branch-free: a load under a
-  // divergent branch whose value is used a chunk later makes the compiler wait, at
-  // the use, for every load in flight, the weight ring's included.
-  const bool sc_tok = lane < 2 * kF8StageRows;
-  const int sc_blk = sc_tok ? lane / kF8StageRows : (lane - 2 * kF8StageRows) / (kF8WScales / 2);
-  const int sc_off = sc_tok ? kF8A + (sc_blk * kF8Rows + w * kF8StageRows + (lane % kF8StageRows)) * 4
-                            : (w == 0 ? kF8A + (2 * kF8Rows + lane - 2 * kF8StageRows) * 4 : kF8Dummy);
-  int wnb;
-  {
-    const int t = lane % (kF8WScales / 2);  // used by lanes >= 32
+  if (lane < 2 * kF8StageRows) {
+    const int t = w * kF8StageRows + (lane & (kF8StageRows - 1));
+    const int row = it.row0 + (t < it.nrows ? t : 0);
+    s.sp = (it.shared ? g.as_shared : g.as_routed) + (size_t)(gather ? lk[kF8Loads] / g.k : row) * s.KB;
+    s.sstep = 1;
+  } else {
+    const int t = lane % (kF8WScales / 2);
     const int w2 = t / kF8CB, cb = t % kF8CB;
     const int g0 = it.group + w2 * kF8GroupsPerWave < groups ? it.group + w2 * kF8GroupsPerWave
                                                              : groups - kF8GroupsPerWave;
     const int j = g0 + (cb >> 1), half = cb & 1;
-    wnb = (SWIGLU ? half * (N / 2) + j * 16 : j * 32 + half * 16) / 128;
+    s.sp = ws + (SWIGLU ? half * (N / 2) + j * 16 : j * 32 + half * 16) / 128;
+    s.sstep = NB;
   }
+}
 
-  f32x4 acc[NRB][kF8CB];
-#pragma unroll
-  for (int rb = 0; rb < NRB; ++rb)
-#pragma unroll
-    for (int cb = 0; cb < kF8CB; ++cb) acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+template <int N>
+struct F8Blocks {
+  static constexpr int value = N;
+};
 
-  // Staging register sets: set (c % kF8StageSets) holds chunk c between its loads and
-  // its LDS write.  Chunk 0 -> LDS buffer 0; chunks 1 .. kF8StageSets (clamped to the
-  // last chunk) -> the sets.  Rows of token blocks past NRB are loaded (their rows
-  // read the item's row 0) and written like the others, and never read.
-  bf16x8 stage[kF8StageSets][kF8Loads];
-  // sstage holds the lane's loaded scale and slive whether its block is inside K (a
-  // block past the end of K, odd K / 128, gets weight scale 0): the zeroing is applied
-  // when the value is written to LDS, so that no instruction needs the loaded value
-  // before the write.
-  float sstage[kF8StageSets];
-  bool slive[kF8StageSets];
-  auto load_stage = [&](const int set, int c) {
-    c = c < NC ? c : NC - 1;
-#pragma unroll
-    for (int i = 0; i < kF8Loads; ++i) stage[set][i] = *reinterpret_cast<const bf16x8*>(arow[i] + a_off(c));
-    const int kb = 2 * c + sc_blk;
-    const int kbc = kb < KB ? kb : KB - 1;
-    sstage[set] = *(sc_tok ? srow + kbc : ws + (size_t)kbc * NB + wnb);
-    slive[set] = sc_tok || kb < KB;
-  };
-  auto write_stage = [&](const int set, int buf) {
-#pragma unroll
-    for (int i = 0; i < kF8Loads; ++i)
-      *reinterpret_cast<bf16x8*>(lds + buf + wr_off + (i >> 2) * 16 * kF8Slot + (i & 3) * 64) = stage[set][i];
-    *reinterpret_cast<float*>(lds + buf + sc_off) = slive[set] ? sstage[set] : 0.f;
-  };
-  // chunk 0's activations are loaded before the weight ring, so that the wait for
-  // them before their LDS write does not include the ring's loads
-  load_stage(0, 0);
-  i32x8 bring[kF8BAhead][kF8CB];
-#pragma unroll
-  for (int u = 0; u < kF8BAhead; ++u) {
-    const int s = u < KB ? u : KB - 1;
-#pragma unroll
-    for (int cb = 0; cb < kF8CB; ++cb) bring[u][cb] = f8_load32(B + (cb >> 1) * group_stride + (s * 2 + (cb & 1)) * 2048);
-  }
-
-  write_stage(0, 0);
-#pragma unroll
-  for (int u = 1; u <= kF8StageSets; ++u) load_stage(u % kF8StageSets, u);
-  __syncthreads();
-
-  // One 128-deep scale block: h is the block within the chunk, r its weight-ring slot
-  // (block % kF8BAhead).
-  auto block = [&](const int c, const int h, const int r, const int buf) {
-    const int kb = 2 * c + h;
-    const float* swl = reinterpret_cast<const float*>(lds + buf + kF8A) + 2 * kF8Rows +
-                       h * (kF8WScales / 2) + w * kF8CB;
-    float wsc[kF8CB];
-#pragma unroll
-    for (int cb = 0; cb < kF8CB; ++cb) wsc[cb] = swl[cb];
-    const float* sbuf = reinterpret_cast<const float*>(lds + buf + kF8A) + h * kF8Rows + (lane & 15);
-    // Software pipeline over token blocks: block rb + D's operand is read from LDS
-    // (D = kF8LdsAhead) and block rb - 1's products are rescaled while block rb's MFMAs
-    // run.  The products alternate between two register sets; operands rotate over
-    // D + 1 slots and token scales over D + 2, as step rb reads block rb + D's while
-    // block rb - 1's is in use.
-    constexpr int D = kF8LdsAhead;
-    f32x4 p[2][kF8CB];
-    i32x8 av[D + 1];
-    float sa[D + 2];
-    auto rd = [&](const int rb) {
-      const unsigned char* ap = lds + buf + (rb * 16 + h * 8) * kF8Slot + rd_off;
-      const i32x4 l4 = *reinterpret_cast<const i32x4*>(ap);
-      const i32x4 h4 = *reinterpret_cast<const i32x4*>(ap + kF8Slot);
-      av[rb % (D + 1)] = i32x8{l4[0], l4[1], l4[2], l4[3], h4[0], h4[1], h4[2], h4[3]};
-      sa[rb % (D + 2)] = sbuf[rb * 16];
-    };
-    auto fm = [&](const int rb) {
-#pragma unroll
-      for (int cb = 0; cb < kF8CB; ++cb) {
-        const float sc = sa[rb % (D + 2)] * wsc[cb];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[rb][cb][i] = fmaf(p[rb & 1][cb][i], sc, acc[rb][cb][i]);
-      }
-    };
-#pragma unroll
-    for (int rb = 0; rb < D; ++rb) rd(rb);
-#pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) {
-      __builtin_amdgcn_sched_barrier(0);
-      if (rb + D < NRB) rd(rb + D);
-      f32x4* pc = p[rb & 1];
-#pragma unroll
-      for (int cb = 0; cb < kF8CB; ++cb) pc[cb] = f8_mfma(bring[r][cb], av[rb % (D + 1)]);
-      if (rb > 0) fm(rb - 1);
-      if (rb + D < NRB) __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
-#pragma unroll
-      for (int cb = 0; cb < kF8CB; ++cb) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (rb > 0) __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
-      }
-      // keep this step's MFMAs and the previous step's rescaling inside the step
-#pragma unroll
-      for (int cb = 0; cb < kF8CB; ++cb) asm volatile("" ::"v"(pc[cb]));
-      if (rb > 0) {
-        f32x4* ac = acc[rb - 1];
-#pragma unroll
-        for (int cb = 0; cb < kF8CB; ++cb) asm volatile("" : "+v"(ac[cb]));
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    fm(NRB - 1);
-    // refill this ring slot with the block kF8BAhead ahead (clamped to the last)
-    int sn = kb + kF8BAhead;
-    sn = sn < KB ? sn : KB - 1;
-#pragma unroll
-    for (int cb = 0; cb < kF8CB; ++cb)
-      bring[r][cb] = f8_load32(B + (cb >> 1) * group_stride + (sn * 2 + (cb & 1)) * 2048);
-    // issue the refill here, not after the chunk's staging writes (which wait for the
-    // staging loads)
-    __builtin_amdgcn_sched_barrier(0);
-  };
-
-  // Chunk c (parity u = c % 2 when unrolled) computes from LDS buffer c % 2; at its
-  // end chunk c + 1 leaves its staging set for the other buffer, and that set starts
-  // loading chunk c + 1 + kF8StageSets (clamped past the end; never consumed there).
-  auto chunk = [&](const int c, const int u) {
-    const int buf = u * kF8Buf;
-    block(c, 0, (2 * u) % kF8BAhead, buf);
-    block(c, 1, (2 * u + 1) % kF8BAhead, buf);
-    const int set = (u + 1) % kF8StageSets;
-    write_stage(set, kF8Buf - buf);
-    __syncthreads();
-    load_stage(set, c + 1 + kF8StageSets);
-  };
-  for (int c = 0; c < NC; c += kF8Unroll) {
-    if (kF8Unroll == 1) {
-      chunk(c, c & 1);
-    } else {
-      chunk(c, 0);
-      if (c + 1 < NC) chunk(c + 1, 1);
-    }
-  }
-
+// Item epilogue: h (gate/up; quantised to e4m3 when the layer asks for it) or O (down)
+// of the item's rows from the accumulators of its NRB 16-row blocks.
+template <bool SWIGLU, int NRB>
+__device__ __forceinline__ void f8_epilogue(const GroupedGemm& g, const Item& it, int w, int lane,
+                                            const f32x4 (&acc)[NRB][kF8CB], float (*qamax)[kF8Rows]) {
+  const int groups = it.shared ? g.groups_shared : g.groups_routed;
+  const bool active = it.group + w * kF8GroupsPerWave < groups;  // wave-uniform
+  const int group0 = active ? it.group + w * kF8GroupsPerWave : groups - kF8GroupsPerWave;
+  const int tok = lane & 15;
+  const int n0 = (lane >> 4) * 4;
   float* qscale = it.shared ? g.outs_shared : g.outs_routed;
   if (SWIGLU && qscale) {
     // h quantised in place of the separate pass: the tile's 8 groups are exactly one
     // 128-channel quantisation group of each of its tokens (gate/up column tiles are
-    // whole, as 2M/32 is a multiple of 8).  Per token: amax over the 4 lanes of
-    // each wave holding it, then over the 4 waves through LDS; scale = amax / 448
-    // (1 for an all-zero group); codes = e4m3(v * (1 / scale)) with the reciprocal
-    // rounded once per token group, one rounding more than the quantisation kernel's
-    // e4m3(v / scale), and SiLU through the hardware reciprocal: h is internal to
-    // the layer, and its codes may differ from the streaming path's by one step.
-    const int tok = lane & 15;
-    const int n0 = (lane >> 4) * 4;
+    // whole, as 2M/32 is a multiple of 8).  Per token: amax over the 4 lanes of each
+    // wave holding it, then over the 8 waves through LDS; scale = amax / 448 (1 for an
+    // all-zero group); codes = e4m3(v * (1 / scale)) with the reciprocal rounded once
+    // per token group, one rounding more than the quantisation kernel's e4m3(v /
+    // scale), and SiLU through the hardware reciprocal: h is internal to the layer, and
+    // its codes may differ from the streaming path's by one step.
     f32x4 hv[NRB][kF8GroupsPerWave];
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
@@ -378,19 +258,17 @@ __device__ __forceinline__ void fp8_tile(const GroupedGemm& g, const Item& it, c
         if (w == 0 && lane < 16) qscale[row * qgroups + it.group / 8] = sc;
       }
     }
+    // the next item's first writes to qamax follow its first chunk's barrier
   } else if (active) {
-    const int tok = lane & 15;
-    const int n0 = (lane >> 4) * 4;
-    float* out = static_cast<float*>(it.shared ? g.out_shared : g.out_routed);
     const int ldo = it.shared ? g.ldo_shared : g.ldo_routed;
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
       const int t = rb * 16 + tok;
       if (t >= it.nrows) continue;
-      float* o = out + (size_t)(it.row0 + t) * ldo;
 #pragma unroll
       for (int j = 0; j < kF8GroupsPerWave; ++j) {
         if (SWIGLU) {
+          float* o = static_cast<float*>(it.shared ? g.out_shared : g.out_routed) + (size_t)(it.row0 + t) * ldo;
           f32x4 v;
 #pragma unroll
           for (int i = 0; i < 4; ++i) v[i] = silu(acc[rb][2 * j][i]) * acc[rb][2 * j + 1][i];
@@ -477,7 +355,11 @@ __device__ __forceinline__ void f8_xcd_range(const GroupedGemm& g, const SegTabl
   end = xcd == kF8Xcds - 1 ? t.prefix[S] : item_at(total_cost * (xcd + 1) / kF8Xcds);
 }
 
-template <bool SWIGLU>
+// The workgroup's items, in runs of equal 16-row block counts (see the item loop).
+// CHAIN (down projection with reductions above 256: at least two chunks per item)
+// chains the items of a run; without it every item loads its own first chunk and
+// weight blocks.
+template <bool SWIGLU, bool CHAIN>
 __global__ void __launch_bounds__(kF8Threads, kF8MinBlocks) gemm_fp8_tiled_kernel(GroupedGemm g) {
   __shared__ SegTable prefix;
   __shared__ int scan_tmp[kF8Waves + 1];
@@ -495,29 +377,230 @@ __global__ void __launch_bounds__(kF8Threads, kF8MinBlocks) gemm_fp8_tiled_kerne
   const int slots = gridDim.x / kF8Xcds;
   int begin, end;
   f8_xcd_range(g, prefix, costp, scan_tmp, xcd, begin, end);
+  int item = begin + slot;
+  if (item >= end) return;  // workgroup-uniform
 
-  for (int item = begin + slot; item < end; item += slots) {
-    const Item it = decode_item_tiled(g, kF8Rows, kF8Groups, prefix, item);
-    // the item's computation is specialised on its count of 16-row blocks, so the
-    // padding of a partly filled tile costs neither matrix-core nor rescaling work
-    const int nb = f8_item_blocks(it.nrows);  // wave-uniform
-    if (nb == 8)
-      fp8_tile<SWIGLU, 8>(g, it, w, lds, qamax);
-    else if (nb == 7)
-      fp8_tile<SWIGLU, 7>(g, it, w, lds, qamax);
-    else if (nb == 6)
-      fp8_tile<SWIGLU, 6>(g, it, w, lds, qamax);
-    else if (nb == 5)
-      fp8_tile<SWIGLU, 5>(g, it, w, lds, qamax);
-    else if (nb == 4)
-      fp8_tile<SWIGLU, 4>(g, it, w, lds, qamax);
-    else
-      fp8_tile<SWIGLU, 2>(g, it, w, lds, qamax);
-    // every LDS read of this item happened before its last chunk's barrier
+  const int lane = lane_id();
+  const int piece = lane & 15;
+  // LDS: write slot of staging load i (token block w, slot = piece, row in block
+  // (i % 4) * 4 + lane / 16)
+  const int wr_off = ((w * (kF8StageRows / 16)) * 16 + piece) * kF8Slot + (lane >> 4) * 16;
+  // read: slot (lane / 16) * 2 (+1 for the upper 16 bytes) of the scale block's 8
+  const int rd_off = ((lane >> 4) * 2) * kF8Slot + (lane & 15) * 16;
+  // Scales staged with the activations (one per lane per chunk): lane l < 32 stages
+  // the value of block l / 16 of the chunk for the wave's row l % 16; lane 32 + u
+  // stages, for block u / 16 of the chunk, the scale of wave (u % 16) / kF8CB's
+  // 16-column block u % kF8CB (wave 0 writes them, the other waves' copies go to the
+  // dummy word).  Loads and LDS writes of the staging are branch-free: a load under a
+  // divergent branch whose value is used a chunk later makes the compiler wait, at
+  // the use, for every load in flight, the weight ring's included.
+  const bool sc_tok = lane < 2 * kF8StageRows;
+  const int sc_blk = sc_tok ? lane / kF8StageRows : (lane - 2 * kF8StageRows) / (kF8WScales / 2);
+  const int sc_off = sc_tok ? kF8A + (sc_blk * kF8Rows + w * kF8StageRows + (lane % kF8StageRows)) * 4
+                            : (w == 0 ? kF8A + (2 * kF8Rows + lane - 2 * kF8StageRows) * 4 : kF8Dummy);
+
+  // The staging registers hold a chunk between its loads and its LDS write.  Rows of
+  // token blocks past an item's row count are loaded (reading its first row) and
+  // written like the others, and never read.  sstage holds the lane's loaded scale and
+  // slive whether its block is inside K (a block past the end of K, odd K / 128, gets
+  // weight scale 0): the zeroing is applied when the value is written to LDS, so that
+  // no instruction needs the loaded value before the write.
+  bf16x8 stage[kF8Loads];
+  float sstage;
+  bool slive;
+  // chunk c of source s's item (clamped to its last chunk; never consumed past it)
+  auto load_stage = [&](const F8Src& s, int c) __attribute__((always_inline)) {
+    const int nc = (s.KB + 1) / 2;
+    c = c < nc ? c : nc - 1;
+    // this lane's piece of the chunk (past the end of K: the block before, which gets
+    // weight scale 0)
+    const unsigned o = c * 256 + piece * 16 < s.K ? piece * 16 : piece * 16 - 128;
+    const uint8_t* ab = s.abase + c * 256;
+#pragma unroll
+    for (int i = 0; i < kF8Loads; ++i) stage[i] = *reinterpret_cast<gbf16x8*>((gu8*)ab + (s.aoff[i] + o));
+    const int kb = 2 * c + sc_blk;
+    const int kbc = kb < s.KB ? kb : s.KB - 1;
+    sstage = ((gf32*)s.sp)[(unsigned)__umul24(kbc, s.sstep)];
+    slive = sc_tok || kb < s.KB;
+  };
+  auto write_stage = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < kF8Loads; ++i)
+      *reinterpret_cast<bf16x8*>(lds + buf + wr_off + (i >> 2) * 16 * kF8Slot + (i & 3) * 64) = stage[i];
+    *reinterpret_cast<float*>(lds + buf + sc_off) = slive ? sstage : 0.f;
+  };
+  // weight ring: slot r holds block b of source s's item (clamped to its last block)
+  i32x8 bring[kF8BAhead][kF8CB];
+  auto load_ring = [&](const int r, const F8Src& s, int b) __attribute__((always_inline)) {
+    b = b < s.KB ? b : s.KB - 1;
+#pragma unroll
+    for (int cb = 0; cb < kF8CB; ++cb)
+      bring[r][cb] = f8_load32g((gu8*)s.Bu + ((cb >> 1) * s.gs + (b * 2 + (cb & 1)) * 2048) + (unsigned)(lane * 16));
+  };
+
+  // One 128-deep scale block of NRB 16-row blocks: h is the block within the chunk, r
+  // its weight-ring slot, buf its LDS buffer.
+  auto block = [&](auto nrb, auto& acc, const int h, const int r, const int buf) __attribute__((always_inline)) {
+    constexpr int NRB = decltype(nrb)::value;
+    const float* swl = reinterpret_cast<const float*>(lds + buf + kF8A) + 2 * kF8Rows + h * (kF8WScales / 2) + w * kF8CB;
+    float wsc[kF8CB];
+#pragma unroll
+    for (int cb = 0; cb < kF8CB; ++cb) wsc[cb] = swl[cb];
+    const float* sbuf = reinterpret_cast<const float*>(lds + buf + kF8A) + h * kF8Rows + (lane & 15);
+    // Software pipeline over token blocks: block rb + D's operand is read from LDS
+    // (D = kF8LdsAhead) and block rb - 1's products are rescaled while block rb's MFMAs
+    // run.  The products alternate between two register sets; operands rotate over
+    // D + 1 slots and token scales over D + 2, as step rb reads block rb + D's while
+    // block rb - 1's is in use.
+    constexpr int D = kF8LdsAhead;
+    f32x4 p[2][kF8CB];
+    i32x8 av[D + 1];
+    float sa[D + 2];
+    auto rd = [&](const int rb) __attribute__((always_inline)) {
+      const unsigned char* ap = lds + buf + (rb * 16 + h * 8) * kF8Slot + rd_off;
+      const i32x4 l4 = *reinterpret_cast<const i32x4*>(ap);
+      const i32x4 h4 = *reinterpret_cast<const i32x4*>(ap + kF8Slot);
+      av[rb % (D + 1)] = i32x8{l4[0], l4[1], l4[2], l4[3], h4[0], h4[1], h4[2], h4[3]};
+      sa[rb % (D + 2)] = sbuf[rb * 16];
+    };
+    auto fm = [&](const int rb) __attribute__((always_inline)) {
+#pragma unroll
+      for (int cb = 0; cb < kF8CB; ++cb) {
+        const float sc = sa[rb % (D + 2)] * wsc[cb];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[rb][cb][i] = fmaf(p[rb & 1][cb][i], sc, acc[rb][cb][i]);
+      }
+    };
+#pragma unroll
+    for (int rb = 0; rb < D; ++rb) rd(rb);
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (rb + D < NRB) rd(rb + D);
+      f32x4* pc = p[rb & 1];
+#pragma unroll
+      for (int cb = 0; cb < kF8CB; ++cb) pc[cb] = f8_mfma(bring[r][cb], av[rb % (D + 1)]);
+      if (rb > 0) fm(rb - 1);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (rb + D < NRB) __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+      if (rb > 0) __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (rb > 0) __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+      // keep this step's MFMAs and the previous step's rescaling inside the step
+#pragma unroll
+      for (int cb = 0; cb < kF8CB; ++cb) asm volatile("" ::"v"(pc[cb]));
+      if (rb > 0) {
+        f32x4* ac = acc[rb - 1];
+#pragma unroll
+        for (int cb = 0; cb < kF8CB; ++cb) asm volatile("" : "+v"(ac[cb]));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    fm(NRB - 1);
+  };
+  Item it = decode_item_tiled(g, kF8Rows, kF8Groups, prefix, item);
+  // A run: consecutive items of this workgroup with the same count of 16-row blocks
+  // NRB (8, 7, 6, 5, 4 or 2; f8_item_blocks), computed by one body specialised on NRB,
+  // so a partly filled tile does no matrix-core or rescale work for its padding.  Inside
+  // a run the items are chained (CHAIN): the last chunk of an item loads, in place of
+  // the clamped loads past its end, the next item's first chunk (written to LDS at that
+  // chunk's end, so the next item starts on it), its second chunk (into the staging
+  // registers) and its first two weight blocks (into the ring); the next item's
+  // sorted_pair lookups are issued when an item starts and used at the end of its first
+  // chunk.  The chained state never crosses the dispatch on NRB: a run's last item
+  // loads its own data again in those places (dead loads, issued unconditionally), and
+  // the next run starts by loading its first item's.  Without CHAIN a run is one item.
+  auto run = [&](auto nrb) __attribute__((always_inline)) {
+    constexpr int NRB = decltype(nrb)::value;
+    int lk[kF8Loads + 1];
+    F8Src ss;  // what the staging loads read: this item's, from its chunk NC - 2's end the next item's
+    F8Src rs;  // what the weight ring loads: this item's, from its chunk NC - 1 the next item's
+    F8Src nx;  // the next item's (the item's own again when the run ends with it)
+    int par = 0;  // LDS buffer of the item's first chunk
+    // the run's first item: its first chunk to LDS buffer 0, its second to the staging
+    // registers, its first two weight blocks to the ring.  The first chunk's loads go out
+    // before the ring's, so that the wait for them before their LDS write does not
+    // include the ring's loads.
+    f8_lookup(g, it, w, lane, lk);
+    f8_source<SWIGLU>(g, it, w, lane, lk, ss);
+    rs = ss;
+    load_stage(ss, 0);
+#pragma unroll
+    for (int u = 0; u < kF8BAhead; ++u) load_ring(u, rs, u);
+    write_stage(0);
+    load_stage(ss, 1);
+    __syncthreads();
+    for (;;) {
+      const int nitem = item + slots;
+      const bool has_next = nitem < end;  // workgroup-uniform
+      const Item nd = has_next ? decode_item_tiled(g, kF8Rows, kF8Groups, prefix, nitem) : it;
+      const bool chain = CHAIN && has_next && f8_item_blocks(nd.nrows) == NRB;  // workgroup-uniform
+      // field by field: a whole-struct copy moves its padding through scratch memory
+      Item nit;
+      nit.seg = chain ? nd.seg : it.seg;
+      nit.shared = chain ? nd.shared : it.shared;
+      nit.group = chain ? nd.group : it.group;
+      nit.row0 = chain ? nd.row0 : it.row0;
+      nit.nrows = chain ? nd.nrows : it.nrows;
+      if (CHAIN) f8_lookup(g, nit, w, lane, lk);
+      const int KB = (it.shared ? g.K_shared : g.K_routed) / 128;
+      const int NC = (KB + 1) / 2;  // 256-deep chunks; an odd KB leaves the last chunk half live
+      f32x4 acc[NRB][kF8CB];
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < kF8CB; ++cb) acc[rb][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      // Chunk c computes from LDS buffer (c + par) % 2; at its end chunk c + 1 leaves the
+      // staging registers for the other buffer, and they start loading chunk c + 2.
+      // Chunk 0 runs outside the loop, so that the wait for the next item's lookups, at
+      // its end, is on every path (else the compiler drains all loads where it reuses
+      // their registers).
+      auto chunk = [&](const int c) __attribute__((always_inline)) {
+        const int buf = ((c + par) & 1) * kF8Buf;
+        const bool ring_next = CHAIN && c == NC - 1;  // this chunk refills the ring with the next item's blocks
+        if (ring_next) rs = nx;
+        const int rbase = ring_next ? 2 * NC : 0;
+        block(nrb, acc, 0, 0, buf);
+        load_ring(0, rs, 2 * c + 2 - rbase);
+        // issue the refill here, not after the next block's LDS traffic
+        __builtin_amdgcn_sched_barrier(0);
+        block(nrb, acc, 1, 1, buf);
+        load_ring(1, rs, 2 * c + 3 - rbase);
+        __builtin_amdgcn_sched_barrier(0);
+        write_stage(kF8Buf - buf);
+        __syncthreads();
+        if (CHAIN && c == 0) f8_source<SWIGLU>(g, nit, w, lane, lk, nx);
+        if (CHAIN && c == NC - 2) ss = nx;
+        load_stage(ss, CHAIN && c >= NC - 2 ? c + 2 - NC : c + 2);
+      };
+      chunk(0);
+      for (int c = 1; c < NC; ++c) chunk(c);
+      f8_epilogue<SWIGLU, NRB>(g, it, w, lane, acc, qamax);
+      par = (par + NC) & 1;
+      it.seg = nd.seg;
+      it.shared = nd.shared;
+      it.group = nd.group;
+      it.row0 = nd.row0;
+      it.nrows = nd.nrows;
+      item = nitem;
+      if (!chain) break;
+    }
+  };
+  // Each case of the dispatch ends in a distinct empty asm statement: the compiler would
+  // otherwise merge the cases' common tails.
+  while (item < end) {  // workgroup-uniform
+    switch (f8_item_blocks(it.nrows)) {
+      case 8: run(F8Blocks<8>{}); asm volatile("; 8 blocks"); break;
+      case 7: run(F8Blocks<7>{}); asm volatile("; 7 blocks"); break;
+      case 6: run(F8Blocks<6>{}); asm volatile("; 6 blocks"); break;
+      case 5: run(F8Blocks<5>{}); asm volatile("; 5 blocks"); break;
+      case 4: run(F8Blocks<4>{}); asm volatile("; 4 blocks"); break;
+      default: run(F8Blocks<2>{}); asm volatile("; 2 blocks"); break;
+    }
   }
 }
 
-template <bool SWIGLU>
+template <bool SWIGLU, bool CHAIN>
 static hipError_t launch_fp8_tiled(const GroupedGemm& g, long long max_items, int max_blocks, hipStream_t st) {
   const size_t smem = 2 * kF8Buf;  // above the default limit: see configure_gemm_fp8_tiled
   // max_blocks counts compute units; the kernel is built for kF8MinBlocks workgroups
@@ -525,7 +608,7 @@ static hipError_t launch_fp8_tiled(const GroupedGemm& g, long long max_items, in
   const long long resident = (long long)max_blocks * kF8MinBlocks;
   long long blocks = max_items < resident ? max_items : resident;
   blocks = blocks < kF8Xcds ? kF8Xcds : blocks / kF8Xcds * kF8Xcds;
-  gemm_fp8_tiled_kernel<SWIGLU><<<(unsigned)blocks, kF8Threads, smem, st>>>(g);
+  gemm_fp8_tiled_kernel<SWIGLU, CHAIN><<<(unsigned)blocks, kF8Threads, smem, st>>>(g);
   return hipGetLastError();
 }
 
@@ -534,16 +617,18 @@ static hipError_t launch_fp8_tiled(const GroupedGemm& g, long long max_items, in
 // Raise the kernels' dynamic LDS limit on the current device (handle creation).
 hipError_t configure_gemm_fp8_tiled() {
   const int smem = 2 * kF8Buf;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_fp8_tiled_kernel<true>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, smem);
-  if (e == hipSuccess)
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_fp8_tiled_kernel<false>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, smem);
-  return e;
+  const void* fns[3] = {reinterpret_cast<const void*>(gemm_fp8_tiled_kernel<true, false>),
+                        reinterpret_cast<const void*>(gemm_fp8_tiled_kernel<false, true>),
+                        reinterpret_cast<const void*>(gemm_fp8_tiled_kernel<false, false>)};
+  for (const void* f : fns) {
+    const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, smem);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
-hipError_t launch_gemm_fp8_tiled(const GroupedGemm& g, bool swiglu, long long max_items, int max_blocks,
-                                 hipStream_t st) {
+hipError_t launch_gemm_fp8_tiled(const GroupedGemm& g, bool swiglu, long long a_rows, long long max_items,
+                                 int max_blocks, hipStream_t st) {
   if (max_items <= 0) return hipSuccess;
   // item costs (at most 8 + kF8ItemFixedCost each) are summed in 32-bit ints
   if (max_items > 0x7fffffff / (kF8RowBlocks + kF8ItemFixedCost)) return hipErrorInvalidValue;
@@ -554,7 +639,14 @@ hipError_t launch_gemm_fp8_tiled(const GroupedGemm& g, bool swiglu, long long ma
   if (swiglu && g.outs_routed &&
       (g.groups_routed % kF8Groups || (g.shared_rows > 0 && g.groups_shared % kF8Groups)))
     return hipErrorInvalidValue;
-  return swiglu ? launch_fp8_tiled<true>(g, max_items, max_blocks, st) : launch_fp8_tiled<false>(g, max_items, max_blocks, st);
+  // activation rows are addressed by 32-bit byte offsets from the matrix's base
+  if (a_rows < 0 || a_rows * g.lda_routed >= (1ll << 32) || (long long)g.shared_rows * g.lda_shared >= (1ll << 32))
+    return hipErrorInvalidValue;
+  if (swiglu) return launch_fp8_tiled<true, false>(g, max_items, max_blocks, st);
+  // chained items need two chunks (K > 256) in every item
+  const bool chain = g.K_routed > 256 && (g.shared_rows == 0 || g.K_shared > 256);
+  return chain ? launch_fp8_tiled<false, true>(g, max_items, max_blocks, st)
+               : launch_fp8_tiled<false, false>(g, max_items, max_blocks, st);
 }
 
 int fp8_tiled_rows() { return kF8Rows; }
