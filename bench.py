@@ -151,7 +151,7 @@ KERNEL_SOURCES = {
     "gemm_bf16_stream_kernel<true>": ("gemm_bf16.hip", "grouped.h", "afd_device.h", "afd_internal.h"),
     "gemm_bf16_tiled_kernel<true>": ("gemm_bf16_tiled.hip", "grouped.h", "afd_device.h", "afd_internal.h"),
     "gemm_fp8_stream_kernel<true>": ("gemm_fp8.hip", "grouped.h", "afd_device.h", "afd_internal.h"),
-    "gemm_fp8_tiled_kernel<true>": ("gemm_fp8_tiled.hip", "grouped.h", "afd_device.h", "afd_internal.h"),
+    "gemm_fp8_tiled_kernel<true, false>": ("gemm_fp8_tiled.hip", "grouped.h", "afd_device.h", "afd_internal.h"),
     "gemm_f32_kernel<true>": ("gemm_f32.hip", "grouped.h", "afd_device.h", "afd_internal.h"),
 }
 
@@ -162,6 +162,8 @@ def gate_up_kernel(w, gemm="auto"):
     if w.dtype == "f32":
         return "gemm_f32_kernel<true>"
     tiled = gemm == "tiled" or (gemm == "auto" and w.T * w.k > (12 if w.dtype == "fp8" else 8) * w.E)
+    if w.dtype == "fp8" and tiled:
+        return "gemm_fp8_tiled_kernel<true, false>"  # <SWIGLU, CHAIN>: gate/up items are not chained
     return f"gemm_{w.dtype}_{'tiled' if tiled else 'stream'}_kernel<true>"
 
 

@@ -54,6 +54,10 @@ def _cfg(**kw):
     (dict(max_tokens=0), _ffi.AFD_EINVAL),
     (dict(max_tokens=1 << 28, top_k=8), _ffi.AFD_EINVAL),
     (dict(dtype=7), _ffi.AFD_EINVAL),
+    # fp8 layers: each activation matrix of max_tokens rows must stay under 4 GiB (x, routed h, shared h)
+    (dict(dtype=_ffi.AFD_FP8_E4M3, hidden=65536, inter=128, max_tokens=65536), _ffi.AFD_EINVAL),
+    (dict(dtype=_ffi.AFD_FP8_E4M3, inter=256, top_k=8, max_tokens=1 << 21), _ffi.AFD_EINVAL),
+    (dict(dtype=_ffi.AFD_FP8_E4M3, shared_inter=4096, max_tokens=1 << 20), _ffi.AFD_EINVAL),
 ])
 def test_create_rejects_bad_config(kw, code):
     lib = _ffi.load()
@@ -62,6 +66,21 @@ def test_create_rejects_bad_config(kw, code):
     assert rc == code
     assert h.value is None
     assert _ffi.afd_ffn_last_error() != ""
+
+
+@pytest.mark.parametrize("kw", [
+    dict(hidden=65536, inter=128, max_tokens=65536),
+    dict(inter=256, top_k=8, max_tokens=1 << 21),
+    dict(shared_inter=4096, max_tokens=1 << 20),
+])
+def test_create_names_the_fp8_activation_limit(kw):
+    # the fp8 128-row GEMMs address activation rows by 32-bit byte offsets
+    lib = _ffi.load()
+    h = ctypes.c_void_p()
+    rc = lib.afd_ffn_create(ctypes.byref(_cfg(dtype=_ffi.AFD_FP8_E4M3, **kw)), 1, 1, None, None, None, None, None,
+                            None, None, ctypes.byref(h))
+    assert rc == _ffi.AFD_EINVAL and h.value is None
+    assert "4 GiB" in _ffi.afd_ffn_last_error()
 
 
 def test_create_rejects_bad_pointers():

@@ -337,6 +337,10 @@ def test_small_shapes(w, kernel):
     small("fp8_shared", dtype="fp8", T=50, H=384, M=256, E=6, k=2, Ms=256),
     small("fp8_one_token", dtype="fp8", T=1, H=128, M=128, E=8, k=2, Ms=128),
     small("fp8_skewed_long_k", dtype="fp8", T=90, H=1024, M=512, E=3, k=2),
+    # more down items (64 experts x 8 column tiles + the shared expert's) than resident
+    # workgroups, row counts of 2 and 4 blocks: the tiled down GEMM chains items within
+    # runs of equal block count and restarts between runs
+    small("fp8_chained_runs", dtype="fp8", T=256, H=2048, M=384, E=64, k=8, Ms=384),
 ], ids=lambda w: w.name)
 @pytest.mark.parametrize("kernel", ["stream", "tiled"])
 def test_fp8_shapes(w, kernel):
