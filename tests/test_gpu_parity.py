@@ -341,6 +341,9 @@ def test_small_shapes(w, kernel):
     # workgroups, row counts of 2 and 4 blocks: the tiled down GEMM chains items within
     # runs of equal block count and restarts between runs
     small("fp8_chained_runs", dtype="fp8", T=256, H=2048, M=384, E=64, k=8, Ms=384),
+    # the same with a shared expert of another width: a chained routed item hands over to a
+    # shared one with another reduction length (chunk count) and back
+    small("fp8_chained_runs_unequal_k", dtype="fp8", T=256, H=2048, M=384, E=64, k=8, Ms=640),
 ], ids=lambda w: w.name)
 @pytest.mark.parametrize("kernel", ["stream", "tiled"])
 def test_fp8_shapes(w, kernel):
