@@ -1,6 +1,6 @@
 """Parity on seeded random layer shapes within the documented limits: dtype, H, M, E,
 k, T, the shared expert and the GEMM kernel all drawn from a fixed seed (the same 24
-cases on every run).  Bars as in the other parity tests: ids, counts and the
+cases on every run), and 6 larger fp8 cases on the tiled GEMMs whose down items chain.  Bars as in the other parity tests: ids, counts and the
 permutation bit-exact; gates within 2e-6; outputs within 1e-4 / 2e-2 / 6e-2 of
 max|ref| (fp32 / bf16 / fp8)."""
 import numpy as np
@@ -34,6 +34,27 @@ def _cases(n=24, seed=2026):
     return out
 
 
+def _chain_cases(n=6, seed=2027):
+    """fp8 layers on the 128-row tiled GEMMs with more down items than resident
+    workgroups (E >= 40 row tiles x 6-8 column tiles of 256), reductions above 256 and
+    mixed row counts per expert: the down GEMM chains items within runs of equal 16-row
+    block count and restarts between runs, also across the hand-over to a shared expert
+    of another width."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        H = 256 * int(rng.integers(6, 9))
+        M = 128 * int(rng.integers(3, 6))
+        E = int(rng.integers(40, 129))
+        k = int(rng.integers(2, 9))
+        T = int(rng.integers(64, 301))
+        Ms = 128 * [0, 3, 5][int(rng.integers(0, 3))]
+        w = workloads.Workload(f"chain{i}_fp8_T{T}_H{H}_M{M}_E{E}_k{k}_Ms{Ms}", 600 + i,
+                               T=T, H=H, M=M, E=E, k=k, Ms=Ms, dtype="fp8")
+        out.append((w, "tiled"))
+    return out
+
+
 @pytest.fixture(scope="module", autouse=True)
 def _gpu():
     if not torch.cuda.is_available():
@@ -41,7 +62,7 @@ def _gpu():
     torch.cuda.set_device(0)
 
 
-@pytest.mark.parametrize("w,kernel", _cases(), ids=lambda v: v.name if hasattr(v, "name") else v)
+@pytest.mark.parametrize("w,kernel", _cases() + _chain_cases(), ids=lambda v: v.name if hasattr(v, "name") else v)
 def test_random_shape(w, kernel):
     print(f"case {w.name} gemm={kernel}", flush=True)
     weights = workloads.make_weights(w, device="cuda")
