@@ -64,3 +64,21 @@ def test_fp8_gate_up_launch_bytes_count_codes_and_scales():
             + (P * M + T * Ms) + (P * 16 + T * 16) * 4)
     assert bench.gate_up_bytes(w, counts) == want
     assert abs(want / 7.70e9 - 1) < 0.01
+
+
+def test_gate_up_kernel_names_match_the_kernels_the_library_defines():
+    """The names bench.py matches against rocprofv3's kernel names (for the committed
+    traffic counters) are instances of kernels defined in the listed sources, with one
+    template argument per template parameter: a renamed or re-templated kernel would
+    leave the counters unmatched."""
+    import os
+    import re
+    csrc = os.path.join(os.path.dirname(bench.__file__), "moe_expert_ffn_softmax_amd", "csrc")
+    for name, files in bench.KERNEL_SOURCES.items():
+        base, args = re.fullmatch(r"(\w+)<(.*)>", name).groups()
+        src = open(os.path.join(csrc, files[0])).read()
+        m = re.search(r"template <([^>]*)>\s*__global__ void (?:__launch_bounds__\([^)]*\) )?" + base + r"\(", src)
+        assert m, name
+        assert len(args.split(",")) == len(m.group(1).split(",")), name
+    seen = {bench.gate_up_kernel(w) for w in workloads.ORDERED + workloads.CONTEXT}
+    assert seen <= set(bench.KERNEL_SOURCES)
